@@ -1,0 +1,442 @@
+"""Pins of the fp64 oracle against what the source pages and mathematics fix.
+
+None of these re-types the oracle's formulas: each checks the oracle against a
+library routine, a closed form, an invariant the pages state, exact
+enumeration of the output law, a Monte-Carlo law test, brute force on tiny
+trees, or the expected-tokens values printed on the speculative-decoding page.
+"""
+import itertools
+import json
+import math
+import multiprocessing as mp
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+
+from oracle import (InvalidRow, chain_verify_one, inverse_cdf, softmax_T, tree_greedy_one,
+                    tree_path_one)
+
+GRID = 2 ** 24          # the library's uniforms are fp32 multiples of 2^-24
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+def sm(z, T):
+    """Library softmax of z / T (scipy), the independent route to a distribution."""
+    return scipy.special.softmax(np.asarray(z, dtype=np.float64) / f32(T))
+
+
+# ---------------------------------------------------------------------------
+# softmax and inverse CDF against library routines
+# ---------------------------------------------------------------------------
+
+
+def test_softmax_matches_scipy():
+    rng = np.random.default_rng(1)
+    for V in (1, 2, 7, 1000, 4099):
+        for T in (1.0, 0.7, 1.9):
+            z = rng.normal(0.0, 3.0, V)
+            if V > 3:
+                z[rng.integers(0, V, 2)] = -np.inf
+            got = softmax_T(z, f32(T))
+            np.testing.assert_allclose(got, sm(z, T), rtol=1e-13, atol=0)
+            lse = scipy.special.logsumexp(z / f32(T))
+            fin = np.isfinite(z)
+            np.testing.assert_allclose(np.log(got[fin]), z[fin] / f32(T) - lse, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("row", [[np.nan, 0.0], [np.inf, 0.0], [-np.inf, -np.inf]])
+def test_softmax_rejects_undefined_rows(row):
+    with pytest.raises(InvalidRow):
+        softmax_T(np.array(row), 1.0)
+
+
+def test_inverse_cdf_matches_searchsorted():
+    rng = np.random.default_rng(2)
+    for _ in range(300):
+        V = int(rng.integers(1, 60))
+        w = rng.random(V)
+        w[rng.random(V) < 0.3] = 0.0
+        if w.sum() == 0.0:
+            w[-1] = 0.5
+        c = np.cumsum(w)
+        us = np.concatenate([[0.0], rng.random(20, dtype=np.float32).astype(np.float64),
+                             [1.0 - 2.0 ** -24]])
+        for u in us:
+            tok, lo, hi = inverse_cdf(w, u)
+            ref = int(np.searchsorted(c, u * c[-1], side="right"))
+            if abs(u * c[-1] - c[min(ref, V - 1)]) > 1e-12 * c[-1]:
+                assert tok == ref
+            assert w[tok] > 0.0                 # zero-weight tokens are never drawn
+            assert lo <= u < hi or (tok == np.nonzero(w)[0][-1] and u >= lo)
+
+
+def test_inverse_cdf_zero_uniform_takes_first_positive():
+    w = np.array([0.0, 0.0, 0.2, 0.0, 0.8])
+    assert inverse_cdf(w, 0.0)[0] == 2
+    assert inverse_cdf(w, 0.2 - 1e-12)[0] == 2
+    assert inverse_cdf(w, 0.2)[0] == 4
+
+
+# ---------------------------------------------------------------------------
+# invariants stated for the method
+# ---------------------------------------------------------------------------
+
+
+def _rows(rng, k, V, sig_q=1.0):
+    zt = rng.normal(0.0, 2.0, (k + 1, V))
+    zq = zt[:k] + rng.normal(0.0, sig_q, (k, V))
+    return zt, zq
+
+
+def test_lambda_one_accepts_every_draft():
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        k, V = int(rng.integers(1, 6)), int(rng.integers(2, 40))
+        zt, zq = _rows(rng, k, V)
+        x = rng.integers(0, V, k)
+        r = chain_verify_one(zt, zq, x, rng.random(k), rng.random(), 1.0, 1.0)
+        assert r.accepted == k and r.bonus
+        assert np.all(r.a == 1.0)
+        assert r.tokens[:k] == [int(v) for v in x]
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.3, 0.7, 1.0])
+def test_identical_target_and_draft_accept_every_draft(lam):
+    rng = np.random.default_rng(4)
+    for _ in range(50):
+        k, V = int(rng.integers(1, 6)), int(rng.integers(2, 40))
+        z = rng.normal(0.0, 2.0, (k + 1, V))
+        x = rng.integers(0, V, k)
+        u = rng.random(k, dtype=np.float32)
+        r = chain_verify_one(z, z[:k], x, u, rng.random(), lam, 0.8)
+        assert r.accepted == k
+
+
+def test_acceptance_rate_closed_form():
+    """E_{x~q}[a(x)] = sum_v min(p~, q) = 1 - (1 - lam) * TV(p_t, q)."""
+    rng = np.random.default_rng(5)
+    for _ in range(40):
+        V = int(rng.integers(2, 30))
+        lam, T = float(rng.choice([0.0, 0.1, 0.3, 0.9])), float(rng.choice([1.0, 0.7, 1.5]))
+        zt, zq = _rows(rng, 1, V)
+        p, q = sm(zt[0], T), sm(zq[0], T)
+        ea = sum(q[x] * chain_verify_one(zt, zq, [x], [0.5], 0.5, lam, T).a[0] for x in range(V))
+        tv = 0.5 * np.abs(p - q).sum()
+        lam32 = f32(lam)
+        assert ea == pytest.approx(1.0 - (1.0 - lam32) * tv, abs=1e-12)
+        alpha = chain_verify_one(zt, zq, [0], [0.5], 0.5, lam, T).alpha[0]
+        assert alpha == pytest.approx(1.0 - (1.0 - lam32) * tv, abs=1e-12)
+
+
+def test_acceptance_probability_at_least_lambda():
+    rng = np.random.default_rng(6)
+    for _ in range(100):
+        V = int(rng.integers(2, 30))
+        lam = float(rng.random())
+        zt, zq = _rows(rng, 3, V, 3.0)
+        r = chain_verify_one(zt, zq, rng.integers(0, V, 3), [0.0] * 3, 0.5, lam, 1.0)
+        assert np.all(r.a >= f32(lam) - 1e-15) and np.all(r.a <= 1.0)
+
+
+def test_residual_law_independent_of_lambda():
+    """max(0, p~ - q) = (1 - lam) max(0, p_t - q): one law for every lam < 1."""
+    rng = np.random.default_rng(7)
+    done = 0
+    while done < 40:
+        V = int(rng.integers(3, 30))
+        zt, zq = _rows(rng, 1, V, 2.0)
+        p, q = sm(zt[0], 1.0), sm(zq[0], 1.0)
+        x = int(np.argmax(q / p))                      # p_t(x) < q(x): rejectable
+        us = rng.random()
+        out = []
+        for lam in (0.0, 0.25, 0.6):
+            a = chain_verify_one(zt, zq, [x], [0.0], us, lam, 1.0).a[0]
+            r = chain_verify_one(zt, zq, [x], [min(a + 1e-9, 1 - 2 ** -24)], us, lam, 1.0)
+            if r.accepted == 0:
+                out.append((r.tokens[0], r.F_lo, r.F_hi))
+        if len(out) == 3:
+            assert out[0][0] == out[1][0] == out[2][0]
+            assert out[0][1] == pytest.approx(out[2][1], abs=1e-12)
+            done += 1
+
+
+def test_bad_token_and_parent_raise():
+    zt, zq = np.zeros((2, 4)), np.zeros((1, 4))
+    with pytest.raises(ValueError):
+        chain_verify_one(zt, zq, [4], [0.1], 0.1, 0.0, 1.0)
+    with pytest.raises(ValueError):
+        tree_greedy_one(np.zeros((3, 4)), [0, 2], [0, 0])
+
+
+# ---------------------------------------------------------------------------
+# exact enumeration of the output law over the fp32 uniform grid
+# ---------------------------------------------------------------------------
+
+
+def _count_true(pred):
+    """#grid points m in [0, GRID) with pred(m / GRID), pred True then False."""
+    lo, hi = 0, GRID
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if pred(mid / GRID):
+            lo = mid + 1
+        else:
+            hi = mid
+    return lo
+
+
+def _enumerate(zt, zq, lam, T):
+    """Exact law of every emitted position, the oracle used as a black box.
+
+    Returns (emit[j, v] = P(position j emits v), stop[j] = P(n = j)).
+    """
+    k, V = zq.shape
+    q = [sm(zq[i], T) for i in range(k)]
+    emit = np.zeros((k + 1, V))
+    stop = np.zeros(k + 1)
+    for xs in itertools.product(range(V), repeat=k):
+        px = math.prod(q[i][xs[i]] for i in range(k))
+        if px == 0.0:
+            continue
+
+        def run(ua, us):
+            return chain_verify_one(zt, zq, list(xs), ua, us, lam, T)
+
+        reach = 1.0
+        theta_m = []
+        for i in range(k):
+            def acc(u, i=i):
+                return run([0.0] * i + [u] + [0.0] * (k - i - 1), 0.5).accepted > i
+            theta_m.append(_count_true(acc) if reach > 0.0 else 0)
+            reach *= theta_m[-1] / GRID
+        reach = 1.0
+        for j in range(k + 1):
+            pj = reach * ((GRID - theta_m[j]) / GRID if j < k else 1.0)
+            if pj > 0.0:
+                ua = [0.0] * j + ([theta_m[j] / GRID] if j < k else []) + [0.0] * max(0, k - j - 1)
+                cnt_prev = 0
+                for v in range(V):
+                    cnt = _count_true(lambda u, v=v: run(ua, u).tokens[-1] <= v)
+                    emit[j, v] += px * pj * (cnt - cnt_prev) / GRID
+                    cnt_prev = cnt
+                for i in range(j):
+                    emit[i, xs[i]] += px * pj
+                stop[j] += px * pj
+            if j < k:
+                reach *= theta_m[j] / GRID
+    return emit, stop
+
+
+@pytest.mark.parametrize("V,k,lam,T,seed", [(3, 2, 0.0, 1.0, 11), (4, 2, 0.3, 0.7, 12),
+                                              (2, 3, 0.5, 1.5, 13), (3, 3, 0.0, 1.0, 14)])
+def test_exact_enumeration_is_lossless(V, k, lam, T, seed):
+    """Each emitted position follows p~ given that it is reached; the bonus follows p_t.
+
+    [SD] "修改的拒绝采样" and [EAGLE] section 1: the output law equals the target
+    law whatever the draft; with RAPID's mixture the target law is p~.
+    """
+    rng = np.random.default_rng(seed)
+    zt, zq = _rows(rng, k, V, 1.5)
+    zt[1, 0] = -np.inf                          # a token the target rules out
+    emit, stop = _enumerate(zt, zq, lam, T)
+    lam32 = f32(lam)
+    reach = 1.0
+    tol = 1e-6                                  # uniforms live on a 2^-24 grid
+    for j in range(k):
+        p, q = sm(zt[j], T), sm(zq[j], T)
+        pm = (1.0 - lam32) * p + lam32 * q      # the mixture equation of the RAPID page
+        assert emit[j].sum() == pytest.approx(reach, abs=tol)
+        np.testing.assert_allclose(emit[j], reach * pm, atol=tol)
+        alpha = np.minimum(pm, q).sum()
+        assert stop[j] == pytest.approx(reach * (1.0 - alpha), abs=tol)
+        reach *= alpha
+    np.testing.assert_allclose(emit[k], reach * sm(zt[k], T), atol=tol)
+    assert stop.sum() == pytest.approx(1.0, abs=tol)
+
+
+# ---------------------------------------------------------------------------
+# Monte-Carlo law test, 10^6 seeded requests at V <= 8
+# ---------------------------------------------------------------------------
+
+_MC = dict(V=6, k=2, lam=0.3, T=0.8, n=1_000_000, workers=8)
+
+
+def _mc_rows():
+    rng = np.random.default_rng(2024)
+    zt = rng.normal(0.0, 1.5, (_MC["k"] + 1, _MC["V"]))
+    zq = zt[:_MC["k"]] + rng.normal(0.0, 1.0, (_MC["k"], _MC["V"]))
+    zt[1, 2] = -np.inf
+    return zt, zq
+
+
+def _mc_worker(args):
+    seed, n = args
+    V, k, lam, T = _MC["V"], _MC["k"], _MC["lam"], _MC["T"]
+    zt, zq = _mc_rows()
+    rng = np.random.default_rng(seed)
+    q = [sm(zq[i], T) for i in range(k)]
+    xs = np.stack([rng.choice(V, size=n, p=q[i]) for i in range(k)], axis=1)
+    ua = rng.random((n, k), dtype=np.float32)
+    us = rng.random(n, dtype=np.float32)
+    first = np.zeros(V, dtype=np.int64)
+    second = np.zeros(V, dtype=np.int64)
+    bonus = np.zeros(V, dtype=np.int64)
+    nh = np.zeros(k + 1, dtype=np.int64)
+    for i in range(n):
+        r = chain_verify_one(zt, zq, xs[i], ua[i], us[i], lam, T)
+        nh[r.accepted] += 1
+        first[r.tokens[0]] += 1
+        if r.accepted >= 1:
+            second[r.tokens[1]] += 1
+        if r.accepted == k:
+            bonus[r.tokens[-1]] += 1
+    return first, second, bonus, nh
+
+
+def _chisq(obs, prob):
+    obs = np.asarray(obs, dtype=np.float64)
+    exp = prob * obs.sum()
+    zero = exp == 0.0
+    assert np.all(obs[zero] == 0)
+    return scipy.stats.chisquare(obs[~zero], exp[~zero] * obs[~zero].sum() / exp[~zero].sum()).pvalue
+
+
+@pytest.mark.slow
+def test_monte_carlo_output_law():
+    """10^6 seeded requests: emitted tokens follow p~ (bonus: p_t), chi-square p > 0.01."""
+    V, k, lam, T, n, W = (_MC[s] for s in ("V", "k", "lam", "T", "n", "workers"))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(W) as pool:
+        parts = pool.map(_mc_worker, [(9000 + w, n // W) for w in range(W)])
+    first, second, bonus, nh = (sum(p[i] for p in parts) for i in range(4))
+    zt, zq = _mc_rows()
+    lam32 = f32(lam)
+    pm = [(1 - lam32) * sm(zt[j], T) + lam32 * sm(zq[j], T) for j in range(k)]
+    alpha = [np.minimum(pm[j], sm(zq[j], T)).sum() for j in range(k)]
+    law_n = np.array([1 - alpha[0], alpha[0] * (1 - alpha[1]), alpha[0] * alpha[1]])
+    assert _chisq(first, pm[0]) > 0.01
+    assert _chisq(second, pm[1]) > 0.01
+    assert _chisq(bonus, sm(zt[2], T)) > 0.01
+    assert _chisq(nh, law_n) > 0.01
+
+
+# ---------------------------------------------------------------------------
+# expected tokens per step: the values printed on the speculative-decoding page
+# ---------------------------------------------------------------------------
+
+
+def test_expected_tokens_match_printed_speedups(golden_dir):
+    """Draft q = (1, 0), target p = (r, 1 - r): every position accepts with prob r.
+
+    The expected number of emitted tokens, 1 + r + ... + r^k, must reproduce
+    the printed 2 / 3.3 / 5 at r = 0.5 / 0.7 / 0.8 (k = 64).
+    """
+    with open(os.path.join(golden_dir, "sd_expected_tokens.json")) as f:
+        gold = json.load(f)
+    k = 64
+    for case in gold["cases"]:
+        r = case["r"]
+        zq = np.tile([0.0, -np.inf], (k, 1))
+        zt = np.tile([math.log(r), math.log(1.0 - r)], (k + 1, 1))
+        theta = _count_true(lambda u: chain_verify_one(zt, zq, [0] * k, [u] + [0.99] * (k - 1),
+                                                       0.5, 0.0, 1.0).accepted > 0) / GRID
+        assert theta == pytest.approx(r, abs=2.0 ** -23)
+        expected = sum(theta ** j for j in range(k + 1))
+        assert abs(expected - case["printed"]) <= case["printed_precision"]
+        # every accepted position emits its draft; the stop emits one more token
+        for j in (0, 3, 17):
+            res = chain_verify_one(zt, zq, [0] * k, [0.0] * j + [0.999] * (k - j), 0.5, 0.0, 1.0)
+            assert res.accepted == j and len(res.tokens) == j + 1
+
+
+# ---------------------------------------------------------------------------
+# greedy tree verification against brute force
+# ---------------------------------------------------------------------------
+
+
+def _brute_greedy(zt, parent, tok):
+    N = len(parent)
+    am = [int(np.argmax(zt[r])) for r in range(N + 1)]
+    best = []
+    for v in range(1, N + 1):
+        path, u = [], v
+        while u != 0:
+            path.append(u)
+            u = int(parent[u - 1])
+        path.reverse()
+        prev, ok = 0, True
+        for u in path:
+            if int(tok[u - 1]) != am[prev]:
+                ok = False
+                break
+            prev = u
+        if ok and len(path) > len(best):
+            best = path
+    last = best[-1] if best else 0
+    return len(best), [int(tok[u - 1]) for u in best] + [am[last]], best
+
+
+def test_greedy_tree_matches_brute_force():
+    rng = np.random.default_rng(21)
+    for _ in range(600):
+        N = int(rng.integers(1, 12))
+        V = int(rng.integers(1, 5))
+        parent = np.array([int(rng.integers(0, i)) for i in range(1, N + 1)])
+        zt = rng.integers(-2, 3, (N + 1, V)).astype(np.float64)     # many ties
+        tok = rng.integers(0, V, N)
+        r = tree_greedy_one(zt, parent, tok)
+        acc, toks, nodes = _brute_greedy(zt, parent, tok)
+        assert (r.accepted, r.tokens, r.nodes) == (acc, toks, nodes)
+
+
+def test_greedy_ties_take_lowest_token():
+    zt = np.array([[1.0, 3.0, 3.0, 0.0], [0.0, 0.0, 5.0, 0.0], [9.0, 0.0, 0.0, 0.0]])
+    r = tree_greedy_one(zt, [0, 0], [2, 1])
+    assert r.accepted == 1 and r.nodes == [2] and r.tokens == [1, 0]
+
+
+def test_greedy_chain_shaped_tree_is_prefix_match():
+    rng = np.random.default_rng(22)
+    for _ in range(100):
+        N, V = int(rng.integers(1, 9)), int(rng.integers(2, 6))
+        zt = rng.normal(size=(N + 1, V))
+        am = np.argmax(zt, axis=1)
+        tok = np.where(rng.random(N) < 0.7, am[:N], rng.integers(0, V, N))
+        j = 0
+        while j < N and tok[j] == am[j]:
+            j += 1
+        r = tree_greedy_one(zt, np.arange(N), tok)
+        assert r.accepted == j and r.tokens[-1] == am[j]
+
+
+def test_greedy_no_match_returns_root_argmax():
+    zt = np.array([[0.0, 2.0, 1.0], [5.0, 0.0, 0.0], [0.0, 0.0, 5.0]])
+    r = tree_greedy_one(zt, [0, 0], [0, 2])
+    assert r.accepted == 0 and r.tokens == [1] and r.nodes == []
+
+
+# ---------------------------------------------------------------------------
+# path mode is the chain on the gathered rows
+# ---------------------------------------------------------------------------
+
+
+def test_path_mode_is_chain_on_gathered_rows():
+    rng = np.random.default_rng(23)
+    parent = np.array([0, 0, 1, 1, 2, 3, 5])          # nodes 1..7
+    N, V = len(parent), 9
+    zt = rng.normal(0, 2, (N + 1, V))
+    zq = zt + rng.normal(0, 1, (N + 1, V))
+    tok = rng.integers(0, V, N)
+    path = np.array([2, 5, 7, -1, 9])                  # root -> 2 -> 5 -> 7 (entry after -1 ignored)
+    for _ in range(30):
+        ua, us = rng.random(5, dtype=np.float32), float(rng.random(dtype=np.float32))
+        r = tree_path_one(zt, zq, tok, path, ua, us, 0.2, 0.9)
+        c = chain_verify_one(zt[[0, 2, 5, 7]], zq[[0, 2, 5]], tok[[1, 4, 6]], ua[:3], us, 0.2, 0.9)
+        assert (r.accepted, r.tokens) == (c.accepted, c.tokens)
+        np.testing.assert_array_equal(r.a, c.a)
