@@ -1,0 +1,204 @@
+/*
+ * libspecverify: the verify step of speculative decoding on MI355X (gfx950).
+ *
+ * Sources the operations follow (cited by page title and section):
+ *   [RAPID] "RAPID：基于检索增强的推测解码长上下文推理" (explainer of arXiv
+ *           2502.20330): section "2) 推理时知识迁移" gives the mixture
+ *           p~ = (1 - lambda) p_t + lambda q; section "3) 候选验证机制（伪代码）"
+ *           gives the per-position accept / first-rejection / resample loop.
+ *   [SD]    "大模型推理的Speculative Decoding原理详解": section "修改的拒绝采样"
+ *           (accept outright when p >= q, else with probability p/q), sections
+ *           "批量投机" (many requests verified in one batch) and
+ *           "Tree Speculation" (a tree of candidates checked in one pass).
+ *   [EAGLE] "投机解码（EAGLE）：让小模型猜、大模型验，无损加速 LLM 生成":
+ *           section "1. 为什么无损" (resample from max(0, p - q)), "核心思路"
+ *           step 3 (greedy: keep a draft equal to the target's most likely
+ *           token) and "3. 验证阶段树形attention" (a node sees its ancestors).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer argument is DEVICE memory owned by the caller, except where
+ *    stated.  The library never allocates, frees or synchronises; all work is
+ *    enqueued on `stream` and outputs are valid once the stream reaches it.
+ *  - Logits are bf16 (SV_BF16) or fp32 (SV_F32).  A logits tensor is laid out
+ *    [B, R, V] with R rows per request; row r of request b starts at element
+ *    (b * R + r) * ld.  `ld` >= V, `ld * sizeof(elem)` must be a multiple of
+ *    16 bytes and the base pointer 16-byte aligned (rows are streamed with
+ *    16-byte loads).
+ *  - Temperature T (> 0, finite) divides both models' logits before the
+ *    softmax.  lambda is in [0, 1].
+ *  - Uniforms are fp32 in [0, 1).  A draft is accepted iff u < a, with
+ *    a = min(1, p~(x) / q(x)).  One sampling uniform per request drives the
+ *    inverse-CDF draw, token = min{ j : F(j) > u }, from the normalised
+ *    residual max(0, p~ - q) after a rejection, or from the target's own
+ *    softmax(z/T) (the bonus token) when every draft is accepted.
+ *  - Argument errors are returned synchronously, before any HIP call.  Data
+ *    errors found on the device are OR-ed into the int32 word `*status`
+ *    (SV_DATA_* bits; the call first clears it); the caller reads it when
+ *    convenient.  HIP launch failures return SV_EHIP.
+ *  - `workspace` is caller-owned device scratch of at least the size the
+ *    matching *_workspace_bytes() reports, 16-byte aligned, and not shared by
+ *    calls that may run concurrently.  Its contents need no initialisation.
+ *  - The library keeps no state and is thread-safe.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SV_OK = 0,
+    SV_EINVAL = 1,      /* a size or scalar is out of range (B < 0, K > SV_MAX_POSITIONS, T <= 0, ...) */
+    SV_ENULL = 2,       /* a required pointer is NULL */
+    SV_EALIGN = 3,      /* a logits pointer or row stride is not 16-byte aligned, or ld < V */
+    SV_EWORKSPACE = 4,  /* workspace NULL, misaligned or smaller than required */
+    SV_EDTYPE = 5,      /* unknown sv_dtype */
+    SV_EHIP = 6         /* a kernel launch failed */
+} sv_status;
+
+typedef enum { SV_BF16 = 0, SV_F32 = 1 } sv_dtype;
+
+/* Largest number of drafted positions per request (chain K, tree path Dmax). */
+#define SV_MAX_POSITIONS 64
+/* Largest number of non-root nodes of a draft tree. */
+#define SV_MAX_TREE_NODES 1024
+
+/* Bits of the device-side status word. */
+#define SV_DATA_BAD_TOKEN   0x01 /* a drafted or node token outside [0, V): that draft is rejected */
+#define SV_DATA_BAD_ROW     0x02 /* a used row has NaN / +inf or is all -inf: rejected there; a
+                                    sampled token from such a row is -1 */
+#define SV_DATA_ZERO_Q      0x04 /* a drafted token has draft probability 0: accepted iff p~(x) > 0 */
+#define SV_DATA_BAD_LENGTH  0x08 /* draft_len[b] outside [0, K]: clamped */
+#define SV_DATA_BAD_TREE    0x10 /* parent or path entry invalid: node never accepted / path cut */
+#define SV_DATA_FALLBACK    0x20 /* residual mass was zero after a rejection: sampled p~ instead */
+#define SV_DATA_DEPTH       0x40 /* accepted tree path deeper than Dmax: cut at Dmax nodes */
+
+/* Human-readable name of a status code (static storage, host memory). */
+const char *sv_status_string(sv_status s);
+
+/* ------------------------------------------------------------------------
+ * Linear chain ([RAPID] verify loop, [SD] batched speculation)
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes for sv_chain_verify with these sizes (either dtype).
+ * Returns 0 for invalid sizes. */
+size_t sv_chain_workspace_bytes(int B, int K, int V);
+
+/*
+ * Verify B requests of up to K drafts each.
+ *
+ *  target_logits  [B, K+1, V], row stride ld_t elements; row k of a request
+ *                 with K_b drafts is the target's prediction for position k,
+ *                 row K_b serves the bonus token.
+ *  draft_logits   [B, K, V], row stride ld_q.
+ *  draft_tokens   [B, K] int32, token drafted at each position.
+ *  draft_len      [B] int32 K_b in [0, K], or NULL (every request drafts K).
+ *  u_accept       [B, K] fp32 acceptance uniforms, u_sample [B] fp32.
+ *  lambda, temperature: host scalars.
+ *  accepted       [B] int32 out: number n_b of accepted drafts (0..K_b).
+ *  out_tokens     [B, K+1] int32 out: the n_b accepted drafts, then the
+ *                 resampled (n_b < K_b) or bonus (n_b = K_b) token, then -1.
+ *  accept_prob    [B, K] fp32 out or NULL: a_i for every i < K_b (also past
+ *                 the first rejection); 0 for i >= K_b.
+ *  status         [1] int32 out (device) or NULL.
+ *  K = 0 is valid: each request then samples one token from target row 0.
+ */
+sv_status sv_chain_verify(const void *target_logits, int64_t ld_t,
+                          const void *draft_logits, int64_t ld_q,
+                          sv_dtype dtype, int B, int K, int V,
+                          const int32_t *draft_tokens, const int32_t *draft_len,
+                          const float *u_accept, const float *u_sample,
+                          float lambda, float temperature,
+                          int32_t *accepted, int32_t *out_tokens, float *accept_prob,
+                          int32_t *status, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * The two launches sv_chain_verify makes, exposed so that a caller can time or
+ * interleave them.  Same arguments and meaning; sv_chain_row_stats streams the
+ * drafted rows once and reduces each to (max, sum of exponentials);
+ * sv_chain_accept_resample must follow it on the same stream with the same
+ * workspace and resolves acceptance, resamples and writes the outputs.
+ */
+sv_status sv_chain_row_stats(const void *target_logits, int64_t ld_t,
+                             const void *draft_logits, int64_t ld_q,
+                             sv_dtype dtype, int B, int K, int V,
+                             const int32_t *draft_tokens, const int32_t *draft_len,
+                             const float *u_accept, const float *u_sample,
+                             float lambda, float temperature,
+                             int32_t *accepted, int32_t *out_tokens, float *accept_prob,
+                             int32_t *status, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+sv_status sv_chain_accept_resample(const void *target_logits, int64_t ld_t,
+                                   const void *draft_logits, int64_t ld_q,
+                                   sv_dtype dtype, int B, int K, int V,
+                                   const int32_t *draft_tokens, const int32_t *draft_len,
+                                   const float *u_accept, const float *u_sample,
+                                   float lambda, float temperature,
+                                   int32_t *accepted, int32_t *out_tokens, float *accept_prob,
+                                   int32_t *status, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Draft trees ([SD] "Tree Speculation", [EAGLE] greedy match + tree attention)
+ *
+ * Node 0 is the root; node i (1..N) has token node_token[b, i-1] and parent
+ * parent[b, i-1] in [0, i-1].  Row r of a request's [N+1, V] logits belongs to
+ * node r: the target's (or draft's) prediction of the token after node r.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes for either tree call with these sizes; 0 for invalid sizes. */
+size_t sv_tree_workspace_bytes(int B, int N, int V);
+
+/*
+ * Greedy verification: node i is accepted iff its parent is accepted and its
+ * token equals the argmax of the parent's target row (lowest token id on
+ * ties).  The deepest accepted node wins (lowest node id on ties).
+ *
+ *  target_logits  [B, N+1, V], stride ld_t.   parent, node_token [B, N] int32.
+ *  accepted       [B] out: depth of the winning node (accepted draft count).
+ *  out_tokens     [B, Dmax+1] out: tokens of the accepted nodes root->leaf,
+ *                 then the argmax of the winning node's row, then -1.
+ *  accepted_nodes [B, Dmax] out: accepted node ids root->leaf, then -1.
+ *  lambda and temperature do not enter (argmax is temperature-free).
+ */
+sv_status sv_tree_verify_greedy(const void *target_logits, int64_t ld_t, sv_dtype dtype,
+                                int B, int N, int V,
+                                const int32_t *parent, const int32_t *node_token,
+                                int32_t *accepted, int32_t *out_tokens, int32_t *accepted_nodes,
+                                int Dmax, int32_t *status, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Stochastic verification along one caller-chosen root->leaf path: chain
+ * acceptance (as sv_chain_verify) where position j drafts node n_{j+1}'s token
+ * and is tested on target row n_j and draft row n_j (n_0 = root); the bonus
+ * row is target row n_d.
+ *
+ *  target_logits, draft_logits [B, N+1, V].   node_token [B, N].
+ *  path     [B, Dmax] int32 node ids n_1..n_d in [1, N], then -1 (or full).
+ *  u_accept [B, Dmax], u_sample [B].
+ *  accepted [B], out_tokens [B, Dmax+1], accept_prob [B, Dmax] (or NULL).
+ */
+sv_status sv_tree_verify_path(const void *target_logits, int64_t ld_t,
+                              const void *draft_logits, int64_t ld_q,
+                              sv_dtype dtype, int B, int N, int V,
+                              const int32_t *node_token, const int32_t *path, int Dmax,
+                              const float *u_accept, const float *u_sample,
+                              float lambda, float temperature,
+                              int32_t *accepted, int32_t *out_tokens, float *accept_prob,
+                              int32_t *status, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

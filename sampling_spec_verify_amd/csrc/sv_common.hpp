@@ -1,0 +1,160 @@
+// Host/device definitions shared by the chain, path and tree kernels:
+// argument records, workspace layout, temperature constants and argument
+// validation.  Validation runs on the host before any HIP call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+// Partial reduction of one wave-chunk of a row: the sum S of 2^(z*c - s) over
+// the chunk's elements, relative to the shift s (fp32).  s = -inf marks a
+// chunk without any finite element.
+struct alignas(16) Part {
+    float s;
+    float pad;
+    double S;
+};
+
+// Per-chunk argmax partial (greedy trees).
+struct alignas(16) ArgPart {
+    float val;
+    int idx;
+    int nan;
+    int pad;
+};
+
+// Request geometry of the chain and path calls.
+struct Geo {
+    const char *tgt;              // target logits base
+    const char *drf;              // draft logits base
+    int64_t ld_t, ld_q;           // row strides (elements)
+    int64_t req_t, req_q;         // rows per request
+    int elem;                     // bytes per element
+    int V;                        // vocabulary
+    int P;                        // positions capacity (chain K, path Dmax): output strides
+    int Pcap;                     // positions a request can hold (chain K, path min(Dmax, N)):
+                                  // stride of the row-partial workspace
+    int N;                        // tree nodes (path mode)
+    const int32_t *tokens;        // chain: draft_tokens [B, K]; path: node_token [B, N]
+    const int32_t *draft_len;     // chain only, may be NULL
+    const int32_t *path;          // path mode; NULL for a chain
+};
+
+struct ChainArgs {
+    Geo g;
+    int B;
+    const float *u_accept;        // [B, P]
+    const float *u_sample;        // [B]
+    float lam;
+    float c_hi, c_lo;             // log2(e)/T = c_hi + c_lo, c_hi > 0, c_lo > 0
+    double c_d;                   // log2(e)/T in double
+    int32_t *accepted;            // [B]
+    int32_t *out_tokens;          // [B, P+1]
+    float *accept_prob;           // [B, P] or NULL
+    int32_t *status;              // [1]
+    int32_t *counters;            // [B] workspace
+    Part *part1;                  // [B, Pcap, 2, C1] workspace
+    Part *part2;                  // [B, C2] workspace
+    int C1;                       // wave-chunks per row in the row-stats pass
+    int C2;                       // block-chunks per row in the sampling pass
+};
+
+struct TreeArgs {
+    const char *tgt;
+    int64_t ld_t;
+    int elem;
+    int B, N, V, Dmax, C1;
+    const int32_t *parent;
+    const int32_t *node_token;
+    int32_t *accepted;
+    int32_t *out_tokens;
+    int32_t *accepted_nodes;
+    int32_t *status;
+    ArgPart *part;                // [B, N+1, C1]
+};
+
+// ---------------------------------------------------------------------------
+// tiling
+// ---------------------------------------------------------------------------
+
+constexpr int kNV2 = 2;                       // vectors per thread in the sampling pass
+constexpr int kMinVec = 4;                    // fp32: 4 elements per 16-byte vector
+constexpr int kMinNV = 2;                     // smallest row-stats vectors per lane
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+// Row-stats wave-chunk: 64 lanes x NV vectors x VEC elements.
+inline int c1_for(int V, int NV, int vec) { return static_cast<int>(cdiv(V, 64LL * NV * vec)); }
+inline int c2_for(int V, int vec) { return static_cast<int>(cdiv(V, 256LL * kNV2 * vec)); }
+
+struct ChainLayout {
+    int64_t counters, status, part1, part2, total;
+};
+
+inline ChainLayout chain_layout(int B, int P, int V) {
+    ChainLayout L;
+    const int64_t c1max = c1_for(V, kMinNV, kMinVec);
+    const int64_t c2max = c2_for(V, kMinVec);
+    L.counters = 0;
+    L.status = align256(int64_t(B) * 4);
+    L.part1 = L.status + 256;
+    L.part2 = L.part1 + align256(int64_t(B) * P * 2 * c1max * int64_t(sizeof(Part)));
+    L.total = L.part2 + align256(int64_t(B) * c2max * int64_t(sizeof(Part)));
+    return L;
+}
+
+struct TreeLayout {
+    int64_t status, part, total;
+};
+
+inline TreeLayout tree_layout(int B, int N, int V) {
+    TreeLayout L;
+    const int64_t c1max = c1_for(V, kMinNV, kMinVec);
+    L.status = 0;
+    L.part = 256;
+    L.total = L.part + align256(int64_t(B) * (N + 1) * c1max * int64_t(sizeof(ArgPart)));
+    return L;
+}
+
+// Temperature constants: c = log2(e) / T split as c_hi + c_lo with both parts
+// strictly positive, so that (-inf) * c_hi + (-inf) * c_lo stays -inf.
+inline bool temperature_split(float T, float *c_hi, float *c_lo, double *c_d) {
+    const double c = 1.4426950408889634074 / static_cast<double>(T);
+    if (!(c > 0.0 && c < 1.0e38)) return false;
+    float hi = static_cast<float>(c);
+    if (static_cast<double>(hi) >= c) hi = nextafterf(hi, 0.0f);
+    float lo = static_cast<float>(c - static_cast<double>(hi));
+    if (!(hi > 0.0f) || !(lo >= 1.1754944e-38f) || !isfinite(hi) || !isfinite(lo)) return false;
+    *c_hi = hi;
+    *c_lo = lo;
+    *c_d = static_cast<double>(hi) + static_cast<double>(lo);
+    return true;
+}
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int elem_bytes(sv_dtype d) { return d == SV_BF16 ? 2 : (d == SV_F32 ? 4 : 0); }
+
+inline sv_status check_logits(const void *p, int64_t ld, int V, int eb) {
+    if (!p) return SV_ENULL;
+    if (ld < V || !aligned16(p) || ((ld * eb) & 15) != 0) return SV_EALIGN;
+    return SV_OK;
+}
+
+inline sv_status check_scalars(float lam, float T) {
+    if (!(lam >= 0.0f && lam <= 1.0f)) return SV_EINVAL;
+    if (!(T > 0.0f) || !isfinite(T)) return SV_EINVAL;
+    float a, b;
+    double c;
+    if (!temperature_split(T, &a, &b, &c)) return SV_EINVAL;
+    return SV_OK;
+}
+
+}  // namespace sv

@@ -1,0 +1,181 @@
+// Device helpers shared by the libspecverify kernels (gfx950, wave64).
+//
+//  * 16-byte row loads and bf16/fp32 unpacking,
+//  * wavefront reductions built from DPP lane moves (quad_perm, row mirrors)
+//    plus one ds_swizzle across the 16-lane rows and a readlane pair across
+//    the two 32-lane halves,
+//  * a block-wide (256-thread) inclusive/exclusive scan of doubles whose
+//    inclusive values form a monotone sequence: every item's exclusive prefix
+//    is bitwise the previous item's inclusive prefix, so "first item whose
+//    inclusive prefix exceeds t" is always unique.
+//
+// Every reduction runs in a fixed order, so results are bitwise reproducible;
+// no floating-point atomics are used anywhere in the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / kWave;
+
+// ---------------------------------------------------------------------------
+// element types
+// ---------------------------------------------------------------------------
+
+struct Bf16 {
+    static constexpr int kVec = 8;     // elements per 16-byte vector
+    static constexpr int kBytes = 2;
+    static constexpr unsigned kNegInfWord = 0xff80ff80u;
+    __device__ static __forceinline__ void unpack(const u32x4 &d, float *f) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[2 * j] = __uint_as_float(d[j] << 16);
+            f[2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+        }
+    }
+    __device__ static __forceinline__ float load1(const char *row, int64_t i) {
+        const unsigned short h = reinterpret_cast<const unsigned short *>(row)[i];
+        return __uint_as_float(static_cast<unsigned>(h) << 16);
+    }
+};
+
+struct F32 {
+    static constexpr int kVec = 4;
+    static constexpr int kBytes = 4;
+    static constexpr unsigned kNegInfWord = 0xff800000u;
+    __device__ static __forceinline__ void unpack(const u32x4 &d, float *f) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] = __uint_as_float(d[j]);
+    }
+    __device__ static __forceinline__ float load1(const char *row, int64_t i) {
+        return reinterpret_cast<const float *>(row)[i];
+    }
+};
+
+__device__ __forceinline__ u32x4 load16(const char *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// ---------------------------------------------------------------------------
+// lane moves
+// ---------------------------------------------------------------------------
+
+// DPP controls (GFX9 encoding)
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+// ds_swizzle bitmask mode: and 0x1f, or 0, xor 0x10 -> lane ^ 16 within 32
+constexpr int kSwzXor16 = 0x401F;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int swz16(int v) { return __builtin_amdgcn_ds_swizzle(v, kSwzXor16); }
+
+__device__ __forceinline__ float f_of(int v) { return __int_as_float(v); }
+__device__ __forceinline__ int i_of(float v) { return __float_as_int(v); }
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const int lo = dpp<CTRL>(__double2loint(v));
+    const int hi = dpp<CTRL>(__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double swz16_d(double v) {
+    const int lo = swz16(__double2loint(v));
+    const int hi = swz16(__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), lane);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), lane);
+    return __hiloint2double(hi, lo);
+}
+
+// ---------------------------------------------------------------------------
+// wavefront reductions (result is wave-uniform)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, f_of(dpp<kDppXor1>(i_of(v))));
+    v = fmaxf(v, f_of(dpp<kDppXor2>(i_of(v))));
+    v = fmaxf(v, f_of(dpp<kDppHalfMirror>(i_of(v))));
+    v = fmaxf(v, f_of(dpp<kDppMirror>(i_of(v))));
+    v = fmaxf(v, f_of(swz16(i_of(v))));
+    return fmaxf(f_of(__builtin_amdgcn_readlane(i_of(v), 0)),
+                 f_of(__builtin_amdgcn_readlane(i_of(v), 32)));
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+    v = min(v, dpp<kDppXor1>(v));
+    v = min(v, dpp<kDppXor2>(v));
+    v = min(v, dpp<kDppHalfMirror>(v));
+    v = min(v, dpp<kDppMirror>(v));
+    v = min(v, swz16(v));
+    return min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+    v += dpp_d<kDppXor1>(v);
+    v += dpp_d<kDppXor2>(v);
+    v += dpp_d<kDppHalfMirror>(v);
+    v += dpp_d<kDppMirror>(v);
+    v += swz16_d(v);
+    return readlane_d(v, 0) + readlane_d(v, 32);
+}
+
+// ---------------------------------------------------------------------------
+// block (256 threads) helpers; every thread of the block must call them
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float block_max(float v, float *sh4) {
+    v = wave_max(v);
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) sh4[w] = v;
+    __syncthreads();
+    const float r = fmaxf(fmaxf(sh4[0], sh4[1]), fmaxf(sh4[2], sh4[3]));
+    __syncthreads();
+    return r;
+}
+
+struct Scan {
+    double incl;    // prefix including this thread's item
+    double excl;    // prefix before it (bitwise the previous item's incl)
+    double total;   // prefix of the whole block (bitwise the last item's incl)
+};
+
+// Inclusive scan of one double per thread, in thread order, offset by `carry`.
+__device__ __forceinline__ Scan block_scan_d(double v, double carry, double *sh4) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    double x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const double o = __shfl_up(x, off, kWave);
+        if (lane >= off) x += o;
+    }
+    if (lane == kWave - 1) sh4[w] = x;
+    __syncthreads();
+    const double b1 = sh4[0];
+    const double b2 = b1 + sh4[1];
+    const double b3 = b2 + sh4[2];
+    const double tot = b3 + sh4[3];
+    const double base = (w == 0) ? 0.0 : (w == 1) ? b1 : (w == 2) ? b2 : b3;
+    const double prev = __shfl_up(x, 1, kWave);
+    Scan s;
+    s.incl = carry + (base + x);
+    s.excl = carry + ((lane == 0) ? base : (base + prev));
+    s.total = carry + tot;
+    __syncthreads();
+    return s;
+}
+
+}  // namespace sv

@@ -1,0 +1,280 @@
+"""Python binding of libspecverify (ctypes; argument marshalling only).
+
+Every function has the name of its C entry point without the ``sv_`` prefix.
+Tensors are torch tensors on the GPU; the binding checks shapes and dtypes,
+allocates outputs and the workspace with torch, and passes raw device pointers
+and ``torch.cuda.current_stream()``.  All computation happens in the HIP
+kernels of ``libspecverify.so``; if that library is missing the binding raises,
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+SV_OK, SV_EINVAL, SV_ENULL, SV_EALIGN, SV_EWORKSPACE, SV_EDTYPE, SV_EHIP = range(7)
+SV_BF16, SV_F32 = 0, 1
+SV_MAX_POSITIONS = 64
+SV_MAX_TREE_NODES = 1024
+DATA_FLAGS = {
+    0x01: "BAD_TOKEN", 0x02: "BAD_ROW", 0x04: "ZERO_Q", 0x08: "BAD_LENGTH",
+    0x10: "BAD_TREE", 0x20: "FALLBACK", 0x40: "DEPTH",
+}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_int64
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+
+_CHAIN_ARGS = [_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _P, _P, _F, _F, _P, _P, _P, _P, _P, _S, _P]
+SIGNATURES = {
+    "sv_status_string": ([_I], ctypes.c_char_p),
+    "sv_chain_workspace_bytes": ([_I, _I, _I], _S),
+    "sv_chain_verify": (_CHAIN_ARGS, _I),
+    "sv_chain_row_stats": (_CHAIN_ARGS, _I),
+    "sv_chain_accept_resample": (_CHAIN_ARGS, _I),
+    "sv_tree_workspace_bytes": ([_I, _I, _I], _S),
+    "sv_tree_verify_greedy": ([_P, _L, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _S, _P], _I),
+    "sv_tree_verify_path": ([_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _I, _P, _P, _F, _F, _P, _P,
+                             _P, _P, _P, _S, _P], _I),
+}
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libspecverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with sampling_spec_verify_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().sv_status_string(int(code)).decode()
+
+
+def decode_flags(word: int):
+    return [name for bit, name in DATA_FLAGS.items() if word & bit]
+
+
+def _check(code: int, what: str):
+    if code != SV_OK:
+        raise SpecVerifyError(f"{what}: {status_string(code)}")
+
+
+def chain_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(lib().sv_chain_workspace_bytes(B, K, V))
+
+
+def tree_workspace_bytes(B: int, N: int, V: int) -> int:
+    return int(lib().sv_tree_workspace_bytes(B, N, V))
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling
+# ---------------------------------------------------------------------------
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _rows(t, B: int, R: int, V: int, name: str) -> int:
+    """Check a [B, R, V] logits tensor with unit last stride; returns its row stride."""
+    if t.dim() != 3 or t.shape[0] != B or t.shape[1] != R or t.shape[2] != V:
+        raise ValueError(f"{name} must be [{B}, {R}, {V}], got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    ld = t.stride(1)
+    if t.stride(2) != 1 or ld < V or (B > 1 and t.stride(0) != R * ld):
+        raise ValueError(f"{name} must be a [B, R, V] view of a contiguous [B, R, ld] buffer")
+    return int(ld)
+
+
+def _i32(t, shape, name):
+    torch = _torch()
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor of shape {tuple(shape)}")
+    return t
+
+
+def _f32(t, shape, name):
+    torch = _torch()
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor of shape {tuple(shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class ChainOut(NamedTuple):
+    accepted: object        # [B] int32
+    out_tokens: object      # [B, K+1] int32
+    accept_prob: object     # [B, K] float32
+    status: object          # [1] int32 (device word of SV_DATA_* bits)
+
+
+class ChainCall:
+    """A chain-verify call with its outputs and workspace bound once.
+
+    ``run()`` launches both kernels; ``row_stats()`` / ``accept_resample()``
+    launch one each (the pair equals ``run()``).  Rebinding inputs with
+    ``set_inputs`` keeps the outputs and workspace.
+    """
+
+    def __init__(self, target, draft, tokens, u_accept, u_sample, lam=0.0, temperature=1.0,
+                 draft_len=None, stream=None, workspace=None):
+        torch = _torch()
+        B, K1, V = target.shape
+        K = K1 - 1
+        dev = target.device
+        self.B, self.K, self.V = B, K, V
+        self.lam, self.temperature = float(lam), float(temperature)
+        self.stream = stream
+        self.out = ChainOut(torch.empty(B, dtype=torch.int32, device=dev),
+                            torch.empty(B, K + 1, dtype=torch.int32, device=dev),
+                            torch.empty(B, K, dtype=torch.float32, device=dev),
+                            torch.empty(1, dtype=torch.int32, device=dev))
+        nbytes = chain_workspace_bytes(B, K, V)
+        if nbytes == 0 and B > 0:
+            raise SpecVerifyError("invalid chain sizes")
+        self.workspace = workspace if workspace is not None else torch.empty(
+            max(nbytes, 16), dtype=torch.uint8, device=dev)
+        self.set_inputs(target, draft, tokens, u_accept, u_sample, draft_len)
+
+    def set_inputs(self, target, draft, tokens, u_accept, u_sample, draft_len=None):
+        B, K, V = self.B, self.K, self.V
+        self.dtype = _dtype_code(target)
+        if draft.dtype != target.dtype:
+            raise TypeError("target and draft logits must share a dtype")
+        self.ld_t = _rows(target, B, K + 1, V, "target")
+        self.ld_q = _rows(draft, B, K, V, "draft") if K > 0 else V
+        self.inputs = (target, draft, _i32(tokens, (B, K), "tokens"),
+                       _i32(draft_len, (B,), "draft_len"),
+                       _f32(u_accept, (B, K), "u_accept"), _f32(u_sample, (B,), "u_sample"))
+
+    def _args(self):
+        t, d, tok, dl, ua, us = self.inputs
+        o = self.out
+        return (_ptr(t), self.ld_t, _ptr(d), self.ld_q, self.dtype, self.B, self.K, self.V,
+                _ptr(tok), _ptr(dl), _ptr(ua), _ptr(us), self.lam, self.temperature,
+                _ptr(o.accepted), _ptr(o.out_tokens), _ptr(o.accept_prob), _ptr(o.status),
+                _ptr(self.workspace), self.workspace.numel(), _stream(self.stream))
+
+    def run(self) -> ChainOut:
+        _check(lib().sv_chain_verify(*self._args()), "sv_chain_verify")
+        return self.out
+
+    def row_stats(self):
+        _check(lib().sv_chain_row_stats(*self._args()), "sv_chain_row_stats")
+
+    def accept_resample(self) -> ChainOut:
+        _check(lib().sv_chain_accept_resample(*self._args()), "sv_chain_accept_resample")
+        return self.out
+
+
+def chain_verify(target, draft, tokens, u_accept, u_sample, lam: float = 0.0,
+                 temperature: float = 1.0, draft_len=None, stream=None) -> ChainOut:
+    """sv_chain_verify on torch tensors: target [B,K+1,V], draft [B,K,V] (bf16 or fp32)."""
+    return ChainCall(target, draft, tokens, u_accept, u_sample, lam, temperature, draft_len,
+                     stream).run()
+
+
+class TreeGreedyOut(NamedTuple):
+    accepted: object        # [B]
+    out_tokens: object      # [B, Dmax+1]
+    accepted_nodes: object  # [B, Dmax]
+    status: object          # [1]
+
+
+def tree_verify_greedy(target, parent, node_token, Dmax: int, stream=None,
+                       workspace=None) -> TreeGreedyOut:
+    """sv_tree_verify_greedy: target [B, N+1, V], parent / node_token [B, N] int32."""
+    torch = _torch()
+    B, N1, V = target.shape
+    N = N1 - 1
+    ld = _rows(target, B, N + 1, V, "target")
+    _i32(parent, (B, N), "parent")
+    _i32(node_token, (B, N), "node_token")
+    dev = target.device
+    out = TreeGreedyOut(torch.empty(B, dtype=torch.int32, device=dev),
+                        torch.empty(B, Dmax + 1, dtype=torch.int32, device=dev),
+                        torch.empty(B, max(Dmax, 0), dtype=torch.int32, device=dev),
+                        torch.empty(1, dtype=torch.int32, device=dev))
+    ws = workspace if workspace is not None else torch.empty(
+        max(tree_workspace_bytes(B, N, V), 16), dtype=torch.uint8, device=dev)
+    code = lib().sv_tree_verify_greedy(_ptr(target), ld, _dtype_code(target), B, N, V, _ptr(parent),
+                                       _ptr(node_token), _ptr(out.accepted), _ptr(out.out_tokens),
+                                       _ptr(out.accepted_nodes), int(Dmax), _ptr(out.status),
+                                       _ptr(ws), ws.numel(), _stream(stream))
+    _check(code, "sv_tree_verify_greedy")
+    return out
+
+
+def tree_verify_path(target, draft, node_token, path, u_accept, u_sample, lam: float = 0.0,
+                     temperature: float = 1.0, stream=None, workspace=None) -> ChainOut:
+    """sv_tree_verify_path: target / draft [B, N+1, V], path [B, Dmax] (-1 terminated)."""
+    torch = _torch()
+    B, N1, V = target.shape
+    N = N1 - 1
+    Dmax = path.shape[1]
+    ld_t = _rows(target, B, N + 1, V, "target")
+    ld_q = _rows(draft, B, N + 1, V, "draft")
+    if draft.dtype != target.dtype:
+        raise TypeError("target and draft logits must share a dtype")
+    _i32(node_token, (B, N), "node_token")
+    _i32(path, (B, Dmax), "path")
+    _f32(u_accept, (B, Dmax), "u_accept")
+    _f32(u_sample, (B,), "u_sample")
+    dev = target.device
+    out = ChainOut(torch.empty(B, dtype=torch.int32, device=dev),
+                   torch.empty(B, Dmax + 1, dtype=torch.int32, device=dev),
+                   torch.empty(B, Dmax, dtype=torch.float32, device=dev),
+                   torch.empty(1, dtype=torch.int32, device=dev))
+    ws = workspace if workspace is not None else torch.empty(
+        max(tree_workspace_bytes(B, N, V), 16), dtype=torch.uint8, device=dev)
+    code = lib().sv_tree_verify_path(_ptr(target), ld_t, _ptr(draft), ld_q, _dtype_code(target), B,
+                                     N, V, _ptr(node_token), _ptr(path), Dmax, _ptr(u_accept),
+                                     _ptr(u_sample), float(lam), float(temperature),
+                                     _ptr(out.accepted), _ptr(out.out_tokens),
+                                     _ptr(out.accept_prob), _ptr(out.status), _ptr(ws), ws.numel(),
+                                     _stream(stream))
+    _check(code, "sv_tree_verify_path")
+    return out

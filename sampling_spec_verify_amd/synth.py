@@ -381,3 +381,36 @@ def config(name: str, seed_offset: int = 0):
         return make_tree(seed, 8, 26, 128256, "bf16", depth=6, sigma_t=3.0, sigma_q=1.0,
                          lam=0.0, temperature=1.0, name="c5")
     raise KeyError(name)
+
+
+def make_random_tree(seed: int, B: int, N: int, V: int, dtype: str = "fp32", *,
+                     int_logits: bool = False, sharp: float = 0.05, sigma_q: float = 1.0,
+                     lam: float = 0.0, temperature: float = 1.0, name: str = "rtree") -> TreeInputs:
+    """Small random trees for edge cases: parent[i] ~ U{0..i}, node tokens drawn
+    from the parent's target row at a low temperature ``sharp`` (so they often
+    hit that row's most likely token).  ``int_logits`` draws integer logits in
+    [-3, 3] to create many equal maxima."""
+    s = _streams(seed)
+    if int_logits:
+        zt = s["target"].integers(-3, 4, size=(B, N + 1, V)).astype(np.float32)
+    else:
+        zt = s["target"].standard_normal((B, N + 1, V), dtype=np.float32) * np.float32(2.0)
+    zq = zt + s["noise"].standard_normal((B, N + 1, V), dtype=np.float32) * np.float32(sigma_q)
+    if dtype == "bf16":
+        t_arr, q_arr = f32_to_bf16_bits(zt), f32_to_bf16_bits(zq)
+        t_w = bf16_bits_to_f32(t_arr)
+    else:
+        t_arr, q_arr = zt, zq.astype(np.float32)
+        t_w = t_arr
+    parent = np.zeros((B, N), dtype=np.int32)
+    node_token = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        for i in range(1, N + 1):
+            parent[b, i - 1] = int(s["tree_shape"].integers(0, i))
+            node_token[b, i - 1] = gumbel_max_sample(s["draft_tok"], t_w[b, parent[b, i - 1]], sharp)
+    Dmax = max(1, max(int(tree_depths(parent[b]).max()) for b in range(B)))
+    path = np.stack([seeded_path(s["tree_path"], parent[b], Dmax) for b in range(B)])
+    u_acc = uniforms(s["u_accept"], (B, Dmax))
+    u_smp = uniforms(s["u_sample"], (B,))
+    return TreeInputs(name, dtype, t_arr, q_arr, parent, node_token, path, u_acc, u_smp,
+                      float(lam), float(temperature))

@@ -1,0 +1,153 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects bad arguments synchronously before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sampling_spec_verify_amd import specverify as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["sv_status_string", "sv_chain_workspace_bytes", "sv_chain_verify",
+                            "sv_chain_row_stats", "sv_chain_accept_resample",
+                            "sv_tree_workspace_bytes", "sv_tree_verify_greedy",
+                            "sv_tree_verify_path"])
+
+
+def test_library_exports_every_declared_symbol():
+    L = sv.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(sv.SIGNATURES)
+
+
+def test_status_strings():
+    for code in range(7):
+        s = sv.status_string(code)
+        assert s.startswith("SV_")
+    assert "unknown" in sv.status_string(99)
+
+
+def test_workspace_sizes():
+    L = sv.lib()
+    assert L.sv_chain_workspace_bytes(-1, 4, 100) == 0
+    assert L.sv_chain_workspace_bytes(1, 65, 100) == 0
+    assert L.sv_chain_workspace_bytes(1, 4, 0) == 0
+    a = L.sv_chain_workspace_bytes(1, 8, 128256)
+    b = L.sv_chain_workspace_bytes(64, 8, 128256)
+    assert 0 < a < b and a % 256 == 0
+    assert L.sv_tree_workspace_bytes(8, 26, 128256) > 0
+    assert L.sv_tree_workspace_bytes(8, 1025, 128256) == 0
+
+
+FAKE = 1 << 20          # an aligned non-null address; never dereferenced (calls fail validation)
+
+
+def chain_call(fn="sv_chain_verify", **kw):
+    args = dict(t=FAKE, ld_t=128, d=FAKE, ld_q=128, dtype=sv.SV_BF16, B=2, K=4, V=128,
+                tok=FAKE, dl=None, ua=FAKE, us=FAKE, lam=0.0, T=1.0, acc=FAKE, out=FAKE,
+                ap=FAKE, st=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    args.update(kw)
+    L = sv.lib()
+    return getattr(L, fn)(args["t"], args["ld_t"], args["d"], args["ld_q"], args["dtype"], args["B"],
+                          args["K"], args["V"], args["tok"], args["dl"], args["ua"], args["us"],
+                          args["lam"], args["T"], args["acc"], args["out"], args["ap"], args["st"],
+                          args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("fn", ["sv_chain_verify", "sv_chain_row_stats", "sv_chain_accept_resample"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), sv.SV_EDTYPE),
+    (dict(B=-1), sv.SV_EINVAL),
+    (dict(K=-1), sv.SV_EINVAL),
+    (dict(K=65), sv.SV_EINVAL),
+    (dict(V=0), sv.SV_EINVAL),
+    (dict(lam=1.5), sv.SV_EINVAL),
+    (dict(lam=-0.1), sv.SV_EINVAL),
+    (dict(lam=float("nan")), sv.SV_EINVAL),
+    (dict(T=0.0), sv.SV_EINVAL),
+    (dict(T=-1.0), sv.SV_EINVAL),
+    (dict(T=float("inf")), sv.SV_EINVAL),
+    (dict(T=float("nan")), sv.SV_EINVAL),
+    (dict(T=1e36), sv.SV_EINVAL),
+    (dict(T=1e-42), sv.SV_EINVAL),
+    (dict(t=None), sv.SV_ENULL),
+    (dict(d=None), sv.SV_ENULL),
+    (dict(tok=None), sv.SV_ENULL),
+    (dict(ua=None), sv.SV_ENULL),
+    (dict(us=None), sv.SV_ENULL),
+    (dict(acc=None), sv.SV_ENULL),
+    (dict(out=None), sv.SV_ENULL),
+    (dict(t=FAKE + 8), sv.SV_EALIGN),
+    (dict(d=FAKE + 2), sv.SV_EALIGN),
+    (dict(ld_t=100), sv.SV_EALIGN),              # ld < V
+    (dict(ld_t=132), sv.SV_EALIGN),              # 264-byte rows are not 16-byte multiples
+    (dict(dtype=sv.SV_F32, ld_q=130), sv.SV_EALIGN),
+    (dict(ws=None), sv.SV_EWORKSPACE),
+    (dict(ws=FAKE + 4), sv.SV_EWORKSPACE),
+    (dict(wsb=512), sv.SV_EWORKSPACE),
+])
+def test_chain_argument_errors(fn, kw, code):
+    assert chain_call(fn, **kw) == code
+
+
+def test_chain_empty_batch_is_a_no_op():
+    assert chain_call(B=0, t=None, d=None, tok=None, ua=None, us=None, acc=None, out=None,
+                      ws=None, wsb=0) == sv.SV_OK
+
+
+def test_chain_without_drafts_needs_no_draft_tensor():
+    # K = 0 still needs the workspace: a too-small one is reported, no launch happens
+    assert chain_call(K=0, d=None, tok=None, ua=None, wsb=16) == sv.SV_EWORKSPACE
+
+
+def greedy_call(**kw):
+    args = dict(t=FAKE, ld=128, dtype=sv.SV_BF16, B=2, N=5, V=128, par=FAKE, tok=FAKE, acc=FAKE,
+                out=FAKE, nodes=FAKE, Dmax=6, st=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    args.update(kw)
+    return sv.lib().sv_tree_verify_greedy(args["t"], args["ld"], args["dtype"], args["B"], args["N"],
+                                          args["V"], args["par"], args["tok"], args["acc"],
+                                          args["out"], args["nodes"], args["Dmax"], args["st"],
+                                          args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), sv.SV_EDTYPE), (dict(B=-2), sv.SV_EINVAL), (dict(N=-1), sv.SV_EINVAL),
+    (dict(N=1025), sv.SV_EINVAL), (dict(V=0), sv.SV_EINVAL), (dict(Dmax=-1), sv.SV_EINVAL),
+    (dict(t=None), sv.SV_ENULL), (dict(par=None), sv.SV_ENULL), (dict(tok=None), sv.SV_ENULL),
+    (dict(acc=None), sv.SV_ENULL), (dict(out=None), sv.SV_ENULL), (dict(nodes=None), sv.SV_ENULL),
+    (dict(t=FAKE + 2), sv.SV_EALIGN), (dict(ld=127), sv.SV_EALIGN),
+    (dict(ws=None), sv.SV_EWORKSPACE), (dict(wsb=100), sv.SV_EWORKSPACE),
+])
+def test_greedy_argument_errors(kw, code):
+    assert greedy_call(**kw) == code
+
+
+def path_call(**kw):
+    args = dict(t=FAKE, ld_t=128, d=FAKE, ld_q=128, dtype=sv.SV_BF16, B=2, N=5, V=128, tok=FAKE,
+                path=FAKE, Dmax=4, ua=FAKE, us=FAKE, lam=0.0, T=1.0, acc=FAKE, out=FAKE, ap=FAKE,
+                st=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    args.update(kw)
+    return sv.lib().sv_tree_verify_path(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=9), sv.SV_EDTYPE), (dict(Dmax=65), sv.SV_EINVAL), (dict(N=2000), sv.SV_EINVAL),
+    (dict(T=0.0), sv.SV_EINVAL), (dict(lam=2.0), sv.SV_EINVAL), (dict(path=None), sv.SV_ENULL),
+    (dict(tok=None), sv.SV_ENULL), (dict(d=None), sv.SV_ENULL), (dict(d=FAKE + 4), sv.SV_EALIGN),
+    (dict(wsb=64), sv.SV_EWORKSPACE),
+])
+def test_path_argument_errors(kw, code):
+    assert path_call(**kw) == code

@@ -1,0 +1,269 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on MI355X.
+
+Bar: accepted counts and emitted tokens bit-exact for every request whose
+draws all lie outside the 1e-6 boundary band (flagged requests are counted and
+printed, not hidden); acceptance probabilities within 1e-5 absolute for every
+drafted position; greedy trees bit-exact.
+"""
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+import torch
+
+import oracle
+from sampling_spec_verify_amd import specverify as sv
+from sampling_spec_verify_amd import synth
+from tests.gpu_util import (chain_call, compare_chain, dev, dev_logits, oracle_chain, path_lengths,
+                            run_chain, run_greedy, run_path, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    sv.lib()
+
+
+def report(name, stats):
+    print(f"[parity] {name}: {stats}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads at full size
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4"])
+def test_chain_workload(cfg):
+    print(f"[parity] generating {cfg}", flush=True)
+    x = synth.config(cfg)
+    g = run_chain(x)
+    assert int(g.status[0]) == 0, sv.decode_flags(int(g.status[0]))
+    stats = compare_chain(x, g, oracle_chain(x))
+    report(cfg, stats)
+    assert stats["flagged"] <= max(2, x.B // 4)
+
+
+def test_tree_workload_greedy():
+    x = synth.config("c5")
+    g = run_greedy(x)
+    assert int(g.status[0]) == 0
+    acc, out, nodes = oracle.tree_greedy(x.widened(x.target), x.parent, x.node_token, x.Dmax)
+    np.testing.assert_array_equal(g.accepted, acc)
+    np.testing.assert_array_equal(g.out_tokens, out)
+    np.testing.assert_array_equal(g.accepted_nodes, nodes)
+    report("c5 greedy", {"accepted": acc.tolist()})
+
+
+def test_tree_workload_path():
+    x = synth.config("c5")
+    g = run_path(x)
+    assert int(g.status[0]) == 0
+    ref = oracle.tree_path(x.widened(x.target), x.widened(x.draft), x.node_token, x.path,
+                           x.u_accept, x.u_sample, x.lam, x.temperature)
+    stats = compare_chain(x, g, ref, lengths=path_lengths(x))
+    report("c5 path", stats)
+
+
+@pytest.mark.parametrize("seed_offset", [1, 2, 3])
+def test_c2_more_seeds(seed_offset):
+    x = synth.config("c2", seed_offset)
+    stats = compare_chain(x, run_chain(x), oracle_chain(x))
+    report(f"c2/{seed_offset}", stats)
+
+
+# ---------------------------------------------------------------------------
+# smaller shapes: several tiles, ragged tails, padded rows, both dtypes
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    # seed, B, K, V, dtype, lam, T, ragged, ld
+    (1, 3, 4, 1000, "fp32", 0.0, 1.0, False, None),
+    (2, 5, 3, 8200, "bf16", 0.3, 0.7, True, None),
+    (3, 2, 8, 33000, "bf16", 0.0, 1.3, False, None),
+    (4, 4, 2, 4097, "fp32", 0.5, 1.0, True, 4100),
+    (5, 3, 5, 1001, "bf16", 0.1, 0.9, True, 1008),
+    (6, 7, 1, 7, "fp32", 0.0, 1.0, False, 8),
+    (7, 2, 6, 1, "bf16", 0.2, 1.0, False, 8),
+    (8, 6, 0, 5000, "bf16", 0.0, 0.8, False, None),
+    (9, 2, 64, 300, "fp32", 0.0, 1.0, False, None),
+    (10, 9, 8, 20000, "fp32", 0.9, 2.0, True, None),
+    (11, 40, 4, 2048, "bf16", 0.0, 1.0, True, None),
+]
+
+
+@pytest.mark.parametrize("seed,B,K,V,dtype,lam,T,ragged,ld", SMALL)
+def test_chain_small(seed, B, K, V, dtype, lam, T, ragged, ld):
+    x = synth.make_chain(100 + seed, B, K, V, dtype, sigma_t=2.0, sigma_q=(0.3, 2.0),
+                         zipf=V > 16, lam=lam, temperature=T, ragged=ragged, k_min=0)
+    g = run_chain(x, ld)
+    assert int(g.status[0]) == 0, sv.decode_flags(int(g.status[0]))
+    report(f"small{seed}", compare_chain(x, g, oracle_chain(x)))
+
+
+def test_identical_rows_accept_every_draft():
+    x = synth.make_chain(201, 6, 5, 3000, "bf16", lam=0.4)
+    x.draft = np.ascontiguousarray(x.target[:, :5, :])
+    g = run_chain(x)
+    assert np.all(g.accepted == 5)
+    assert np.all(g.accept_prob == 1.0)
+    report("p==q", compare_chain(x, g, oracle_chain(x)))
+
+
+def test_lambda_one_accepts_every_draft():
+    x = synth.make_chain(202, 4, 6, 2000, "fp32", lam=1.0, sigma_q=3.0)
+    g = run_chain(x)
+    assert np.all(g.accepted == 6)
+    compare_chain(x, g, oracle_chain(x))
+
+
+def test_masked_vocabulary():
+    x = synth.make_chain(203, 4, 4, 9000, "fp32", sigma_q=1.0, temperature=0.8)
+    x.target[:, :, 5000:] = -np.inf             # target rules out the upper vocabulary
+    x.draft[:, :, 7000:] = -np.inf
+    x.tokens = np.minimum(x.tokens, 6999)
+    g = run_chain(x)
+    assert int(g.status[0]) == 0
+    report("masked", compare_chain(x, g, oracle_chain(x)))
+    assert np.all(g.out_tokens[g.out_tokens >= 0] < 7000)
+
+
+def test_stage_calls_equal_full_call():
+    x = synth.make_chain(204, 5, 4, 12000, "bf16", ragged=True, lam=0.2)
+    call = chain_call(x)
+    full = to_host(call.run())
+    call.row_stats()
+    split = to_host(call.accept_resample())
+    for a, b in zip(full, split):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_bitwise_deterministic():
+    x = synth.make_chain(205, 16, 8, 50000, "bf16", ragged=True, lam=0.3)
+    a = run_chain(x)
+    b = run_chain(x)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+# ---------------------------------------------------------------------------
+# data errors reported in the status word
+# ---------------------------------------------------------------------------
+
+
+def test_status_bad_token_and_length():
+    x = synth.make_chain(206, 3, 4, 1000, "fp32")
+    x.tokens[1, 2] = 1000 + 5
+    x.draft_len = np.array([4, 4, 9], dtype=np.int32)
+    g = run_chain(x)
+    flags = sv.decode_flags(int(g.status[0]))
+    assert "BAD_TOKEN" in flags and "BAD_LENGTH" in flags
+    assert g.accepted[1] <= 2 and g.accept_prob[1, 2] == 0.0
+    # request 2 is clamped to K = 4 and otherwise normal
+    x2 = synth.make_chain(206, 3, 4, 1000, "fp32")
+    ref = oracle_chain(x2, requests=[2])
+    if not ref.flagged[2]:
+        assert g.accepted[2] == ref.accepted[2]
+        np.testing.assert_array_equal(g.out_tokens[2], ref.out_tokens[2])
+
+
+def test_status_bad_row():
+    x = synth.make_chain(207, 2, 3, 1000, "fp32")
+    x.target[0, 1, 10] = np.nan
+    g = run_chain(x)
+    assert "BAD_ROW" in sv.decode_flags(int(g.status[0]))
+    assert g.accepted[0] <= 1
+    ref = oracle_chain(x, requests=[1])
+    compare_chain(x, g, ref, requests=[1])
+
+
+# ---------------------------------------------------------------------------
+# greedy and path tree verification on small random trees
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("seed,B,N,V,dtype,ints", [
+    (1, 6, 12, 50, "fp32", True), (2, 4, 30, 20000, "fp32", True), (3, 5, 20, 9000, "bf16", False),
+    (4, 3, 1, 4, "fp32", True), (5, 2, 200, 100, "bf16", True), (6, 8, 0, 500, "fp32", False),
+])
+def test_greedy_random_trees(seed, B, N, V, dtype, ints):
+    x = synth.make_random_tree(300 + seed, B, N, V, dtype, int_logits=ints)
+    g = run_greedy(x)
+    assert int(g.status[0]) == 0
+    acc, out, nodes = oracle.tree_greedy(x.widened(x.target), x.parent, x.node_token, x.Dmax)
+    np.testing.assert_array_equal(g.accepted, acc)
+    np.testing.assert_array_equal(g.out_tokens, out)
+    np.testing.assert_array_equal(g.accepted_nodes, nodes)
+
+
+def test_greedy_depth_cut_and_bad_parent():
+    x = synth.make_random_tree(311, 2, 10, 64, "fp32", int_logits=True, sharp=1e-4)
+    x.parent[0] = np.arange(10)                 # a chain: accepted as deep as tokens match
+    g = run_greedy(x, Dmax=2)
+    acc, out, nodes = oracle.tree_greedy(x.widened(x.target), x.parent, x.node_token, 12)
+    for b in range(2):
+        keep = min(acc[b], 2)
+        assert g.accepted[b] == keep
+        np.testing.assert_array_equal(g.accepted_nodes[b, :keep], nodes[b, :keep])
+    x.parent[1, 3] = 7                          # parent not below the node
+    g = run_greedy(x)
+    assert "BAD_TREE" in sv.decode_flags(int(g.status[0]))
+
+
+@pytest.mark.parametrize("seed,B,N,V,dtype,lam,T", [
+    (1, 6, 12, 3000, "fp32", 0.0, 1.0), (2, 4, 40, 20000, "bf16", 0.3, 0.8),
+    (3, 3, 5, 17, "fp32", 0.5, 1.2),
+])
+def test_path_random_trees(seed, B, N, V, dtype, lam, T):
+    x = synth.make_random_tree(400 + seed, B, N, V, dtype, sharp=1.0, lam=lam, temperature=T)
+    # path tokens must be draws of the draft at each path node's parent row for
+    # the law to hold; parity holds for any tokens
+    g = run_path(x)
+    assert int(g.status[0]) == 0
+    ref = oracle.tree_path(x.widened(x.target), x.widened(x.draft), x.node_token, x.path,
+                           x.u_accept, x.u_sample, x.lam, x.temperature)
+    report(f"path{seed}", compare_chain(x, g, ref, lengths=path_lengths(x)))
+
+
+# ---------------------------------------------------------------------------
+# the output law on the GPU: 10^6 requests at V = 6
+# ---------------------------------------------------------------------------
+
+
+def test_gpu_output_law_monte_carlo():
+    V, K, lam, T, n = 6, 2, 0.3, 0.8, 1_000_000
+    rng = np.random.default_rng(77)
+    zt = rng.normal(0.0, 1.5, (K + 1, V))
+    zq = zt[:K] + rng.normal(0.0, 1.0, (K, V))
+    zt[1, 2] = -np.inf
+    zt32, zq32 = zt.astype(np.float32), zq.astype(np.float32)
+    q = [scipy.special.softmax(zq32[i].astype(np.float64) / np.float32(T)) for i in range(K)]
+    p = [scipy.special.softmax(zt32[i].astype(np.float64) / np.float32(T)) for i in range(K + 1)]
+    tokens = np.stack([rng.choice(V, size=n, p=q[i]) for i in range(K)], axis=1).astype(np.int32)
+    x = synth.ChainInputs("mc", "fp32", np.broadcast_to(zt32, (n, K + 1, V)).copy(),
+                          np.broadcast_to(zq32, (n, K, V)).copy(), tokens, None,
+                          rng.random((n, K), dtype=np.float32), rng.random(n, dtype=np.float32),
+                          lam, T)
+    g = run_chain(x, ld=8)
+    lam32 = float(np.float32(lam))
+    pm = [(1 - lam32) * p[j] + lam32 * q[j] for j in range(K)]
+    alpha = [np.minimum(pm[j], q[j]).sum() for j in range(K)]
+
+    def chisq(obs, prob):
+        keep = prob > 0
+        assert np.all(obs[~keep] == 0)
+        exp = prob[keep] / prob[keep].sum() * obs[keep].sum()
+        return scipy.stats.chisquare(obs[keep], exp).pvalue
+
+    first = np.bincount(g.out_tokens[:, 0], minlength=V)
+    sel = g.accepted >= 1
+    second = np.bincount(g.out_tokens[sel, 1], minlength=V)
+    bonus = np.bincount(g.out_tokens[g.accepted == K, K], minlength=V)
+    nh = np.bincount(g.accepted, minlength=K + 1)
+    law_n = np.array([1 - alpha[0], alpha[0] * (1 - alpha[1]), alpha[0] * alpha[1]])
+    pv = [chisq(first, pm[0]), chisq(second, pm[1]), chisq(bonus, p[K]), chisq(nh, law_n)]
+    print(f"[parity] MC p-values {pv}", flush=True)
+    assert min(pv) > 0.01
