@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Throughput of the speculative-decoding verify step (libspecverify) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
+
+One step is one full verify call on one batch of seeded synthetic logits that
+already sit in HBM: for a chain workload both launches (row statistics, then
+accept / first rejection / residual-or-bonus resample / emit); for ``c5`` the
+greedy tree call.  ``R`` copies of the inputs (at least 1 GiB in all, four
+times the 256 MB Infinity Cache) are rotated so that every step reads HBM.
+
+Prints one JSON line.  ``roofline`` rates the row-statistics kernel (the
+dominant one) on its algorithmic bytes, 2 * V * bytes_per_logit per drafted
+position, over its average duration measured with HIP events on the launch
+stream; ``traffic`` comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+under ``profiles/`` when it was taken on the current kernel source, else null.
+``cpu_baseline`` times the fp64 oracle on the same host arrays.
+
+``--copy-calibration`` instead runs a plain 1 GiB device copy (the reference
+kernel for scaling the FETCH_SIZE / WRITE_SIZE counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verified draft positions/sec + achieved HBM GB/s (% of peak) at V=128256 bf16"
+UNIT = "verified positions/s"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+ROTATE_BYTES = 1 << 30
+KERNEL_SOURCES = ["sampling_spec_verify_amd/csrc/sv_chain.hip",
+                  "sampling_spec_verify_amd/csrc/sv_tree.hip",
+                  "sampling_spec_verify_amd/csrc/sv_device.hpp",
+                  "sampling_spec_verify_amd/csrc/sv_common.hpp"]
+COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_{kernel}_{workload}.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if still current."""
+    path = COUNTER_FILE.format(kernel=kernel, workload=workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    rec = json.loads(text[start + 7:end])
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="bound on the oracle's CPU time for cpu_baseline (0 disables)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 5}), flush=True)
+
+
+def device_copies(arr, dtype, R, torch):
+    import numpy as np
+    host = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16) if dtype == "bf16" else arr)
+    base = host.to("cuda:0")
+    if dtype == "bf16":
+        base = base.view(torch.bfloat16)
+    return [base] + [base.clone() for _ in range(R - 1)]
+
+
+def cpu_baseline_chain(x, seconds, gpu_out):
+    """Oracle over the batch's requests in order (cycling) for about `seconds`."""
+    import numpy as np
+
+    import oracle
+    t = x.widened(x.target)
+    d = x.widened(x.draft)
+    lens = x.lengths()
+    done, pos, flagged, mismatch = 0, 0, 0, 0
+    checked = set()
+    t0 = time.perf_counter()
+    while True:
+        b = done % x.B
+        k = int(lens[b])
+        r = oracle.chain_verify_one(t[b, :k + 1], d[b, :k], x.tokens[b, :k], x.u_accept[b, :k],
+                                    x.u_sample[b], x.lam, x.temperature)
+        pos += k
+        done += 1
+        if b not in checked:
+            checked.add(b)
+            tok = np.full(x.K + 1, -1, dtype=np.int32)
+            tok[:len(r.tokens)] = r.tokens
+            same = gpu_out[0][b] == r.accepted and np.array_equal(gpu_out[1][b], tok)
+            flagged += int(r.flagged)
+            mismatch += int(not same and not r.flagged)
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    sample = (f"{done} oracle request verifications ({pos} drafted positions) cycling over the "
+              f"{x.B} requests of the same seeded batch, fp64 numpy, one process")
+    return ({"value": pos / el, "unit": UNIT, "cores": 1, "kind": "oracle", "sample": sample,
+             "seconds": round(el, 2)},
+            {"requests_checked": len(checked), "flagged": flagged, "unflagged_mismatches": mismatch})
+
+
+def cpu_baseline_tree(x, seconds, gpu_out):
+    import numpy as np
+
+    import oracle
+    t = x.widened(x.target)
+    done, nodes, mismatch = 0, 0, 0
+    checked = set()
+    t0 = time.perf_counter()
+    while True:
+        b = done % x.B
+        r = oracle.tree_greedy_one(t[b], x.parent[b], x.node_token[b])
+        nodes += x.N
+        done += 1
+        if b not in checked:
+            checked.add(b)
+            tok = np.full(x.Dmax + 1, -1, dtype=np.int32)
+            tok[:len(r.tokens)] = r.tokens
+            mismatch += int(not (gpu_out[0][b] == r.accepted and np.array_equal(gpu_out[1][b], tok)))
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    sample = (f"{done} oracle greedy tree verifications ({nodes} nodes) cycling over the {x.B} "
+              f"trees of the same seeded batch, fp64 numpy, one process")
+    return ({"value": nodes / el, "unit": UNIT, "cores": 1, "kind": "oracle", "sample": sample,
+             "seconds": round(el, 2)},
+            {"requests_checked": len(checked), "unflagged_mismatches": mismatch})
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the verify step is data-parallel over requests and "
+              f"this build runs on a single MI355X; --gpus {args.gpus} is not supported.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    from sampling_spec_verify_amd import specverify as sv
+    from sampling_spec_verify_amd import synth
+
+    sv.lib()
+    x = synth.config(args.workload)
+    elem = 2 if x.dtype == "bf16" else 4
+    tree = args.workload == "c5"
+    if tree:
+        positions = x.B * x.N
+        algo_bytes = x.B * (x.N + 1) * x.V * elem
+        footprint = x.target.nbytes
+    else:
+        positions = x.positions()
+        algo_bytes = 2 * x.V * elem * positions
+        footprint = x.target.nbytes + x.draft.nbytes
+    R = max(2, min(512, math.ceil(ROTATE_BYTES / footprint)))
+
+    dev = "cuda:0"
+    tgts = device_copies(x.target, x.dtype, R, torch)
+    if tree:
+        par = torch.from_numpy(x.parent).to(dev)
+        ntok = torch.from_numpy(x.node_token).to(dev)
+        calls = [sv.TreeGreedyCall(tgts[i], par, ntok, x.Dmax) for i in range(R)]
+
+        def step(i, ev_a=None, ev_b=None):
+            c = calls[i % R]
+            if ev_a is not None:
+                ev_a.record()
+            c.run()
+            if ev_b is not None:
+                ev_b.record()
+    else:
+        drfs = device_copies(x.draft, x.dtype, R, torch)
+        tok = torch.from_numpy(x.tokens).to(dev)
+        ua = torch.from_numpy(x.u_accept).to(dev)
+        us = torch.from_numpy(x.u_sample).to(dev)
+        dl = None if x.draft_len is None else torch.from_numpy(x.draft_len).to(dev)
+        calls = [sv.ChainCall(tgts[i], drfs[i], tok, ua, us, x.lam, x.temperature, dl)
+                 for i in range(R)]
+
+        def step(i, ev_a=None, ev_b=None):
+            c = calls[i % R]
+            if ev_a is not None:
+                ev_a.record()
+            c.row_stats()
+            if ev_b is not None:
+                ev_b.record()
+            c.accept_resample()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    mid = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, ev[i], mid[i])
+    ev[K].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    gpu_ms = ev[0].elapsed_time(ev[K])
+    first_ms = np.array([ev[i].elapsed_time(mid[i]) for i in range(K)])
+    rest_ms = np.array([mid[i].elapsed_time(ev[i + 1]) for i in range(K)])
+    ms_per_step = wall * 1e3 / K
+    value = positions * K / wall
+    kern_ms = float(first_ms.mean())
+    achieved = algo_bytes / (kern_ms * 1e-3) / 1e9
+    kname = "row_argmax" if tree else "row_stats"
+    traffic = load_traffic(kname, args.workload)
+
+    out = calls[0].out
+    torch.cuda.synchronize()
+    status = int(out.status[0].item())
+    gpu_out = [o.cpu().numpy() for o in out]
+
+    cpu = None
+    parity = None
+    if args.cpu_seconds > 0:
+        if tree:
+            cpu, parity = cpu_baseline_tree(x, args.cpu_seconds, gpu_out)
+        else:
+            cpu, parity = cpu_baseline_chain(x, args.cpu_seconds, gpu_out)
+
+    config = {"workload": f"{args.workload}: {synth.CONFIGS[args.workload]}",
+              "B": x.B, "V": x.V, "logits": x.dtype,
+              "positions_per_step": positions, "buffer_sets_rotated": R}
+    if not tree:
+        config.update({"K": x.K, "ragged": x.draft_len is not None, "lambda": x.lam,
+                       "temperature": x.temperature})
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": config,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": kname, "algorithmic_bytes_per_launch": algo_bytes,
+                     "kernel_ms_mean": kern_ms, "kernel_ms_median": float(np.median(first_ms))},
+        "cpu_baseline": cpu,
+        "step_hbm_gbps": algo_bytes * K / (wall * 1e9),
+        "step_hbm_frac": algo_bytes * K / (wall * 1e9) / PEAK_HBM_GBS,
+        "gpu_ms_per_step": gpu_ms / K,
+        "second_launch_ms_mean": float(rest_ms.mean()),
+        "status_word": status,
+        "parity_sample": parity,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

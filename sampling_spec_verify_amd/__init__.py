@@ -3,6 +3,7 @@
 The compute path is the HIP library ``libspecverify.so`` (C ABI declared in
 ``include/specverify.h``); ``specverify`` is its ctypes binding.
 """
-from .specverify import (ChainCall, ChainOut, SpecVerifyError, TreeGreedyOut,  # noqa: F401
+from .specverify import (ChainCall, ChainOut, SpecVerifyError, TreeGreedyCall,  # noqa: F401
+                         TreeGreedyOut,
                          chain_verify, chain_workspace_bytes, decode_flags, lib, status_string,
                          tree_verify_greedy, tree_verify_path, tree_workspace_bytes)

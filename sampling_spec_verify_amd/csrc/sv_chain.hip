@@ -9,29 +9,36 @@
 //   "大模型推理的Speculative Decoding原理详解", "修改的拒绝采样", and the EAGLE
 //     explainer, "1. 为什么无损": the resample law is max(0, p - q), normalised.
 //
-// Two launches per call:
+// Three launches per call:
 //
 //  1. k_row_stats: one wavefront per (request, position, tensor, chunk) streams
 //     64 lanes x NV x 16 bytes of one drafted row with coalesced 16-byte loads
-//     and reduces it to (shift s, S = sum 2^(z c - s)) with c = log2(e)/T.
-//     Every drafted target and draft row is read exactly once.  Waves are
-//     independent (no LDS, no barrier); block 0 also clears the per-request
-//     completion counters and the status word used by launch 2.
+//     and reduces it to (shift s, S = sum 2^(z c - s)) with c = log2(e)/T; the
+//     wave whose chunk holds the drafted token also records its logit.  Every
+//     drafted target and draft row is read exactly once.  Waves are
+//     independent (no LDS, no barrier); block 0 also clears the status word.
 //
-//  2. k_accept_resample: grid (C2 chunks, B requests), 256 threads.  Every
-//     block first resolves its request (combines the row partials in fp64,
-//     gathers z(x_i), computes a_i in fp64, ballots the first rejection n),
-//     then reduces its chunk of the sampling row: the residual
-//     max(0, p_t - q) at row n (the same normalised law as max(0, p~ - q),
-//     since p~ - q = (1 - lambda)(p_t - q)), or the bonus softmax(z/T) at the
-//     request's last target row.  Chunk masses go to the workspace; the last
-//     block of the request (integer done-counter) scans them in fp64, finds
-//     the chunk holding u * W, re-reads that chunk (L2 / MALL resident),
-//     scans it in LDS and writes the outputs.
+//  2. k_resolve_mass: grid (B requests, C2 chunks) of 1024-thread blocks.
+//     Every block stages its request's row partials in LDS, combines them in
+//     fp64, computes every a_i in fp64 and ballots the first rejection n;
+//     block 0 writes every output but the sampled token.  Each block then
+//     reduces its chunk of the sampling row: the residual max(0, p_t - q) at
+//     row n (the same normalised law as max(0, p~ - q), since
+//     p~ - q = (1 - lambda)(p_t - q)), or the bonus softmax(z/T) at the
+//     request's last target row, to fp64 sums of its 32 pieces.
+//
+//  3. k_locate: one block per request scales the pieces to a common frame,
+//     finds the piece holding u * W with a monotone fp64 block scan, reloads
+//     that piece's 64 vectors and finds the token with a lane scan.
+//
+// Blocks never exchange data inside a launch, so no device-scope fences or
+// data atomics are needed; every reduction has a fixed order (bitwise
+// reproducible).
 //
 // Path mode reuses both launches with a row indirection: position j of a
 // request uses target and draft row n_j of its draft tree (n_0 = root).
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 
 #include <algorithm>
@@ -45,27 +52,18 @@ namespace sv {
 // request geometry
 // ---------------------------------------------------------------------------
 
-// Number of drafted positions of request b; data errors OR-ed into *flags.
-__device__ __forceinline__ int geo_positions(const Geo &g, int b, int *flags) {
+// Whether position i of request b is drafted (cheaper than counting them all).
+__device__ __forceinline__ bool geo_position_valid(const Geo &g, int b, int i) {
     if (g.path == nullptr) {
-        if (g.draft_len == nullptr) return g.P;
-        int k = g.draft_len[b];
-        if (k < 0 || k > g.P) {
-            *flags |= SV_DATA_BAD_LENGTH;
-            k = min(max(k, 0), g.P);
-        }
-        return k;
+        if (g.draft_len == nullptr) return i < g.P;
+        const int k = g.draft_len[b];
+        return i < min(max(k, 0), g.P);
     }
-    int d = 0;
-    for (; d < g.Pcap; ++d) {
+    for (int d = 0; d <= i; ++d) {
         const int v = g.path[int64_t(b) * g.P + d];
-        if (v == -1) break;
-        if (v < 1 || v > g.N) {
-            *flags |= SV_DATA_BAD_TREE;
-            break;
-        }
+        if (v < 1 || v > g.N) return false;
     }
-    return d;
+    return true;
 }
 
 // Row (within the request) of position i, for 0 <= i <= positions.
@@ -91,51 +89,34 @@ __device__ __forceinline__ const char *row_ptr(const Geo &g, int tensor, int b, 
 // launch 1: row statistics
 // ---------------------------------------------------------------------------
 
+// One job: wave-chunk c of one drafted row, reduced by one wavefront.
 template <class DT, int NV>
-__global__ __launch_bounds__(kBlock) void k_row_stats(ChainArgs a, int64_t n_jobs) {
-    if (blockIdx.x == 0) {
-        for (int i = threadIdx.x; i < a.B; i += kBlock) a.counters[i] = 0;
-        if (threadIdx.x == 0) *a.status = 0;
-    }
-    const int64_t job = int64_t(blockIdx.x) * kWaves + (threadIdx.x / kWave);
-    if (job >= n_jobs) return;
-    const int C1 = a.C1;
+__device__ __forceinline__ void row_chunk_stats(const ChainArgs &a, unsigned job) {
+    const unsigned C1 = static_cast<unsigned>(a.C1);
     const int c = static_cast<int>(job % C1);
-    int64_t rest = job / C1;
-    const int tensor = static_cast<int>(rest & 1);
+    unsigned rest = job / C1;
+    const int tensor = static_cast<int>(rest & 1u);
     rest >>= 1;
-    const int i = static_cast<int>(rest % a.g.Pcap);
-    const int b = static_cast<int>(rest / a.g.Pcap);
-    int flags = 0;
-    if (i >= geo_positions(a.g, b, &flags)) return;
+    const unsigned Pc = static_cast<unsigned>(a.g.Pcap);
+    const int i = static_cast<int>(rest % Pc);
+    const int b = static_cast<int>(rest / Pc);
+    if (!geo_position_valid(a.g, b, i)) return;
     const char *row = row_ptr(a.g, tensor, b, geo_row(a.g, b, i));
+    // the wave whose chunk holds the drafted token also gathers its logit
+    const int x = geo_token(a.g, b, i);
+    const bool own_x = x >= 0 && x < a.g.V && x / a.ch1 == c;
 
     constexpr int VEC = DT::kVec;
     const int lane = threadIdx.x & (kWave - 1);
     const int V = a.g.V;
-    const int64_t v0 = int64_t(c) * (kWave * NV);
+    const int v0 = c * (kWave * NV);
 
     u32x4 d[NV];
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {
-        const int64_t gv = v0 + n * kWave + lane;
-        if (gv * VEC < V) {
-            d[n] = load16(row + gv * 16);
-        } else {
-            d[n] = u32x4{DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord};
-        }
-    }
+    for (int n = 0; n < NV; ++n) d[n] = load_row_vec<DT>(row, v0 + n * kWave + lane, V);
     float f[NV][VEC];
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {
-        DT::unpack(d[n], f[n]);
-        const int64_t lim = int64_t(V) - (v0 + n * kWave + lane) * VEC;
-        if (lim < VEC) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                if (e >= lim) f[n][e] = -INFINITY;
-        }
-    }
+    for (int n = 0; n < NV; ++n) DT::unpack(d[n], f[n]);
     float m = -INFINITY;
 #pragma unroll
     for (int n = 0; n < NV; ++n)
@@ -163,20 +144,32 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(ChainArgs a, int64_t n_job
     if (lane == 0) {
         Part p;
         p.s = s_w;
-        p.pad = 0.0f;
+        p.z = own_x ? DT::load1(row, x) : 0.0f;
         p.S = S_w;
-        a.part1[((int64_t(b) * a.g.Pcap + i) * 2 + tensor) * C1 + c] = p;
+        a.part1[(int64_t(b) * a.g.Pcap + i) * 2 * a.C1 + int64_t(tensor) * a.C1 + c] = p;
     }
 }
 
+// One wavefront per job; the job index is made wave-uniform so that its
+// decode runs as 32-bit scalar arithmetic.  Jobs of undrafted positions exit
+// after a few instructions.
+template <class DT, int NV>
+__global__ __launch_bounds__(kBlock) void k_row_stats(ChainArgs a, int n_jobs) {
+    const int job = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves +
+                                                   static_cast<int>(threadIdx.x) / kWave);
+    if (job < n_jobs) row_chunk_stats<DT, NV>(a, static_cast<unsigned>(job));
+    // cleared last: a store ahead of the job's reads would keep the compiler
+    // from issuing them as scalar loads
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
+}
+
 // ---------------------------------------------------------------------------
-// launch 2: resolve + resample
+// launch 2: resolve + chunk masses; launch 3: inverse-CDF locate
 // ---------------------------------------------------------------------------
 
 enum SampleMode { kResidual = 0, kBonus = 1, kMixture = 2 };
 
 struct SampleCtx {
-    int mode;
     const char *row_t;      // target row of the sampling position
     const char *row_q;      // draft row (residual / mixture)
     float c_hi, c_lo;
@@ -190,67 +183,43 @@ __device__ __forceinline__ float log2_prob(float z, float c_hi, float c_lo, floa
     return fmaf(z, c_lo, fmaf(z, c_hi, -s_hi)) - s_lo;
 }
 
-// Weights of this thread's NV2 vectors of chunk `chunk` (elements past V get 0).
-// In bonus mode the block first finds the chunk maximum and uses the shift
-// s = max * c_hi (returned in *s_chunk; -inf when the chunk has no finite
-// element).  Every thread of the block must call this.
-template <class DT>
-__device__ void chunk_weights(const SampleCtx &S, int chunk, float (&w)[kNV2][DT::kVec],
-                              float *sh4, float *s_chunk) {
+// The sampling row is cut into chunks of kBlock2 lanes x NV2 vectors, one
+// chunk per block of launch 2.  Wave w of the block owns the contiguous
+// vectors [w * 64 * NV2, (w+1) * 64 * NV2) of the chunk and its lane l holds
+// vectors n * 64 + l, n < NV2 (coalesced per n).  A "piece" is one such
+// vector row (chunk, w, n): 64 contiguous vectors.  The inverse CDF runs in
+// element order: chunk, wave, n, lane, element.
+template <int NV2>
+__device__ __forceinline__ int64_t piece_vec(int chunk, int wv, int n, int lane) {
+    return int64_t(chunk) * (kBlock2 * NV2) + int64_t(wv) * (kWave * NV2) + int64_t(n) * kWave + lane;
+}
+
+template <class DT, int MODE>
+__device__ __forceinline__ void load_vec(const SampleCtx &S, int64_t gv, u32x4 &dt, u32x4 &dq) {
+    dt = load_row_vec<DT>(S.row_t, static_cast<int>(gv), S.V);
+    if (MODE != kBonus) dq = load_row_vec<DT>(S.row_q, static_cast<int>(gv), S.V);
+}
+
+// Weights of one 16-byte vector; elements past V hold -inf logits and weigh 0.
+// `s_use` is the bonus shift.
+template <class DT, int MODE>
+__device__ __forceinline__ void vec_weights(const SampleCtx &S, const u32x4 &dt, const u32x4 &dq,
+                                            int64_t e0, float s_use, float *w) {
     constexpr int VEC = DT::kVec;
-    const int64_t v0 = int64_t(chunk) * (kBlock * kNV2);
-    u32x4 dt[kNV2], dq[kNV2];
+    (void)e0;
+    float ft[VEC], fq[VEC];
+    DT::unpack(dt, ft);
+    if (MODE != kBonus) DT::unpack(dq, fq);
 #pragma unroll
-    for (int n = 0; n < kNV2; ++n) {
-        const int64_t gv = v0 + n * kBlock + threadIdx.x;
-        const bool ok = gv * VEC < S.V;
-        dt[n] = ok ? load16(S.row_t + gv * 16)
-                   : u32x4{DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord};
-        if (S.mode != kBonus)
-            dq[n] = ok ? load16(S.row_q + gv * 16)
-                       : u32x4{DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord};
-    }
-    float ft[kNV2][VEC], fq[kNV2][VEC];
-#pragma unroll
-    for (int n = 0; n < kNV2; ++n) {
-        DT::unpack(dt[n], ft[n]);
-        if (S.mode != kBonus) DT::unpack(dq[n], fq[n]);
-        const int64_t lim = int64_t(S.V) - (v0 + n * kBlock + threadIdx.x) * VEC;
-        if (lim < VEC) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                if (e >= lim) {
-                    ft[n][e] = -INFINITY;
-                    fq[n][e] = -INFINITY;
-                }
+    for (int e = 0; e < VEC; ++e) {
+        if (MODE == kBonus) {
+            w[e] = __builtin_amdgcn_exp2f(fmaf(ft[e], S.c_lo, fmaf(ft[e], S.c_hi, -s_use)));
+        } else {
+            const float pt = __builtin_amdgcn_exp2f(log2_prob(ft[e], S.c_hi, S.c_lo, S.st_hi, S.st_lo));
+            const float pq = __builtin_amdgcn_exp2f(log2_prob(fq[e], S.c_hi, S.c_lo, S.sq_hi, S.sq_lo));
+            w[e] = (MODE == kResidual) ? fmaxf(pt - pq, 0.0f) : fmaf(S.w_t, pt, S.w_q * pq);
         }
     }
-    if (S.mode == kBonus) {
-        float m = -INFINITY;
-#pragma unroll
-        for (int n = 0; n < kNV2; ++n)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) m = fmaxf(m, ft[n][e]);
-        m = block_max(m, sh4);
-        const float s = (m == -INFINITY) ? -INFINITY : m * S.c_hi;
-        const float s_use = (m == -INFINITY) ? 0.0f : s;
-        *s_chunk = s;
-#pragma unroll
-        for (int n = 0; n < kNV2; ++n)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                w[n][e] = __builtin_amdgcn_exp2f(fmaf(ft[n][e], S.c_lo, fmaf(ft[n][e], S.c_hi, -s_use)));
-        return;
-    }
-    *s_chunk = 0.0f;
-#pragma unroll
-    for (int n = 0; n < kNV2; ++n)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const float pt = __builtin_amdgcn_exp2f(log2_prob(ft[n][e], S.c_hi, S.c_lo, S.st_hi, S.st_lo));
-            const float pq = __builtin_amdgcn_exp2f(log2_prob(fq[n][e], S.c_hi, S.c_lo, S.sq_hi, S.sq_lo));
-            w[n][e] = (S.mode == kResidual) ? fmaxf(pt - pq, 0.0f) : fmaf(S.w_t, pt, S.w_q * pq);
-        }
 }
 
 template <int VEC>
@@ -261,62 +230,116 @@ __device__ __forceinline__ double vec_sum(const float *w) {
     return s;
 }
 
-// Mass of a chunk: the paged block scan's total (the same arithmetic the
-// locate step repeats, so both agree bitwise).
-template <class DT>
-__device__ double chunk_mass(const float (&w)[kNV2][DT::kVec], double *shd) {
-    double carry = 0.0;
-#pragma unroll
-    for (int n = 0; n < kNV2; ++n) carry = block_scan_d(vec_sum<DT::kVec>(w[n]), carry, shd).total;
-    return carry;
-}
-
-struct Resolve {
-    int K;          // drafted positions of the request
-    int n;          // accepted drafts
-    int flags;
-};
-
-// Shared state of launch 2.
 struct ResolveShared {
-    float s[2 * SV_MAX_POSITIONS];
-    double S[2 * SV_MAX_POSITIONS];
-    float zx[2 * SV_MAX_POSITIONS];
+    float s[2 * SV_MAX_POSITIONS];      // row shift
+    double S[2 * SV_MAX_POSITIONS];     // row sum of 2^(z c - s)
+    float zx[2 * SV_MAX_POSITIONS];     // logit of the drafted token
+    int row_bad[2 * SV_MAX_POSITIONS];
     double a[SV_MAX_POSITIONS];
     int x[SV_MAX_POSITIONS];
-    int row_bad[2 * SV_MAX_POSITIONS];
-    int n;
-    int flags;
+    int rowi[SV_MAX_POSITIONS + 1];     // request row of position i (i <= K)
+    int pathv[SV_MAX_POSITIONS];
+    float u[SV_MAX_POSITIONS];
+    float f[kWaves2];
+    int K, n, flags;
 };
 
-// Resolve request b: row statistics, acceptance probabilities, first rejection.
+// Resolve request b: positions, row statistics (from the staged partials of
+// launch 1, which also carry the drafted token's logit), acceptance
+// probabilities and the first rejection.  One parallel load round (path mode:
+// two).
 template <class DT>
-__device__ Resolve resolve_request(const ChainArgs &a, int b, ResolveShared &sh) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
-    int flags = 0;
-    const int K = geo_positions(a.g, b, &flags);
-    const int V = a.g.V;
-    for (int j = wv; j < 2 * K; j += kWaves) {
-        const int i = j >> 1, tensor = j & 1;
-        const Part *p = a.part1 + ((int64_t(b) * a.g.Pcap + i) * 2 + tensor) * a.C1;
+__device__ __forceinline__ void resolve_request(const ChainArgs &a, int b, ResolveShared &sh,
+                                                float *ps, double *pS, float *pz, bool staged) {
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wv = t / kWave;
+    const Geo &g = a.g;
+    const int P = g.P, Pc = g.Pcap, C1 = a.C1;
+    const int64_t pbase = int64_t(b) * Pc * 2 * C1;
+    if (staged) {
+        for (int idx = t; idx < 2 * Pc * C1; idx += kBlock2) {
+            const Part p = a.part1[pbase + idx];
+            ps[idx] = p.s;
+            pz[idx] = p.z;
+            pS[idx] = p.S;
+        }
+    }
+    if (t < Pc) {
+        sh.u[t] = a.u_accept[int64_t(b) * P + t];
+        if (g.path == nullptr) sh.x[t] = g.tokens[int64_t(b) * P + t];
+        else sh.pathv[t] = g.path[int64_t(b) * P + t];
+    }
+    if (t == 0 && g.path == nullptr) {
+        int fl = 0;
+        int k = P;
+        if (g.draft_len != nullptr) {
+            k = g.draft_len[b];
+            if (k < 0 || k > P) {
+                fl |= SV_DATA_BAD_LENGTH;
+                k = min(max(k, 0), P);
+            }
+        }
+        sh.K = k;
+        sh.flags = fl;
+    }
+    __syncthreads();
+    if (g.path != nullptr) {
+        if (t == 0) {
+            int d = 0, fl = 0;
+            for (; d < Pc; ++d) {
+                const int v = sh.pathv[d];
+                if (v == -1) break;
+                if (v < 1 || v > g.N) {
+                    fl |= SV_DATA_BAD_TREE;
+                    break;
+                }
+            }
+            sh.K = d;
+            sh.flags = fl;
+        }
+        __syncthreads();
+        if (t < sh.K) sh.x[t] = g.tokens[int64_t(b) * g.N + sh.pathv[t] - 1];
+        if (t <= sh.K) sh.rowi[t] = (t == 0) ? 0 : sh.pathv[t - 1];
+    } else if (t <= Pc) {
+        sh.rowi[t] = t;
+    }
+    __syncthreads();
+    const int K = sh.K;
+    // row statistics: combine the C1 chunk partials of every row in fp64
+#pragma unroll 1
+    for (int j = wv; j < 2 * K; j += kWaves2) {
         float smax = -INFINITY;
-        for (int c = lane; c < a.C1; c += kWave) smax = fmaxf(smax, p[c].s);
+#pragma unroll 1
+        for (int c = lane; c < C1; c += kWave)
+            smax = fmaxf(smax, staged ? ps[j * C1 + c] : a.part1[pbase + int64_t(j) * C1 + c].s);
         smax = wave_max(smax);
         double S = 0.0;
-        for (int c = lane; c < a.C1; c += kWave) {
-            const Part q = p[c];
-            if (q.s != -INFINITY) S += q.S * exp2(static_cast<double>(q.s) - static_cast<double>(smax));
+#pragma unroll 1
+        for (int c = lane; c < C1; c += kWave) {
+            float s;
+            double Sc;
+            if (staged) {
+                s = ps[j * C1 + c];
+                Sc = pS[j * C1 + c];
+            } else {
+                const Part p = a.part1[pbase + int64_t(j) * C1 + c];
+                s = p.s;
+                Sc = p.S;
+            }
+            if (s != -INFINITY) S += Sc * exp2(static_cast<double>(s) - static_cast<double>(smax));
         }
         S = wave_sum_d(S);
         if (lane == 0) {
+            const int x = sh.x[j >> 1];
+            float zx = NAN;
+            if (x >= 0 && x < g.V) {
+                const int cx = x / a.ch1;
+                zx = staged ? pz[j * C1 + cx] : a.part1[pbase + int64_t(j) * C1 + cx].z;
+            }
+            sh.zx[j] = zx;
             sh.s[j] = smax;
             sh.S[j] = S;
-            const int x = geo_token(a.g, b, i);
-            const bool tok_ok = x >= 0 && x < V;
-            const char *row = row_ptr(a.g, tensor, b, geo_row(a.g, b, i));
-            sh.zx[j] = tok_ok ? DT::load1(row, x) : NAN;
-            if (tensor == 0) sh.x[i] = x;
             sh.row_bad[j] = !(S > 0.0) || !isfinite(S) || !isfinite(smax);
         }
     }
@@ -328,7 +351,7 @@ __device__ Resolve resolve_request(const ChainArgs &a, int b, ResolveShared &sh)
             const int i = lane;
             const float zt = sh.zx[2 * i], zq = sh.zx[2 * i + 1];
             double acc_p;
-            if (!(sh.x[i] >= 0 && sh.x[i] < V)) {
+            if (!(sh.x[i] >= 0 && sh.x[i] < g.V)) {
                 fl |= SV_DATA_BAD_TOKEN;
                 acc_p = 0.0;
             } else if (sh.row_bad[2 * i] || sh.row_bad[2 * i + 1]) {
@@ -351,216 +374,299 @@ __device__ Resolve resolve_request(const ChainArgs &a, int b, ResolveShared &sh)
                 }
             }
             sh.a[i] = acc_p;
-            const double u = static_cast<double>(a.u_accept[int64_t(b) * a.g.P + i]);
-            rej = !(u < acc_p);
+            rej = !(static_cast<double>(sh.u[i]) < acc_p);
         }
         const unsigned long long mask = __ballot(rej);
-        // OR the per-lane flags
         int fl_all = fl;
         for (int off = 1; off < kWave; off <<= 1) fl_all |= __shfl_xor(fl_all, off, kWave);
         if (lane == 0) {
             sh.n = mask ? (__ffsll(static_cast<long long>(mask)) - 1) : K;
-            sh.flags = flags | fl_all;
+            sh.flags |= fl_all;
         }
     }
     __syncthreads();
-    Resolve r;
-    r.K = K;
-    r.n = sh.n;
-    r.flags = sh.flags;
-    return r;
 }
 
-// Sampling context of request b after the resolve.
-template <class DT>
-__device__ SampleCtx make_ctx(const ChainArgs &a, int b, const Resolve &r, const ResolveShared &sh) {
+// Sampling context of request b from its hand-over record.
+__device__ __forceinline__ SampleCtx sample_ctx(const ChainArgs &a, int b, const ReqRecord &r) {
     SampleCtx S;
     S.V = a.g.V;
     S.c_hi = a.c_hi;
     S.c_lo = a.c_lo;
     S.w_t = 1.0f - a.lam;
     S.w_q = a.lam;
-    S.st_hi = S.st_lo = S.sq_hi = S.sq_lo = 0.0f;
-    if (r.n < r.K) {
-        const int row = geo_row(a.g, b, r.n);
-        S.mode = kResidual;
-        S.row_t = row_ptr(a.g, 0, b, row);
-        S.row_q = row_ptr(a.g, 1, b, row);
-        // p(v) = 2^(z c - sigma), sigma = s + log2 S, split into hi + lo floats
-        const double st = static_cast<double>(sh.s[2 * r.n]) + log2(sh.S[2 * r.n]);
-        const double sq = static_cast<double>(sh.s[2 * r.n + 1]) + log2(sh.S[2 * r.n + 1]);
-        S.st_hi = static_cast<float>(st);
-        S.st_lo = static_cast<float>(st - static_cast<double>(S.st_hi));
-        S.sq_hi = static_cast<float>(sq);
-        S.sq_lo = static_cast<float>(sq - static_cast<double>(S.sq_hi));
-    } else {
-        S.mode = kBonus;
-        S.row_t = row_ptr(a.g, 0, b, geo_row(a.g, b, r.K));
-        S.row_q = nullptr;
-    }
+    S.row_t = row_ptr(a.g, 0, b, r.row);
+    S.row_q = (r.mode != kBonus) ? row_ptr(a.g, 1, b, r.row) : nullptr;
+    S.st_hi = r.st_hi;
+    S.st_lo = r.st_lo;
+    S.sq_hi = r.sq_hi;
+    S.sq_lo = r.sq_lo;
     return S;
 }
 
-struct LocateShared {
-    float f4[kWaves];
-    double d4[kWaves];
-    int found;
-    int lastpos;
-    double excl;
-    double scale;
-};
-
-// Total sampling mass W of request b from its chunk records, and (when
-// t >= 0) the chunk c* whose prefix interval holds t.
-__device__ double chunk_scan(const ChainArgs &a, int b, double t, LocateShared &L) {
-    const Part *rec = a.part2 + int64_t(b) * a.C2;
-    float smax = -INFINITY;
-    for (int c = threadIdx.x; c < a.C2; c += kBlock) smax = fmaxf(smax, rec[c].s);
-    smax = block_max(smax, L.f4);
-    double carry = 0.0;
-    for (int base = 0; base < a.C2; base += kBlock) {
-        const int c = base + threadIdx.x;
-        double m = 0.0, scale = 0.0;
-        if (c < a.C2) {
-            const Part p = rec[c];
-            if (p.s != -INFINITY) {
-                scale = exp2(static_cast<double>(p.s) - static_cast<double>(smax));
-                m = p.S * scale;
-            }
+// Chunk c of the sampling row: the bonus shift (largest logit times c_hi,
+// block-wide) and the fp64 wave sum of every piece, written to the chunk
+// record: [shift, unused, piece sums (wave-major)].  Every thread must call this.
+template <class DT, int MODE, int NV2>
+__device__ __forceinline__ void chunk_pieces(const SampleCtx &S, int c, double *rec, float *f16) {
+    constexpr int VEC = DT::kVec;
+    const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    u32x4 dt[NV2], dq[NV2];
+#pragma unroll
+    for (int n = 0; n < NV2; ++n) load_vec<DT, MODE>(S, piece_vec<NV2>(c, wv, n, lane), dt[n], dq[n]);
+    float s_use = 0.0f, s_rec = 0.0f;
+    if (MODE == kBonus) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int n = 0; n < NV2; ++n) {
+            float f[VEC];
+            DT::unpack(dt[n], f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) m = fmaxf(m, f[e]);
         }
-        const Scan sc = block_scan_d(m, carry, L.d4);
-        if (t >= 0.0 && c < a.C2 && sc.excl <= t && t < sc.incl) {
-            L.found = c;
-            L.excl = sc.excl;
-            L.scale = scale;
-        }
-        carry = sc.total;
+        m = wave_max(m);
+        if (lane == 0) f16[wv] = m;
+        __syncthreads();
+        m = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves2; ++w) m = fmaxf(m, f16[w]);
+        s_rec = (m == -INFINITY) ? -INFINITY : m * S.c_hi;
+        s_use = (m == -INFINITY) ? 0.0f : s_rec;
     }
-    __syncthreads();
-    return carry;
+#pragma unroll
+    for (int n = 0; n < NV2; ++n) {
+        float w[VEC];
+        vec_weights<DT, MODE>(S, dt[n], dq[n], piece_vec<NV2>(c, wv, n, lane) * VEC, s_use, w);
+        const double ws = wave_sum_d(vec_sum<VEC>(w));
+        if (lane == 0) rec[2 + wv * NV2 + n] = ws;
+    }
+    if (threadIdx.x == 0) rec[0] = static_cast<double>(s_rec);
 }
 
-// Token of the sampling row: the first index whose running mass exceeds
-// u * W.  Returns -1 when the row has no positive finite mass.
-template <class DT>
-__device__ int locate(const ChainArgs &a, const SampleCtx &S, int b, double u, LocateShared &L) {
+template <class DT, int NV2>
+__global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int staged) {
+    __shared__ ResolveShared sh;
+    extern __shared__ double dyn[];
+    const int b = blockIdx.x;
+    const int c = blockIdx.y;
+    const int stage_n = staged ? 2 * a.g.Pcap * a.C1 : 0;
+    double *pS = dyn;
+    float *ps = reinterpret_cast<float *>(dyn + stage_n);
+    float *pz = ps + stage_n;
+    resolve_request<DT>(a, b, sh, ps, pS, pz, staged != 0);
+
+    const int n = sh.n, K = sh.K;
+    ReqRecord r;
+    r.n = n;
+    r.st_hi = r.st_lo = r.sq_hi = r.sq_lo = 0.0f;
+    if (n < K) {
+        r.mode = kResidual;
+        r.row = sh.rowi[n];
+        r.rows_ok = !sh.row_bad[2 * n] && !sh.row_bad[2 * n + 1];
+        // p(v) = 2^(z c - sigma), sigma = s + log2 S, split into hi + lo floats
+        const double st = static_cast<double>(sh.s[2 * n]) + log2(sh.S[2 * n]);
+        const double sq = static_cast<double>(sh.s[2 * n + 1]) + log2(sh.S[2 * n + 1]);
+        r.st_hi = static_cast<float>(st);
+        r.st_lo = static_cast<float>(st - static_cast<double>(r.st_hi));
+        r.sq_hi = static_cast<float>(sq);
+        r.sq_lo = static_cast<float>(sq - static_cast<double>(r.sq_hi));
+    } else {
+        r.mode = kBonus;
+        r.row = sh.rowi[K];
+        r.rows_ok = 1;
+    }
+    if (c == 0) {
+        // every output but the sampled token
+        const int P = a.g.P;
+        const int t = threadIdx.x;
+        if (t <= P && t != n) a.out_tokens[int64_t(b) * (P + 1) + t] = (t < n) ? sh.x[t] : -1;
+        if (a.accept_prob != nullptr && t < P)
+            a.accept_prob[int64_t(b) * P + t] = (t < K) ? static_cast<float>(sh.a[t]) : 0.0f;
+        if (t == 0) {
+            a.accepted[b] = n;
+            a.rec[b] = r;
+            if (sh.flags) atomicOr(a.status, sh.flags);
+        }
+    }
+    const SampleCtx S = sample_ctx(a, b, r);
+    double *cr = a.chunks + (int64_t(b) * a.C2 + c) * a.rec_stride;
+    if (r.mode == kResidual) chunk_pieces<DT, kResidual, NV2>(S, c, cr, sh.f);
+    else chunk_pieces<DT, kBonus, NV2>(S, c, cr, sh.f);
+}
+
+struct LocateShared {
+    double d4[kWaves];
+    float f4[kWaves];
+    int pstar, tok, lastpos;
+    double excl, scale, W;
+};
+
+// Inverse CDF over the request's pieces: scale every chunk to the common
+// frame 2^(-max shift), fp64 block scan over the pieces in element order,
+// then a lane scan inside the chosen piece.  Every thread must call this;
+// returns -1 when the row carries no positive mass.
+template <class DT, int MODE, int NV2>
+__device__ __forceinline__ int locate(const ChainArgs &a, const SampleCtx &S, int b, double u,
+                                      LocateShared &L) {
     constexpr int VEC = DT::kVec;
+    constexpr int kPieces = kWaves2 * NV2;
+    const double *cr = a.chunks + int64_t(b) * a.C2 * a.rec_stride;
+    auto rec_s = [&](int c) -> float { return static_cast<float>(cr[int64_t(c) * a.rec_stride]); };
+    auto rec_m = [&](int p) -> double { return cr[int64_t(p / kPieces) * a.rec_stride + 2 + p % kPieces]; };
+    const int np = a.C2 * kPieces;
+    float smax = -INFINITY;
+    for (int c = threadIdx.x; c < a.C2; c += kBlock) smax = fmaxf(smax, rec_s(c));
+    smax = block_max(smax, L.f4);
+    auto scale_of = [&](int c) -> double {
+        const float s = rec_s(c);
+        return (s == -INFINITY) ? 0.0 : exp2(static_cast<double>(s) - static_cast<double>(smax));
+    };
+    // pass 1: total mass
+    double carry = 0.0;
+    for (int base = 0; base < np; base += kBlock) {
+        const int p = base + threadIdx.x;
+        const double m = (p < np) ? rec_m(p) * scale_of(p / kPieces) : 0.0;
+        carry = block_scan_d(m, carry, L.d4).total;
+    }
+    const double W = carry;
+    if (!(W > 0.0) || !isfinite(W)) return -1;
+    const double t = u * W;
+    // pass 2: the piece whose prefix interval holds t (unique: the inclusive
+    // prefixes are monotone and every exclusive prefix is the previous one)
     if (threadIdx.x == 0) {
-        L.found = -1;
+        L.pstar = -1;
+        L.tok = INT_MAX;
         L.lastpos = -1;
     }
     __syncthreads();
-    const double W = chunk_scan(a, b, -1.0, L);
-    if (!(W > 0.0) || !isfinite(W)) return -1;
-    const double t = u * W;
-    chunk_scan(a, b, t, L);
-    const int cs = L.found;
-    if (cs < 0) return -1;
-    const double tc = (t - L.excl) / L.scale;
-    float w[kNV2][VEC];
-    float s_unused;
-    chunk_weights<DT>(S, cs, w, L.f4, &s_unused);
-    if (threadIdx.x == 0) L.found = INT_MAX;
+    carry = 0.0;
+    for (int base = 0; base < np; base += kBlock) {
+        const int p = base + threadIdx.x;
+        double sc = 0.0, m = 0.0;
+        if (p < np) {
+            sc = scale_of(p / kPieces);
+            m = rec_m(p) * sc;
+        }
+        const Scan s = block_scan_d(m, carry, L.d4);
+        if (p < np && s.excl <= t && t < s.incl) {
+            L.pstar = p;
+            L.excl = s.excl;
+            L.scale = sc;
+        }
+        carry = s.total;
+    }
     __syncthreads();
-    const int64_t v0 = int64_t(cs) * (kBlock * kNV2);
-    double carry = 0.0;
-    int mylast = -1;
+    const int ps = L.pstar;
+    if (ps < 0) return -1;
+    const int cs = ps / kPieces, wsv = (ps % kPieces) / NV2, ns = ps % NV2;
+    const double tp = (t - L.excl) / L.scale;        // target inside the piece, chunk frame
+    const float s_rec = rec_s(cs);
+    const float s_use = (MODE == kBonus && s_rec != -INFINITY) ? s_rec : 0.0f;
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        const int64_t gv = piece_vec<NV2>(cs, wsv, ns, lane);
+        u32x4 dt, dq;
+        load_vec<DT, MODE>(S, gv, dt, dq);
+        float w[VEC];
+        vec_weights<DT, MODE>(S, dt, dq, gv * VEC, s_use, w);
+        double x = vec_sum<VEC>(w);
 #pragma unroll
-    for (int n = 0; n < kNV2; ++n) {
-        const Scan sc = block_scan_d(vec_sum<VEC>(w[n]), carry, L.d4);
-        const int64_t e0 = (v0 + n * kBlock + threadIdx.x) * VEC;
-        if (sc.excl <= tc && tc < sc.incl) {
-            double cum = sc.excl;
-            int pick = -1, last = -1;
+        for (int off = 1; off < kWave; off <<= 1) {
+            const double o = __shfl_up(x, off, kWave);
+            if (lane >= off) x += o;
+        }
+        const double prev = __shfl_up(x, 1, kWave);
+        const double excl = (lane == 0) ? 0.0 : prev;
+        int last = -1;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            if (w[e] > 0.0f) last = e;
+        if (last >= 0) atomicMax(&L.lastpos, static_cast<int>(gv * VEC + last));
+        if (excl <= tp && tp < x) {
+            double cum = excl;
+            int pick = -1;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                if (w[n][e] > 0.0f) {
-                    last = e;
-                    cum += static_cast<double>(w[n][e]);
-                    if (pick < 0 && cum > tc) pick = e;
+                if (w[e] > 0.0f) {
+                    cum += static_cast<double>(w[e]);
+                    if (pick < 0 && cum > tp) pick = e;
                 }
             }
             if (pick < 0) pick = last;
-            if (pick >= 0) atomicMin(&L.found, static_cast<int>(e0 + pick));
+            if (pick >= 0) atomicMin(&L.tok, static_cast<int>(gv * VEC + pick));
         }
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            if (w[n][e] > 0.0f) mylast = static_cast<int>(e0 + e);
-        carry = sc.total;
     }
-    if (mylast >= 0) atomicMax(&L.lastpos, mylast);
     __syncthreads();
-    const int tok = (L.found != INT_MAX) ? L.found : L.lastpos;
+    // rounding can hide the crossing inside the piece: then its last positive
+    // weight is taken
+    const int tok = (L.tok != INT_MAX) ? L.tok : L.lastpos;
     __syncthreads();
     return tok;
 }
 
+// Zero residual mass after a rejection (reachable only through rounding):
+// draw from p~ = (1 - lambda) p_t + lambda q at that row instead.  A compact
+// two-pass scan over 256-element pages in index order (rare path: small code
+// rather than speed).
 template <class DT>
-__global__ __launch_bounds__(kBlock) void k_accept_resample(ChainArgs a) {
-    __shared__ ResolveShared sh;
-    __shared__ LocateShared L;
-    __shared__ int sh_last;
-    const int b = blockIdx.x;
-    const int c = blockIdx.y;
-    const Resolve r = resolve_request<DT>(a, b, sh);
-    SampleCtx S = make_ctx<DT>(a, b, r, sh);
-
-    float w[kNV2][DT::kVec];
-    float s_chunk;
-    chunk_weights<DT>(S, c, w, L.f4, &s_chunk);
-    const double M = chunk_mass<DT>(w, L.d4);
-    if (threadIdx.x == 0) {
-        Part p;
-        p.s = s_chunk;
-        p.pad = 0.0f;
-        p.S = M;
-        a.part2[int64_t(b) * a.C2 + c] = p;
-        __threadfence();
-        const int prev = atomicAdd(&a.counters[b], 1);
-        sh_last = (prev == a.C2 - 1);
+__device__ __forceinline__ int sample_mixture(const SampleCtx &S, double u, LocateShared &L) {
+    const int V = S.V;
+    auto weight = [&](int v) -> float {
+        if (v >= V) return 0.0f;
+        const float pt = __builtin_amdgcn_exp2f(log2_prob(DT::load1(S.row_t, v), S.c_hi, S.c_lo, S.st_hi, S.st_lo));
+        const float pq = __builtin_amdgcn_exp2f(log2_prob(DT::load1(S.row_q, v), S.c_hi, S.c_lo, S.sq_hi, S.sq_lo));
+        return fmaf(S.w_t, pt, S.w_q * pq);
+    };
+    double carry = 0.0;
+#pragma unroll 1
+    for (int base = 0; base < V; base += kBlock)
+        carry = block_scan_d(static_cast<double>(weight(base + threadIdx.x)), carry, L.d4).total;
+    const double W = carry;
+    if (!(W > 0.0) || !isfinite(W)) return -1;
+    const double t = u * W;
+    if (threadIdx.x == 0) L.tok = -1;
+    __syncthreads();
+    carry = 0.0;
+#pragma unroll 1
+    for (int base = 0; base < V; base += kBlock) {
+        const float w = weight(base + threadIdx.x);
+        const Scan sc = block_scan_d(static_cast<double>(w), carry, L.d4);
+        if (w > 0.0f && sc.excl <= t && t < sc.incl) L.tok = base + threadIdx.x;
+        carry = sc.total;
+        __syncthreads();
+        if (L.tok >= 0) break;
+    }
+    if (L.tok < 0 && threadIdx.x == 0) {   // t at the very top by rounding: last positive weight
+        for (int v = V - 1; v >= 0; --v)
+            if (weight(v) > 0.0f) {
+                L.tok = v;
+                break;
+            }
     }
     __syncthreads();
-    if (!sh_last) return;
-    __threadfence();
+    return L.tok;
+}
 
-    int flags = r.flags;
+template <class DT, int NV2>
+__global__ __launch_bounds__(kBlock) void k_locate(ChainArgs a) {
+    __shared__ LocateShared L;
+    const int b = blockIdx.x;
+    const ReqRecord r = a.rec[b];
+    const SampleCtx S = sample_ctx(a, b, r);
     const double u = static_cast<double>(a.u_sample[b]);
-    int tok = locate<DT>(a, S, b, u, L);
-    if (tok < 0 && S.mode == kResidual) {
-        // Zero residual mass after a rejection (possible only through
-        // rounding): draw from p~ at that row instead.
-        const bool rows_ok = !sh.row_bad[2 * r.n] && !sh.row_bad[2 * r.n + 1];
-        if (rows_ok) {
-            flags |= SV_DATA_FALLBACK;
-            S.mode = kMixture;
-            for (int cc = 0; cc < a.C2; ++cc) {
-                chunk_weights<DT>(S, cc, w, L.f4, &s_chunk);
-                const double Mc = chunk_mass<DT>(w, L.d4);
-                if (threadIdx.x == 0) {
-                    Part p;
-                    p.s = 0.0f;
-                    p.pad = 0.0f;
-                    p.S = Mc;
-                    a.part2[int64_t(b) * a.C2 + cc] = p;
-                }
-            }
-            __threadfence();
-            __syncthreads();
-            tok = locate<DT>(a, S, b, u, L);
-        }
+    int flags = 0;
+    int tok = (r.mode == kResidual) ? locate<DT, kResidual, NV2>(a, S, b, u, L)
+                                    : locate<DT, kBonus, NV2>(a, S, b, u, L);
+    if (tok < 0 && r.mode == kResidual && r.rows_ok) {
+        flags |= SV_DATA_FALLBACK;
+        tok = sample_mixture<DT>(S, u, L);
     }
-    if (tok < 0) flags |= SV_DATA_BAD_ROW;
-
-    const int P = a.g.P;
-    const int t = threadIdx.x;
-    if (t <= P) {
-        const int v = (t < r.n) ? sh.x[t] : (t == r.n ? tok : -1);
-        a.out_tokens[int64_t(b) * (P + 1) + t] = v;
+    if (tok < 0) {
+        tok = -1;
+        flags |= SV_DATA_BAD_ROW;
     }
-    if (a.accept_prob != nullptr && t < P)
-        a.accept_prob[int64_t(b) * P + t] = (t < r.K) ? static_cast<float>(sh.a[t]) : 0.0f;
-    if (t == 0) {
-        a.accepted[b] = r.n;
+    if (threadIdx.x == 0) {
+        a.out_tokens[int64_t(b) * (a.g.P + 1) + r.n] = tok;
         if (flags) atomicOr(a.status, flags);
     }
 }
@@ -607,7 +713,7 @@ sv_status validate(const ChainReq &q) {
     const int eb = elem_bytes(q.dtype);
     if (eb == 0) return SV_EDTYPE;
     if (q.B < 0 || q.P < 0 || q.P > SV_MAX_POSITIONS || q.V < 1 || q.N < 0 ||
-        q.N > SV_MAX_TREE_NODES || q.B > (1 << 30))
+        q.N > SV_MAX_TREE_NODES || q.B > (1 << 30) || c2_for(q.V, 16 / eb, 2) > kMaxC2)
         return SV_EINVAL;
     sv_status st = check_scalars(q.lam, q.T);
     if (st != SV_OK) return st;
@@ -623,6 +729,7 @@ sv_status validate(const ChainReq &q) {
             return SV_ENULL;
         }
     }
+    if (int64_t(q.B) * pcap(q) * 2 * c1_for(q.V, kMinNV, kMinVec) >= (int64_t(1) << 31)) return SV_EINVAL;
     const ChainLayout L = chain_layout(q.B, pcap(q), q.V);
     if (!q.ws || !aligned16(q.ws) || q.ws_bytes < static_cast<size_t>(L.total)) return SV_EWORKSPACE;
     return SV_OK;
@@ -654,12 +761,15 @@ ChainArgs make_args(const ChainReq &q, int vec, int nv) {
     a.accepted = q.accepted;
     a.out_tokens = q.out_tokens;
     a.accept_prob = q.accept_prob;
-    a.counters = reinterpret_cast<int32_t *>(ws + L.counters);
     a.status = q.status ? q.status : reinterpret_cast<int32_t *>(ws + L.status);
     a.part1 = reinterpret_cast<Part *>(ws + L.part1);
-    a.part2 = reinterpret_cast<Part *>(ws + L.part2);
+    a.rec = reinterpret_cast<ReqRecord *>(ws + L.rec);
+    a.chunks = reinterpret_cast<double *>(ws + L.chunks);
     a.C1 = c1_for(q.V, nv, vec);
-    a.C2 = c2_for(q.V, vec);
+    a.ch1 = 64 * nv * vec;
+    a.NV2 = choose_nv2(q.B, q.V, vec);
+    a.C2 = c2_for(q.V, vec, a.NV2);
+    a.rec_stride = chunk_rec_doubles(a.NV2);
     return a;
 }
 
@@ -668,10 +778,8 @@ sv_status run_typed(const ChainReq &q, int which) {
     const int nv = choose_nv(q.B, pcap(q), q.V, DT::kVec);
     const ChainArgs a = make_args(q, DT::kVec, nv);
     if (which & 1) {
-        const int64_t jobs = int64_t(q.B) * a.g.Pcap * 2 * a.C1;
-        const int64_t blocks = jobs > 0 ? cdiv(jobs, kWaves) : 1;
-        if (blocks > 0x7fffffffLL) return SV_EINVAL;
-        const dim3 grid(static_cast<unsigned>(blocks));
+        const int jobs = static_cast<int>(int64_t(q.B) * a.g.Pcap * 2 * a.C1);
+        const dim3 grid(static_cast<unsigned>(jobs > 0 ? cdiv(jobs, kWaves) : 1));
         if (nv == 8)
             hipLaunchKernelGGL((k_row_stats<DT, 8>), grid, dim3(kBlock), 0, q.stream, a, jobs);
         else if (nv == 4)
@@ -681,8 +789,21 @@ sv_status run_typed(const ChainReq &q, int which) {
         if (hipGetLastError() != hipSuccess) return SV_EHIP;
     }
     if (which & 2) {
+        const int64_t stage_n = int64_t(2) * a.g.Pcap * a.C1;
+        const int staged = stage_n <= kStageMax ? 1 : 0;
+        const size_t lds = staged ? static_cast<size_t>(stage_n) * (sizeof(double) + 2 * sizeof(float)) : 0;
         const dim3 grid(static_cast<unsigned>(q.B), static_cast<unsigned>(a.C2));
-        hipLaunchKernelGGL((k_accept_resample<DT>), grid, dim3(kBlock), 0, q.stream, a);
+        const dim3 gridB(static_cast<unsigned>(q.B));
+        if (a.NV2 == 8) {
+            hipLaunchKernelGGL((k_resolve_mass<DT, 8>), grid, dim3(kBlock2), lds, q.stream, a, staged);
+            hipLaunchKernelGGL((k_locate<DT, 8>), gridB, dim3(kBlock), 0, q.stream, a);
+        } else if (a.NV2 == 4) {
+            hipLaunchKernelGGL((k_resolve_mass<DT, 4>), grid, dim3(kBlock2), lds, q.stream, a, staged);
+            hipLaunchKernelGGL((k_locate<DT, 4>), gridB, dim3(kBlock), 0, q.stream, a);
+        } else {
+            hipLaunchKernelGGL((k_resolve_mass<DT, 2>), grid, dim3(kBlock2), lds, q.stream, a, staged);
+            hipLaunchKernelGGL((k_locate<DT, 2>), gridB, dim3(kBlock), 0, q.stream, a);
+        }
         if (hipGetLastError() != hipSuccess) return SV_EHIP;
     }
     return SV_OK;

@@ -17,7 +17,7 @@ namespace sv {
 // chunk without any finite element.
 struct alignas(16) Part {
     float s;
-    float pad;
+    float z;        // the drafted token's logit, in the partial of the chunk holding it
     double S;
 };
 
@@ -27,6 +27,15 @@ struct alignas(16) ArgPart {
     int idx;
     int nan;
     int pad;
+};
+
+// Per-request hand-over from launch 2 to launch 3 of a chain call.
+struct alignas(16) ReqRecord {
+    int n;          // accepted drafts
+    int mode;       // residual (0) or bonus (1)
+    int row;        // request row of the sampling position
+    int rows_ok;    // the residual rows have valid statistics
+    float st_hi, st_lo, sq_hi, sq_lo;   // log2 normaliser shifts (target, draft)
 };
 
 // Request geometry of the chain and path calls.
@@ -58,11 +67,14 @@ struct ChainArgs {
     int32_t *out_tokens;          // [B, P+1]
     float *accept_prob;           // [B, P] or NULL
     int32_t *status;              // [1]
-    int32_t *counters;            // [B] workspace
-    Part *part1;                  // [B, Pcap, 2, C1] workspace
-    Part *part2;                  // [B, C2] workspace
+    Part *part1;                  // [B, Pcap, 2, C1] workspace: row partials
+    ReqRecord *rec;               // [B] workspace: per-request hand-over
+    double *chunks;               // [B, C2, rec_stride] workspace: sampling-chunk records
     int C1;                       // wave-chunks per row in the row-stats pass
-    int C2;                       // block-chunks per row in the sampling pass
+    int ch1;                      // elements per row-stats chunk
+    int NV2;                      // vectors per lane per sampling chunk (2, 4 or 8)
+    int C2;                       // chunks per row in the sampling pass
+    int rec_stride;               // doubles per chunk record: shift, pad, 16 * NV2 piece sums
 };
 
 struct TreeArgs {
@@ -83,30 +95,58 @@ struct TreeArgs {
 // tiling
 // ---------------------------------------------------------------------------
 
-constexpr int kNV2 = 2;                       // vectors per thread in the sampling pass
+constexpr int kBlock2 = 1024;                 // threads of a resolve / mass block
+constexpr int kWaves2 = kBlock2 / 64;
+constexpr int kMaxC2 = 128;                   // sampling chunks per row at NV2 = 2 (bounds V)
 constexpr int kMinVec = 4;                    // fp32: 4 elements per 16-byte vector
 constexpr int kMinNV = 2;                     // smallest row-stats vectors per lane
+constexpr int kStageMax = 2048;               // row partials staged in LDS per request
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 // Row-stats wave-chunk: 64 lanes x NV vectors x VEC elements.
 inline int c1_for(int V, int NV, int vec) { return static_cast<int>(cdiv(V, 64LL * NV * vec)); }
-inline int c2_for(int V, int vec) { return static_cast<int>(cdiv(V, 256LL * kNV2 * vec)); }
+inline int c2_for(int V, int vec, int nv2) {
+    return static_cast<int>(cdiv(V, int64_t(kBlock2) * nv2 * vec));
+}
+
+// Vectors per lane of a sampling chunk: the smallest of 2, 4, 8 that keeps
+// the chunk grid of launch 2 within one block per compute unit (256), as far
+// as larger chunks still help.
+inline int choose_nv2(int B, int V, int vec) {
+    int nv2 = 2;
+    while (nv2 < 8 && int64_t(B) * c2_for(V, vec, nv2) > 256 &&
+           c2_for(V, vec, 2 * nv2) < c2_for(V, vec, nv2))
+        nv2 *= 2;
+    return nv2;
+}
+
+inline int chunk_rec_doubles(int nv2) { return 2 + 16 * nv2; }
+
+// Bytes of the chunk records for either element type.
+inline int64_t chunk_bytes(int B, int V) {
+    int64_t m = 0;
+    for (int vec = 4; vec <= 8; vec += 4) {
+        const int nv2 = choose_nv2(B, V, vec);
+        const int64_t b = int64_t(B) * c2_for(V, vec, nv2) * chunk_rec_doubles(nv2) * 8;
+        m = b > m ? b : m;
+    }
+    return m;
+}
 
 struct ChainLayout {
-    int64_t counters, status, part1, part2, total;
+    int64_t status, rec, chunks, part1, total;
 };
 
 inline ChainLayout chain_layout(int B, int P, int V) {
     ChainLayout L;
     const int64_t c1max = c1_for(V, kMinNV, kMinVec);
-    const int64_t c2max = c2_for(V, kMinVec);
-    L.counters = 0;
-    L.status = align256(int64_t(B) * 4);
-    L.part1 = L.status + 256;
-    L.part2 = L.part1 + align256(int64_t(B) * P * 2 * c1max * int64_t(sizeof(Part)));
-    L.total = L.part2 + align256(int64_t(B) * c2max * int64_t(sizeof(Part)));
+    L.status = 0;
+    L.rec = 256;
+    L.chunks = L.rec + align256(int64_t(B) * int64_t(sizeof(ReqRecord)));
+    L.part1 = L.chunks + align256(chunk_bytes(B, V));
+    L.total = L.part1 + align256(int64_t(B) * P * 2 * c1max * int64_t(sizeof(Part)));
     return L;
 }
 

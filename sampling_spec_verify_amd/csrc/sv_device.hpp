@@ -62,6 +62,31 @@ __device__ __forceinline__ u32x4 load16(const char *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
+// 16-byte vector gv (in units of DT::kVec elements) of a row of V elements:
+// vectors past the row read as -inf; in the one partial vector the elements
+// past V are set to -inf on the packed words.  The partial-vector test only
+// runs when V is not a multiple of kVec (a wave-uniform condition).
+template <class DT>
+__device__ __forceinline__ u32x4 load_row_vec(const char *row, int gv, int V) {
+    constexpr int VEC = DT::kVec;
+    const int nvec = (V + VEC - 1) / VEC;
+    u32x4 d = (gv < nvec) ? load16(row + int64_t(gv) * 16)
+                          : u32x4{DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord};
+    if ((V % VEC) != 0 && gv == nvec - 1) {
+        const int valid = V - gv * VEC;             // 1 .. VEC-1 elements stay
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (DT::kVec == 8) {
+                if (2 * j >= valid) d[j] = 0xff80ff80u;
+                else if (2 * j + 1 >= valid) d[j] = (d[j] & 0x0000ffffu) | 0xff800000u;
+            } else if (j >= valid) {
+                d[j] = 0xff800000u;
+            }
+        }
+    }
+    return d;
+}
+
 // ---------------------------------------------------------------------------
 // lane moves
 // ---------------------------------------------------------------------------

@@ -21,31 +21,30 @@
 #include <limits.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "sv_common.hpp"
 #include "sv_device.hpp"
 
 namespace sv {
 
+// One job: the largest value (lowest index among equals) of wave-chunk c of
+// one target row, by one wavefront.
 template <class DT, int NV>
-__global__ __launch_bounds__(kBlock) void k_row_argmax(TreeArgs a, int64_t n_jobs) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
-    const int64_t job = int64_t(blockIdx.x) * kWaves + (threadIdx.x / kWave);
-    if (job >= n_jobs) return;
-    const int c = static_cast<int>(job % a.C1);
-    const int64_t row_id = job / a.C1;                 // b * (N+1) + r
+__device__ __forceinline__ void row_chunk_argmax(const TreeArgs &a, unsigned job) {
+    const int c = static_cast<int>(job % static_cast<unsigned>(a.C1));
+    const int64_t row_id = job / static_cast<unsigned>(a.C1);   // b * (N+1) + r
     const char *row = a.tgt + row_id * a.ld_t * a.elem;
 
     constexpr int VEC = DT::kVec;
     const int lane = threadIdx.x & (kWave - 1);
     const int V = a.V;
-    const int64_t v0 = int64_t(c) * (kWave * NV);
+    const int v0 = c * (kWave * NV);
     u32x4 d[NV];
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {
-        const int64_t gv = v0 + n * kWave + lane;
-        d[n] = (gv * VEC < V) ? load16(row + gv * 16)
-                              : u32x4{DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord};
-    }
+    for (int n = 0; n < NV; ++n) d[n] = load_row_vec<DT>(row, v0 + n * kWave + lane, V);
+    // elements past V read as -inf and sit above every valid index, so they
+    // never win: a lane keeps the first index of its largest value
     float best = -INFINITY;
     int best_i = INT_MAX;
     bool nan = false;
@@ -53,18 +52,13 @@ __global__ __launch_bounds__(kBlock) void k_row_argmax(TreeArgs a, int64_t n_job
     for (int n = 0; n < NV; ++n) {
         float f[VEC];
         DT::unpack(d[n], f);
-        const int64_t i0 = (v0 + n * kWave + lane) * VEC;
+        const int i0 = (v0 + n * kWave + lane) * VEC;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            if (i0 + e >= V) continue;
-            if (f[e] != f[e]) {
-                nan = true;
-                continue;
-            }
-            // first index of the largest value (an all -inf lane keeps its first index)
+            nan |= (f[e] != f[e]);
             if (f[e] > best || best_i == INT_MAX) {
-                best = f[e];
-                best_i = static_cast<int>(i0 + e);
+                best = (f[e] != f[e]) ? best : f[e];
+                best_i = (f[e] != f[e]) ? best_i : i0 + e;
             }
         }
     }
@@ -79,6 +73,16 @@ __global__ __launch_bounds__(kBlock) void k_row_argmax(TreeArgs a, int64_t n_job
         p.pad = 0;
         a.part[row_id * a.C1 + c] = p;
     }
+}
+
+// One wavefront per job (wave-uniform index, 32-bit scalar decode).
+template <class DT, int NV>
+__global__ __launch_bounds__(kBlock) void k_row_argmax(TreeArgs a, int n_jobs) {
+    const int job = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves +
+                                                   static_cast<int>(threadIdx.x) / kWave);
+    if (job < n_jobs) row_chunk_argmax<DT, NV>(a, static_cast<unsigned>(job));
+    // cleared last (a store ahead of the reads would keep them off the scalar path)
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
 }
 
 __global__ __launch_bounds__(kBlock) void k_greedy_walk(TreeArgs a) {
@@ -189,10 +193,9 @@ sv_status run_tree(const TreeArgs &a0, hipStream_t stream) {
     int nv = 8;
     while (nv > kMinNV && rows * c1_for(a.V, nv, DT::kVec) < 8192) nv >>= 1;
     a.C1 = c1_for(a.V, nv, DT::kVec);
-    const int64_t jobs = rows * a.C1;
-    const int64_t blocks = cdiv(jobs, kWaves);
-    if (blocks > 0x7fffffffLL) return SV_EINVAL;
-    const dim3 grid(static_cast<unsigned>(blocks));
+    if (rows * a.C1 >= (int64_t(1) << 31)) return SV_EINVAL;
+    const int jobs = static_cast<int>(rows * a.C1);
+    const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, cdiv(jobs, kWaves))));
     if (nv == 8)
         hipLaunchKernelGGL((k_row_argmax<DT, 8>), grid, dim3(kBlock), 0, stream, a, jobs);
     else if (nv == 4)

@@ -156,7 +156,8 @@ class ChainCall:
 
     ``run()`` launches both kernels; ``row_stats()`` / ``accept_resample()``
     launch one each (the pair equals ``run()``).  Rebinding inputs with
-    ``set_inputs`` keeps the outputs and workspace.
+    ``set_inputs`` keeps the outputs and workspace.  The stream (default: the
+    current torch stream) is bound when the inputs are.
     """
 
     def __init__(self, target, draft, tokens, u_accept, u_sample, lam=0.0, temperature=1.0,
@@ -189,6 +190,7 @@ class ChainCall:
         self.inputs = (target, draft, _i32(tokens, (B, K), "tokens"),
                        _i32(draft_len, (B,), "draft_len"),
                        _f32(u_accept, (B, K), "u_accept"), _f32(u_sample, (B,), "u_sample"))
+        self._cached = self._args()
 
     def _args(self):
         t, d, tok, dl, ua, us = self.inputs
@@ -199,14 +201,14 @@ class ChainCall:
                 _ptr(self.workspace), self.workspace.numel(), _stream(self.stream))
 
     def run(self) -> ChainOut:
-        _check(lib().sv_chain_verify(*self._args()), "sv_chain_verify")
+        _check(lib().sv_chain_verify(*self._cached), "sv_chain_verify")
         return self.out
 
     def row_stats(self):
-        _check(lib().sv_chain_row_stats(*self._args()), "sv_chain_row_stats")
+        _check(lib().sv_chain_row_stats(*self._cached), "sv_chain_row_stats")
 
     def accept_resample(self) -> ChainOut:
-        _check(lib().sv_chain_accept_resample(*self._args()), "sv_chain_accept_resample")
+        _check(lib().sv_chain_accept_resample(*self._cached), "sv_chain_accept_resample")
         return self.out
 
 
@@ -224,28 +226,39 @@ class TreeGreedyOut(NamedTuple):
     status: object          # [1]
 
 
+class TreeGreedyCall:
+    """A greedy tree-verify call with outputs and workspace bound once (see ChainCall)."""
+
+    def __init__(self, target, parent, node_token, Dmax: int, stream=None, workspace=None):
+        torch = _torch()
+        B, N1, V = target.shape
+        N = N1 - 1
+        ld = _rows(target, B, N + 1, V, "target")
+        _i32(parent, (B, N), "parent")
+        _i32(node_token, (B, N), "node_token")
+        dev = target.device
+        self.out = TreeGreedyOut(torch.empty(B, dtype=torch.int32, device=dev),
+                                 torch.empty(B, Dmax + 1, dtype=torch.int32, device=dev),
+                                 torch.empty(B, max(Dmax, 0), dtype=torch.int32, device=dev),
+                                 torch.empty(1, dtype=torch.int32, device=dev))
+        self.workspace = workspace if workspace is not None else torch.empty(
+            max(tree_workspace_bytes(B, N, V), 16), dtype=torch.uint8, device=dev)
+        self.inputs = (target, parent, node_token)
+        o = self.out
+        self._cached = (_ptr(target), ld, _dtype_code(target), B, N, V, _ptr(parent),
+                        _ptr(node_token), _ptr(o.accepted), _ptr(o.out_tokens),
+                        _ptr(o.accepted_nodes), int(Dmax), _ptr(o.status), _ptr(self.workspace),
+                        self.workspace.numel(), _stream(stream))
+
+    def run(self) -> TreeGreedyOut:
+        _check(lib().sv_tree_verify_greedy(*self._cached), "sv_tree_verify_greedy")
+        return self.out
+
+
 def tree_verify_greedy(target, parent, node_token, Dmax: int, stream=None,
                        workspace=None) -> TreeGreedyOut:
     """sv_tree_verify_greedy: target [B, N+1, V], parent / node_token [B, N] int32."""
-    torch = _torch()
-    B, N1, V = target.shape
-    N = N1 - 1
-    ld = _rows(target, B, N + 1, V, "target")
-    _i32(parent, (B, N), "parent")
-    _i32(node_token, (B, N), "node_token")
-    dev = target.device
-    out = TreeGreedyOut(torch.empty(B, dtype=torch.int32, device=dev),
-                        torch.empty(B, Dmax + 1, dtype=torch.int32, device=dev),
-                        torch.empty(B, max(Dmax, 0), dtype=torch.int32, device=dev),
-                        torch.empty(1, dtype=torch.int32, device=dev))
-    ws = workspace if workspace is not None else torch.empty(
-        max(tree_workspace_bytes(B, N, V), 16), dtype=torch.uint8, device=dev)
-    code = lib().sv_tree_verify_greedy(_ptr(target), ld, _dtype_code(target), B, N, V, _ptr(parent),
-                                       _ptr(node_token), _ptr(out.accepted), _ptr(out.out_tokens),
-                                       _ptr(out.accepted_nodes), int(Dmax), _ptr(out.status),
-                                       _ptr(ws), ws.numel(), _stream(stream))
-    _check(code, "sv_tree_verify_greedy")
-    return out
+    return TreeGreedyCall(target, parent, node_token, Dmax, stream, workspace).run()
 
 
 def tree_verify_path(target, draft, node_token, path, u_accept, u_sample, lam: float = 0.0,

@@ -97,9 +97,11 @@ def chain_call(fn="sv_chain_verify", **kw):
     (dict(dtype=sv.SV_F32, ld_q=130), sv.SV_EALIGN),
     (dict(ws=None), sv.SV_EWORKSPACE),
     (dict(ws=FAKE + 4), sv.SV_EWORKSPACE),
-    (dict(wsb=512), sv.SV_EWORKSPACE),
+    (dict(wsb="short"), sv.SV_EWORKSPACE),
 ])
 def test_chain_argument_errors(fn, kw, code):
+    if kw.get("wsb") == "short":
+        kw = dict(wsb=sv.lib().sv_chain_workspace_bytes(2, 4, 128) - 16)
     assert chain_call(fn, **kw) == code
 
 
@@ -147,7 +149,7 @@ def path_call(**kw):
     (dict(dtype=9), sv.SV_EDTYPE), (dict(Dmax=65), sv.SV_EINVAL), (dict(N=2000), sv.SV_EINVAL),
     (dict(T=0.0), sv.SV_EINVAL), (dict(lam=2.0), sv.SV_EINVAL), (dict(path=None), sv.SV_ENULL),
     (dict(tok=None), sv.SV_ENULL), (dict(d=None), sv.SV_ENULL), (dict(d=FAKE + 4), sv.SV_EALIGN),
-    (dict(wsb=64), sv.SV_EWORKSPACE),
+    (dict(wsb=16), sv.SV_EWORKSPACE),
 ])
 def test_path_argument_errors(kw, code):
     assert path_call(**kw) == code
