@@ -37,16 +37,18 @@ METRIC = "verified draft positions/sec + achieved HBM GB/s (% of peak) at V=1282
 UNIT = "verified positions/s"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30
-KERNEL_SOURCES = ["sampling_spec_verify_amd/csrc/sv_chain.hip",
-                  "sampling_spec_verify_amd/csrc/sv_tree.hip",
-                  "sampling_spec_verify_amd/csrc/sv_device.hpp",
-                  "sampling_spec_verify_amd/csrc/sv_common.hpp"]
+_CSRC = "sampling_spec_verify_amd/csrc/"
+KERNEL_SOURCES = {
+    "row_stats": [_CSRC + "sv_chain.hip", _CSRC + "sv_device.hpp", _CSRC + "sv_common.hpp"],
+    "row_argmax": [_CSRC + "sv_tree.hip", _CSRC + "sv_device.hpp", _CSRC + "sv_common.hpp"],
+}
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_{kernel}_{workload}.md")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "row_stats") -> str:
+    """Hash of the sources the named kernel is built from."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -63,7 +65,7 @@ def load_traffic(kernel: str, workload: str):
         return None
     end = text.find("```", start + 7)
     rec = json.loads(text[start + 7:end])
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -296,7 +298,7 @@ def main():
         "second_launch_ms_mean": float(rest_ms.mean()),
         "status_word": status,
         "parity_sample": parity,
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash(kname),
     }
     print(json.dumps(line), flush=True)
 

@@ -700,12 +700,7 @@ struct ChainReq {
     hipStream_t stream;
 };
 
-int choose_nv(int B, int P, int V, int vec) {
-    const int64_t rows = 2LL * B * P;
-    int nv = 8;
-    while (nv > kMinNV && rows * c1_for(V, nv, vec) < 8192) nv >>= 1;
-    return nv;
-}
+int choose_nv(int B, int P, int V, int vec) { return choose_stream_nv(2LL * B * P, V, vec); }
 
 int pcap(const ChainReq &q) { return q.path_mode ? std::min(q.P, q.N) : q.P; }
 

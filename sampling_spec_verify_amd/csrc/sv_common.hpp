@@ -101,12 +101,21 @@ constexpr int kMaxC2 = 128;                   // sampling chunks per row at NV2 
 constexpr int kMinVec = 4;                    // fp32: 4 elements per 16-byte vector
 constexpr int kMinNV = 2;                     // smallest row-stats vectors per lane
 constexpr int kStageMax = 2048;               // row partials staged in LDS per request
+constexpr int kGreedyStageMax = 2048;         // argmax partials staged in LDS per tree
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 // Row-stats wave-chunk: 64 lanes x NV vectors x VEC elements.
 inline int c1_for(int V, int NV, int vec) { return static_cast<int>(cdiv(V, 64LL * NV * vec)); }
+// Vectors per lane of a streaming wave-job: 8 (8 KB of bf16 per wave) unless
+// that leaves fewer than 2048 jobs to spread over the chip, then 4 or 2.
+inline int choose_stream_nv(int64_t rows, int V, int vec) {
+    int nv = 8;
+    while (nv > kMinNV && rows * c1_for(V, nv, vec) < 2048) nv >>= 1;
+    return nv;
+}
+
 inline int c2_for(int V, int vec, int nv2) {
     return static_cast<int>(cdiv(V, int64_t(kBlock2) * nv2 * vec));
 }

@@ -12,7 +12,7 @@
 //  1. k_row_argmax: one wavefront per (request, row, chunk) streams 64 lanes x
 //     NV x 16 bytes of a target row and keeps the largest value with its
 //     lowest index (no exponentials: argmax is temperature-free).
-//  2. k_greedy_walk: one block per request combines the chunk partials into
+//  2. k_greedy_walk: one 1024-thread block per request combines the chunk partials into
 //     the argmax of each row, then walks the parent array in node order:
 //     ok[i] = ok[parent[i]] and token[i] == argmax[parent[i]]; the deepest ok
 //     node (lowest id on ties) and its root path are emitted, followed by the
@@ -85,27 +85,43 @@ __global__ __launch_bounds__(kBlock) void k_row_argmax(TreeArgs a, int n_jobs) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
 }
 
-__global__ __launch_bounds__(kBlock) void k_greedy_walk(TreeArgs a) {
+// One 1024-thread block per request.  All of the request's chunk partials,
+// parents and node tokens arrive in one parallel load round (partials staged
+// in LDS when they fit), sixteen waves combine the rows, then one thread walks
+// the parent array.
+__global__ __launch_bounds__(kBlock2) void k_greedy_walk(TreeArgs a, int staged) {
     __shared__ int am[SV_MAX_TREE_NODES + 1];
     __shared__ int par[SV_MAX_TREE_NODES + 1];
     __shared__ int tok[SV_MAX_TREE_NODES + 1];
     __shared__ int path[SV_MAX_TREE_NODES + 1];
     __shared__ int sh_flags, sh_depth, sh_best;
+    extern __shared__ ArgPart stage[];
     const int b = blockIdx.x;
     const int N = a.N;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
-    if (threadIdx.x == 0) sh_flags = 0;
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wv = t / kWave;
+    const int64_t pbase = int64_t(b) * (N + 1) * a.C1;
+    if (t == 0) sh_flags = 0;
+    if (staged)
+        for (int idx = t; idx < (N + 1) * a.C1; idx += kBlock2) stage[idx] = a.part[pbase + idx];
+    for (int i = t; i < N; i += kBlock2) {
+        par[i + 1] = a.parent[int64_t(b) * N + i];
+        tok[i + 1] = a.node_token[int64_t(b) * N + i];
+    }
     __syncthreads();
 
     // argmax of every row: largest value, lowest index among equals
-    for (int r = wv; r <= N; r += kWaves) {
-        const ArgPart *p = a.part + (int64_t(b) * (N + 1) + r) * a.C1;
+#pragma unroll 1
+    for (int r = wv; r <= N; r += kWaves2) {
+        const ArgPart *p = staged ? stage + r * a.C1 : a.part + pbase + int64_t(r) * a.C1;
         float v = -INFINITY;
+#pragma unroll 1
         for (int c = lane; c < a.C1; c += kWave) v = fmaxf(v, p[c].val);
         v = wave_max(v);
         int idx = INT_MAX;
         int nan = 0;
+#pragma unroll 1
         for (int c = lane; c < a.C1; c += kWave) {
             const ArgPart q = p[c];
             if (q.val == v) idx = min(idx, q.idx);
@@ -118,13 +134,9 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(TreeArgs a) {
             if (idx == INT_MAX || anynan) atomicOr(&sh_flags, SV_DATA_BAD_ROW);
         }
     }
-    for (int i = threadIdx.x; i < N; i += kBlock) {
-        par[i + 1] = a.parent[int64_t(b) * N + i];
-        tok[i + 1] = a.node_token[int64_t(b) * N + i];
-    }
     __syncthreads();
 
-    if (threadIdx.x == 0) {
+    if (t == 0) {
         // ok / depth packed into path[] (reused): depth+1 when ok, 0 otherwise
         int flags = 0;
         path[0] = 1;                         // root: ok, depth 0
@@ -145,36 +157,30 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(TreeArgs a) {
                 best = i;
             }
         }
+        // nodes root -> best (path[d] = node at depth d), cut to Dmax nodes
+        int v = best;
+        for (int d = best_d; d >= 1; --d) {
+            path[d] = v;
+            v = par[v];
+        }
+        if (best_d > a.Dmax) flags |= SV_DATA_DEPTH;
         sh_best = best;
         sh_depth = best_d;
         sh_flags |= flags;
     }
     __syncthreads();
-    const int best = sh_best;
-    const int depth = sh_depth;
     const int Dmax = a.Dmax;
-    const int keep = min(depth, Dmax);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        // nodes root -> best, cut to the first Dmax when deeper
-        int v = best;
-        for (int d = depth; d >= 1; --d) {
-            path[d] = v;
-            v = par[v];
-        }
-        if (depth > Dmax) sh_flags |= SV_DATA_DEPTH;
-    }
-    __syncthreads();
+    const int keep = min(sh_depth, Dmax);
     const int last = keep > 0 ? path[keep] : 0;
     const int bonus = am[last];
-    for (int t = threadIdx.x; t <= Dmax; t += kBlock) {
+    for (int i = t; i <= Dmax; i += kBlock2) {
         int v = -1;
-        if (t < keep) v = tok[path[t + 1]];
-        else if (t == keep) v = bonus;
-        a.out_tokens[int64_t(b) * (Dmax + 1) + t] = v;
-        if (t < Dmax) a.accepted_nodes[int64_t(b) * Dmax + t] = (t < keep) ? path[t + 1] : -1;
+        if (i < keep) v = tok[path[i + 1]];
+        else if (i == keep) v = bonus;
+        a.out_tokens[int64_t(b) * (Dmax + 1) + i] = v;
+        if (i < Dmax) a.accepted_nodes[int64_t(b) * Dmax + i] = (i < keep) ? path[i + 1] : -1;
     }
-    if (threadIdx.x == 0) {
+    if (t == 0) {
         a.accepted[b] = keep;
         if (sh_flags) atomicOr(a.status, sh_flags);
     }
@@ -190,8 +196,7 @@ template <class DT>
 sv_status run_tree(const TreeArgs &a0, hipStream_t stream) {
     TreeArgs a = a0;
     const int64_t rows = int64_t(a.B) * (a.N + 1);
-    int nv = 8;
-    while (nv > kMinNV && rows * c1_for(a.V, nv, DT::kVec) < 8192) nv >>= 1;
+    const int nv = choose_stream_nv(rows, a.V, DT::kVec);
     a.C1 = c1_for(a.V, nv, DT::kVec);
     if (rows * a.C1 >= (int64_t(1) << 31)) return SV_EINVAL;
     const int jobs = static_cast<int>(rows * a.C1);
@@ -203,7 +208,11 @@ sv_status run_tree(const TreeArgs &a0, hipStream_t stream) {
     else
         hipLaunchKernelGGL((k_row_argmax<DT, 2>), grid, dim3(kBlock), 0, stream, a, jobs);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
-    hipLaunchKernelGGL(k_greedy_walk, dim3(static_cast<unsigned>(a.B)), dim3(kBlock), 0, stream, a);
+    const int64_t stage_n = int64_t(a.N + 1) * a.C1;
+    const int staged = stage_n <= kGreedyStageMax ? 1 : 0;
+    const size_t lds = staged ? static_cast<size_t>(stage_n) * sizeof(ArgPart) : 0;
+    hipLaunchKernelGGL(k_greedy_walk, dim3(static_cast<unsigned>(a.B)), dim3(kBlock2), lds, stream, a,
+                       staged);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
