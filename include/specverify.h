@@ -177,6 +177,27 @@ sv_status sv_tree_verify_greedy(const void *target_logits, int64_t ld_t, sv_dtyp
                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The two launches sv_tree_verify_greedy makes, exposed so that a caller can
+ * time or interleave them.  Same arguments and meaning; sv_tree_row_argmax
+ * streams every target row once and reduces it to per-chunk (max, lowest
+ * index) partials; sv_tree_greedy_walk must follow it on the same stream with
+ * the same workspace, combines the partials into row argmaxes, walks the
+ * parent array and writes the outputs.
+ */
+sv_status sv_tree_row_argmax(const void *target_logits, int64_t ld_t, sv_dtype dtype,
+                             int B, int N, int V,
+                             const int32_t *parent, const int32_t *node_token,
+                             int32_t *accepted, int32_t *out_tokens, int32_t *accepted_nodes,
+                             int Dmax, int32_t *status, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+sv_status sv_tree_greedy_walk(const void *target_logits, int64_t ld_t, sv_dtype dtype,
+                              int B, int N, int V,
+                              const int32_t *parent, const int32_t *node_token,
+                              int32_t *accepted, int32_t *out_tokens, int32_t *accepted_nodes,
+                              int Dmax, int32_t *status, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Stochastic verification along one caller-chosen root->leaf path: chain
  * acceptance (as sv_chain_verify) where position j drafts node n_{j+1}'s token
  * and is tested on target row n_j and draft row n_j (n_0 = root); the bonus

@@ -25,11 +25,13 @@
 //     reduces its chunk of the sampling row: the residual max(0, p_t - q) at
 //     row n (the same normalised law as max(0, p~ - q), since
 //     p~ - q = (1 - lambda)(p_t - q)), or the bonus softmax(z/T) at the
-//     request's last target row, to fp64 sums of its 32 pieces.
+//     request's last target row, to fp64 sums of its 16 * NV2 pieces.
 //
-//  3. k_locate: one block per request scales the pieces to a common frame,
-//     finds the piece holding u * W with a monotone fp64 block scan, reloads
-//     that piece's 64 vectors and finds the token with a lane scan.
+//  3. k_locate: one block per request loads every piece mass in one round
+//     (up to kLocPP per thread, in registers), scales them to a common frame,
+//     finds the piece holding u * W with one monotone fp64 block scan over
+//     per-thread totals and a walk inside the owning thread, reloads that
+//     piece's 64 vectors and finds the token with a lane scan.
 //
 // Blocks never exchange data inside a launch, so no device-scope fences or
 // data atomics are needed; every reduction has a fixed order (bitwise
@@ -498,70 +500,119 @@ struct LocateShared {
     double d4[kWaves];
     float f4[kWaves];
     int pstar, tok, lastpos;
-    double excl, scale, W;
+    float spick;
+    double excl, scale;
 };
 
+// Pieces of the request held by one locate thread (thread t owns the
+// contiguous pieces [t * pp, (t + 1) * pp), pp = ceil(np / kBlock) <= kLocPP).
+struct LocatePieces {
+    double m[kLocPP];       // piece mass in its chunk's frame
+    float s[kLocPP];        // the chunk's shift
+};
+
+// One load round: every piece mass this thread owns and its chunk's shift.
+template <int NV2>
+__device__ __forceinline__ void load_pieces(const ChainArgs &a, int b, int pp, LocatePieces &P) {
+    constexpr int kPieces = kWaves2 * NV2;
+    const double *cr = a.chunks + int64_t(b) * a.C2 * a.rec_stride;
+    const int np = a.C2 * kPieces;
+    const int p0 = threadIdx.x * pp;
+#pragma unroll
+    for (int j = 0; j < kLocPP; ++j) {
+        const int p = p0 + j;
+        if (j < pp && p < np) {
+            const double *rc = cr + int64_t(p / kPieces) * a.rec_stride;
+            P.m[j] = rc[2 + p % kPieces];
+            P.s[j] = static_cast<float>(rc[0]);
+        } else {
+            P.m[j] = 0.0;
+            P.s[j] = -INFINITY;
+        }
+    }
+}
+
 // Inverse CDF over the request's pieces: scale every chunk to the common
-// frame 2^(-max shift), fp64 block scan over the pieces in element order,
-// then a lane scan inside the chosen piece.  Every thread must call this;
-// returns -1 when the row carries no positive mass.
+// frame 2^(-max shift) (bonus rows only; residual chunks share shift 0), one
+// fp64 block scan over per-thread totals, a sequential walk inside the owning
+// thread, then a lane scan inside the chosen piece.  The interval of a piece
+// is [prefix before it, prefix after it); the first and last boundary of each
+// thread are the block scan's, so the intervals tile [0, W) and the owner is
+// unique.  Every thread must call this; returns -1 when the row carries no
+// positive mass.
 template <class DT, int MODE, int NV2>
-__device__ __forceinline__ int locate(const ChainArgs &a, const SampleCtx &S, int b, double u,
+__device__ __forceinline__ int locate(const SampleCtx &S, const LocatePieces &P, int pp, double u,
                                       LocateShared &L) {
     constexpr int VEC = DT::kVec;
     constexpr int kPieces = kWaves2 * NV2;
-    const double *cr = a.chunks + int64_t(b) * a.C2 * a.rec_stride;
-    auto rec_s = [&](int c) -> float { return static_cast<float>(cr[int64_t(c) * a.rec_stride]); };
-    auto rec_m = [&](int p) -> double { return cr[int64_t(p / kPieces) * a.rec_stride + 2 + p % kPieces]; };
-    const int np = a.C2 * kPieces;
-    float smax = -INFINITY;
-    for (int c = threadIdx.x; c < a.C2; c += kBlock) smax = fmaxf(smax, rec_s(c));
-    smax = block_max(smax, L.f4);
-    auto scale_of = [&](int c) -> double {
-        const float s = rec_s(c);
-        return (s == -INFINITY) ? 0.0 : exp2(static_cast<double>(s) - static_cast<double>(smax));
-    };
-    // pass 1: total mass
-    double carry = 0.0;
-    for (int base = 0; base < np; base += kBlock) {
-        const int p = base + threadIdx.x;
-        const double m = (p < np) ? rec_m(p) * scale_of(p / kPieces) : 0.0;
-        carry = block_scan_d(m, carry, L.d4).total;
+    float smax = 0.0f;
+    if (MODE == kBonus) {
+        float sm = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kLocPP; ++j) sm = fmaxf(sm, P.s[j]);
+        smax = block_max(sm, L.f4);
     }
-    const double W = carry;
-    if (!(W > 0.0) || !isfinite(W)) return -1;
-    const double t = u * W;
-    // pass 2: the piece whose prefix interval holds t (unique: the inclusive
-    // prefixes are monotone and every exclusive prefix is the previous one)
+    double sc[kLocPP];
+    double tot = 0.0;
+#pragma unroll
+    for (int j = 0; j < kLocPP; ++j) {
+        sc[j] = 1.0;
+        if (MODE == kBonus)
+            sc[j] = (P.s[j] == -INFINITY) ? 0.0 : exp2(static_cast<double>(P.s[j]) - static_cast<double>(smax));
+        tot += P.m[j] * sc[j];
+    }
     if (threadIdx.x == 0) {
         L.pstar = -1;
         L.tok = INT_MAX;
         L.lastpos = -1;
     }
-    __syncthreads();
-    carry = 0.0;
-    for (int base = 0; base < np; base += kBlock) {
-        const int p = base + threadIdx.x;
-        double sc = 0.0, m = 0.0;
-        if (p < np) {
-            sc = scale_of(p / kPieces);
-            m = rec_m(p) * sc;
+    const Scan s = block_scan_d(tot, 0.0, L.d4);
+    const double W = s.total;
+    if (!(W > 0.0) || !isfinite(W)) return -1;
+    const double t = u * W;
+    if (s.excl <= t && t < s.incl) {
+        // walk this thread's pieces; the last interval ends at s.incl
+        double lo = s.excl;
+        int pick = -1, last = -1;
+        double pick_lo = lo, last_lo = lo;
+#pragma unroll
+        for (int j = 0; j < kLocPP; ++j) {
+            const double mj = P.m[j] * sc[j];
+            if (j < pp && mj > 0.0) {
+                last = j;
+                last_lo = lo;
+                const double hi = (j == pp - 1) ? s.incl : lo + mj;
+                if (pick < 0 && t < hi) {
+                    pick = j;
+                    pick_lo = lo;
+                }
+                lo = hi;
+            }
         }
-        const Scan s = block_scan_d(m, carry, L.d4);
-        if (p < np && s.excl <= t && t < s.incl) {
-            L.pstar = p;
-            L.excl = s.excl;
-            L.scale = sc;
+        if (pick < 0) {                     // t rounded past the walk: the last positive piece
+            pick = last;
+            pick_lo = last_lo;
         }
-        carry = s.total;
+        L.pstar = threadIdx.x * pp + pick;
+        L.excl = pick_lo;
+        double scp = 1.0;
+        float spk = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kLocPP; ++j)
+            if (j == pick) {
+                scp = sc[j];
+                spk = P.s[j];
+            }
+        L.scale = scp;
+        L.spick = spk;
     }
     __syncthreads();
     const int ps = L.pstar;
     if (ps < 0) return -1;
     const int cs = ps / kPieces, wsv = (ps % kPieces) / NV2, ns = ps % NV2;
     const double tp = (t - L.excl) / L.scale;        // target inside the piece, chunk frame
-    const float s_rec = rec_s(cs);
-    const float s_use = (MODE == kBonus && s_rec != -INFINITY) ? s_rec : 0.0f;
+    // the chosen piece's own chunk shift, as the mass kernel used it
+    const float s_use = (MODE == kBonus && L.spick != -INFINITY) ? L.spick : 0.0f;
     if (threadIdx.x < kWave) {
         const int lane = threadIdx.x;
         const int64_t gv = piece_vec<NV2>(cs, wsv, ns, lane);
@@ -651,12 +702,15 @@ template <class DT, int NV2>
 __global__ __launch_bounds__(kBlock) void k_locate(ChainArgs a) {
     __shared__ LocateShared L;
     const int b = blockIdx.x;
+    const int pp = (a.C2 * kWaves2 * NV2 + kBlock - 1) / kBlock;
+    LocatePieces P;
+    load_pieces<NV2>(a, b, pp, P);
     const ReqRecord r = a.rec[b];
     const SampleCtx S = sample_ctx(a, b, r);
     const double u = static_cast<double>(a.u_sample[b]);
     int flags = 0;
-    int tok = (r.mode == kResidual) ? locate<DT, kResidual, NV2>(a, S, b, u, L)
-                                    : locate<DT, kBonus, NV2>(a, S, b, u, L);
+    int tok = (r.mode == kResidual) ? locate<DT, kResidual, NV2>(S, P, pp, u, L)
+                                    : locate<DT, kBonus, NV2>(S, P, pp, u, L);
     if (tok < 0 && r.mode == kResidual && r.rows_ok) {
         flags |= SV_DATA_FALLBACK;
         tok = sample_mixture<DT>(S, u, L);
@@ -772,6 +826,9 @@ template <class DT>
 sv_status run_typed(const ChainReq &q, int which) {
     const int nv = choose_nv(q.B, pcap(q), q.V, DT::kVec);
     const ChainArgs a = make_args(q, DT::kVec, nv);
+    // every locate thread holds at most kLocPP piece masses (always true for
+    // the vocabularies validate() accepts; checked before any launch)
+    if (int64_t(a.C2) * kWaves2 * a.NV2 > int64_t(kBlock) * kLocPP) return SV_EINVAL;
     if (which & 1) {
         const int jobs = static_cast<int>(int64_t(q.B) * a.g.Pcap * 2 * a.C1);
         const dim3 grid(static_cast<unsigned>(jobs > 0 ? cdiv(jobs, kWaves) : 1));

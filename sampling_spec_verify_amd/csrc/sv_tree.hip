@@ -29,7 +29,13 @@
 namespace sv {
 
 // One job: the largest value (lowest index among equals) of wave-chunk c of
-// one target row, by one wavefront.
+// one target row, by one wavefront.  Maximum first, position second: every
+// lane reduces each of its 16-byte vectors to a maximum, the wave takes the
+// maximum of those, and only then does each lane look for its first element
+// equal to it (a lane's vectors, and the elements inside one, are in index
+// order).  NaNs are reported through a separate flag that marks the whole row
+// bad, so the maximum may ignore them.  Elements past V read as -inf and sit
+// above every valid index, so they never win a tie.
 template <class DT, int NV>
 __device__ __forceinline__ void row_chunk_argmax(const TreeArgs &a, unsigned job) {
     const int c = static_cast<int>(job % static_cast<unsigned>(a.C1));
@@ -43,31 +49,47 @@ __device__ __forceinline__ void row_chunk_argmax(const TreeArgs &a, unsigned job
     u32x4 d[NV];
 #pragma unroll
     for (int n = 0; n < NV; ++n) d[n] = load_row_vec<DT>(row, v0 + n * kWave + lane, V);
-    // elements past V read as -inf and sit above every valid index, so they
-    // never win: a lane keeps the first index of its largest value
-    float best = -INFINITY;
-    int best_i = INT_MAX;
+    float vm[NV];
     bool nan = false;
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
         float f[VEC];
         DT::unpack(d[n], f);
-        const int i0 = (v0 + n * kWave + lane) * VEC;
+        float m = f[0];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            nan |= (f[e] != f[e]);
-            if (f[e] > best || best_i == INT_MAX) {
-                best = (f[e] != f[e]) ? best : f[e];
-                best_i = (f[e] != f[e]) ? best_i : i0 + e;
-            }
-        }
+        for (int e = 1; e < VEC; ++e) m = fmaxf(m, f[e]);
+        vm[n] = m;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) nan |= (f[e] != f[e]);
     }
-    const float wbest = wave_max(best);
-    const int widx = wave_min_i(best == wbest ? best_i : INT_MAX);
+    float lm = vm[0];
+#pragma unroll
+    for (int n = 1; n < NV; ++n) lm = fmaxf(lm, vm[n]);
+    const float wm = wave_max(lm);
+    // this lane's first vector, then first element, equal to the wave maximum
+    int nsel = -1;
+#pragma unroll
+    for (int n = NV - 1; n >= 0; --n)
+        if (vm[n] == wm) nsel = n;
+    int idx = INT_MAX;
+    if (nsel >= 0) {
+        u32x4 dv = d[0];
+#pragma unroll
+        for (int n = 1; n < NV; ++n)
+            if (nsel == n) dv = d[n];
+        float f[VEC];
+        DT::unpack(dv, f);
+        int esel = VEC - 1;
+#pragma unroll
+        for (int e = VEC - 1; e >= 0; --e)
+            if (f[e] == wm) esel = e;
+        idx = (v0 + nsel * kWave + lane) * VEC + esel;
+    }
+    const int widx = wave_min_i(idx);
     const bool wnan = __ballot(nan) != 0ull;
     if (lane == 0) {
         ArgPart p;
-        p.val = wbest;
+        p.val = wm;
         p.idx = widx;
         p.nan = wnan ? 1 : 0;
         p.pad = 0;
@@ -87,14 +109,26 @@ __global__ __launch_bounds__(kBlock) void k_row_argmax(TreeArgs a, int n_jobs) {
 
 // One 1024-thread block per request.  All of the request's chunk partials,
 // parents and node tokens arrive in one parallel load round (partials staged
-// in LDS when they fit), sixteen waves combine the rows, then one thread walks
-// the parent array.
+// in LDS when they fit) and sixteen waves combine the rows.  The walk is
+// parallel over nodes: node i matches when its parent is valid and its token
+// is the argmax of the parent's row; ok[i] (every node from i up to the root
+// matches) and depth[i] come from pointer jumping, O(log depth) rounds over
+// (ancestor, value) pairs where the value is the depth while every node
+// passed so far matched and a large negative number once one did not.  The
+// deepest ok node (lowest id on ties) is a block maximum of
+// depth * 2048 + (2047 - i); only its own root path is walked serially.
+constexpr int kNodes = SV_MAX_TREE_NODES + 1;
+constexpr int kRejected = -(1 << 20);       // below any sum of <= kNodes depths
+
 __global__ __launch_bounds__(kBlock2) void k_greedy_walk(TreeArgs a, int staged) {
-    __shared__ int am[SV_MAX_TREE_NODES + 1];
-    __shared__ int par[SV_MAX_TREE_NODES + 1];
-    __shared__ int tok[SV_MAX_TREE_NODES + 1];
-    __shared__ int path[SV_MAX_TREE_NODES + 1];
-    __shared__ int sh_flags, sh_depth, sh_best;
+    __shared__ int am[kNodes];
+    __shared__ int par[kNodes];
+    __shared__ int tok[kNodes];
+    __shared__ int path[kNodes];        // ancestor buffer of the jumps, then the output path
+    __shared__ int anc[kNodes];
+    __shared__ int dep[2][kNodes];
+    __shared__ int wkey[kWaves2];
+    __shared__ int sh_flags;
     extern __shared__ ArgPart stage[];
     const int b = blockIdx.x;
     const int N = a.N;
@@ -136,41 +170,82 @@ __global__ __launch_bounds__(kBlock2) void k_greedy_walk(TreeArgs a, int staged)
     }
     __syncthreads();
 
-    if (t == 0) {
-        // ok / depth packed into path[] (reused): depth+1 when ok, 0 otherwise
-        int flags = 0;
-        path[0] = 1;                         // root: ok, depth 0
-        int best = 0, best_d = 0;
-        for (int i = 1; i <= N; ++i) {
+    // one edge per node: parent and whether the node's token matches
+    int flags = 0;
+    for (int i = t; i <= N; i += kBlock2) {
+        int up = 0, val = 0;                 // the root: depth 0, ok
+        if (i > 0) {
             const int p = par[i];
-            int st = 0;
+            val = kRejected;
             if (p < 0 || p >= i) {
-                flags |= SV_DATA_BAD_TREE;
-            } else if (tok[i] < 0 || tok[i] >= a.V) {
-                flags |= SV_DATA_BAD_TOKEN;
-            } else if (path[p] > 0 && am[p] >= 0 && tok[i] == am[p]) {
-                st = path[p] + 1;
-            }
-            path[i] = st;
-            if (st - 1 > best_d) {
-                best_d = st - 1;
-                best = i;
+                flags |= SV_DATA_BAD_TREE;   // never followed: treated as a rejected root child
+            } else {
+                up = p;
+                if (tok[i] < 0 || tok[i] >= a.V) flags |= SV_DATA_BAD_TOKEN;
+                else if (am[p] >= 0 && tok[i] == am[p]) val = 1;
             }
         }
+        anc[i] = up;
+        dep[0][i] = val;
+    }
+    // pointer jumping: (anc, dep) -> (anc[anc], dep + dep[anc]) until every
+    // chain reaches the root; anc and path alternate as the ancestor buffer
+    int cur = 0;
+    int *A0 = anc, *A1 = path;
+    bool more = true;
+#pragma unroll 1
+    while (more) {
+        __syncthreads();
+        bool any = false;
+        for (int i = t; i <= N; i += kBlock2) {
+            const int u = A0[i];
+            int d = dep[cur][i], nu = 0;
+            if (u != 0) {
+                d += dep[cur][u];
+                nu = A0[u];
+            }
+            A1[i] = nu;
+            dep[cur ^ 1][i] = d;
+            any |= (nu != 0);
+        }
+        more = __syncthreads_or(any) != 0;
+        cur ^= 1;
+        int *tmp = A0;
+        A0 = A1;
+        A1 = tmp;
+    }
+    // deepest ok node, lowest id on ties (node ids are < 2048)
+    int key = -1;
+    for (int i = t; i <= N; i += kBlock2) {
+        const int d = dep[cur][i];
+        if (d >= 0) key = max(key, d * 2048 + (2047 - i));
+    }
+    key = -wave_min_i(-key);
+    const unsigned long long fl_mask = __ballot(flags != 0);
+    if (lane == 0) wkey[wv] = key;
+    if (fl_mask) {
+        int fl_all = flags;
+        for (int off = 1; off < kWave; off <<= 1) fl_all |= __shfl_xor(fl_all, off, kWave);
+        if (lane == 0) atomicOr(&sh_flags, fl_all);
+    }
+    __syncthreads();
+    int best_key = wkey[0];
+#pragma unroll
+    for (int w = 1; w < kWaves2; ++w) best_key = max(best_key, wkey[w]);
+    const int best = 2047 - best_key % 2048;
+    const int best_d = best_key / 2048;
+    const int Dmax = a.Dmax;
+    const int keep = min(best_d, Dmax);
+    if (t == 0) {
         // nodes root -> best (path[d] = node at depth d), cut to Dmax nodes
         int v = best;
         for (int d = best_d; d >= 1; --d) {
-            path[d] = v;
+            if (d <= keep) path[d] = v;
             v = par[v];
         }
-        if (best_d > a.Dmax) flags |= SV_DATA_DEPTH;
-        sh_best = best;
-        sh_depth = best_d;
-        sh_flags |= flags;
+        if (best_d > Dmax) sh_flags |= SV_DATA_DEPTH;
     }
     __syncthreads();
-    const int Dmax = a.Dmax;
-    const int keep = min(sh_depth, Dmax);
     const int last = keep > 0 ? path[keep] : 0;
     const int bonus = am[last];
     for (int i = t; i <= Dmax; i += kBlock2) {
@@ -193,46 +268,40 @@ namespace {
 using namespace sv;
 
 template <class DT>
-sv_status run_tree(const TreeArgs &a0, hipStream_t stream) {
+sv_status run_tree(const TreeArgs &a0, hipStream_t stream, int which) {
     TreeArgs a = a0;
     const int64_t rows = int64_t(a.B) * (a.N + 1);
     const int nv = choose_stream_nv(rows, a.V, DT::kVec);
     a.C1 = c1_for(a.V, nv, DT::kVec);
     if (rows * a.C1 >= (int64_t(1) << 31)) return SV_EINVAL;
-    const int jobs = static_cast<int>(rows * a.C1);
-    const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, cdiv(jobs, kWaves))));
-    if (nv == 8)
-        hipLaunchKernelGGL((k_row_argmax<DT, 8>), grid, dim3(kBlock), 0, stream, a, jobs);
-    else if (nv == 4)
-        hipLaunchKernelGGL((k_row_argmax<DT, 4>), grid, dim3(kBlock), 0, stream, a, jobs);
-    else
-        hipLaunchKernelGGL((k_row_argmax<DT, 2>), grid, dim3(kBlock), 0, stream, a, jobs);
-    if (hipGetLastError() != hipSuccess) return SV_EHIP;
-    const int64_t stage_n = int64_t(a.N + 1) * a.C1;
-    const int staged = stage_n <= kGreedyStageMax ? 1 : 0;
-    const size_t lds = staged ? static_cast<size_t>(stage_n) * sizeof(ArgPart) : 0;
-    hipLaunchKernelGGL(k_greedy_walk, dim3(static_cast<unsigned>(a.B)), dim3(kBlock2), lds, stream, a,
-                       staged);
-    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    if (which & 1) {
+        const int jobs = static_cast<int>(rows * a.C1);
+        const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, cdiv(jobs, kWaves))));
+        if (nv == 8)
+            hipLaunchKernelGGL((k_row_argmax<DT, 8>), grid, dim3(kBlock), 0, stream, a, jobs);
+        else if (nv == 4)
+            hipLaunchKernelGGL((k_row_argmax<DT, 4>), grid, dim3(kBlock), 0, stream, a, jobs);
+        else
+            hipLaunchKernelGGL((k_row_argmax<DT, 2>), grid, dim3(kBlock), 0, stream, a, jobs);
+        if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    }
+    if (which & 2) {
+        const int64_t stage_n = int64_t(a.N + 1) * a.C1;
+        const int staged = stage_n <= kGreedyStageMax ? 1 : 0;
+        const size_t lds = staged ? static_cast<size_t>(stage_n) * sizeof(ArgPart) : 0;
+        hipLaunchKernelGGL(k_greedy_walk, dim3(static_cast<unsigned>(a.B)), dim3(kBlock2), lds,
+                           stream, a, staged);
+        if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    }
     return SV_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t sv_tree_workspace_bytes(int B, int N, int V) {
-    if (B < 0 || N < 0 || N > SV_MAX_TREE_NODES || V < 1) return 0;
-    const int64_t greedy = tree_layout(B, N, V).total;
-    const int64_t path = chain_layout(B, N < SV_MAX_POSITIONS ? N : SV_MAX_POSITIONS, V).total;
-    return static_cast<size_t>(greedy > path ? greedy : path);
-}
-
-sv_status sv_tree_verify_greedy(const void *target_logits, int64_t ld_t, sv_dtype dtype, int B,
-                                int N, int V, const int32_t *parent, const int32_t *node_token,
-                                int32_t *accepted, int32_t *out_tokens, int32_t *accepted_nodes,
-                                int Dmax, int32_t *status, void *workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+// Validates the greedy call and runs the launches in `which` (1: row argmax,
+// 2: walk).  Argument errors return before any HIP call.
+sv_status greedy_call(const void *target_logits, int64_t ld_t, sv_dtype dtype, int B, int N,
+                      int V, const int32_t *parent, const int32_t *node_token, int32_t *accepted,
+                      int32_t *out_tokens, int32_t *accepted_nodes, int Dmax, int32_t *status,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream, int which) {
     const int eb = elem_bytes(dtype);
     if (eb == 0) return SV_EDTYPE;
     if (B < 0 || N < 0 || N > SV_MAX_TREE_NODES || V < 1 || Dmax < 0 || B > (1 << 30))
@@ -262,7 +331,45 @@ sv_status sv_tree_verify_greedy(const void *target_logits, int64_t ld_t, sv_dtyp
     a.accepted_nodes = accepted_nodes;
     a.status = status ? status : reinterpret_cast<int32_t *>(ws + L.status);
     a.part = reinterpret_cast<ArgPart *>(ws + L.part);
-    return dtype == SV_BF16 ? run_tree<Bf16>(a, stream) : run_tree<F32>(a, stream);
+    return dtype == SV_BF16 ? run_tree<Bf16>(a, stream, which) : run_tree<F32>(a, stream, which);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_tree_workspace_bytes(int B, int N, int V) {
+    if (B < 0 || N < 0 || N > SV_MAX_TREE_NODES || V < 1) return 0;
+    const int64_t greedy = tree_layout(B, N, V).total;
+    const int64_t path = chain_layout(B, N < SV_MAX_POSITIONS ? N : SV_MAX_POSITIONS, V).total;
+    return static_cast<size_t>(greedy > path ? greedy : path);
+}
+
+sv_status sv_tree_verify_greedy(const void *target_logits, int64_t ld_t, sv_dtype dtype, int B,
+                                int N, int V, const int32_t *parent, const int32_t *node_token,
+                                int32_t *accepted, int32_t *out_tokens, int32_t *accepted_nodes,
+                                int Dmax, int32_t *status, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    return greedy_call(target_logits, ld_t, dtype, B, N, V, parent, node_token, accepted, out_tokens,
+                       accepted_nodes, Dmax, status, workspace, workspace_bytes, stream, 3);
+}
+
+sv_status sv_tree_row_argmax(const void *target_logits, int64_t ld_t, sv_dtype dtype, int B, int N,
+                             int V, const int32_t *parent, const int32_t *node_token,
+                             int32_t *accepted, int32_t *out_tokens, int32_t *accepted_nodes,
+                             int Dmax, int32_t *status, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    return greedy_call(target_logits, ld_t, dtype, B, N, V, parent, node_token, accepted, out_tokens,
+                       accepted_nodes, Dmax, status, workspace, workspace_bytes, stream, 1);
+}
+
+sv_status sv_tree_greedy_walk(const void *target_logits, int64_t ld_t, sv_dtype dtype, int B, int N,
+                              int V, const int32_t *parent, const int32_t *node_token,
+                              int32_t *accepted, int32_t *out_tokens, int32_t *accepted_nodes,
+                              int Dmax, int32_t *status, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    return greedy_call(target_logits, ld_t, dtype, B, N, V, parent, node_token, accepted, out_tokens,
+                       accepted_nodes, Dmax, status, workspace, workspace_bytes, stream, 2);
 }
 
 }  // extern "C"

@@ -32,6 +32,8 @@ _F = ctypes.c_float
 _S = ctypes.c_size_t
 
 _CHAIN_ARGS = [_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _P, _P, _F, _F, _P, _P, _P, _P, _P, _S, _P]
+_GREEDY_ARGS = [_P, _L, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _S, _P]
+
 SIGNATURES = {
     "sv_status_string": ([_I], ctypes.c_char_p),
     "sv_chain_workspace_bytes": ([_I, _I, _I], _S),
@@ -39,7 +41,9 @@ SIGNATURES = {
     "sv_chain_row_stats": (_CHAIN_ARGS, _I),
     "sv_chain_accept_resample": (_CHAIN_ARGS, _I),
     "sv_tree_workspace_bytes": ([_I, _I, _I], _S),
-    "sv_tree_verify_greedy": ([_P, _L, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _S, _P], _I),
+    "sv_tree_verify_greedy": (_GREEDY_ARGS, _I),
+    "sv_tree_row_argmax": (_GREEDY_ARGS, _I),
+    "sv_tree_greedy_walk": (_GREEDY_ARGS, _I),
     "sv_tree_verify_path": ([_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _I, _P, _P, _F, _F, _P, _P,
                              _P, _P, _P, _S, _P], _I),
 }
@@ -252,6 +256,13 @@ class TreeGreedyCall:
 
     def run(self) -> TreeGreedyOut:
         _check(lib().sv_tree_verify_greedy(*self._cached), "sv_tree_verify_greedy")
+        return self.out
+
+    def row_argmax(self):
+        _check(lib().sv_tree_row_argmax(*self._cached), "sv_tree_row_argmax")
+
+    def walk(self) -> TreeGreedyOut:
+        _check(lib().sv_tree_greedy_walk(*self._cached), "sv_tree_greedy_walk")
         return self.out
 
 

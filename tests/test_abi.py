@@ -23,6 +23,7 @@ def test_header_declares_the_boundary():
     assert names == sorted(["sv_status_string", "sv_chain_workspace_bytes", "sv_chain_verify",
                             "sv_chain_row_stats", "sv_chain_accept_resample",
                             "sv_tree_workspace_bytes", "sv_tree_verify_greedy",
+                            "sv_tree_row_argmax", "sv_tree_greedy_walk",
                             "sv_tree_verify_path"])
 
 
@@ -115,14 +116,17 @@ def test_chain_without_drafts_needs_no_draft_tensor():
     assert chain_call(K=0, d=None, tok=None, ua=None, wsb=16) == sv.SV_EWORKSPACE
 
 
-def greedy_call(**kw):
+GREEDY_ENTRIES = ["sv_tree_verify_greedy", "sv_tree_row_argmax", "sv_tree_greedy_walk"]
+
+
+def greedy_call(fn="sv_tree_verify_greedy", **kw):
     args = dict(t=FAKE, ld=128, dtype=sv.SV_BF16, B=2, N=5, V=128, par=FAKE, tok=FAKE, acc=FAKE,
                 out=FAKE, nodes=FAKE, Dmax=6, st=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
     args.update(kw)
-    return sv.lib().sv_tree_verify_greedy(args["t"], args["ld"], args["dtype"], args["B"], args["N"],
-                                          args["V"], args["par"], args["tok"], args["acc"],
-                                          args["out"], args["nodes"], args["Dmax"], args["st"],
-                                          args["ws"], args["wsb"], args["stream"])
+    return getattr(sv.lib(), fn)(args["t"], args["ld"], args["dtype"], args["B"], args["N"],
+                                 args["V"], args["par"], args["tok"], args["acc"], args["out"],
+                                 args["nodes"], args["Dmax"], args["st"], args["ws"], args["wsb"],
+                                 args["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -133,8 +137,10 @@ def greedy_call(**kw):
     (dict(t=FAKE + 2), sv.SV_EALIGN), (dict(ld=127), sv.SV_EALIGN),
     (dict(ws=None), sv.SV_EWORKSPACE), (dict(wsb=100), sv.SV_EWORKSPACE),
 ])
-def test_greedy_argument_errors(kw, code):
-    assert greedy_call(**kw) == code
+@pytest.mark.parametrize("fn", GREEDY_ENTRIES)
+def test_greedy_argument_errors(fn, kw, code):
+    # the split launches validate exactly like the whole call
+    assert greedy_call(fn, **kw) == code
 
 
 def path_call(**kw):

@@ -213,6 +213,45 @@ def test_greedy_depth_cut_and_bad_parent():
     assert "BAD_TREE" in sv.decode_flags(int(g.status[0]))
 
 
+def test_greedy_special_values():
+    """NaN rows are reported, never argmax'd; -inf rows, signed zeros and +inf
+    in the partial last vector follow the oracle's first-maximum rule."""
+    x = synth.make_random_tree(321, 5, 6, 3001, "bf16", int_logits=True)
+    t = x.target                                 # bf16 bit patterns
+    t[0, 2, 1500] = 0x7FC0                       # quiet NaN
+    t[1, 0, :] = 0xFF80                          # a row of -inf: argmax is 0
+    t[2, 0, :] = 0xFF80
+    t[2, 0, 17] = 0x8000                         # -0 ties +0: the lower index wins
+    t[2, 0, 2999] = 0x0000
+    t[3, 0, 3000] = 0x7F80                       # +inf at the last element (partial vector)
+    t[4, 1, 5] = 0x7F81                          # signalling-NaN bit pattern
+    x.node_token[1:4, 0] = [0, 17, 3000]         # node 1 (a root child) matches row 0's argmax
+    g = run_greedy(x)
+    assert "BAD_ROW" in sv.decode_flags(int(g.status[0]))
+    zt = x.widened(t)
+    for b in (1, 2, 3):
+        r = oracle.tree_greedy_one(zt[b], x.parent[b], x.node_token[b])
+        assert r.accepted >= 1
+        assert g.accepted[b] == r.accepted
+        np.testing.assert_array_equal(g.out_tokens[b, :r.accepted + 1], r.tokens)
+    assert oracle.tree_greedy_one(zt[1], x.parent[1], x.node_token[1]).argmax[0] == 0
+    assert oracle.tree_greedy_one(zt[2], x.parent[2], x.node_token[2]).argmax[0] == 17
+    assert oracle.tree_greedy_one(zt[3], x.parent[3], x.node_token[3]).argmax[0] == 3000
+    for b in (0, 4):                             # the oracle refuses these requests
+        with pytest.raises(oracle.InvalidRow):
+            oracle.tree_greedy_one(zt[b], x.parent[b], x.node_token[b])
+
+
+def test_greedy_split_calls_equal_full_call():
+    x = synth.make_random_tree(322, 4, 20, 20000, "bf16", int_logits=True)
+    call = sv.TreeGreedyCall(dev_logits(x.target, x.dtype), dev(x.parent), dev(x.node_token), x.Dmax)
+    full = to_host(call.run())
+    call.row_argmax()
+    split = to_host(call.walk())
+    for a, b in zip(full, split):
+        np.testing.assert_array_equal(a, b)
+
+
 @pytest.mark.parametrize("seed,B,N,V,dtype,lam,T", [
     (1, 6, 12, 3000, "fp32", 0.0, 1.0), (2, 4, 40, 20000, "bf16", 0.3, 0.8),
     (3, 3, 5, 17, "fp32", 0.5, 1.2),
