@@ -114,8 +114,7 @@ __device__ __forceinline__ void row_chunk_stats(const ChainArgs &a, unsigned job
     const int v0 = c * (kWave * NV);
 
     u32x4 d[NV];
-#pragma unroll
-    for (int n = 0; n < NV; ++n) d[n] = load_row_vec<DT>(row, v0 + n * kWave + lane, V);
+    load_chunk<DT, NV>(row, v0, lane, V, d);
     float f[NV][VEC];
 #pragma unroll
     for (int n = 0; n < NV; ++n) DT::unpack(d[n], f[n]);

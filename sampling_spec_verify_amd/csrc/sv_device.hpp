@@ -87,6 +87,21 @@ __device__ __forceinline__ u32x4 load_row_vec(const char *row, int gv, int V) {
     return d;
 }
 
+// The NV vectors v0 + n * 64 + lane (n < NV) of a row, as load_row_vec reads
+// them.  When the whole chunk lies inside the row's full vectors (v0 is
+// wave-uniform, so the test is too; it holds for every chunk but a row's
+// last), the loads go out without per-vector guards or masking.
+template <class DT, int NV>
+__device__ __forceinline__ void load_chunk(const char *row, int v0, int lane, int V, u32x4 (&d)[NV]) {
+    if (v0 + NV * kWave <= V / DT::kVec) {
+#pragma unroll
+        for (int n = 0; n < NV; ++n) d[n] = load16(row + int64_t(v0 + n * kWave + lane) * 16);
+    } else {
+#pragma unroll
+        for (int n = 0; n < NV; ++n) d[n] = load_row_vec<DT>(row, v0 + n * kWave + lane, V);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // lane moves
 // ---------------------------------------------------------------------------

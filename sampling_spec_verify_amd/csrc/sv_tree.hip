@@ -33,9 +33,12 @@ namespace sv {
 // lane reduces each of its 16-byte vectors to a maximum, the wave takes the
 // maximum of those, and only then does each lane look for its first element
 // equal to it (a lane's vectors, and the elements inside one, are in index
-// order).  NaNs are reported through a separate flag that marks the whole row
-// bad, so the maximum may ignore them.  Elements past V read as -inf and sit
-// above every valid index, so they never win a tie.
+// order).  The lane maxima use the NaN-propagating maximum (v_maximum3_f32),
+// so a NaN anywhere in a lane shows up in that lane's maximum and marks the
+// whole row bad; the wave maximum then ignores such lanes.  Signed zeros
+// compare equal in the position search, as in the first-maximum rule.
+// Elements past V read as -inf and sit above every valid index, so they never
+// win a tie.
 template <class DT, int NV>
 __device__ __forceinline__ void row_chunk_argmax(const TreeArgs &a, unsigned job) {
     const int c = static_cast<int>(job % static_cast<unsigned>(a.C1));
@@ -47,24 +50,21 @@ __device__ __forceinline__ void row_chunk_argmax(const TreeArgs &a, unsigned job
     const int V = a.V;
     const int v0 = c * (kWave * NV);
     u32x4 d[NV];
-#pragma unroll
-    for (int n = 0; n < NV; ++n) d[n] = load_row_vec<DT>(row, v0 + n * kWave + lane, V);
+    load_chunk<DT, NV>(row, v0, lane, V, d);
     float vm[NV];
-    bool nan = false;
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
         float f[VEC];
         DT::unpack(d[n], f);
         float m = f[0];
 #pragma unroll
-        for (int e = 1; e < VEC; ++e) m = fmaxf(m, f[e]);
+        for (int e = 1; e < VEC; ++e) m = __builtin_elementwise_maximum(m, f[e]);
         vm[n] = m;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) nan |= (f[e] != f[e]);
     }
     float lm = vm[0];
 #pragma unroll
-    for (int n = 1; n < NV; ++n) lm = fmaxf(lm, vm[n]);
+    for (int n = 1; n < NV; ++n) lm = __builtin_elementwise_maximum(lm, vm[n]);
+    const bool nan = (lm != lm);
     const float wm = wave_max(lm);
     // this lane's first vector, then first element, equal to the wave maximum
     int nsel = -1;
