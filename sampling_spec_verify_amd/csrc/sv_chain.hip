@@ -13,14 +13,17 @@
 //
 //  1. k_row_stats: one wavefront per (request, position, tensor, chunk) streams
 //     64 lanes x NV x 16 bytes of one drafted row with coalesced 16-byte loads
-//     and reduces it to (shift s, S = sum 2^(z c - s)) with c = log2(e)/T; the
-//     wave whose chunk holds the drafted token also records its logit.  Every
+//     and reduces it to (shift s, S = sum 2^(z c - s)) with c = log2(e)/T and
+//     s an integer, so partials combine by exact powers of two; the wave whose
+//     chunk holds the drafted token also records its logit.  Every
 //     drafted target and draft row is read exactly once.  Waves are
 //     independent (no LDS, no barrier); block 0 also clears the status word.
 //
 //  2. k_resolve_mass: grid (B requests, C2 chunks) of 1024-thread blocks.
 //     Every block stages its request's row partials in LDS, combines them in
-//     fp64, computes every a_i in fp64 and ballots the first rejection n;
+//     fp64, computes every a_i in fp64 from the ratio
+//     p_t(x) / q(x) = 2^((z_t(x) - z_q(x)) c - (s_t - s_q)) S_q / S_t (no
+//     logarithms) and ballots the first rejection n;
 //     block 0 writes every output but the sampled token.  Each block then
 //     reduces its chunk of the sampling row: the residual max(0, p_t - q) at
 //     row n (the same normalised law as max(0, p~ - q), since
@@ -125,7 +128,9 @@ __device__ __forceinline__ void row_chunk_stats(const ChainArgs &a, unsigned job
         for (int e = 0; e < VEC; ++e) m = fmaxf(m, f[n][e]);
 
     const float c_hi = a.c_hi, c_lo = a.c_lo;
-    const float s_lane = (m == -INFINITY) ? -INFINITY : m * c_hi;
+    // integer shift at or above the lane's largest z * c_hi: every weight is
+    // at most about 1 and lanes rescale by exact powers of two
+    const float s_lane = (m == -INFINITY) ? -INFINITY : ceilf(m * c_hi);
     const float s_use = (m == -INFINITY) ? 0.0f : s_lane;
     float acc[VEC];
 #pragma unroll
@@ -140,7 +145,7 @@ __device__ __forceinline__ void row_chunk_stats(const ChainArgs &a, unsigned job
     for (int e = 0; e < VEC; ++e) S_lane += acc[e];
 
     const float s_w = wave_max(s_lane);
-    const float fac = (s_lane == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_lane - s_w);
+    const float fac = (s_lane == -INFINITY) ? 0.0f : pow2_shift(s_lane - s_w);
     const double S_w = wave_sum_d(static_cast<double>(S_lane) * static_cast<double>(fac));
     if (lane == 0) {
         Part p;
@@ -174,14 +179,15 @@ struct SampleCtx {
     const char *row_t;      // target row of the sampling position
     const char *row_q;      // draft row (residual / mixture)
     float c_hi, c_lo;
-    float st_hi, st_lo;     // log2-domain normaliser shift of the target row
-    float sq_hi, sq_lo;     // ... of the draft row
+    float st, it;           // target row: p_t(v) = 2^(z c - st) * it
+    float sq, iq;           // draft row:  q(v)   = 2^(z c - sq) * iq
     float w_t, w_q;         // mixture weights (1 - lambda, lambda)
     int V;
 };
 
-__device__ __forceinline__ float log2_prob(float z, float c_hi, float c_lo, float s_hi, float s_lo) {
-    return fmaf(z, c_lo, fmaf(z, c_hi, -s_hi)) - s_lo;
+// 2^(z c - s) with c = c_hi + c_lo, the argument formed with two fmas
+__device__ __forceinline__ float pow2_logit(float z, float c_hi, float c_lo, float s) {
+    return __builtin_amdgcn_exp2f(fmaf(z, c_lo, fmaf(z, c_hi, -s)));
 }
 
 // The sampling row is cut into chunks of kBlock2 lanes x NV2 vectors, one
@@ -214,21 +220,30 @@ __device__ __forceinline__ void vec_weights(const SampleCtx &S, const u32x4 &dt,
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
         if (MODE == kBonus) {
-            w[e] = __builtin_amdgcn_exp2f(fmaf(ft[e], S.c_lo, fmaf(ft[e], S.c_hi, -s_use)));
+            w[e] = pow2_logit(ft[e], S.c_hi, S.c_lo, s_use);
         } else {
-            const float pt = __builtin_amdgcn_exp2f(log2_prob(ft[e], S.c_hi, S.c_lo, S.st_hi, S.st_lo));
-            const float pq = __builtin_amdgcn_exp2f(log2_prob(fq[e], S.c_hi, S.c_lo, S.sq_hi, S.sq_lo));
-            w[e] = (MODE == kResidual) ? fmaxf(pt - pq, 0.0f) : fmaf(S.w_t, pt, S.w_q * pq);
+            const float et = pow2_logit(ft[e], S.c_hi, S.c_lo, S.st);
+            const float pq = pow2_logit(fq[e], S.c_hi, S.c_lo, S.sq) * S.iq;
+            w[e] = (MODE == kResidual) ? fmaxf(fmaf(et, S.it, -pq), 0.0f)
+                                       : fmaf(S.w_t, et * S.it, S.w_q * pq);
         }
     }
 }
 
+// Sum of one vector's weights: a pairwise fp32 tree (adjacent pairs first),
+// widened once.  Its relative error stays below 3 * 2^-24 of the vector's
+// mass, so every inverse-CDF boundary built from these sums moves by less
+// than 2e-7 of the total.
 template <int VEC>
 __device__ __forceinline__ double vec_sum(const float *w) {
-    double s = 0.0;
+    float p[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) s += static_cast<double>(w[e]);
-    return s;
+    for (int e = 0; e < VEC; ++e) p[e] = w[e];
+#pragma unroll
+    for (int h = 1; h < VEC; h *= 2)
+#pragma unroll
+        for (int e = 0; e + h < VEC; e += 2 * h) p[e] = p[e] + p[e + h];
+    return static_cast<double>(p[0]);
 }
 
 struct ResolveShared {
@@ -328,7 +343,7 @@ __device__ __forceinline__ void resolve_request(const ChainArgs &a, int b, Resol
                 s = p.s;
                 Sc = p.S;
             }
-            if (s != -INFINITY) S += Sc * exp2(static_cast<double>(s) - static_cast<double>(smax));
+            if (s != -INFINITY) S += Sc * pow2_shift_d(static_cast<double>(s) - static_cast<double>(smax));
         }
         S = wave_sum_d(S);
         if (lane == 0) {
@@ -364,14 +379,16 @@ __device__ __forceinline__ void resolve_request(const ChainArgs &a, int b, Resol
             } else if (a.lam >= 1.0f) {
                 acc_p = 1.0;
             } else {
-                // log2 p(x) = z(x) c - s - log2 S for either model
-                const double lt = static_cast<double>(zt) * a.c_d - static_cast<double>(sh.s[2 * i]) - log2(sh.S[2 * i]);
-                const double lq = static_cast<double>(zq) * a.c_d - static_cast<double>(sh.s[2 * i + 1]) - log2(sh.S[2 * i + 1]);
-                if (lt >= lq) {
+                // p(x) = 2^(z(x) c - s) / S for either model, so
+                // p_t(x) / q(x) = 2^E S_q / S_t with E = (z_t(x) - z_q(x)) c - (s_t - s_q)
+                const double E = (static_cast<double>(zt) - static_cast<double>(zq)) * a.c_d -
+                                 (static_cast<double>(sh.s[2 * i]) - static_cast<double>(sh.s[2 * i + 1]));
+                const double ratio = exp2_d(E) * (sh.S[2 * i + 1] / sh.S[2 * i]);
+                if (ratio >= 1.0) {
                     acc_p = 1.0;
                 } else {
                     const double lam = static_cast<double>(a.lam);
-                    acc_p = fmin(1.0, (1.0 - lam) * exp2(lt - lq) + lam);
+                    acc_p = fmin(1.0, (1.0 - lam) * ratio + lam);
                 }
             }
             sh.a[i] = acc_p;
@@ -398,10 +415,10 @@ __device__ __forceinline__ SampleCtx sample_ctx(const ChainArgs &a, int b, const
     S.w_q = a.lam;
     S.row_t = row_ptr(a.g, 0, b, r.row);
     S.row_q = (r.mode != kBonus) ? row_ptr(a.g, 1, b, r.row) : nullptr;
-    S.st_hi = r.st_hi;
-    S.st_lo = r.st_lo;
-    S.sq_hi = r.sq_hi;
-    S.sq_lo = r.sq_lo;
+    S.st = r.st;
+    S.it = r.it;
+    S.sq = r.sq;
+    S.iq = r.iq;
     return S;
 }
 
@@ -431,7 +448,7 @@ __device__ __forceinline__ void chunk_pieces(const SampleCtx &S, int c, double *
         m = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves2; ++w) m = fmaxf(m, f16[w]);
-        s_rec = (m == -INFINITY) ? -INFINITY : m * S.c_hi;
+        s_rec = (m == -INFINITY) ? -INFINITY : ceilf(m * S.c_hi);   // integer: chunks rescale exactly
         s_use = (m == -INFINITY) ? 0.0f : s_rec;
     }
 #pragma unroll
@@ -459,18 +476,16 @@ __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int stage
     const int n = sh.n, K = sh.K;
     ReqRecord r;
     r.n = n;
-    r.st_hi = r.st_lo = r.sq_hi = r.sq_lo = 0.0f;
+    r.st = r.sq = r.it = r.iq = 0.0f;
     if (n < K) {
         r.mode = kResidual;
         r.row = sh.rowi[n];
         r.rows_ok = !sh.row_bad[2 * n] && !sh.row_bad[2 * n + 1];
-        // p(v) = 2^(z c - sigma), sigma = s + log2 S, split into hi + lo floats
-        const double st = static_cast<double>(sh.s[2 * n]) + log2(sh.S[2 * n]);
-        const double sq = static_cast<double>(sh.s[2 * n + 1]) + log2(sh.S[2 * n + 1]);
-        r.st_hi = static_cast<float>(st);
-        r.st_lo = static_cast<float>(st - static_cast<double>(r.st_hi));
-        r.sq_hi = static_cast<float>(sq);
-        r.sq_lo = static_cast<float>(sq - static_cast<double>(r.sq_hi));
+        // p(v) = 2^(z c - s) / S
+        r.st = sh.s[2 * n];
+        r.sq = sh.s[2 * n + 1];
+        r.it = static_cast<float>(1.0 / sh.S[2 * n]);
+        r.iq = static_cast<float>(1.0 / sh.S[2 * n + 1]);
     } else {
         r.mode = kBonus;
         r.row = sh.rowi[K];
@@ -519,14 +534,15 @@ __device__ __forceinline__ void load_pieces(const ChainArgs &a, int b, int pp, L
     const int p0 = threadIdx.x * pp;
 #pragma unroll
     for (int j = 0; j < kLocPP; ++j) {
-        const int p = p0 + j;
-        if (j < pp && p < np) {
-            const double *rc = cr + int64_t(p / kPieces) * a.rec_stride;
-            P.m[j] = rc[2 + p % kPieces];
-            P.s[j] = static_cast<float>(rc[0]);
-        } else {
-            P.m[j] = 0.0;
-            P.s[j] = -INFINITY;
+        P.m[j] = 0.0;
+        P.s[j] = -INFINITY;
+        if (j < pp) {                        // pp is uniform: whole iterations are skipped
+            const int p = p0 + j;
+            if (p < np) {
+                const double *rc = cr + int64_t(p / kPieces) * a.rec_stride;
+                P.m[j] = rc[2 + p % kPieces];
+                P.s[j] = static_cast<float>(rc[0]);
+            }
         }
     }
 }
@@ -548,7 +564,8 @@ __device__ __forceinline__ int locate(const SampleCtx &S, const LocatePieces &P,
     if (MODE == kBonus) {
         float sm = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < kLocPP; ++j) sm = fmaxf(sm, P.s[j]);
+        for (int j = 0; j < kLocPP; ++j)
+            if (j < pp) sm = fmaxf(sm, P.s[j]);
         smax = block_max(sm, L.f4);
     }
     double sc[kLocPP];
@@ -556,9 +573,11 @@ __device__ __forceinline__ int locate(const SampleCtx &S, const LocatePieces &P,
 #pragma unroll
     for (int j = 0; j < kLocPP; ++j) {
         sc[j] = 1.0;
-        if (MODE == kBonus)
-            sc[j] = (P.s[j] == -INFINITY) ? 0.0 : exp2(static_cast<double>(P.s[j]) - static_cast<double>(smax));
-        tot += P.m[j] * sc[j];
+        if (j < pp) {
+            if (MODE == kBonus)
+                sc[j] = (P.s[j] == -INFINITY) ? 0.0 : pow2_shift_d(static_cast<double>(P.s[j]) - static_cast<double>(smax));
+            tot += P.m[j] * sc[j];
+        }
     }
     if (threadIdx.x == 0) {
         L.pstar = -1;
@@ -619,14 +638,8 @@ __device__ __forceinline__ int locate(const SampleCtx &S, const LocatePieces &P,
         load_vec<DT, MODE>(S, gv, dt, dq);
         float w[VEC];
         vec_weights<DT, MODE>(S, dt, dq, gv * VEC, s_use, w);
-        double x = vec_sum<VEC>(w);
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const double o = __shfl_up(x, off, kWave);
-            if (lane >= off) x += o;
-        }
-        const double prev = __shfl_up(x, 1, kWave);
-        const double excl = (lane == 0) ? 0.0 : prev;
+        const double x = wave_scan_d(vec_sum<VEC>(w));
+        const double excl = dpp_shift_d<kDppWaveShr1, 0xF, 0xF>(x);   // 0 at lane 0
         int last = -1;
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
@@ -663,8 +676,8 @@ __device__ __forceinline__ int sample_mixture(const SampleCtx &S, double u, Loca
     const int V = S.V;
     auto weight = [&](int v) -> float {
         if (v >= V) return 0.0f;
-        const float pt = __builtin_amdgcn_exp2f(log2_prob(DT::load1(S.row_t, v), S.c_hi, S.c_lo, S.st_hi, S.st_lo));
-        const float pq = __builtin_amdgcn_exp2f(log2_prob(DT::load1(S.row_q, v), S.c_hi, S.c_lo, S.sq_hi, S.sq_lo));
+        const float pt = pow2_logit(DT::load1(S.row_t, v), S.c_hi, S.c_lo, S.st) * S.it;
+        const float pq = pow2_logit(DT::load1(S.row_q, v), S.c_hi, S.c_lo, S.sq) * S.iq;
         return fmaf(S.w_t, pt, S.w_q * pq);
     };
     double carry = 0.0;

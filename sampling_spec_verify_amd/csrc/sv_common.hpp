@@ -13,8 +13,10 @@
 namespace sv {
 
 // Partial reduction of one wave-chunk of a row: the sum S of 2^(z*c - s) over
-// the chunk's elements, relative to the shift s (fp32).  s = -inf marks a
-// chunk without any finite element.
+// the chunk's elements, relative to the shift s, an integer (held as a float:
+// the ceiling of the chunk's largest logit times c_hi), so that partials
+// rescale exactly by powers of two.  s = -inf marks a chunk without any finite
+// element.
 struct alignas(16) Part {
     float s;
     float z;        // the drafted token's logit, in the partial of the chunk holding it
@@ -35,7 +37,8 @@ struct alignas(16) ReqRecord {
     int mode;       // residual (0) or bonus (1)
     int row;        // request row of the sampling position
     int rows_ok;    // the residual rows have valid statistics
-    float st_hi, st_lo, sq_hi, sq_lo;   // log2 normaliser shifts (target, draft)
+    float st, sq;   // integer shifts of the target and draft rows: p(v) = 2^(z c - s) / S
+    float it, iq;   // 1 / S of the target and draft rows
 };
 
 // Request geometry of the chain and path calls.

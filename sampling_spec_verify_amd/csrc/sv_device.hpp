@@ -102,6 +102,42 @@ __device__ __forceinline__ void load_chunk(const char *row, int v0, int lane, in
     }
 }
 
+// 2^d for an integer-valued d <= 0 (a difference of two integer shifts),
+// exactly; 0 below the smallest subnormal.
+__device__ __forceinline__ float pow2_shift(float d) {
+    return d < -149.0f ? 0.0f : ldexpf(1.0f, static_cast<int>(d));
+}
+__device__ __forceinline__ double pow2_shift_d(double d) {
+    return d < -1074.0 ? 0.0 : ldexp(1.0, static_cast<int>(d));
+}
+
+// 2^x in fp64: x = k + f with k = floor(x), 2^f = sqrt(2) e^y with
+// y = (f - 1/2) ln 2 in [-0.35, 0.35], e^y by its Taylor series through y^13
+// (truncation below 2e-16 relative).  0 below -1100, +inf above 1100, NaN
+// passes through.
+__device__ __forceinline__ double exp2_d(double x) {
+    if (x != x) return x;
+    if (x < -1100.0) return 0.0;
+    if (x > 1100.0) return INFINITY;
+    const double k = floor(x);
+    const double y = (x - k - 0.5) * 0.69314718055994530942;
+    double p = 1.0 / 6227020800.0;                    // 1/13!
+    p = fma(p, y, 1.0 / 479001600.0);                 // 1/12!
+    p = fma(p, y, 1.0 / 39916800.0);
+    p = fma(p, y, 1.0 / 3628800.0);
+    p = fma(p, y, 1.0 / 362880.0);
+    p = fma(p, y, 1.0 / 40320.0);
+    p = fma(p, y, 1.0 / 5040.0);
+    p = fma(p, y, 1.0 / 720.0);
+    p = fma(p, y, 1.0 / 120.0);
+    p = fma(p, y, 1.0 / 24.0);
+    p = fma(p, y, 1.0 / 6.0);
+    p = fma(p, y, 0.5);
+    p = fma(p, y, 1.0);
+    p = fma(p, y, 1.0);
+    return ldexp(1.41421356237309504880 * p, static_cast<int>(k));
+}
+
 // ---------------------------------------------------------------------------
 // lane moves
 // ---------------------------------------------------------------------------
@@ -163,6 +199,33 @@ __device__ __forceinline__ int wave_min_i(int v) {
     return min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
 }
 
+// Lane l of a wave receives v of lane l - n within its 16-lane row (row_shr),
+// of lane l - 1 across the wave (wave_shr), or lane 15 / 31 broadcast to the
+// following rows (row_bcast), only where the row mask (rows 0..3) and bank
+// mask allow; every other lane receives 0.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ double dpp_shift_d(double v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, BANK_MASK, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, BANK_MASK, false);
+    return __hiloint2double(hi, lo);
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+constexpr int kDppWaveShr1 = 0x138;    // whole wave, lane l receives lane l - 1
+
+// Inclusive scan of one double per lane, in lane order (log-step: shifts by
+// 1, 2, 4, 8 inside each 16-lane row, then lane 15 into rows 1 and 3, then
+// lane 31 into rows 2 and 3).
+__device__ __forceinline__ double wave_scan_d(double v) {
+    v += dpp_shift_d<kDppRowShr1, 0xF, 0xF>(v);
+    v += dpp_shift_d<kDppRowShr2, 0xF, 0xF>(v);
+    v += dpp_shift_d<kDppRowShr4, 0xF, 0xF>(v);
+    v += dpp_shift_d<kDppRowShr8, 0xF, 0xF>(v);
+    v += dpp_shift_d<kDppRowBcast15, 0xA, 0xF>(v);
+    v += dpp_shift_d<kDppRowBcast31, 0xC, 0xF>(v);
+    return v;
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
     v += dpp_d<kDppXor1>(v);
     v += dpp_d<kDppXor2>(v);
@@ -196,12 +259,7 @@ struct Scan {
 __device__ __forceinline__ Scan block_scan_d(double v, double carry, double *sh4) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
-    double x = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const double o = __shfl_up(x, off, kWave);
-        if (lane >= off) x += o;
-    }
+    const double x = wave_scan_d(v);
     if (lane == kWave - 1) sh4[w] = x;
     __syncthreads();
     const double b1 = sh4[0];
@@ -209,7 +267,7 @@ __device__ __forceinline__ Scan block_scan_d(double v, double carry, double *sh4
     const double b3 = b2 + sh4[2];
     const double tot = b3 + sh4[3];
     const double base = (w == 0) ? 0.0 : (w == 1) ? b1 : (w == 2) ? b2 : b3;
-    const double prev = __shfl_up(x, 1, kWave);
+    const double prev = dpp_shift_d<kDppWaveShr1, 0xF, 0xF>(x);   // lane l - 1 (0 at lane 0)
     Scan s;
     s.incl = carry + (base + x);
     s.excl = carry + ((lane == 0) ? base : (base + prev));
