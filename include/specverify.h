@@ -146,6 +146,26 @@ sv_status sv_chain_accept_resample(const void *target_logits, int64_t ld_t,
                                    int32_t *status, void *workspace, size_t workspace_bytes,
                                    hipStream_t stream);
 
+/*
+ * sv_chain_row_stats with the row-statistics kernel timed: the launch records
+ * kernel_start at the kernel's first wave and kernel_stop after its last (the
+ * dispatch's own begin and end timestamps), so hipEventElapsedTime on the pair
+ * gives the kernel duration without launch gaps or queueing.  Either event may
+ * be NULL (then neither is recorded).  The events are owned by the caller,
+ * created with hipEventCreate on the device that runs the stream; errors as
+ * sv_chain_row_stats.
+ */
+sv_status sv_chain_row_stats_timed(const void *target_logits, int64_t ld_t,
+                                   const void *draft_logits, int64_t ld_q,
+                                   sv_dtype dtype, int B, int K, int V,
+                                   const int32_t *draft_tokens, const int32_t *draft_len,
+                                   const float *u_accept, const float *u_sample,
+                                   float lambda, float temperature,
+                                   int32_t *accepted, int32_t *out_tokens, float *accept_prob,
+                                   int32_t *status, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream, hipEvent_t kernel_start,
+                                   hipEvent_t kernel_stop);
+
 /* ------------------------------------------------------------------------
  * Draft trees ([SD] "Tree Speculation", [EAGLE] greedy match + tree attention)
  *
@@ -196,6 +216,18 @@ sv_status sv_tree_greedy_walk(const void *target_logits, int64_t ld_t, sv_dtype 
                               int32_t *accepted, int32_t *out_tokens, int32_t *accepted_nodes,
                               int Dmax, int32_t *status, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sv_tree_row_argmax with the row-argmax kernel timed by kernel_start /
+ * kernel_stop, exactly as sv_chain_row_stats_timed times its kernel.
+ */
+sv_status sv_tree_row_argmax_timed(const void *target_logits, int64_t ld_t, sv_dtype dtype,
+                                   int B, int N, int V,
+                                   const int32_t *parent, const int32_t *node_token,
+                                   int32_t *accepted, int32_t *out_tokens,
+                                   int32_t *accepted_nodes, int Dmax, int32_t *status,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                   hipEvent_t kernel_start, hipEvent_t kernel_stop);
 
 /*
  * Stochastic verification along one caller-chosen root->leaf path: chain

@@ -764,6 +764,7 @@ struct ChainReq {
     void *ws;
     size_t ws_bytes;
     hipStream_t stream;
+    hipEvent_t ev_start, ev_stop;   // optional: attached to the row-statistics launch
 };
 
 int choose_nv(int B, int P, int V, int vec) { return choose_stream_nv(2LL * B * P, V, vec); }
@@ -845,11 +846,11 @@ sv_status run_typed(const ChainReq &q, int which) {
         const int jobs = static_cast<int>(int64_t(q.B) * a.g.Pcap * 2 * a.C1);
         const dim3 grid(static_cast<unsigned>(jobs > 0 ? cdiv(jobs, kWaves) : 1));
         if (nv == 8)
-            hipLaunchKernelGGL((k_row_stats<DT, 8>), grid, dim3(kBlock), 0, q.stream, a, jobs);
+            launch_timed(k_row_stats<DT, 8>, grid, dim3(kBlock), 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
         else if (nv == 4)
-            hipLaunchKernelGGL((k_row_stats<DT, 4>), grid, dim3(kBlock), 0, q.stream, a, jobs);
+            launch_timed(k_row_stats<DT, 4>, grid, dim3(kBlock), 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
         else
-            hipLaunchKernelGGL((k_row_stats<DT, 2>), grid, dim3(kBlock), 0, q.stream, a, jobs);
+            launch_timed(k_row_stats<DT, 2>, grid, dim3(kBlock), 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
         if (hipGetLastError() != hipSuccess) return SV_EHIP;
     }
     if (which & 2) {
@@ -908,6 +909,8 @@ ChainReq chain_req(const void *t, int64_t ld_t, const void *d, int64_t ld_q, sv_
     q.ws = ws;
     q.ws_bytes = wsb;
     q.stream = s;
+    q.ev_start = nullptr;
+    q.ev_stop = nullptr;
     return q;
 }
 
@@ -959,6 +962,23 @@ sv_status sv_chain_row_stats(const void *target_logits, int64_t ld_t, const void
                                accepted, out_tokens, accept_prob, status, workspace,
                                workspace_bytes, stream),
                      1);
+}
+
+sv_status sv_chain_row_stats_timed(const void *target_logits, int64_t ld_t,
+                                   const void *draft_logits, int64_t ld_q, sv_dtype dtype, int B,
+                                   int K, int V, const int32_t *draft_tokens,
+                                   const int32_t *draft_len, const float *u_accept,
+                                   const float *u_sample, float lambda, float temperature,
+                                   int32_t *accepted, int32_t *out_tokens, float *accept_prob,
+                                   int32_t *status, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream, hipEvent_t kernel_start,
+                                   hipEvent_t kernel_stop) {
+    ChainReq q = chain_req(target_logits, ld_t, draft_logits, ld_q, dtype, B, K, V, draft_tokens,
+                           draft_len, u_accept, u_sample, lambda, temperature, accepted,
+                           out_tokens, accept_prob, status, workspace, workspace_bytes, stream);
+    q.ev_start = kernel_start;
+    q.ev_stop = kernel_stop;
+    return run_chain(q, 1);
 }
 
 sv_status sv_chain_accept_resample(const void *target_logits, int64_t ld_t,

@@ -3,6 +3,7 @@
 // validation.  Validation runs on the host before any HIP call.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stddef.h>
@@ -189,6 +190,18 @@ inline bool temperature_split(float T, float *c_hi, float *c_lo, double *c_d) {
     *c_lo = lo;
     *c_d = static_cast<double>(hi) + static_cast<double>(lo);
     return true;
+}
+
+// Launches `kernel` on `stream`; when either event is given, the launch
+// records them at the kernel's own begin and end (the dispatch timestamps),
+// so their elapsed time is the kernel duration without queueing gaps.
+template <typename Kernel, typename... Args>
+inline void launch_timed(Kernel kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream,
+                         hipEvent_t ev_start, hipEvent_t ev_stop, Args... args) {
+    if (ev_start != nullptr || ev_stop != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev_start, ev_stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
 }
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

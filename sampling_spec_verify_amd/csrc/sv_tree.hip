@@ -268,7 +268,8 @@ namespace {
 using namespace sv;
 
 template <class DT>
-sv_status run_tree(const TreeArgs &a0, hipStream_t stream, int which) {
+sv_status run_tree(const TreeArgs &a0, hipStream_t stream, int which, hipEvent_t ev_start,
+                   hipEvent_t ev_stop) {
     TreeArgs a = a0;
     const int64_t rows = int64_t(a.B) * (a.N + 1);
     const int nv = choose_stream_nv(rows, a.V, DT::kVec);
@@ -278,11 +279,11 @@ sv_status run_tree(const TreeArgs &a0, hipStream_t stream, int which) {
         const int jobs = static_cast<int>(rows * a.C1);
         const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, cdiv(jobs, kWaves))));
         if (nv == 8)
-            hipLaunchKernelGGL((k_row_argmax<DT, 8>), grid, dim3(kBlock), 0, stream, a, jobs);
+            launch_timed(k_row_argmax<DT, 8>, grid, dim3(kBlock), 0, stream, ev_start, ev_stop, a, jobs);
         else if (nv == 4)
-            hipLaunchKernelGGL((k_row_argmax<DT, 4>), grid, dim3(kBlock), 0, stream, a, jobs);
+            launch_timed(k_row_argmax<DT, 4>, grid, dim3(kBlock), 0, stream, ev_start, ev_stop, a, jobs);
         else
-            hipLaunchKernelGGL((k_row_argmax<DT, 2>), grid, dim3(kBlock), 0, stream, a, jobs);
+            launch_timed(k_row_argmax<DT, 2>, grid, dim3(kBlock), 0, stream, ev_start, ev_stop, a, jobs);
         if (hipGetLastError() != hipSuccess) return SV_EHIP;
     }
     if (which & 2) {
@@ -301,7 +302,8 @@ sv_status run_tree(const TreeArgs &a0, hipStream_t stream, int which) {
 sv_status greedy_call(const void *target_logits, int64_t ld_t, sv_dtype dtype, int B, int N,
                       int V, const int32_t *parent, const int32_t *node_token, int32_t *accepted,
                       int32_t *out_tokens, int32_t *accepted_nodes, int Dmax, int32_t *status,
-                      void *workspace, size_t workspace_bytes, hipStream_t stream, int which) {
+                      void *workspace, size_t workspace_bytes, hipStream_t stream, int which,
+                      hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
     const int eb = elem_bytes(dtype);
     if (eb == 0) return SV_EDTYPE;
     if (B < 0 || N < 0 || N > SV_MAX_TREE_NODES || V < 1 || Dmax < 0 || B > (1 << 30))
@@ -331,7 +333,8 @@ sv_status greedy_call(const void *target_logits, int64_t ld_t, sv_dtype dtype, i
     a.accepted_nodes = accepted_nodes;
     a.status = status ? status : reinterpret_cast<int32_t *>(ws + L.status);
     a.part = reinterpret_cast<ArgPart *>(ws + L.part);
-    return dtype == SV_BF16 ? run_tree<Bf16>(a, stream, which) : run_tree<F32>(a, stream, which);
+    return dtype == SV_BF16 ? run_tree<Bf16>(a, stream, which, ev_start, ev_stop)
+                            : run_tree<F32>(a, stream, which, ev_start, ev_stop);
 }
 
 }  // namespace
@@ -361,6 +364,17 @@ sv_status sv_tree_row_argmax(const void *target_logits, int64_t ld_t, sv_dtype d
                              hipStream_t stream) {
     return greedy_call(target_logits, ld_t, dtype, B, N, V, parent, node_token, accepted, out_tokens,
                        accepted_nodes, Dmax, status, workspace, workspace_bytes, stream, 1);
+}
+
+sv_status sv_tree_row_argmax_timed(const void *target_logits, int64_t ld_t, sv_dtype dtype, int B,
+                                   int N, int V, const int32_t *parent, const int32_t *node_token,
+                                   int32_t *accepted, int32_t *out_tokens,
+                                   int32_t *accepted_nodes, int Dmax, int32_t *status,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                   hipEvent_t kernel_start, hipEvent_t kernel_stop) {
+    return greedy_call(target_logits, ld_t, dtype, B, N, V, parent, node_token, accepted, out_tokens,
+                       accepted_nodes, Dmax, status, workspace, workspace_bytes, stream, 1,
+                       kernel_start, kernel_stop);
 }
 
 sv_status sv_tree_greedy_walk(const void *target_logits, int64_t ld_t, sv_dtype dtype, int B, int N,

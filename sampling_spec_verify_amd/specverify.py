@@ -40,10 +40,12 @@ SIGNATURES = {
     "sv_chain_verify": (_CHAIN_ARGS, _I),
     "sv_chain_row_stats": (_CHAIN_ARGS, _I),
     "sv_chain_accept_resample": (_CHAIN_ARGS, _I),
+    "sv_chain_row_stats_timed": (_CHAIN_ARGS + [_P, _P], _I),
     "sv_tree_workspace_bytes": ([_I, _I, _I], _S),
     "sv_tree_verify_greedy": (_GREEDY_ARGS, _I),
     "sv_tree_row_argmax": (_GREEDY_ARGS, _I),
     "sv_tree_greedy_walk": (_GREEDY_ARGS, _I),
+    "sv_tree_row_argmax_timed": (_GREEDY_ARGS + [_P, _P], _I),
     "sv_tree_verify_path": ([_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _I, _P, _P, _F, _F, _P, _P,
                              _P, _P, _P, _S, _P], _I),
 }
@@ -68,6 +70,42 @@ def lib() -> ctypes.CDLL:
             fn.restype = res
         _lib = L
     return _lib
+
+
+class KernelTimer:
+    """``n`` pairs of HIP events for the ``*_timed`` calls.
+
+    A timed call attaches pair ``i`` to its kernel launch, so that
+    ``elapsed_ms(i)`` is that kernel's own duration (dispatch begin to end).
+    """
+
+    def __init__(self, n: int):
+        _torch().cuda.init()
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(_P)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(_F), _P, _P]
+        self._hip.hipEventDestroy.argtypes = [_P]
+        self.start, self.stop = [], []
+        for _ in range(n):
+            for lst in (self.start, self.stop):
+                ev = _P()
+                if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                    raise SpecVerifyError("hipEventCreate failed")
+                lst.append(ev)
+
+    def pair(self, i: int):
+        return self.start[i], self.stop[i]
+
+    def elapsed_ms(self, i: int) -> float:
+        ms = _F()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i]) != 0:
+            raise SpecVerifyError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for ev in self.start + self.stop:
+            self._hip.hipEventDestroy(ev)
+        self.start, self.stop = [], []
 
 
 def status_string(code: int) -> str:
@@ -208,8 +246,13 @@ class ChainCall:
         _check(lib().sv_chain_verify(*self._cached), "sv_chain_verify")
         return self.out
 
-    def row_stats(self):
-        _check(lib().sv_chain_row_stats(*self._cached), "sv_chain_row_stats")
+    def row_stats(self, events=None):
+        """Launch the row-statistics kernel; ``events`` = (start, stop) times it."""
+        if events is None:
+            _check(lib().sv_chain_row_stats(*self._cached), "sv_chain_row_stats")
+        else:
+            _check(lib().sv_chain_row_stats_timed(*self._cached, *events),
+                   "sv_chain_row_stats_timed")
 
     def accept_resample(self) -> ChainOut:
         _check(lib().sv_chain_accept_resample(*self._cached), "sv_chain_accept_resample")
@@ -258,8 +301,13 @@ class TreeGreedyCall:
         _check(lib().sv_tree_verify_greedy(*self._cached), "sv_tree_verify_greedy")
         return self.out
 
-    def row_argmax(self):
-        _check(lib().sv_tree_row_argmax(*self._cached), "sv_tree_row_argmax")
+    def row_argmax(self, events=None):
+        """Launch the row-argmax kernel; ``events`` = (start, stop) times it."""
+        if events is None:
+            _check(lib().sv_tree_row_argmax(*self._cached), "sv_tree_row_argmax")
+        else:
+            _check(lib().sv_tree_row_argmax_timed(*self._cached, *events),
+                   "sv_tree_row_argmax_timed")
 
     def walk(self) -> TreeGreedyOut:
         _check(lib().sv_tree_greedy_walk(*self._cached), "sv_tree_greedy_walk")

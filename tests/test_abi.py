@@ -22,9 +22,10 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["sv_status_string", "sv_chain_workspace_bytes", "sv_chain_verify",
                             "sv_chain_row_stats", "sv_chain_accept_resample",
+                            "sv_chain_row_stats_timed",
                             "sv_tree_workspace_bytes", "sv_tree_verify_greedy",
                             "sv_tree_row_argmax", "sv_tree_greedy_walk",
-                            "sv_tree_verify_path"])
+                            "sv_tree_row_argmax_timed", "sv_tree_verify_path"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -62,13 +63,15 @@ def chain_call(fn="sv_chain_verify", **kw):
                 ap=FAKE, st=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
     args.update(kw)
     L = sv.lib()
+    timed = (FAKE, FAKE) if fn.endswith("_timed") else ()
     return getattr(L, fn)(args["t"], args["ld_t"], args["d"], args["ld_q"], args["dtype"], args["B"],
                           args["K"], args["V"], args["tok"], args["dl"], args["ua"], args["us"],
                           args["lam"], args["T"], args["acc"], args["out"], args["ap"], args["st"],
-                          args["ws"], args["wsb"], args["stream"])
+                          args["ws"], args["wsb"], args["stream"], *timed)
 
 
-@pytest.mark.parametrize("fn", ["sv_chain_verify", "sv_chain_row_stats", "sv_chain_accept_resample"])
+@pytest.mark.parametrize("fn", ["sv_chain_verify", "sv_chain_row_stats", "sv_chain_accept_resample",
+                                "sv_chain_row_stats_timed"])
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), sv.SV_EDTYPE),
     (dict(B=-1), sv.SV_EINVAL),
@@ -116,17 +119,19 @@ def test_chain_without_drafts_needs_no_draft_tensor():
     assert chain_call(K=0, d=None, tok=None, ua=None, wsb=16) == sv.SV_EWORKSPACE
 
 
-GREEDY_ENTRIES = ["sv_tree_verify_greedy", "sv_tree_row_argmax", "sv_tree_greedy_walk"]
+GREEDY_ENTRIES = ["sv_tree_verify_greedy", "sv_tree_row_argmax", "sv_tree_greedy_walk",
+                  "sv_tree_row_argmax_timed"]
 
 
 def greedy_call(fn="sv_tree_verify_greedy", **kw):
     args = dict(t=FAKE, ld=128, dtype=sv.SV_BF16, B=2, N=5, V=128, par=FAKE, tok=FAKE, acc=FAKE,
                 out=FAKE, nodes=FAKE, Dmax=6, st=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
     args.update(kw)
+    timed = (FAKE, FAKE) if fn.endswith("_timed") else ()
     return getattr(sv.lib(), fn)(args["t"], args["ld"], args["dtype"], args["B"], args["N"],
                                  args["V"], args["par"], args["tok"], args["acc"], args["out"],
                                  args["nodes"], args["Dmax"], args["st"], args["ws"], args["wsb"],
-                                 args["stream"])
+                                 args["stream"], *timed)
 
 
 @pytest.mark.parametrize("kw,code", [
