@@ -4,9 +4,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
 
 One step is one full verify call on one batch of seeded synthetic logits that
-already sit in HBM: for a chain workload both launches (row statistics, then
-accept / first rejection / residual-or-bonus resample / emit); for ``c5`` the
-greedy tree call.  ``R`` copies of the inputs (at least 1 GiB in all, four
+already sit in HBM: for a chain workload ``sv_chain_verify`` (row statistics,
+then accept / first rejection / residual-or-bonus resample / emit); for ``c5``
+``sv_tree_verify_greedy``.  On every n-th step the same kernels run through
+the two stage calls instead, the first of them timed.  ``R`` copies of the inputs (at least 1 GiB in all, four
 times the 256 MB Infinity Cache) are rotated so that every step reads HBM.
 
 Prints one JSON line.  ``roofline`` rates the row-statistics kernel (the
@@ -211,8 +212,11 @@ def main():
 
         def step(i, events=None):
             c = calls[i % R]
-            c.row_argmax(events)
-            c.walk()
+            if events is None:
+                c.run()
+            else:
+                c.row_argmax(events)
+                c.walk()
     else:
         drfs = device_copies(x.draft, x.dtype, R, torch)
         tok = torch.from_numpy(x.tokens).to(dev)
@@ -224,8 +228,11 @@ def main():
 
         def step(i, events=None):
             c = calls[i % R]
-            c.row_stats(events)
-            c.accept_resample()
+            if events is None:
+                c.run()
+            else:
+                c.row_stats(events)
+                c.accept_resample()
 
     for i in range(args.warmup):
         step(i)

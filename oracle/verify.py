@@ -286,6 +286,50 @@ def tree_path_one(zt: np.ndarray, zq: np.ndarray, node_token, path, u_acc, u_s: 
                             np.asarray(u_acc)[:d], u_s, lam, T)
 
 
+@dataclasses.dataclass
+class TreeMask:
+    mask: np.ndarray           # [N+1, N+1] bool: row i may attend to column j
+    depth: np.ndarray          # [N+1] int: edges from the root
+    bad: bool                  # some parent was out of range
+
+
+def tree_attention_mask_one(parent) -> TreeMask:
+    """Tree-attention mask of one draft tree.
+
+    [EAGLE] "3. 验证阶段树形attention": to verify a whole tree in one target
+    pass, every candidate token may only see its own ancestor path.  Reading:
+    position i (node i; 0 is the root) sees itself and every ancestor, the
+    root included; depth[i] is the number of edges from the root (the offset
+    of node i's position after the root).  A node whose parent is not in
+    [0, i) is read as a child of the root and reported as bad.
+    """
+    N = len(parent)
+    mask = np.zeros((N + 1, N + 1), dtype=bool)
+    depth = np.zeros(N + 1, dtype=np.int64)
+    par = [-1] + [int(p) for p in parent]
+    bad = False
+    for i in range(1, N + 1):
+        if not 0 <= par[i] < i:
+            par[i] = 0
+            bad = True
+    for i in range(N + 1):
+        v = i
+        while v >= 0:                 # walk to the root; parents decrease, so this ends
+            mask[i, v] = True
+            v = par[v]
+        depth[i] = mask[i].sum() - 1
+    return TreeMask(mask, depth, bad)
+
+
+def pack_mask_rows(mask: np.ndarray, words: int) -> np.ndarray:
+    """Bit j of 32-bit word j // 32 of a row holds column j (little-endian)."""
+    R, C = mask.shape
+    out = np.zeros((R, words), dtype=np.uint32)
+    for j in range(C):
+        out[:, j // 32] |= mask[:, j].astype(np.uint32) << np.uint32(j % 32)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # batches ([SD] "批量投机": every request is verified independently)
 # ---------------------------------------------------------------------------
@@ -355,3 +399,17 @@ def tree_path(target, draft, node_token, path, u_accept, u_sample, lam, T,
         flag[b] = r.flagged
         det[b] = r
     return BatchResult(acc, out, ap, flag, det)
+
+
+def tree_attention_mask(parent, words: int):
+    """A batch of trees: (mask [B, N+1, words] uint32, depth [B, N+1], bad [B])."""
+    B, N = parent.shape
+    mask = np.zeros((B, N + 1, words), dtype=np.uint32)
+    depth = np.zeros((B, N + 1), dtype=np.int64)
+    bad = np.zeros(B, dtype=bool)
+    for b in range(B):
+        r = tree_attention_mask_one(parent[b])
+        mask[b] = pack_mask_rows(r.mask, words)
+        depth[b] = r.depth
+        bad[b] = r.bad
+    return mask, depth, bad

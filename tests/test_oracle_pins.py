@@ -16,8 +16,8 @@ import pytest
 import scipy.special
 import scipy.stats
 
-from oracle import (InvalidRow, chain_verify_one, inverse_cdf, softmax_T, tree_greedy_one,
-                    tree_path_one)
+from oracle import (InvalidRow, chain_verify_one, inverse_cdf, pack_mask_rows, softmax_T,
+                    tree_attention_mask_one, tree_greedy_one, tree_path_one)
 
 GRID = 2 ** 24          # the library's uniforms are fp32 multiples of 2^-24
 
@@ -440,3 +440,73 @@ def test_path_mode_is_chain_on_gathered_rows():
         c = chain_verify_one(zt[[0, 2, 5, 7]], zq[[0, 2, 5]], tok[[1, 4, 6]], ua[:3], us, 0.2, 0.9)
         assert (r.accepted, r.tokens) == (c.accepted, c.tokens)
         np.testing.assert_array_equal(r.a, c.a)
+
+
+# ---------------------------------------------------------------------------
+# tree-attention mask: each node sees its ancestor path (and itself)
+# ---------------------------------------------------------------------------
+
+
+def _closure(parent):
+    """Ancestor-or-self relation by boolean matrix powers of the parent map
+    (an independent route: no walk, no depth recursion)."""
+    N = len(parent)
+    A = np.zeros((N + 1, N + 1), dtype=np.int64)
+    for i, p in enumerate(parent, start=1):
+        A[i, p] = 1
+    R = np.eye(N + 1, dtype=np.int64)
+    while True:
+        nxt = np.minimum(R + R @ A, 1)
+        if np.array_equal(nxt, R):
+            return R.astype(bool)
+        R = nxt
+
+
+def test_mask_of_chain_is_causal():
+    for N in (0, 1, 5, 40):
+        r = tree_attention_mask_one(np.arange(N))
+        np.testing.assert_array_equal(r.mask, np.tril(np.ones((N + 1, N + 1), dtype=bool)))
+        np.testing.assert_array_equal(r.depth, np.arange(N + 1))
+
+
+def test_mask_of_star_is_root_plus_self():
+    N = 9
+    r = tree_attention_mask_one(np.zeros(N, dtype=int))
+    want = np.eye(N + 1, dtype=bool)
+    want[:, 0] = True
+    np.testing.assert_array_equal(r.mask, want)
+    np.testing.assert_array_equal(r.depth, [0] + [1] * N)
+
+
+def test_mask_matches_matrix_closure():
+    rng = np.random.default_rng(31)
+    for _ in range(200):
+        N = int(rng.integers(1, 40))
+        parent = np.array([int(rng.integers(0, i)) for i in range(1, N + 1)])
+        r = tree_attention_mask_one(parent)
+        np.testing.assert_array_equal(r.mask, _closure(parent))
+        # depth by the recursion depth[i] = depth[parent] + 1 in node order
+        d = [0] * (N + 1)
+        for i in range(1, N + 1):
+            d[i] = d[parent[i - 1]] + 1
+        np.testing.assert_array_equal(r.depth, d)
+        assert not r.bad
+
+
+def test_mask_bad_parent_reads_as_root_child():
+    r = tree_attention_mask_one([0, 5, 1, -1])          # nodes 2 and 4 have bad parents
+    assert r.bad
+    good = tree_attention_mask_one([0, 0, 1, 0])
+    np.testing.assert_array_equal(r.mask, good.mask)
+
+
+def test_mask_packing_matches_packbits():
+    rng = np.random.default_rng(32)
+    m = rng.random((7, 70)) < 0.5
+    words = 3
+    packed = pack_mask_rows(m, words)
+    pad = np.zeros((7, words * 32), dtype=bool)
+    pad[:, :70] = m
+    ref = np.packbits(pad, axis=1, bitorder="little").view("<u4")
+    np.testing.assert_array_equal(packed, ref)
+
