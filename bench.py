@@ -79,7 +79,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "c5mask"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU time for cpu_baseline (0 disables)")
     ap.add_argument("--time-every", type=int, default=4,
@@ -172,6 +172,92 @@ def cpu_baseline_tree(x, seconds, gpu_out):
             {"requests_checked": len(checked), "unflagged_mismatches": mismatch})
 
 
+def cpu_baseline_mask(x, seconds, gpu_mask, gpu_depth):
+    import numpy as np
+
+    import oracle
+    done, nodes, mismatch = 0, 0, 0
+    checked = set()
+    W = gpu_mask.shape[2]
+    t0 = time.perf_counter()
+    while True:
+        b = done % x.B
+        r = oracle.tree_attention_mask_one(x.parent[b])
+        nodes += x.N
+        done += 1
+        if b not in checked:
+            checked.add(b)
+            same = (np.array_equal(oracle.pack_mask_rows(r.mask, W), gpu_mask[b])
+                    and np.array_equal(r.depth, gpu_depth[b]))
+            mismatch += int(not same)
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    sample = (f"{done} oracle tree masks ({nodes} nodes) cycling over the {x.B} trees of the "
+              f"same seeded batch, numpy, one process")
+    return ({"value": nodes / el, "unit": "tree nodes masked/s", "cores": 1, "kind": "oracle",
+             "sample": sample, "seconds": round(el, 2)},
+            {"requests_checked": len(checked), "unflagged_mismatches": mismatch})
+
+
+def bench_mask(args):
+    """The tree-attention mask of the c5 trees: one mask call per step."""
+    import numpy as np
+    import torch
+
+    from sampling_spec_verify_amd import specverify as sv
+    from sampling_spec_verify_amd import synth
+
+    sv.lib()
+    x = synth.config("c5")
+    par = torch.from_numpy(x.parent).to("cuda:0")
+    call = sv.TreeMaskCall(par, x.N)
+    W = call.out.mask.shape[2]
+    algo_bytes = 4 * (x.B * x.N + x.B * (x.N + 1) * W + x.B * (x.N + 1))
+    for _ in range(args.warmup):
+        call.run()
+    torch.cuda.synchronize()
+    K = args.steps
+    every = max(1, args.time_every)
+    timer = sv.KernelTimer(len(range(0, K, every)))
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(K):
+        call.run(timer.pair(i // every) if i % every == 0 else None)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = np.array([timer.elapsed_ms(j) for j in range(len(timer.start))])
+    timer.close()
+    mask = call.out.mask.cpu().numpy().view(np.uint32)
+    depth = call.out.depth.cpu().numpy()
+    cpu, parity = (None, None)
+    if args.cpu_seconds > 0:
+        cpu, parity = cpu_baseline_mask(x, args.cpu_seconds, mask, depth)
+    km = float(kern.mean())
+    line = {
+        "metric": "tree nodes masked/sec (tree-attention ancestor mask)",
+        "value": x.B * x.N * K / wall, "unit": "tree nodes masked/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / K, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": f"c5mask: ancestor mask of the {synth.CONFIGS['c5']}",
+                   "B": x.B, "N": x.N, "mask_words": W},
+        "roofline": {"bound": "hbm", "achieved": algo_bytes / (km * 1e-3) / 1e9,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": algo_bytes / (km * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "tree_mask", "algorithmic_bytes_per_launch": algo_bytes,
+                     "kernel_ms_mean": km, "kernel_ms_median": float(np.median(kern)),
+                     "kernel_timing": f"HIP events attached to the launch in every {every}-th "
+                                      f"timed step ({len(kern)} launches)",
+                     "note": "launch-latency bound: a few KB per call"},
+        "cpu_baseline": cpu, "gpu_ms_per_step": ev0.elapsed_time(ev1) / K,
+        "status_word": int(call.out.status[0].item()), "parity_sample": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -181,6 +267,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload == "c5mask":
+        bench_mask(args)
         return
 
     import numpy as np

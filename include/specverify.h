@@ -230,6 +230,39 @@ sv_status sv_tree_row_argmax_timed(const void *target_logits, int64_t ld_t, sv_d
                                    hipEvent_t kernel_start, hipEvent_t kernel_stop);
 
 /*
+ * Tree-attention mask of a batch of draft trees ([EAGLE] "3. 验证阶段树形
+ * attention": to verify a whole tree in one target pass, each candidate token
+ * may attend only to its ancestor path).  Node i (0 = root) may attend to
+ * node j iff j == i or j is an ancestor of i; the root is an ancestor of
+ * every node.
+ *
+ *  parent [B, N] int32 as in the tree calls (node i has parent parent[b, i-1]
+ *         in [0, i-1]); may be NULL when N == 0.
+ *  mask   [B, N+1, mask_words] uint32 out: bit j % 32 of word j / 32 of row i
+ *         is set iff node i may attend to node j; mask_words >= (N + 32) / 32
+ *         (words past column N are written as 0).
+ *  depth  [B, N+1] int32 out or NULL: edges from the root to node i (the
+ *         offset of node i's position after the root's).
+ *  status [1] int32 or NULL: OR-ed with SV_DATA_BAD_TREE when a parent is out
+ *         of range (that node is then treated as a child of the root).  Unlike
+ *         the verify calls, this call does not clear *status first.
+ *
+ * Errors: SV_EINVAL for B < 0, N outside [0, SV_MAX_TREE_NODES] or too few
+ * mask_words; SV_ENULL for a missing mask (or parent when N > 0); SV_EHIP.
+ * Needs no workspace.
+ */
+sv_status sv_tree_attention_mask(const int32_t *parent, int B, int N,
+                                 uint32_t *mask, int mask_words, int32_t *depth,
+                                 int32_t *status, hipStream_t stream);
+
+/* sv_tree_attention_mask with its kernel timed by kernel_start / kernel_stop,
+ * exactly as sv_chain_row_stats_timed times its kernel. */
+sv_status sv_tree_attention_mask_timed(const int32_t *parent, int B, int N,
+                                       uint32_t *mask, int mask_words, int32_t *depth,
+                                       int32_t *status, hipStream_t stream,
+                                       hipEvent_t kernel_start, hipEvent_t kernel_stop);
+
+/*
  * Stochastic verification along one caller-chosen root->leaf path: chain
  * acceptance (as sv_chain_verify) where position j drafts node n_{j+1}'s token
  * and is tested on target row n_j and draft row n_j (n_0 = root); the bonus

@@ -261,6 +261,64 @@ __global__ __launch_bounds__(kBlock2) void k_greedy_walk(TreeArgs a, int staged)
     }
 }
 
+// Tree-attention mask (EAGLE explainer, "3. 验证阶段树形attention": to verify
+// a tree in one target pass each candidate may attend only to its ancestor
+// path).  Grid (request, slice): every block stages its request's parent
+// array in LDS (an out-of-range parent reads as the root), then each thread
+// produces whole 32-bit mask words: word w of row i holds, at bit j, whether
+// node 32 w + j is i or an ancestor of i.  Parents are smaller than their
+// children, so a node's ancestors decrease along the walk: the walk first
+// climbs past the word's range, then sets at most 32 bits and stops below it.
+// The word-0 walk reaches the root and also gives the node's depth.
+constexpr int kMaskBlock = 256;
+
+__global__ __launch_bounds__(kMaskBlock) void k_tree_mask(const int32_t *parent, int N,
+                                                          uint32_t *mask, int W, int32_t *depth,
+                                                          int32_t *status) {
+    __shared__ int par[kNodes];
+    __shared__ int sh_bad;
+    const int b = blockIdx.x;
+    const int t = threadIdx.x;
+    if (t == 0) sh_bad = 0;
+    __syncthreads();
+    int bad = 0;
+    for (int i = t; i <= N; i += kMaskBlock) {
+        int p = -1;
+        if (i > 0) {
+            p = parent[int64_t(b) * N + i - 1];
+            if (p < 0 || p >= i) {
+                bad = 1;
+                p = 0;
+            }
+        }
+        par[i] = p;
+    }
+    if (bad) atomicOr(&sh_bad, 1);
+    __syncthreads();
+    const int64_t items = int64_t(N + 1) * W;
+    uint32_t *out = mask + int64_t(b) * items;
+    for (int64_t it = int64_t(blockIdx.y) * kMaskBlock + t; it < items;
+         it += int64_t(gridDim.y) * kMaskBlock) {
+        const int i = static_cast<int>(it / W);
+        const int w = static_cast<int>(it - int64_t(i) * W);
+        const int lo = 32 * w;
+        int a = i, steps = 0;
+        uint32_t bits = 0;
+        while (a >= lo + 32) {           // the root's parent is -1, so this ends
+            a = par[a];
+            ++steps;
+        }
+        while (a >= lo) {
+            bits |= 1u << (a - lo);
+            a = par[a];
+            ++steps;
+        }
+        out[it] = bits;
+        if (w == 0 && depth != nullptr) depth[int64_t(b) * (N + 1) + i] = steps - 1;
+    }
+    if (t == 0 && blockIdx.y == 0 && sh_bad && status != nullptr) atomicOr(status, SV_DATA_BAD_TREE);
+}
+
 }  // namespace sv
 
 namespace {
@@ -375,6 +433,29 @@ sv_status sv_tree_row_argmax_timed(const void *target_logits, int64_t ld_t, sv_d
     return greedy_call(target_logits, ld_t, dtype, B, N, V, parent, node_token, accepted, out_tokens,
                        accepted_nodes, Dmax, status, workspace, workspace_bytes, stream, 1,
                        kernel_start, kernel_stop);
+}
+
+sv_status sv_tree_attention_mask_timed(const int32_t *parent, int B, int N, uint32_t *mask,
+                                       int mask_words, int32_t *depth, int32_t *status,
+                                       hipStream_t stream, hipEvent_t kernel_start,
+                                       hipEvent_t kernel_stop) {
+    if (B < 0 || N < 0 || N > SV_MAX_TREE_NODES || B > (1 << 30) || mask_words < (N + 32) / 32 ||
+        mask_words > (1 << 20))
+        return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    if (!mask || (N > 0 && !parent)) return SV_ENULL;
+    const int64_t items = int64_t(N + 1) * mask_words;
+    const int slices = static_cast<int>(std::min<int64_t>(64, cdiv(items, kMaskBlock)));
+    launch_timed(k_tree_mask, dim3(static_cast<unsigned>(B), static_cast<unsigned>(slices)),
+                 dim3(kMaskBlock), 0, stream, kernel_start, kernel_stop, parent, N, mask,
+                 mask_words, depth, status);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+sv_status sv_tree_attention_mask(const int32_t *parent, int B, int N, uint32_t *mask, int mask_words,
+                                 int32_t *depth, int32_t *status, hipStream_t stream) {
+    return sv_tree_attention_mask_timed(parent, B, N, mask, mask_words, depth, status, stream,
+                                        nullptr, nullptr);
 }
 
 sv_status sv_tree_greedy_walk(const void *target_logits, int64_t ld_t, sv_dtype dtype, int B, int N,

@@ -46,6 +46,8 @@ SIGNATURES = {
     "sv_tree_row_argmax": (_GREEDY_ARGS, _I),
     "sv_tree_greedy_walk": (_GREEDY_ARGS, _I),
     "sv_tree_row_argmax_timed": (_GREEDY_ARGS + [_P, _P], _I),
+    "sv_tree_attention_mask": ([_P, _I, _I, _P, _I, _P, _P, _P], _I),
+    "sv_tree_attention_mask_timed": ([_P, _I, _I, _P, _I, _P, _P, _P, _P, _P], _I),
     "sv_tree_verify_path": ([_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _I, _P, _P, _F, _F, _P, _P,
                              _P, _P, _P, _S, _P], _I),
 }
@@ -318,6 +320,53 @@ def tree_verify_greedy(target, parent, node_token, Dmax: int, stream=None,
                        workspace=None) -> TreeGreedyOut:
     """sv_tree_verify_greedy: target [B, N+1, V], parent / node_token [B, N] int32."""
     return TreeGreedyCall(target, parent, node_token, Dmax, stream, workspace).run()
+
+
+class TreeMaskOut(NamedTuple):
+    mask: object            # [B, N+1, W] int32 words (bit patterns of the uint32 mask)
+    depth: object           # [B, N+1] int32
+    status: object          # [1] int32
+
+
+class TreeMaskCall:
+    """A tree-attention-mask call with its outputs bound once.
+
+    The mask tensor is int32 (torch has no uint32 arithmetic); its bits are the
+    uint32 words the C call writes.  ``status`` (a [1] int32 tensor) is OR-ed
+    into, not cleared; a fresh zeroed one is made when omitted.
+    """
+
+    def __init__(self, parent, N: Optional[int] = None, mask_words: Optional[int] = None,
+                 stream=None, status=None):
+        torch = _torch()
+        B = parent.shape[0]
+        N = parent.shape[1] if N is None else N
+        _i32(parent, (B, N), "parent")
+        W = (N + 32) // 32 if mask_words is None else int(mask_words)
+        dev = parent.device
+        self.out = TreeMaskOut(torch.empty(B, N + 1, W, dtype=torch.int32, device=dev),
+                               torch.empty(B, N + 1, dtype=torch.int32, device=dev),
+                               torch.zeros(1, dtype=torch.int32, device=dev) if status is None
+                               else status)
+        o = self.out
+        self.inputs = (parent,)
+        self._cached = (_ptr(parent), B, N, _ptr(o.mask), W, _ptr(o.depth), _ptr(o.status),
+                        _stream(stream))
+
+    def run(self, events=None) -> TreeMaskOut:
+        """Launch the mask kernel; ``events`` = (start, stop) times it."""
+        if events is None:
+            _check(lib().sv_tree_attention_mask(*self._cached), "sv_tree_attention_mask")
+        else:
+            _check(lib().sv_tree_attention_mask_timed(*self._cached, *events),
+                   "sv_tree_attention_mask_timed")
+        return self.out
+
+
+def tree_attention_mask(parent, N: Optional[int] = None, mask_words: Optional[int] = None,
+                        stream=None, status=None) -> TreeMaskOut:
+    """sv_tree_attention_mask: parent [B, N] int32 -> ancestor mask words and depths."""
+    return TreeMaskCall(parent, N, mask_words, stream, status).run()
 
 
 def tree_verify_path(target, draft, node_token, path, u_accept, u_sample, lam: float = 0.0,

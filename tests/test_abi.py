@@ -25,7 +25,8 @@ def test_header_declares_the_boundary():
                             "sv_chain_row_stats_timed",
                             "sv_tree_workspace_bytes", "sv_tree_verify_greedy",
                             "sv_tree_row_argmax", "sv_tree_greedy_walk",
-                            "sv_tree_row_argmax_timed", "sv_tree_verify_path"])
+                            "sv_tree_row_argmax_timed", "sv_tree_attention_mask",
+                            "sv_tree_attention_mask_timed", "sv_tree_verify_path"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -164,3 +165,22 @@ def path_call(**kw):
 ])
 def test_path_argument_errors(kw, code):
     assert path_call(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), sv.SV_EINVAL), (dict(N=-1), sv.SV_EINVAL), (dict(N=1025), sv.SV_EINVAL),
+    (dict(W=0), sv.SV_EINVAL), (dict(N=32, W=1), sv.SV_EINVAL), (dict(par=None), sv.SV_ENULL),
+    (dict(mask=None), sv.SV_ENULL),
+])
+@pytest.mark.parametrize("fn", ["sv_tree_attention_mask", "sv_tree_attention_mask_timed"])
+def test_mask_argument_errors(kw, code, fn):
+    args = dict(par=FAKE, B=2, N=5, mask=FAKE, W=1, depth=None, st=None, stream=None)
+    args.update(kw)
+    timed = (FAKE, FAKE) if fn.endswith("_timed") else ()
+    assert getattr(sv.lib(), fn)(*args.values(), *timed) == code
+
+
+def test_mask_empty_batch_and_rootless_tree_need_no_parent():
+    L = sv.lib()
+    assert L.sv_tree_attention_mask(None, 0, 5, None, 1, None, None, None) == sv.SV_OK
+

@@ -306,3 +306,54 @@ def test_gpu_output_law_monte_carlo():
     pv = [chisq(first, pm[0]), chisq(second, pm[1]), chisq(bonus, p[K]), chisq(nh, law_n)]
     print(f"[parity] MC p-values {pv}", flush=True)
     assert min(pv) > 0.01
+
+
+# ---------------------------------------------------------------------------
+# tree-attention mask (bit-exact against the oracle)
+# ---------------------------------------------------------------------------
+
+
+def _mask_case(parent: np.ndarray, words=None):
+    B, N = parent.shape
+    W = (N + 32) // 32 if words is None else words
+    g = sv.tree_attention_mask(dev(parent.astype(np.int32)), N, W)
+    torch.cuda.synchronize()
+    mask = g.mask.cpu().numpy().view(np.uint32)
+    depth = g.depth.cpu().numpy()
+    ref_mask, ref_depth, bad = oracle.tree_attention_mask(parent, W)
+    np.testing.assert_array_equal(mask, ref_mask)
+    np.testing.assert_array_equal(depth, ref_depth)
+    return int(g.status[0].item()), bad
+
+
+def test_mask_tree_workload():
+    x = synth.config("c5")
+    st, bad = _mask_case(x.parent)
+    assert st == 0 and not bad.any()
+
+
+@pytest.mark.parametrize("seed,B,N,words", [
+    (1, 5, 0, None), (2, 3, 1, None), (3, 7, 31, None), (4, 4, 32, None), (5, 6, 33, 3),
+    (6, 2, 200, None), (7, 3, 1024, None), (8, 9, 70, 40),
+])
+def test_mask_random_trees(seed, B, N, words):
+    rng = np.random.default_rng(500 + seed)
+    parent = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        shape = b % 3
+        for i in range(1, N + 1):
+            if shape == 0:
+                parent[b, i - 1] = i - 1                    # chain: causal mask, deepest walks
+            elif shape == 1:
+                parent[b, i - 1] = int(rng.integers(0, i))  # uniform random recursive tree
+            else:
+                parent[b, i - 1] = int(rng.integers(max(0, i - 3), i))  # deep, narrow
+    st, bad = _mask_case(parent, words)
+    assert st == 0 and not bad.any()
+
+
+def test_mask_bad_parent_is_reported_and_read_as_root_child():
+    parent = np.array([[0, 1, 7, 2, -3, 4], [0, 0, 1, 1, 2, 2]], dtype=np.int32)
+    st, bad = _mask_case(parent)
+    assert bad.tolist() == [True, False]
+    assert "BAD_TREE" in sv.decode_flags(st)
