@@ -78,6 +78,23 @@ def mixture(p_t: np.ndarray, q: np.ndarray, lam: float) -> np.ndarray:
     return (1.0 - lam) * p_t + lam * q
 
 
+def enhanced_logits(zt: np.ndarray, zq: np.ndarray, lam: float) -> np.ndarray:
+    """The RAPID pseudocode's logit-space mixture: (1 - lam) z_t + lam z_q.
+
+    [RAPID] "3) 候选验证机制（伪代码）": ``enhanced_target = (1 - λ) *
+    target_logits + λ * draft_logits``, then a softmax per position.  At
+    lam = 0 and lam = 1 the other model's logits carry weight 0 and are left
+    out (so a -inf there does not turn into NaN).
+    """
+    zt = np.asarray(zt, dtype=np.float64)
+    zq = np.asarray(zq, dtype=np.float64)
+    if lam == 0.0:
+        return zt.copy()
+    if lam == 1.0:
+        return zq.copy()
+    return (1.0 - lam) * zt + lam * zq
+
+
 def accept_prob(p_mix_x: float, q_x: float) -> float:
     """Acceptance probability of a drafted token x: min(1, p~(x) / q(x)).
 
@@ -142,8 +159,11 @@ class ChainResult:
     flagged: bool              # some draw lies within FLAG_BAND of its boundary
 
 
+MIX_SPACES = ("prob", "logit")
+
+
 def chain_verify_one(zt: np.ndarray, zq: np.ndarray, x, u_acc, u_s: float,
-                     lam: float, T: float) -> ChainResult:
+                     lam: float, T: float, space: str = "prob") -> ChainResult:
     """Verify one request's linear chain of k drafts.
 
     zt [k+1, V] target logits (row k serves the bonus token), zq [k, V] draft
@@ -158,7 +178,15 @@ def chain_verify_one(zt: np.ndarray, zq: np.ndarray, x, u_acc, u_s: float,
     target's row k at temperature T (its draft row does not exist, so no
     mixture applies there); the one sampling uniform u_s serves whichever of
     the residual or bonus draws happens.
+
+    ``space`` picks where the two models mix: "prob" is the mixture equation
+    of [RAPID] section 2, p~ = (1 - lam) p_t + lam q; "logit" is the form the
+    [RAPID] pseudocode writes, p~ = softmax(((1 - lam) z_t + lam z_q) / T).
+    Either p~ then takes the target's place in the acceptance ratio, the
+    residual and the fallback.
     """
+    if space not in MIX_SPACES:
+        raise ValueError(f"unknown mixture space {space!r}")
     lam = as_f32_scalar(lam)
     T = as_f32_scalar(T)
     u_s = float(np.float32(u_s))
@@ -173,9 +201,11 @@ def chain_verify_one(zt: np.ndarray, zq: np.ndarray, x, u_acc, u_s: float,
         xi = int(x[i])
         if not 0 <= xi < V:
             raise ValueError(f"drafted token {xi} outside [0, {V})")
-        p_t = softmax_T(zt[i], T)
         q = softmax_T(zq[i], T)
-        p_mix = mixture(p_t, q, lam)
+        if space == "prob":
+            p_mix = mixture(softmax_T(zt[i], T), q, lam)
+        else:
+            p_mix = softmax_T(enhanced_logits(zt[i], zq[i], lam), T)
         a[i] = accept_prob(p_mix[xi], q[xi])
         alpha[i] = np.minimum(p_mix, q).sum()
         p_mix_rows.append(p_mix)
@@ -270,7 +300,7 @@ def path_rows(path) -> List[int]:
 
 
 def tree_path_one(zt: np.ndarray, zq: np.ndarray, node_token, path, u_acc, u_s: float,
-                  lam: float, T: float) -> ChainResult:
+                  lam: float, T: float, space: str = "prob") -> ChainResult:
     """Stochastic verification along one root->leaf path of a draft tree.
 
     Reading: chain acceptance ([RAPID] verify loop) along the nodes
@@ -283,7 +313,7 @@ def tree_path_one(zt: np.ndarray, zq: np.ndarray, node_token, path, u_acc, u_s: 
     rows = [0] + nodes
     x = [int(node_token[v - 1]) for v in nodes]
     return chain_verify_one(np.asarray(zt)[rows], np.asarray(zq)[rows[:d]], x,
-                            np.asarray(u_acc)[:d], u_s, lam, T)
+                            np.asarray(u_acc)[:d], u_s, lam, T, space)
 
 
 @dataclasses.dataclass
@@ -345,7 +375,7 @@ class BatchResult:
 
 
 def chain_verify(target, draft, tokens, draft_len: Optional[np.ndarray], u_accept, u_sample,
-                 lam: float, T: float, requests=None) -> BatchResult:
+                 lam: float, T: float, requests=None, space: str = "prob") -> BatchResult:
     """All requests of a chain batch.  target [B,K+1,V], draft [B,K,V] (float arrays)."""
     B, K = tokens.shape
     req = range(B) if requests is None else requests
@@ -357,7 +387,7 @@ def chain_verify(target, draft, tokens, draft_len: Optional[np.ndarray], u_accep
     for b in req:
         k = K if draft_len is None else int(draft_len[b])
         r = chain_verify_one(target[b, :k + 1], draft[b, :k], tokens[b, :k], u_accept[b, :k],
-                             u_sample[b], lam, T)
+                             u_sample[b], lam, T, space)
         acc[b] = r.accepted
         out[b, :len(r.tokens)] = r.tokens
         ap[b, :k] = r.a
@@ -382,7 +412,7 @@ def tree_greedy(target, parent, node_token, Dmax: int, requests=None):
 
 
 def tree_path(target, draft, node_token, path, u_accept, u_sample, lam, T,
-              requests=None) -> BatchResult:
+              requests=None, space: str = "prob") -> BatchResult:
     B, Dmax = path.shape
     req = range(B) if requests is None else requests
     acc = np.zeros(B, dtype=np.int32)
@@ -392,7 +422,7 @@ def tree_path(target, draft, node_token, path, u_accept, u_sample, lam, T,
     det = [None] * B
     for b in req:
         r = tree_path_one(target[b], draft[b], node_token[b], path[b], u_accept[b],
-                          u_sample[b], lam, T)
+                          u_sample[b], lam, T, space)
         acc[b] = r.accepted
         out[b, :len(r.tokens)] = r.tokens
         ap[b, :len(r.a)] = r.a

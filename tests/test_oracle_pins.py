@@ -191,7 +191,7 @@ def _count_true(pred):
     return lo
 
 
-def _enumerate(zt, zq, lam, T):
+def _enumerate(zt, zq, lam, T, space="prob"):
     """Exact law of every emitted position, the oracle used as a black box.
 
     Returns (emit[j, v] = P(position j emits v), stop[j] = P(n = j)).
@@ -206,7 +206,7 @@ def _enumerate(zt, zq, lam, T):
             continue
 
         def run(ua, us):
-            return chain_verify_one(zt, zq, list(xs), ua, us, lam, T)
+            return chain_verify_one(zt, zq, list(xs), ua, us, lam, T, space)
 
         reach = 1.0
         theta_m = []
@@ -233,24 +233,30 @@ def _enumerate(zt, zq, lam, T):
     return emit, stop
 
 
-@pytest.mark.parametrize("V,k,lam,T,seed", [(3, 2, 0.0, 1.0, 11), (4, 2, 0.3, 0.7, 12),
-                                              (2, 3, 0.5, 1.5, 13), (3, 3, 0.0, 1.0, 14)])
-def test_exact_enumeration_is_lossless(V, k, lam, T, seed):
+@pytest.mark.parametrize("V,k,lam,T,seed,space", [
+    (3, 2, 0.0, 1.0, 11, "prob"), (4, 2, 0.3, 0.7, 12, "prob"), (2, 3, 0.5, 1.5, 13, "prob"),
+    (3, 3, 0.0, 1.0, 14, "prob"), (4, 2, 0.3, 0.7, 15, "logit"), (3, 3, 0.6, 1.2, 16, "logit"),
+])
+def test_exact_enumeration_is_lossless(V, k, lam, T, seed, space):
     """Each emitted position follows p~ given that it is reached; the bonus follows p_t.
 
     [SD] "修改的拒绝采样" and [EAGLE] section 1: the output law equals the target
-    law whatever the draft; with RAPID's mixture the target law is p~.
+    law whatever the draft; with RAPID's mixture the target law is p~ (the
+    mixture equation of section 2, or the pseudocode's softmax of mixed logits).
     """
     rng = np.random.default_rng(seed)
     zt, zq = _rows(rng, k, V, 1.5)
     zt[1, 0] = -np.inf                          # a token the target rules out
-    emit, stop = _enumerate(zt, zq, lam, T)
+    emit, stop = _enumerate(zt, zq, lam, T, space)
     lam32 = f32(lam)
     reach = 1.0
     tol = 1e-6                                  # uniforms live on a 2^-24 grid
     for j in range(k):
         p, q = sm(zt[j], T), sm(zq[j], T)
-        pm = (1.0 - lam32) * p + lam32 * q      # the mixture equation of the RAPID page
+        if space == "prob":
+            pm = (1.0 - lam32) * p + lam32 * q  # the mixture equation of the RAPID page
+        else:                                   # the pseudocode's mixed logits, via scipy
+            pm = scipy.special.softmax(((1.0 - lam32) * zt[j] + lam32 * zq[j]) / f32(T))
         assert emit[j].sum() == pytest.approx(reach, abs=tol)
         np.testing.assert_allclose(emit[j], reach * pm, atol=tol)
         alpha = np.minimum(pm, q).sum()
@@ -509,4 +515,64 @@ def test_mask_packing_matches_packbits():
     pad[:, :70] = m
     ref = np.packbits(pad, axis=1, bitorder="little").view("<u4")
     np.testing.assert_array_equal(packed, ref)
+
+
+# ---------------------------------------------------------------------------
+# logit-space mixture (the RAPID pseudocode's form)
+# ---------------------------------------------------------------------------
+
+
+def test_logit_mixture_at_lambda_zero_is_the_plain_chain():
+    rng = np.random.default_rng(41)
+    for _ in range(50):
+        k, V = int(rng.integers(1, 5)), int(rng.integers(2, 30))
+        zt, zq = _rows(rng, k, V, 2.0)
+        x = rng.integers(0, V, k)
+        ua, us = rng.random(k, dtype=np.float32), float(rng.random(dtype=np.float32))
+        a = chain_verify_one(zt, zq, x, ua, us, 0.0, 0.9, "logit")
+        b = chain_verify_one(zt, zq, x, ua, us, 0.0, 0.9, "prob")
+        assert (a.accepted, a.tokens) == (b.accepted, b.tokens)
+        np.testing.assert_array_equal(a.a, b.a)
+
+
+def test_logit_mixture_at_lambda_one_accepts_every_draft():
+    rng = np.random.default_rng(42)
+    zt, zq = _rows(rng, 4, 12, 2.0)
+    zt[0, :] = -np.inf                          # the target's own row no longer matters
+    zt[0, 3] = 0.0
+    for _ in range(20):
+        x = rng.integers(0, 12, 4)
+        r = chain_verify_one(zt, zq, x, rng.random(4, dtype=np.float32), 0.5, 1.0, 1.0, "logit")
+        assert r.accepted == 4 and np.all(r.a == 1.0)
+
+
+def test_logit_mixture_is_the_normalised_geometric_mixture():
+    """softmax((1-l) z_t + l z_q) = p_t^(1-l) q^l / sum: an independent route
+    through scipy's log_softmax, checked on the acceptance probabilities and
+    the expected acceptance sum_v min(p~, q)."""
+    rng = np.random.default_rng(43)
+    for _ in range(60):
+        k, V = int(rng.integers(1, 4)), int(rng.integers(2, 40))
+        lam, T = float(rng.uniform(0.05, 0.95)), float(rng.uniform(0.5, 2.0))
+        zt, zq = _rows(rng, k, V, 2.5)
+        x = rng.integers(0, V, k)
+        r = chain_verify_one(zt, zq, x, np.zeros(k, dtype=np.float32), 0.5, lam, T, "logit")
+        l32, T32 = f32(lam), f32(T)
+        for i in range(k):
+            lp = scipy.special.log_softmax(zt[i] / T32)
+            lq = scipy.special.log_softmax(zq[i] / T32)
+            pe = scipy.special.softmax((1.0 - l32) * lp + l32 * lq)
+            q = np.exp(lq)
+            assert r.a[i] == pytest.approx(min(1.0, pe[x[i]] / q[x[i]]), rel=1e-12, abs=1e-15)
+            assert r.alpha[i] == pytest.approx(np.minimum(pe, q).sum(), rel=1e-12)
+
+
+def test_logit_mixture_identical_rows_accept_every_draft():
+    rng = np.random.default_rng(44)
+    zt, _ = _rows(rng, 3, 20, 2.0)
+    zq = zt[:3].copy()
+    for lam in (0.2, 0.5, 0.9):
+        r = chain_verify_one(zt, zq, rng.integers(0, 20, 3), rng.random(3, dtype=np.float32),
+                             0.3, lam, 1.1, "logit")
+        assert r.accepted == 3
 
