@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "c5mask"])
+    ap.add_argument("--space", default="prob", choices=["prob", "logit"],
+                    help="chain workloads: mix the two models in probability space (the "
+                         "mixture equation) or logit space (the pseudocode's form)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU time for cpu_baseline (0 disables)")
     ap.add_argument("--time-every", type=int, default=4,
@@ -109,7 +112,7 @@ def device_copies(arr, dtype, R, torch):
     return [base] + [base.clone() for _ in range(R - 1)]
 
 
-def cpu_baseline_chain(x, seconds, gpu_out):
+def cpu_baseline_chain(x, seconds, gpu_out, space="prob"):
     """Oracle over the batch's requests in order (cycling) for about `seconds`."""
     import numpy as np
 
@@ -124,7 +127,7 @@ def cpu_baseline_chain(x, seconds, gpu_out):
         b = done % x.B
         k = int(lens[b])
         r = oracle.chain_verify_one(t[b, :k + 1], d[b, :k], x.tokens[b, :k], x.u_accept[b, :k],
-                                    x.u_sample[b], x.lam, x.temperature)
+                                    x.u_sample[b], x.lam, x.temperature, space)
         pos += k
         done += 1
         if b not in checked:
@@ -312,8 +315,8 @@ def main():
         ua = torch.from_numpy(x.u_accept).to(dev)
         us = torch.from_numpy(x.u_sample).to(dev)
         dl = None if x.draft_len is None else torch.from_numpy(x.draft_len).to(dev)
-        calls = [sv.ChainCall(tgts[i], drfs[i], tok, ua, us, x.lam, x.temperature, dl)
-                 for i in range(R)]
+        calls = [sv.ChainCall(tgts[i], drfs[i], tok, ua, us, x.lam, x.temperature, dl,
+                              space=args.space) for i in range(R)]
 
         def step(i, events=None):
             c = calls[i % R]
@@ -363,14 +366,14 @@ def main():
         if tree:
             cpu, parity = cpu_baseline_tree(x, args.cpu_seconds, gpu_out)
         else:
-            cpu, parity = cpu_baseline_chain(x, args.cpu_seconds, gpu_out)
+            cpu, parity = cpu_baseline_chain(x, args.cpu_seconds, gpu_out, args.space)
 
     config = {"workload": f"{args.workload}: {synth.CONFIGS[args.workload]}",
               "B": x.B, "V": x.V, "logits": x.dtype,
               "positions_per_step": positions, "buffer_sets_rotated": R}
     if not tree:
         config.update({"K": x.K, "ragged": x.draft_len is not None, "lambda": x.lam,
-                       "temperature": x.temperature})
+                       "temperature": x.temperature, "mixture_space": args.space})
     line = {
         "metric": METRIC,
         "value": value,

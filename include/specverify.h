@@ -66,6 +66,16 @@ typedef enum {
 typedef enum { SV_BF16 = 0, SV_F32 = 1 } sv_dtype;
 
 /* Largest number of drafted positions per request (chain K, tree path Dmax). */
+/* Where the target and draft models are mixed ([RAPID]): SV_MIX_PROB is the
+ * mixture equation of section "2) 推理时知识迁移", p~ = (1 - lambda) p_t +
+ * lambda q; SV_MIX_LOGIT is the form of the section-3 pseudocode, p~ =
+ * softmax(((1 - lambda) z_t + lambda z_q) / T).  Either p~ takes the target's
+ * place in the acceptance ratio min(1, p~(x) / q(x)), in the residual
+ * max(0, p~ - q) and in the zero-residual fallback; the bonus token is always
+ * drawn from the target's own softmax(z/T).  At lambda = 0 or 1 the two
+ * coincide. */
+typedef enum { SV_MIX_PROB = 0, SV_MIX_LOGIT = 1 } sv_mix_space;
+
 #define SV_MAX_POSITIONS 64
 /* Largest number of non-root nodes of a draft tree. */
 #define SV_MAX_TREE_NODES 1024
@@ -165,6 +175,27 @@ sv_status sv_chain_row_stats_timed(const void *target_logits, int64_t ld_t,
                                    int32_t *status, void *workspace, size_t workspace_bytes,
                                    hipStream_t stream, hipEvent_t kernel_start,
                                    hipEvent_t kernel_stop);
+
+/*
+ * sv_chain_verify with the mixture space chosen (mix_space, an sv_mix_space)
+ * and the launches selected: stages = 1 runs the row-statistics launch,
+ * 2 the accept / resample launches (after a stage-1 call of the same
+ * arguments on the same stream and workspace), 3 both.  kernel_start /
+ * kernel_stop (either may be NULL) time the row-statistics kernel as in
+ * sv_chain_row_stats_timed.  In logit space a row-statistics job reads the
+ * target and draft chunks of a position together, so each drafted row is
+ * still read once.  SV_EINVAL also for an unknown mix_space or stages.
+ */
+sv_status sv_chain_verify_ex(const void *target_logits, int64_t ld_t,
+                             const void *draft_logits, int64_t ld_q,
+                             sv_dtype dtype, int B, int K, int V,
+                             const int32_t *draft_tokens, const int32_t *draft_len,
+                             const float *u_accept, const float *u_sample,
+                             float lambda, float temperature,
+                             int32_t *accepted, int32_t *out_tokens, float *accept_prob,
+                             int32_t *status, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream, int mix_space, int stages,
+                             hipEvent_t kernel_start, hipEvent_t kernel_stop);
 
 /* ------------------------------------------------------------------------
  * Draft trees ([SD] "Tree Speculation", [EAGLE] greedy match + tree attention)
@@ -282,6 +313,18 @@ sv_status sv_tree_verify_path(const void *target_logits, int64_t ld_t,
                               int32_t *accepted, int32_t *out_tokens, float *accept_prob,
                               int32_t *status, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/* sv_tree_verify_path with the mixture space chosen (mix_space, an
+ * sv_mix_space); SV_EINVAL also for an unknown mix_space. */
+sv_status sv_tree_verify_path_ex(const void *target_logits, int64_t ld_t,
+                                 const void *draft_logits, int64_t ld_q,
+                                 sv_dtype dtype, int B, int N, int V,
+                                 const int32_t *node_token, const int32_t *path, int Dmax,
+                                 const float *u_accept, const float *u_sample,
+                                 float lambda, float temperature,
+                                 int32_t *accepted, int32_t *out_tokens, float *accept_prob,
+                                 int32_t *status, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream, int mix_space);
 
 #ifdef __cplusplus
 }

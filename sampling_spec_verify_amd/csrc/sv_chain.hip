@@ -169,11 +169,118 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(ChainArgs a, int n_jobs) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
 }
 
+// Logit-space mixture (the RAPID pseudocode mixes logits, enhanced =
+// (1 - lambda) z_t + lambda z_q, then takes a softmax): one job is wave-chunk
+// c of drafted position i with its target and draft chunks together, so each
+// drafted row is still read once.  Slot 0 of the position receives the
+// enhanced row's partial: its exponent y = alpha z_t + beta z_q - s
+// (alpha = (1 - lambda) c, beta = lambda c) is formed in fp64, since a mixed
+// logit is not exact in fp32 while bf16 / fp32 logits times fp64 constants
+// are; the lane shift ceil(alpha m_t + beta m_q) bounds the lane's largest
+// alpha z_t + beta z_q from above (alpha, beta >= 0), and the slot carries the
+// drafted token's target logit.  Slot 1 receives the draft row's partial
+// exactly as in probability space.
+template <class DT, int NV>
+__device__ __forceinline__ void row_chunk_stats_logit(const ChainArgs &a, unsigned job) {
+    const unsigned C1 = static_cast<unsigned>(a.C1);
+    const int c = static_cast<int>(job % C1);
+    const unsigned rest = job / C1;
+    const unsigned Pc = static_cast<unsigned>(a.g.Pcap);
+    const int i = static_cast<int>(rest % Pc);
+    const int b = static_cast<int>(rest / Pc);
+    if (!geo_position_valid(a.g, b, i)) return;
+    const int r = geo_row(a.g, b, i);
+    const char *row_t = row_ptr(a.g, 0, b, r);
+    const char *row_q = row_ptr(a.g, 1, b, r);
+    const int x = geo_token(a.g, b, i);
+    const bool own_x = x >= 0 && x < a.g.V && x / a.ch1 == c;
+
+    constexpr int VEC = DT::kVec;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int V = a.g.V;
+    const int v0 = c * (kWave * NV);
+    u32x4 dt[NV], dq[NV];
+    load_chunk<DT, NV>(row_t, v0, lane, V, dt);
+    load_chunk<DT, NV>(row_q, v0, lane, V, dq);
+    float ft[NV][VEC], fq[NV][VEC];
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        DT::unpack(dt[n], ft[n]);
+        DT::unpack(dq[n], fq[n]);
+    }
+    float mt = -INFINITY, mq = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            mt = fmaxf(mt, ft[n][e]);
+            mq = fmaxf(mq, fq[n][e]);
+        }
+    const float c_hi = a.c_hi, c_lo = a.c_lo;
+    const double al = a.alpha_c, be = a.beta_c;
+    // draft row, as in probability space
+    const float sq_lane = (mq == -INFINITY) ? -INFINITY : ceilf(mq * c_hi);
+    const float sq_use = (mq == -INFINITY) ? 0.0f : sq_lane;
+    // enhanced row: -inf in either model leaves every mixed logit of the lane at -inf
+    const bool e_none = (mt == -INFINITY) || (mq == -INFINITY);
+    const float se_lane = e_none ? -INFINITY
+                                 : static_cast<float>(ceil(al * static_cast<double>(mt) +
+                                                           be * static_cast<double>(mq)));
+    const double se_use = e_none ? 0.0 : static_cast<double>(se_lane);
+    float accq[VEC], acce[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) accq[e] = acce[e] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            accq[e] += __builtin_amdgcn_exp2f(fmaf(fq[n][e], c_lo, fmaf(fq[n][e], c_hi, -sq_use)));
+            const double y = fma(static_cast<double>(ft[n][e]), al,
+                                 fma(static_cast<double>(fq[n][e]), be, -se_use));
+            acce[e] += __builtin_amdgcn_exp2f(static_cast<float>(y));
+        }
+    float Sq_lane = 0.0f, Se_lane = 0.0f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        Sq_lane += accq[e];
+        Se_lane += acce[e];
+    }
+    const float sq_w = wave_max(sq_lane);
+    const float se_w = wave_max(se_lane);
+    const float fq_ = (sq_lane == -INFINITY) ? 0.0f : pow2_shift(sq_lane - sq_w);
+    const float fe_ = (se_lane == -INFINITY) ? 0.0f : pow2_shift(se_lane - se_w);
+    const double Sq_w = wave_sum_d(static_cast<double>(Sq_lane) * static_cast<double>(fq_));
+    const double Se_w = wave_sum_d(static_cast<double>(Se_lane) * static_cast<double>(fe_));
+    if (lane == 0) {
+        Part* dst = a.part1 + (int64_t(b) * a.g.Pcap + i) * 2 * a.C1;
+        Part pe, pq;
+        pe.s = se_w;
+        pe.z = own_x ? DT::load1(row_t, x) : 0.0f;
+        pe.S = Se_w;
+        pq.s = sq_w;
+        pq.z = own_x ? DT::load1(row_q, x) : 0.0f;
+        pq.S = Sq_w;
+        dst[c] = pe;
+        dst[a.C1 + c] = pq;
+    }
+}
+
+template <class DT, int NV>
+__global__ __launch_bounds__(kBlock) void k_row_stats_logit(ChainArgs a, int n_jobs) {
+    const int job = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves +
+                                                   static_cast<int>(threadIdx.x) / kWave);
+    if (job < n_jobs) row_chunk_stats_logit<DT, NV>(a, static_cast<unsigned>(job));
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
+}
+
 // ---------------------------------------------------------------------------
 // launch 2: resolve + chunk masses; launch 3: inverse-CDF locate
 // ---------------------------------------------------------------------------
 
-enum SampleMode { kResidual = 0, kBonus = 1, kMixture = 2 };
+// kResidualLogit: the residual max(0, p~ - q) of the logit-space mixture,
+// p~ = softmax of the mixed logits (the target slot of the record holds its
+// shift and 1 / sum).
+enum SampleMode { kResidual = 0, kBonus = 1, kMixture = 2, kResidualLogit = 3 };
 
 struct SampleCtx {
     const char *row_t;      // target row of the sampling position
@@ -182,12 +289,20 @@ struct SampleCtx {
     float st, it;           // target row: p_t(v) = 2^(z c - st) * it
     float sq, iq;           // draft row:  q(v)   = 2^(z c - sq) * iq
     float w_t, w_q;         // mixture weights (1 - lambda, lambda)
+    double al, be;          // logit space: (1 - lambda) c, lambda c
+    int logit;              // the target-slot statistics are those of the mixed logits
     int V;
 };
 
 // 2^(z c - s) with c = c_hi + c_lo, the argument formed with two fmas
 __device__ __forceinline__ float pow2_logit(float z, float c_hi, float c_lo, float s) {
     return __builtin_amdgcn_exp2f(fmaf(z, c_lo, fmaf(z, c_hi, -s)));
+}
+
+// 2^(alpha z_t + beta z_q - s) of the logit-space mixture, the argument in fp64
+__device__ __forceinline__ float pow2_mixed(float zt, float zq, double al, double be, float s) {
+    return __builtin_amdgcn_exp2f(static_cast<float>(
+        fma(static_cast<double>(zt), al, fma(static_cast<double>(zq), be, -static_cast<double>(s)))));
 }
 
 // The sampling row is cut into chunks of kBlock2 lanes x NV2 vectors, one
@@ -221,6 +336,10 @@ __device__ __forceinline__ void vec_weights(const SampleCtx &S, const u32x4 &dt,
     for (int e = 0; e < VEC; ++e) {
         if (MODE == kBonus) {
             w[e] = pow2_logit(ft[e], S.c_hi, S.c_lo, s_use);
+        } else if (MODE == kResidualLogit) {
+            const float pe = pow2_mixed(ft[e], fq[e], S.al, S.be, S.st) * S.it;
+            const float pq = pow2_logit(fq[e], S.c_hi, S.c_lo, S.sq) * S.iq;
+            w[e] = fmaxf(pe - pq, 0.0f);
         } else {
             const float et = pow2_logit(ft[e], S.c_hi, S.c_lo, S.st);
             const float pq = pow2_logit(fq[e], S.c_hi, S.c_lo, S.sq) * S.iq;
@@ -374,10 +493,21 @@ __device__ __forceinline__ void resolve_request(const ChainArgs &a, int b, Resol
                 fl |= SV_DATA_BAD_ROW;
                 acc_p = 0.0;
             } else if (zq == -INFINITY) {
+                // q(x) = 0: accept iff p~(x) > 0.  In logit space the mixed
+                // logit of x is -inf too, so p~(x) = 0.
                 fl |= SV_DATA_ZERO_Q;
-                acc_p = (a.lam < 1.0f && zt != -INFINITY) ? 1.0 : 0.0;
+                acc_p = (a.space == 0 && a.lam < 1.0f && zt != -INFINITY) ? 1.0 : 0.0;
             } else if (a.lam >= 1.0f) {
                 acc_p = 1.0;
+            } else if (a.space == 1) {
+                // slot 0 holds the mixed row (shift s_e, sum S_e) and z_t(x):
+                // p~(x) / q(x) = 2^E S_q / S_e with
+                // E = (alpha z_t(x) + beta z_q(x)) - c z_q(x) - (s_e - s_q)
+                //   = alpha (z_t(x) - z_q(x)) - (s_e - s_q), as alpha + beta = c
+                const double E = a.alpha_c * (static_cast<double>(zt) - static_cast<double>(zq)) -
+                                 (static_cast<double>(sh.s[2 * i]) - static_cast<double>(sh.s[2 * i + 1]));
+                const double ratio = exp2_d(E) * (sh.S[2 * i + 1] / sh.S[2 * i]);
+                acc_p = fmin(1.0, ratio);
             } else {
                 // p(x) = 2^(z(x) c - s) / S for either model, so
                 // p_t(x) / q(x) = 2^E S_q / S_t with E = (z_t(x) - z_q(x)) c - (s_t - s_q)
@@ -413,6 +543,9 @@ __device__ __forceinline__ SampleCtx sample_ctx(const ChainArgs &a, int b, const
     S.c_lo = a.c_lo;
     S.w_t = 1.0f - a.lam;
     S.w_q = a.lam;
+    S.al = a.alpha_c;
+    S.be = a.beta_c;
+    S.logit = a.space;
     S.row_t = row_ptr(a.g, 0, b, r.row);
     S.row_q = (r.mode != kBonus) ? row_ptr(a.g, 1, b, r.row) : nullptr;
     S.st = r.st;
@@ -478,7 +611,7 @@ __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int stage
     r.n = n;
     r.st = r.sq = r.it = r.iq = 0.0f;
     if (n < K) {
-        r.mode = kResidual;
+        r.mode = (a.space == 1) ? kResidualLogit : kResidual;
         r.row = sh.rowi[n];
         r.rows_ok = !sh.row_bad[2 * n] && !sh.row_bad[2 * n + 1];
         // p(v) = 2^(z c - s) / S
@@ -507,6 +640,7 @@ __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int stage
     const SampleCtx S = sample_ctx(a, b, r);
     double *cr = a.chunks + (int64_t(b) * a.C2 + c) * a.rec_stride;
     if (r.mode == kResidual) chunk_pieces<DT, kResidual, NV2>(S, c, cr, sh.f);
+    else if (r.mode == kResidualLogit) chunk_pieces<DT, kResidualLogit, NV2>(S, c, cr, sh.f);
     else chunk_pieces<DT, kBonus, NV2>(S, c, cr, sh.f);
 }
 
@@ -676,8 +810,11 @@ __device__ __forceinline__ int sample_mixture(const SampleCtx &S, double u, Loca
     const int V = S.V;
     auto weight = [&](int v) -> float {
         if (v >= V) return 0.0f;
-        const float pt = pow2_logit(DT::load1(S.row_t, v), S.c_hi, S.c_lo, S.st) * S.it;
-        const float pq = pow2_logit(DT::load1(S.row_q, v), S.c_hi, S.c_lo, S.sq) * S.iq;
+        const float zt = DT::load1(S.row_t, v);
+        const float zq = DT::load1(S.row_q, v);
+        if (S.logit) return pow2_mixed(zt, zq, S.al, S.be, S.st) * S.it;   // p~ itself
+        const float pt = pow2_logit(zt, S.c_hi, S.c_lo, S.st) * S.it;
+        const float pq = pow2_logit(zq, S.c_hi, S.c_lo, S.sq) * S.iq;
         return fmaf(S.w_t, pt, S.w_q * pq);
     };
     double carry = 0.0;
@@ -721,9 +858,17 @@ __global__ __launch_bounds__(kBlock) void k_locate(ChainArgs a) {
     const SampleCtx S = sample_ctx(a, b, r);
     const double u = static_cast<double>(a.u_sample[b]);
     int flags = 0;
-    int tok = (r.mode == kResidual) ? locate<DT, kResidual, NV2>(S, P, pp, u, L)
-                                    : locate<DT, kBonus, NV2>(S, P, pp, u, L);
-    if (tok < 0 && r.mode == kResidual && r.rows_ok) {
+    // At lambda = 1, p~ = q and the residual max(0, p~ - q) is identically
+    // zero (a rejection there means q(x) = 0): straight to the fallback, p~.
+    // The chunk records hold max(0, p_t - q), which is no longer the same law.
+    int tok;
+    if (r.mode == kResidual)
+        tok = (a.lam >= 1.0f) ? -1 : locate<DT, kResidual, NV2>(S, P, pp, u, L);
+    else if (r.mode == kResidualLogit)
+        tok = locate<DT, kResidualLogit, NV2>(S, P, pp, u, L);
+    else
+        tok = locate<DT, kBonus, NV2>(S, P, pp, u, L);
+    if (tok < 0 && r.mode != kBonus && r.rows_ok) {
         flags |= SV_DATA_FALLBACK;
         tok = sample_mixture<DT>(S, u, L);
     }
@@ -765,11 +910,22 @@ struct ChainReq {
     size_t ws_bytes;
     hipStream_t stream;
     hipEvent_t ev_start, ev_stop;   // optional: attached to the row-statistics launch
+    int space;                      // 1: logit-space mixture (only for 0 < lambda < 1)
 };
 
 int choose_nv(int B, int P, int V, int vec) { return choose_stream_nv(2LL * B * P, V, vec); }
 
+
 int pcap(const ChainReq &q) { return q.path_mode ? std::min(q.P, q.N) : q.P; }
+
+// Vectors per lane and tensor of a row-stats job.  Logit-space jobs read the
+// target and draft chunks together: 4 vectors of each (8 KB per wave) unless
+// that leaves fewer than 2048 jobs, then 2.  Depends only on the call's sizes
+// and mode, so both launches of a call agree on the chunk geometry.
+int choose_nv_mode(const ChainReq &q, int vec) {
+    if (q.space == 1) return int64_t(q.B) * pcap(q) * c1_for(q.V, 4, vec) < 2048 ? 2 : 4;
+    return choose_nv(q.B, pcap(q), q.V, vec);
+}
 
 sv_status validate(const ChainReq &q) {
     const int eb = elem_bytes(q.dtype);
@@ -832,17 +988,28 @@ ChainArgs make_args(const ChainReq &q, int vec, int nv) {
     a.NV2 = choose_nv2(q.B, q.V, vec);
     a.C2 = c2_for(q.V, vec, a.NV2);
     a.rec_stride = chunk_rec_doubles(a.NV2);
+    a.space = q.space;
+    a.alpha_c = (1.0 - static_cast<double>(q.lam)) * a.c_d;
+    a.beta_c = static_cast<double>(q.lam) * a.c_d;
     return a;
 }
 
 template <class DT>
 sv_status run_typed(const ChainReq &q, int which) {
-    const int nv = choose_nv(q.B, pcap(q), q.V, DT::kVec);
+    const int nv = choose_nv_mode(q, DT::kVec);
     const ChainArgs a = make_args(q, DT::kVec, nv);
     // every locate thread holds at most kLocPP piece masses (always true for
     // the vocabularies validate() accepts; checked before any launch)
     if (int64_t(a.C2) * kWaves2 * a.NV2 > int64_t(kBlock) * kLocPP) return SV_EINVAL;
-    if (which & 1) {
+    if ((which & 1) && a.space == 1) {
+        const int jobs = static_cast<int>(int64_t(q.B) * a.g.Pcap * a.C1);
+        const dim3 grid(static_cast<unsigned>(jobs > 0 ? cdiv(jobs, kWaves) : 1));
+        if (nv == 4)
+            launch_timed(k_row_stats_logit<DT, 4>, grid, dim3(kBlock), 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
+        else
+            launch_timed(k_row_stats_logit<DT, 2>, grid, dim3(kBlock), 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
+        if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    } else if (which & 1) {
         const int jobs = static_cast<int>(int64_t(q.B) * a.g.Pcap * 2 * a.C1);
         const dim3 grid(static_cast<unsigned>(jobs > 0 ? cdiv(jobs, kWaves) : 1));
         if (nv == 8)
@@ -911,6 +1078,7 @@ ChainReq chain_req(const void *t, int64_t ld_t, const void *d, int64_t ld_q, sv_
     q.stream = s;
     q.ev_start = nullptr;
     q.ev_stop = nullptr;
+    q.space = 0;
     return q;
 }
 
@@ -981,6 +1149,27 @@ sv_status sv_chain_row_stats_timed(const void *target_logits, int64_t ld_t,
     return run_chain(q, 1);
 }
 
+sv_status sv_chain_verify_ex(const void *target_logits, int64_t ld_t, const void *draft_logits,
+                             int64_t ld_q, sv_dtype dtype, int B, int K, int V,
+                             const int32_t *draft_tokens, const int32_t *draft_len,
+                             const float *u_accept, const float *u_sample, float lambda,
+                             float temperature, int32_t *accepted, int32_t *out_tokens,
+                             float *accept_prob, int32_t *status, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream, int mix_space, int stages,
+                             hipEvent_t kernel_start, hipEvent_t kernel_stop) {
+    if ((mix_space != SV_MIX_PROB && mix_space != SV_MIX_LOGIT) || stages < 1 || stages > 3)
+        return SV_EINVAL;
+    ChainReq q = chain_req(target_logits, ld_t, draft_logits, ld_q, dtype, B, K, V, draft_tokens,
+                           draft_len, u_accept, u_sample, lambda, temperature, accepted,
+                           out_tokens, accept_prob, status, workspace, workspace_bytes, stream);
+    // at lambda = 0 or 1 the logit mixture is one model's own logits: the
+    // probability-space path computes exactly that
+    q.space = (mix_space == SV_MIX_LOGIT && lambda > 0.0f && lambda < 1.0f) ? 1 : 0;
+    q.ev_start = kernel_start;
+    q.ev_stop = kernel_stop;
+    return run_chain(q, stages);
+}
+
 sv_status sv_chain_accept_resample(const void *target_logits, int64_t ld_t,
                                    const void *draft_logits, int64_t ld_q, sv_dtype dtype, int B,
                                    int K, int V, const int32_t *draft_tokens,
@@ -1010,6 +1199,25 @@ sv_status sv_tree_verify_path(const void *target_logits, int64_t ld_t, const voi
     q.N = N;
     q.path_mode = true;
     q.path = path;
+    return run_chain(q, 3);
+}
+
+sv_status sv_tree_verify_path_ex(const void *target_logits, int64_t ld_t, const void *draft_logits,
+                                 int64_t ld_q, sv_dtype dtype, int B, int N, int V,
+                                 const int32_t *node_token, const int32_t *path, int Dmax,
+                                 const float *u_accept, const float *u_sample, float lambda,
+                                 float temperature, int32_t *accepted, int32_t *out_tokens,
+                                 float *accept_prob, int32_t *status, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream, int mix_space) {
+    if (mix_space != SV_MIX_PROB && mix_space != SV_MIX_LOGIT) return SV_EINVAL;
+    if (N < 0 || N > SV_MAX_TREE_NODES || Dmax < 0 || Dmax > SV_MAX_POSITIONS) return SV_EINVAL;
+    ChainReq q = chain_req(target_logits, ld_t, draft_logits, ld_q, dtype, B, Dmax, V, node_token,
+                           nullptr, u_accept, u_sample, lambda, temperature, accepted, out_tokens,
+                           accept_prob, status, workspace, workspace_bytes, stream);
+    q.N = N;
+    q.path_mode = true;
+    q.path = path;
+    q.space = (mix_space == SV_MIX_LOGIT && lambda > 0.0f && lambda < 1.0f) ? 1 : 0;
     return run_chain(q, 3);
 }
 

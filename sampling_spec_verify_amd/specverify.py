@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_OK, SV_EINVAL, SV_ENULL, SV_EALIGN, SV_EWORKSPACE, SV_EDTYPE, SV_EHIP = range(7)
 SV_BF16, SV_F32 = 0, 1
+SV_MIX_PROB, SV_MIX_LOGIT = 0, 1
+MIX_SPACES = {"prob": SV_MIX_PROB, "logit": SV_MIX_LOGIT}
 SV_MAX_POSITIONS = 64
 SV_MAX_TREE_NODES = 1024
 DATA_FLAGS = {
@@ -33,6 +35,8 @@ _S = ctypes.c_size_t
 
 _CHAIN_ARGS = [_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _P, _P, _F, _F, _P, _P, _P, _P, _P, _S, _P]
 _GREEDY_ARGS = [_P, _L, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _S, _P]
+_PATH_ARGS = [_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _I, _P, _P, _F, _F, _P, _P, _P, _P, _P, _S,
+              _P]
 
 SIGNATURES = {
     "sv_status_string": ([_I], ctypes.c_char_p),
@@ -41,6 +45,7 @@ SIGNATURES = {
     "sv_chain_row_stats": (_CHAIN_ARGS, _I),
     "sv_chain_accept_resample": (_CHAIN_ARGS, _I),
     "sv_chain_row_stats_timed": (_CHAIN_ARGS + [_P, _P], _I),
+    "sv_chain_verify_ex": (_CHAIN_ARGS + [_I, _I, _P, _P], _I),
     "sv_tree_workspace_bytes": ([_I, _I, _I], _S),
     "sv_tree_verify_greedy": (_GREEDY_ARGS, _I),
     "sv_tree_row_argmax": (_GREEDY_ARGS, _I),
@@ -48,8 +53,8 @@ SIGNATURES = {
     "sv_tree_row_argmax_timed": (_GREEDY_ARGS + [_P, _P], _I),
     "sv_tree_attention_mask": ([_P, _I, _I, _P, _I, _P, _P, _P], _I),
     "sv_tree_attention_mask_timed": ([_P, _I, _I, _P, _I, _P, _P, _P, _P, _P], _I),
-    "sv_tree_verify_path": ([_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _I, _P, _P, _F, _F, _P, _P,
-                             _P, _P, _P, _S, _P], _I),
+    "sv_tree_verify_path": (_PATH_ARGS, _I),
+    "sv_tree_verify_path_ex": (_PATH_ARGS + [_I], _I),
 }
 
 _lib = None
@@ -201,12 +206,16 @@ class ChainCall:
     ``run()`` launches both kernels; ``row_stats()`` / ``accept_resample()``
     launch one each (the pair equals ``run()``).  Rebinding inputs with
     ``set_inputs`` keeps the outputs and workspace.  The stream (default: the
-    current torch stream) is bound when the inputs are.
+    current torch stream) is bound when the inputs are.  ``space`` is "prob"
+    (the mixture equation) or "logit" (the pseudocode's mixed logits).
     """
 
     def __init__(self, target, draft, tokens, u_accept, u_sample, lam=0.0, temperature=1.0,
-                 draft_len=None, stream=None, workspace=None):
+                 draft_len=None, stream=None, workspace=None, space: str = "prob"):
         torch = _torch()
+        if space not in MIX_SPACES:
+            raise ValueError(f"space must be one of {sorted(MIX_SPACES)}, got {space!r}")
+        self.space = MIX_SPACES[space]
         B, K1, V = target.shape
         K = K1 - 1
         dev = target.device
@@ -244,28 +253,42 @@ class ChainCall:
                 _ptr(o.accepted), _ptr(o.out_tokens), _ptr(o.accept_prob), _ptr(o.status),
                 _ptr(self.workspace), self.workspace.numel(), _stream(self.stream))
 
+    def _ex(self, stages: int, events=None):
+        ev = (None, None) if events is None else events
+        _check(lib().sv_chain_verify_ex(*self._cached, self.space, stages, *ev),
+               "sv_chain_verify_ex")
+
     def run(self) -> ChainOut:
-        _check(lib().sv_chain_verify(*self._cached), "sv_chain_verify")
+        if self.space == SV_MIX_PROB:
+            _check(lib().sv_chain_verify(*self._cached), "sv_chain_verify")
+        else:
+            self._ex(3)
         return self.out
 
     def row_stats(self, events=None):
         """Launch the row-statistics kernel; ``events`` = (start, stop) times it."""
-        if events is None:
+        if self.space != SV_MIX_PROB:
+            self._ex(1, events)
+        elif events is None:
             _check(lib().sv_chain_row_stats(*self._cached), "sv_chain_row_stats")
         else:
             _check(lib().sv_chain_row_stats_timed(*self._cached, *events),
                    "sv_chain_row_stats_timed")
 
     def accept_resample(self) -> ChainOut:
-        _check(lib().sv_chain_accept_resample(*self._cached), "sv_chain_accept_resample")
+        if self.space != SV_MIX_PROB:
+            self._ex(2)
+        else:
+            _check(lib().sv_chain_accept_resample(*self._cached), "sv_chain_accept_resample")
         return self.out
 
 
 def chain_verify(target, draft, tokens, u_accept, u_sample, lam: float = 0.0,
-                 temperature: float = 1.0, draft_len=None, stream=None) -> ChainOut:
+                 temperature: float = 1.0, draft_len=None, stream=None,
+                 space: str = "prob") -> ChainOut:
     """sv_chain_verify on torch tensors: target [B,K+1,V], draft [B,K,V] (bf16 or fp32)."""
     return ChainCall(target, draft, tokens, u_accept, u_sample, lam, temperature, draft_len,
-                     stream).run()
+                     stream, space=space).run()
 
 
 class TreeGreedyOut(NamedTuple):
@@ -370,7 +393,8 @@ def tree_attention_mask(parent, N: Optional[int] = None, mask_words: Optional[in
 
 
 def tree_verify_path(target, draft, node_token, path, u_accept, u_sample, lam: float = 0.0,
-                     temperature: float = 1.0, stream=None, workspace=None) -> ChainOut:
+                     temperature: float = 1.0, stream=None, workspace=None,
+                     space: str = "prob") -> ChainOut:
     """sv_tree_verify_path: target / draft [B, N+1, V], path [B, Dmax] (-1 terminated)."""
     torch = _torch()
     B, N1, V = target.shape
@@ -391,11 +415,14 @@ def tree_verify_path(target, draft, node_token, path, u_accept, u_sample, lam: f
                    torch.empty(1, dtype=torch.int32, device=dev))
     ws = workspace if workspace is not None else torch.empty(
         max(tree_workspace_bytes(B, N, V), 16), dtype=torch.uint8, device=dev)
-    code = lib().sv_tree_verify_path(_ptr(target), ld_t, _ptr(draft), ld_q, _dtype_code(target), B,
-                                     N, V, _ptr(node_token), _ptr(path), Dmax, _ptr(u_accept),
-                                     _ptr(u_sample), float(lam), float(temperature),
-                                     _ptr(out.accepted), _ptr(out.out_tokens),
-                                     _ptr(out.accept_prob), _ptr(out.status), _ptr(ws), ws.numel(),
-                                     _stream(stream))
-    _check(code, "sv_tree_verify_path")
+    if space not in MIX_SPACES:
+        raise ValueError(f"space must be one of {sorted(MIX_SPACES)}, got {space!r}")
+    args = (_ptr(target), ld_t, _ptr(draft), ld_q, _dtype_code(target), B, N, V, _ptr(node_token),
+            _ptr(path), Dmax, _ptr(u_accept), _ptr(u_sample), float(lam), float(temperature),
+            _ptr(out.accepted), _ptr(out.out_tokens), _ptr(out.accept_prob), _ptr(out.status),
+            _ptr(ws), ws.numel(), _stream(stream))
+    if space == "prob":
+        _check(lib().sv_tree_verify_path(*args), "sv_tree_verify_path")
+    else:
+        _check(lib().sv_tree_verify_path_ex(*args, MIX_SPACES[space]), "sv_tree_verify_path_ex")
     return out

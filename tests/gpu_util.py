@@ -34,10 +34,10 @@ def dev(a: np.ndarray | None):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def chain_call(x: ChainInputs, ld: int | None = None) -> sv.ChainCall:
+def chain_call(x: ChainInputs, ld: int | None = None, space: str = "prob") -> sv.ChainCall:
     return sv.ChainCall(dev_logits(x.target, x.dtype, ld), dev_logits(x.draft, x.dtype, ld),
                         dev(x.tokens), dev(x.u_accept), dev(x.u_sample), x.lam, x.temperature,
-                        dev(x.draft_len))
+                        dev(x.draft_len), space=space)
 
 
 def to_host(out):
@@ -45,13 +45,13 @@ def to_host(out):
     return type(out)(*[t.cpu().numpy() for t in out])
 
 
-def run_chain(x: ChainInputs, ld: int | None = None):
-    return to_host(chain_call(x, ld).run())
+def run_chain(x: ChainInputs, ld: int | None = None, space: str = "prob"):
+    return to_host(chain_call(x, ld, space).run())
 
 
-def oracle_chain(x: ChainInputs, requests=None):
+def oracle_chain(x: ChainInputs, requests=None, space: str = "prob"):
     return oracle.chain_verify(x.widened(x.target), x.widened(x.draft), x.tokens, x.draft_len,
-                               x.u_accept, x.u_sample, x.lam, x.temperature, requests)
+                               x.u_accept, x.u_sample, x.lam, x.temperature, requests, space)
 
 
 def compare_chain(x: ChainInputs, g, ref, requests=None, lengths=None):
@@ -83,10 +83,10 @@ def run_greedy(x: TreeInputs, Dmax: int | None = None, ld: int | None = None):
     return to_host(out)
 
 
-def run_path(x: TreeInputs, ld: int | None = None):
+def run_path(x: TreeInputs, ld: int | None = None, space: str = "prob"):
     out = sv.tree_verify_path(dev_logits(x.target, x.dtype, ld), dev_logits(x.draft, x.dtype, ld),
                               dev(x.node_token), dev(x.path), dev(x.u_accept), dev(x.u_sample),
-                              x.lam, x.temperature)
+                              x.lam, x.temperature, space=space)
     return to_host(out)
 
 

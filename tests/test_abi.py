@@ -22,11 +22,12 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["sv_status_string", "sv_chain_workspace_bytes", "sv_chain_verify",
                             "sv_chain_row_stats", "sv_chain_accept_resample",
-                            "sv_chain_row_stats_timed",
+                            "sv_chain_row_stats_timed", "sv_chain_verify_ex",
                             "sv_tree_workspace_bytes", "sv_tree_verify_greedy",
                             "sv_tree_row_argmax", "sv_tree_greedy_walk",
                             "sv_tree_row_argmax_timed", "sv_tree_attention_mask",
-                            "sv_tree_attention_mask_timed", "sv_tree_verify_path"])
+                            "sv_tree_attention_mask_timed", "sv_tree_verify_path",
+                            "sv_tree_verify_path_ex"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -65,6 +66,8 @@ def chain_call(fn="sv_chain_verify", **kw):
     args.update(kw)
     L = sv.lib()
     timed = (FAKE, FAKE) if fn.endswith("_timed") else ()
+    if fn == "sv_chain_verify_ex":
+        timed = (args.get("space", sv.SV_MIX_LOGIT), args.get("stages", 3), None, None)
     return getattr(L, fn)(args["t"], args["ld_t"], args["d"], args["ld_q"], args["dtype"], args["B"],
                           args["K"], args["V"], args["tok"], args["dl"], args["ua"], args["us"],
                           args["lam"], args["T"], args["acc"], args["out"], args["ap"], args["st"],
@@ -72,7 +75,7 @@ def chain_call(fn="sv_chain_verify", **kw):
 
 
 @pytest.mark.parametrize("fn", ["sv_chain_verify", "sv_chain_row_stats", "sv_chain_accept_resample",
-                                "sv_chain_row_stats_timed"])
+                                "sv_chain_row_stats_timed", "sv_chain_verify_ex"])
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), sv.SV_EDTYPE),
     (dict(B=-1), sv.SV_EINVAL),
@@ -108,6 +111,11 @@ def test_chain_argument_errors(fn, kw, code):
     if kw.get("wsb") == "short":
         kw = dict(wsb=sv.lib().sv_chain_workspace_bytes(2, 4, 128) - 16)
     assert chain_call(fn, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(space=2), dict(space=-1), dict(stages=0), dict(stages=4)])
+def test_chain_ex_rejects_unknown_mode_or_stages(kw):
+    assert chain_call("sv_chain_verify_ex", **kw) == sv.SV_EINVAL
 
 
 def test_chain_empty_batch_is_a_no_op():
@@ -155,6 +163,15 @@ def path_call(**kw):
                 st=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
     args.update(kw)
     return sv.lib().sv_tree_verify_path(*args.values())
+
+
+def test_path_ex_rejects_unknown_mode():
+    args = dict(t=FAKE, ld_t=128, d=FAKE, ld_q=128, dtype=sv.SV_BF16, B=2, N=5, V=128, tok=FAKE,
+                path=FAKE, Dmax=4, ua=FAKE, us=FAKE, lam=0.3, T=1.0, acc=FAKE, out=FAKE, ap=FAKE,
+                st=FAKE, ws=FAKE, wsb=16, stream=None)
+    L = sv.lib()
+    assert L.sv_tree_verify_path_ex(*args.values(), 5) == sv.SV_EINVAL
+    assert L.sv_tree_verify_path_ex(*args.values(), sv.SV_MIX_LOGIT) == sv.SV_EWORKSPACE
 
 
 @pytest.mark.parametrize("kw,code", [

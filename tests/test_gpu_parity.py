@@ -357,3 +357,89 @@ def test_mask_bad_parent_is_reported_and_read_as_root_child():
     st, bad = _mask_case(parent)
     assert bad.tolist() == [True, False]
     assert "BAD_TREE" in sv.decode_flags(st)
+
+
+# ---------------------------------------------------------------------------
+# logit-space mixture (the RAPID pseudocode's form)
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("cfg,lam", [("c3", None), ("c4", 0.3), ("c2", 0.5)])
+def test_logit_mixture_workload(cfg, lam):
+    x = synth.config(cfg)
+    if lam is not None:
+        x.lam = lam
+    g = run_chain(x, space="logit")
+    assert int(g.status[0]) == 0, sv.decode_flags(int(g.status[0]))
+    stats = compare_chain(x, g, oracle_chain(x, space="logit"))
+    report(f"{cfg} logit", stats)
+    assert stats["flagged"] <= max(2, x.B // 4)
+
+
+LOGIT_SMALL = [
+    # seed, B, K, V, dtype, lam, T, ragged, ld
+    (21, 3, 4, 1000, "fp32", 0.3, 1.0, False, None),
+    (22, 5, 3, 8200, "bf16", 0.7, 0.7, True, None),
+    (23, 2, 8, 33000, "bf16", 0.05, 1.3, False, None),
+    (24, 4, 2, 4097, "fp32", 0.5, 1.0, True, 4100),
+    (25, 7, 1, 7, "fp32", 0.4, 1.0, False, 8),
+    (26, 6, 0, 5000, "bf16", 0.2, 0.8, False, None),
+    (27, 2, 64, 300, "fp32", 0.6, 1.0, False, None),
+    (28, 40, 4, 2048, "bf16", 0.95, 1.0, True, None),
+]
+
+
+@pytest.mark.parametrize("seed,B,K,V,dtype,lam,T,ragged,ld", LOGIT_SMALL)
+def test_logit_mixture_small(seed, B, K, V, dtype, lam, T, ragged, ld):
+    x = synth.make_chain(100 + seed, B, K, V, dtype, sigma_t=2.0, sigma_q=(0.3, 2.0),
+                         zipf=V > 16, lam=lam, temperature=T, ragged=ragged, k_min=0)
+    g = run_chain(x, ld, space="logit")
+    assert int(g.status[0]) == 0, sv.decode_flags(int(g.status[0]))
+    report(f"logit{seed}", compare_chain(x, g, oracle_chain(x, space="logit")))
+
+
+@pytest.mark.parametrize("lam", [0.0, 1.0])
+def test_logit_mixture_at_the_ends_equals_probability_space(lam):
+    x = synth.make_chain(231, 5, 4, 6000, "bf16", lam=lam, sigma_q=1.5, ragged=True)
+    a = run_chain(x, space="logit")
+    b = run_chain(x)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+    compare_chain(x, a, oracle_chain(x, space="logit"))
+
+
+def test_logit_mixture_identical_rows_and_stage_calls():
+    x = synth.make_chain(232, 4, 5, 3000, "fp32", lam=0.45)
+    x.draft = np.ascontiguousarray(x.target[:, :5, :])
+    g = run_chain(x, space="logit")
+    assert np.all(g.accepted == 5)
+    x = synth.make_chain(233, 5, 4, 12000, "bf16", ragged=True, lam=0.35)
+    call = chain_call(x, space="logit")
+    full = to_host(call.run())
+    call.row_stats()
+    split = to_host(call.accept_resample())
+    for u, v in zip(full, split):
+        np.testing.assert_array_equal(u, v)
+    compare_chain(x, full, oracle_chain(x, space="logit"))
+
+
+def test_logit_mixture_path_mode():
+    x = synth.make_random_tree(433, 5, 30, 9000, "bf16", sharp=1.0, lam=0.4, temperature=0.9)
+    g = run_path(x, space="logit")
+    assert int(g.status[0]) == 0
+    ref = oracle.tree_path(x.widened(x.target), x.widened(x.draft), x.node_token, x.path,
+                           x.u_accept, x.u_sample, x.lam, x.temperature, space="logit")
+    report("path logit", compare_chain(x, g, ref, lengths=path_lengths(x)))
+
+
+def test_lambda_one_with_unreachable_draft_samples_the_draft():
+    """lambda = 1 and q(x) = 0: the draft is rejected and, the residual
+    max(0, p~ - q) being zero, the token is drawn from p~ = q."""
+    x = synth.make_chain(234, 6, 3, 3000, "fp32", lam=1.0, sigma_q=2.0)
+    for b in range(x.B):
+        x.draft[b, 1, x.tokens[b, 1]] = -np.inf      # position 1's draft cannot produce x
+    g = run_chain(x)
+    flags = sv.decode_flags(int(g.status[0]))
+    assert "ZERO_Q" in flags and "FALLBACK" in flags
+    assert np.all(g.accepted == 1)
+    report("lambda=1 q(x)=0", compare_chain(x, g, oracle_chain(x)))
