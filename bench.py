@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "c5mask"])
+    ap.add_argument("--alpha", action="store_true",
+                    help="chain workloads: time the acceptance-rate call instead of the verify call")
     ap.add_argument("--space", default="prob", choices=["prob", "logit"],
                     help="chain workloads: mix the two models in probability space (the "
                          "mixture equation) or logit space (the pseudocode's form)")
@@ -261,6 +263,77 @@ def bench_mask(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_alpha(args):
+    """The acceptance-rate call on a chain workload: one call per step."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sampling_spec_verify_amd import specverify as sv
+    from sampling_spec_verify_amd import synth
+
+    sv.lib()
+    x = synth.config(args.workload)
+    elem = 2 if x.dtype == "bf16" else 4
+    positions = x.positions()
+    algo_bytes = 2 * 2 * x.V * elem * positions          # two passes over the drafted rows
+    R = max(2, min(512, math.ceil(ROTATE_BYTES / (x.target.nbytes + x.draft.nbytes))))
+    tgts = device_copies(x.target, x.dtype, R, torch)
+    drfs = device_copies(x.draft, x.dtype, R, torch)
+    dl = None if x.draft_len is None else torch.from_numpy(x.draft_len).to("cuda:0")
+    calls = [sv.AcceptanceRateCall(tgts[i], drfs[i], x.lam, x.temperature, dl, space=args.space)
+             for i in range(R)]
+    for i in range(args.warmup):
+        calls[i % R].run()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(K):
+        calls[i % R].run()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    alpha = calls[0].alpha.cpu().numpy()
+    cpu = None
+    if args.cpu_seconds > 0:
+        t = x.widened(x.target)
+        d = x.widened(x.draft)
+        lens = x.lengths()
+        done = pos = 0
+        err = 0.0
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < args.cpu_seconds:
+            b = done % x.B
+            k = int(lens[b])
+            r = oracle.chain_verify_one(t[b, :k + 1], d[b, :k], x.tokens[b, :k],
+                                        x.u_accept[b, :k], x.u_sample[b], x.lam, x.temperature,
+                                        args.space)
+            if done < x.B and k:
+                err = max(err, float(np.abs(alpha[b, :k] - r.alpha).max()))
+            pos += k
+            done += 1
+        el = time.perf_counter() - t1
+        cpu = {"value": pos / el, "unit": "positions/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} oracle request verifications (each computes alpha), fp64 numpy",
+               "seconds": round(el, 2), "alpha_max_abs_err": err}
+    line = {
+        "metric": "drafted positions/sec through the acceptance-rate call",
+        "value": positions * K / wall, "unit": "positions/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / K, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {synth.CONFIGS[args.workload]}",
+                   "mixture_space": args.space, "buffer_sets_rotated": R},
+        "step_hbm_gbps": algo_bytes * K / (wall * 1e9),
+        "step_hbm_frac": algo_bytes * K / (wall * 1e9) / PEAK_HBM_GBS,
+        "algorithmic_bytes_per_step": algo_bytes, "gpu_ms_per_step": ev0.elapsed_time(ev1) / K,
+        "cpu_baseline": cpu, "status_word": int(calls[0].status[0].item()),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -273,6 +346,9 @@ def main():
         return
     if args.workload == "c5mask":
         bench_mask(args)
+        return
+    if args.alpha:
+        bench_alpha(args)
         return
 
     import numpy as np

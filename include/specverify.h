@@ -197,6 +197,30 @@ sv_status sv_chain_verify_ex(const void *target_logits, int64_t ld_t,
                              hipStream_t stream, int mix_space, int stages,
                              hipEvent_t kernel_start, hipEvent_t kernel_stop);
 
+/*
+ * Acceptance rate of every drafted position: alpha[b, i] = sum_v
+ * min(p~(v), q(v)), the probability that position i accepts a draft drawn
+ * from q ([SD] and [EAGLE] define the acceptance rate as the share of drafts
+ * the target keeps; with the rule min(1, p~/q) its expectation under q is
+ * this sum).  It needs no drafted tokens or uniforms.  Telemetry for a host
+ * policy that adapts the draft length or lambda ([EAGLE] "4. 草稿长度和接受率
+ * 的权衡"; [RAPID] section 2: lambda is schedulable).  Costs one more read of
+ * every drafted row: three launches (row statistics, per-chunk min masses,
+ * a fixed-order reduce).
+ *
+ *  Arguments as sv_chain_verify (draft_len may be NULL); mix_space an
+ *  sv_mix_space.  alpha [B, K] float out (0 past draft_len[b]; NaN where a
+ *  row is bad, with SV_DATA_BAD_ROW in *status).  workspace of at least
+ *  sv_chain_acceptance_workspace_bytes(B, K, V) bytes.
+ */
+size_t sv_chain_acceptance_workspace_bytes(int B, int K, int V);
+sv_status sv_chain_acceptance_rate(const void *target_logits, int64_t ld_t,
+                                   const void *draft_logits, int64_t ld_q,
+                                   sv_dtype dtype, int B, int K, int V,
+                                   const int32_t *draft_len, float lambda, float temperature,
+                                   int mix_space, float *alpha, int32_t *status,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Draft trees ([SD] "Tree Speculation", [EAGLE] greedy match + tree attention)
  *

@@ -108,7 +108,8 @@ __device__ __forceinline__ void row_chunk_stats(const ChainArgs &a, unsigned job
     if (!geo_position_valid(a.g, b, i)) return;
     const char *row = row_ptr(a.g, tensor, b, geo_row(a.g, b, i));
     // the wave whose chunk holds the drafted token also gathers its logit
-    const int x = geo_token(a.g, b, i);
+    // no drafted tokens (the acceptance-rate call): nothing to gather
+    const int x = (a.g.tokens != nullptr) ? geo_token(a.g, b, i) : -1;
     const bool own_x = x >= 0 && x < a.g.V && x / a.ch1 == c;
 
     constexpr int VEC = DT::kVec;
@@ -192,7 +193,7 @@ __device__ __forceinline__ void row_chunk_stats_logit(const ChainArgs &a, unsign
     const int r = geo_row(a.g, b, i);
     const char *row_t = row_ptr(a.g, 0, b, r);
     const char *row_q = row_ptr(a.g, 1, b, r);
-    const int x = geo_token(a.g, b, i);
+    const int x = (a.g.tokens != nullptr) ? geo_token(a.g, b, i) : -1;
     const bool own_x = x >= 0 && x < a.g.V && x / a.ch1 == c;
 
     constexpr int VEC = DT::kVec;
@@ -363,6 +364,113 @@ __device__ __forceinline__ double vec_sum(const float *w) {
 #pragma unroll
         for (int e = 0; e + h < VEC; e += 2 * h) p[e] = p[e] + p[e + h];
     return static_cast<double>(p[0]);
+}
+
+// ---------------------------------------------------------------------------
+// acceptance rate alpha_i = sum_v min(p~(v), q(v)) of every drafted position
+// ---------------------------------------------------------------------------
+
+// Row statistics (shift s, 1 / S) of one row from its C1 chunk partials, by
+// one wavefront, in fp64 and in a fixed order; S = 0 or non-finite marks the
+// row bad (1 / S is then NaN).
+__device__ __forceinline__ void combine_row(const Part *p, int C1, float &s_out, float &inv_out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float smax = -INFINITY;
+    for (int c = lane; c < C1; c += kWave) smax = fmaxf(smax, p[c].s);
+    smax = wave_max(smax);
+    double S = 0.0;
+    for (int c = lane; c < C1; c += kWave) {
+        const Part q = p[c];
+        if (q.s != -INFINITY) S += q.S * pow2_shift_d(static_cast<double>(q.s) - static_cast<double>(smax));
+    }
+    S = wave_sum_d(S);
+    s_out = smax;
+    inv_out = (S > 0.0 && isfinite(S) && isfinite(smax)) ? static_cast<float>(1.0 / S) : NAN;
+}
+
+// One block per (request, position, group of 4 chunks): wave 0 combines the
+// target (or mixed, in logit space) row's statistics and wave 1 the draft
+// row's, then wave w reduces chunk 4 g + w to the fp64 sum of
+// min(p~(v), q(v)) over its elements.  Per element (probability space)
+// p~ = (1 - lambda) p_t + lambda q with p(v) = 2^(z c - s) / S; in logit
+// space p~(v) = 2^(alpha z_t + beta z_q - s_e) / S_e.
+template <class DT, int NV, int LOGIT>
+__global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
+    __shared__ float st_s, st_i, sq_s, sq_i;
+    const int groups = (a.C1 + kWaves - 1) / kWaves;
+    const int job = blockIdx.x;
+    const int grp = job % groups;
+    const int pos = job / groups;
+    const int i = pos % a.g.Pcap;
+    const int b = pos / a.g.Pcap;
+    if (!geo_position_valid(a.g, b, i)) return;            // uniform over the block
+    const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const Part *parts = a.part1 + (int64_t(b) * a.g.Pcap + i) * 2 * a.C1;
+    if (wv < 2) {
+        float s_, inv_;
+        combine_row(parts + wv * a.C1, a.C1, s_, inv_);
+        if (lane == 0) {
+            if (wv == 0) {
+                st_s = s_;
+                st_i = inv_;
+            } else {
+                sq_s = s_;
+                sq_i = inv_;
+            }
+        }
+    }
+    __syncthreads();
+    const int c = grp * kWaves + wv;
+    if (c >= a.C1) return;
+    constexpr int VEC = DT::kVec;
+    const int V = a.g.V;
+    const int r = geo_row(a.g, b, i);
+    const char *row_t = row_ptr(a.g, 0, b, r);
+    const char *row_q = row_ptr(a.g, 1, b, r);
+    const int v0 = c * (kWave * NV);
+    u32x4 dt[NV], dq[NV];
+    load_chunk<DT, NV>(row_t, v0, lane, V, dt);
+    load_chunk<DT, NV>(row_q, v0, lane, V, dq);
+    const float c_hi = a.c_hi, c_lo = a.c_lo;
+    const float ts = st_s, ti = st_i, qs = sq_s, qi = sq_i;
+    const float w_t = 1.0f - a.lam, w_q = a.lam;
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        float ft[VEC], fq[VEC];
+        DT::unpack(dt[n], ft);
+        DT::unpack(dq[n], fq);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float q = pow2_logit(fq[e], c_hi, c_lo, qs) * qi;
+            float pm;
+            if (LOGIT) pm = pow2_mixed(ft[e], fq[e], a.alpha_c, a.beta_c, ts) * ti;
+            else pm = fmaf(w_t, pow2_logit(ft[e], c_hi, c_lo, ts) * ti, w_q * q);
+            acc[e] += fminf(pm, q);
+        }
+    }
+    const double tot = wave_sum_d(vec_sum<VEC>(acc));
+    if (lane == 0) a.alpha_part[(int64_t(b) * a.g.Pcap + i) * a.C1 + c] = tot;
+}
+
+// alpha of every position, summing its chunk partials in chunk order; 0 for
+// undrafted positions.  Sets SV_DATA_BAD_ROW when a drafted row is bad.
+__global__ __launch_bounds__(kBlock) void k_alpha_reduce(ChainArgs a) {
+    const int64_t pos = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+    if (pos >= int64_t(a.B) * a.g.P) return;
+    const int b = static_cast<int>(pos / a.g.P);
+    const int i = static_cast<int>(pos % a.g.P);
+    float out = 0.0f;
+    if (i < a.g.Pcap && geo_position_valid(a.g, b, i)) {
+        const double *p = a.alpha_part + (int64_t(b) * a.g.Pcap + i) * a.C1;
+        double s = 0.0;
+        for (int c = 0; c < a.C1; ++c) s += p[c];
+        out = static_cast<float>(s);
+        if (!(out == out)) atomicOr(a.status, SV_DATA_BAD_ROW);
+    }
+    a.alpha[pos] = out;
 }
 
 struct ResolveShared {
@@ -1041,6 +1149,38 @@ sv_status run_typed(const ChainReq &q, int which) {
     return SV_OK;
 }
 
+template <class DT, int NV>
+void launch_alpha(const ChainArgs &a, hipStream_t stream) {
+    const int groups = (a.C1 + kWaves - 1) / kWaves;
+    const dim3 grid(static_cast<unsigned>(int64_t(a.B) * a.g.Pcap * groups));
+    if (a.space == 1)
+        hipLaunchKernelGGL((k_alpha_mass<DT, NV, 1>), grid, dim3(kBlock), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_alpha_mass<DT, NV, 0>), grid, dim3(kBlock), 0, stream, a);
+}
+
+// The acceptance-rate call: row statistics (as the verify call's first
+// launch, no drafted tokens), the per-chunk min(p~, q) masses, the reduce.
+template <class DT>
+sv_status run_alpha_typed(const ChainReq &q, float *alpha) {
+    const int nv = choose_nv_mode(q, DT::kVec);
+    ChainArgs a = make_args(q, DT::kVec, nv);
+    a.alpha_part = reinterpret_cast<double *>(static_cast<char *>(q.ws) +
+                                              alpha_layout_parts(q.B, pcap(q), q.V));
+    a.alpha = alpha;
+    sv_status st = run_typed<DT>(q, 1);
+    if (st != SV_OK) return st;
+    if (a.g.Pcap > 0) {
+        if (nv == 8) launch_alpha<DT, 8>(a, q.stream);
+        else if (nv == 4) launch_alpha<DT, 4>(a, q.stream);
+        else launch_alpha<DT, 2>(a, q.stream);
+        const int64_t n = int64_t(q.B) * q.P;
+        hipLaunchKernelGGL(k_alpha_reduce, dim3(static_cast<unsigned>(cdiv(n, kBlock))), dim3(kBlock), 0,
+                           q.stream, a);
+    }
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
 sv_status run_chain(const ChainReq &q, int which) {
     const sv_status st = validate(q);
     if (st != SV_OK || q.B == 0) return st;
@@ -1168,6 +1308,37 @@ sv_status sv_chain_verify_ex(const void *target_logits, int64_t ld_t, const void
     q.ev_start = kernel_start;
     q.ev_stop = kernel_stop;
     return run_chain(q, stages);
+}
+
+size_t sv_chain_acceptance_workspace_bytes(int B, int K, int V) {
+    if (B < 0 || K < 0 || K > SV_MAX_POSITIONS || V < 1) return 0;
+    return static_cast<size_t>(alpha_layout_total(B, K, V));
+}
+
+sv_status sv_chain_acceptance_rate(const void *target_logits, int64_t ld_t, const void *draft_logits,
+                                   int64_t ld_q, sv_dtype dtype, int B, int K, int V,
+                                   const int32_t *draft_len, float lambda, float temperature,
+                                   int mix_space, float *alpha, int32_t *status, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    if (mix_space != SV_MIX_PROB && mix_space != SV_MIX_LOGIT) return SV_EINVAL;
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return SV_EDTYPE;
+    if (B < 0 || K < 0 || K > SV_MAX_POSITIONS || V < 1 || B > (1 << 30)) return SV_EINVAL;
+    sv_status st = check_scalars(lambda, temperature);
+    if (st != SV_OK) return st;
+    if (B == 0 || K == 0) return SV_OK;
+    if (!alpha) return SV_ENULL;
+    if ((st = check_logits(target_logits, ld_t, V, eb)) != SV_OK) return st;
+    if ((st = check_logits(draft_logits, ld_q, V, eb)) != SV_OK) return st;
+    if (int64_t(B) * K * 2 * c1_for(V, kMinNV, kMinVec) >= (int64_t(1) << 31)) return SV_EINVAL;
+    if (!workspace || !aligned16(workspace) ||
+        workspace_bytes < static_cast<size_t>(alpha_layout_total(B, K, V)))
+        return SV_EWORKSPACE;
+    ChainReq q = chain_req(target_logits, ld_t, draft_logits, ld_q, dtype, B, K, V, nullptr,
+                           draft_len, nullptr, nullptr, lambda, temperature, nullptr, nullptr,
+                           nullptr, status, workspace, workspace_bytes, stream);
+    q.space = (mix_space == SV_MIX_LOGIT && lambda > 0.0f && lambda < 1.0f) ? 1 : 0;
+    return dtype == SV_BF16 ? run_alpha_typed<Bf16>(q, alpha) : run_alpha_typed<F32>(q, alpha);
 }
 
 sv_status sv_chain_accept_resample(const void *target_logits, int64_t ld_t,

@@ -81,6 +81,8 @@ struct ChainArgs {
     int rec_stride;               // doubles per chunk record: shift, pad, 16 * NV2 piece sums
     int space;                    // 0: probability-space mixture; 1: logit space (0 < lambda < 1)
     double alpha_c, beta_c;       // logit space: (1 - lambda) c and lambda c, c = log2(e)/T, fp64
+    double *alpha_part;           // [B, Pcap, C1] workspace: per-chunk sum of min(p~, q)
+    float *alpha;                 // [B, P] out: expected acceptance of each drafted position
 };
 
 struct TreeArgs {
@@ -164,6 +166,14 @@ inline ChainLayout chain_layout(int B, int P, int V) {
     L.part1 = L.chunks + align256(chunk_bytes(B, V));
     L.total = L.part1 + align256(int64_t(B) * P * 2 * c1max * int64_t(sizeof(Part)));
     return L;
+}
+
+// The acceptance-rate call: the chain layout, then the per-chunk partial sums
+// of min(p~, q), one double per (request, position, chunk).
+inline int64_t alpha_layout_parts(int B, int P, int V) { return chain_layout(B, P, V).total; }
+inline int64_t alpha_layout_total(int B, int P, int V) {
+    return alpha_layout_parts(B, P, V) +
+           align256(int64_t(B) * P * c1_for(V, kMinNV, kMinVec) * int64_t(sizeof(double)));
 }
 
 struct TreeLayout {

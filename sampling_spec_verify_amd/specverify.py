@@ -46,6 +46,9 @@ SIGNATURES = {
     "sv_chain_accept_resample": (_CHAIN_ARGS, _I),
     "sv_chain_row_stats_timed": (_CHAIN_ARGS + [_P, _P], _I),
     "sv_chain_verify_ex": (_CHAIN_ARGS + [_I, _I, _P, _P], _I),
+    "sv_chain_acceptance_workspace_bytes": ([_I, _I, _I], _S),
+    "sv_chain_acceptance_rate": ([_P, _L, _P, _L, _I, _I, _I, _I, _P, _F, _F, _I, _P, _P, _P, _S,
+                                  _P], _I),
     "sv_tree_workspace_bytes": ([_I, _I, _I], _S),
     "sv_tree_verify_greedy": (_GREEDY_ARGS, _I),
     "sv_tree_row_argmax": (_GREEDY_ARGS, _I),
@@ -289,6 +292,48 @@ def chain_verify(target, draft, tokens, u_accept, u_sample, lam: float = 0.0,
     """sv_chain_verify on torch tensors: target [B,K+1,V], draft [B,K,V] (bf16 or fp32)."""
     return ChainCall(target, draft, tokens, u_accept, u_sample, lam, temperature, draft_len,
                      stream, space=space).run()
+
+
+class AcceptanceRateCall:
+    """sv_chain_acceptance_rate with its output and workspace bound once:
+    alpha[b, i] = sum_v min(p~(v), q(v)) for every drafted position."""
+
+    def __init__(self, target, draft, lam=0.0, temperature=1.0, draft_len=None, stream=None,
+                 workspace=None, space: str = "prob"):
+        torch = _torch()
+        if space not in MIX_SPACES:
+            raise ValueError(f"space must be one of {sorted(MIX_SPACES)}, got {space!r}")
+        B, K1, V = target.shape
+        K = K1 - 1
+        if draft.dtype != target.dtype:
+            raise TypeError("target and draft logits must share a dtype")
+        ld_t = _rows(target, B, K + 1, V, "target")
+        ld_q = _rows(draft, B, K, V, "draft") if K > 0 else V
+        _i32(draft_len, (B,), "draft_len")
+        dev = target.device
+        self.alpha = torch.empty(B, K, dtype=torch.float32, device=dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        nbytes = int(lib().sv_chain_acceptance_workspace_bytes(B, K, V))
+        if nbytes == 0 and B > 0:
+            raise SpecVerifyError("invalid sizes")
+        self.workspace = workspace if workspace is not None else torch.empty(
+            max(nbytes, 16), dtype=torch.uint8, device=dev)
+        self.inputs = (target, draft, draft_len)
+        self._cached = (_ptr(target), ld_t, _ptr(draft), ld_q, _dtype_code(target), B, K, V,
+                        _ptr(draft_len), float(lam), float(temperature), MIX_SPACES[space],
+                        _ptr(self.alpha), _ptr(self.status), _ptr(self.workspace),
+                        self.workspace.numel(), _stream(stream))
+
+    def run(self):
+        _check(lib().sv_chain_acceptance_rate(*self._cached), "sv_chain_acceptance_rate")
+        return self.alpha, self.status
+
+
+def chain_acceptance_rate(target, draft, lam: float = 0.0, temperature: float = 1.0,
+                          draft_len=None, stream=None, space: str = "prob"):
+    """alpha [B, K] (and the status word) for target [B,K+1,V], draft [B,K,V]."""
+    return AcceptanceRateCall(target, draft, lam, temperature, draft_len, stream,
+                              space=space).run()
 
 
 class TreeGreedyOut(NamedTuple):

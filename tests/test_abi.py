@@ -21,6 +21,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["sv_status_string", "sv_chain_workspace_bytes", "sv_chain_verify",
+                            "sv_chain_acceptance_workspace_bytes", "sv_chain_acceptance_rate",
                             "sv_chain_row_stats", "sv_chain_accept_resample",
                             "sv_chain_row_stats_timed", "sv_chain_verify_ex",
                             "sv_tree_workspace_bytes", "sv_tree_verify_greedy",
@@ -200,4 +201,33 @@ def test_mask_argument_errors(kw, code, fn):
 def test_mask_empty_batch_and_rootless_tree_need_no_parent():
     L = sv.lib()
     assert L.sv_tree_attention_mask(None, 0, 5, None, 1, None, None, None) == sv.SV_OK
+
+
+def alpha_call(**kw):
+    args = dict(t=FAKE, ld_t=128, d=FAKE, ld_q=128, dtype=sv.SV_BF16, B=2, K=4, V=128, dl=None,
+                lam=0.3, T=1.0, space=sv.SV_MIX_PROB, alpha=FAKE, st=None, ws=FAKE, wsb=1 << 30,
+                stream=None)
+    args.update(kw)
+    return sv.lib().sv_chain_acceptance_rate(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(space=3), sv.SV_EINVAL), (dict(dtype=5), sv.SV_EDTYPE), (dict(B=-1), sv.SV_EINVAL),
+    (dict(K=65), sv.SV_EINVAL), (dict(V=0), sv.SV_EINVAL), (dict(lam=-1.0), sv.SV_EINVAL),
+    (dict(T=0.0), sv.SV_EINVAL), (dict(alpha=None), sv.SV_ENULL), (dict(t=None), sv.SV_ENULL),
+    (dict(d=FAKE + 2), sv.SV_EALIGN), (dict(ld_q=100), sv.SV_EALIGN), (dict(ws=None), sv.SV_EWORKSPACE),
+    (dict(wsb="short"), sv.SV_EWORKSPACE), (dict(B=0, t=None, alpha=None), sv.SV_OK),
+    (dict(K=0, d=None, alpha=None), sv.SV_OK),
+])
+def test_acceptance_rate_argument_errors(kw, code):
+    if kw.get("wsb") == "short":
+        kw = dict(wsb=sv.lib().sv_chain_acceptance_workspace_bytes(2, 4, 128) - 16)
+    assert alpha_call(**kw) == code
+
+
+def test_acceptance_workspace_covers_the_chain_layout():
+    L = sv.lib()
+    for B, K, V in [(1, 8, 128256), (64, 8, 128256), (3, 0, 10)]:
+        assert L.sv_chain_acceptance_workspace_bytes(B, K, V) >= L.sv_chain_workspace_bytes(B, K, V)
+    assert L.sv_chain_acceptance_workspace_bytes(1, 65, 10) == 0
 

@@ -443,3 +443,66 @@ def test_lambda_one_with_unreachable_draft_samples_the_draft():
     assert "ZERO_Q" in flags and "FALLBACK" in flags
     assert np.all(g.accepted == 1)
     report("lambda=1 q(x)=0", compare_chain(x, g, oracle_chain(x)))
+
+
+# ---------------------------------------------------------------------------
+# acceptance-rate telemetry: alpha_i = sum_v min(p~, q), within 1e-5
+# ---------------------------------------------------------------------------
+
+ALPHA_TOL = 1e-5
+
+
+def _alpha_case(x, space="prob", ld=None):
+    alpha, status = sv.chain_acceptance_rate(dev_logits(x.target, x.dtype, ld),
+                                             dev_logits(x.draft, x.dtype, ld), x.lam,
+                                             x.temperature, dev(x.draft_len), space=space)
+    torch.cuda.synchronize()
+    g = alpha.cpu().numpy().astype(np.float64)
+    ref = oracle_chain(x, space=space)
+    lens = x.lengths()
+    err = 0.0
+    for b in range(x.B):
+        k = int(lens[b])
+        if k:
+            err = max(err, float(np.abs(g[b, :k] - ref.details[b].alpha).max()))
+        assert np.all(g[b, k:] == 0.0)
+    assert err <= ALPHA_TOL, err
+    return int(status[0].item()), err
+
+
+@pytest.mark.parametrize("cfg,space", [("c3", "prob"), ("c3", "logit"), ("c4", "prob"),
+                                       ("c1", "prob"), ("c2", "prob")])
+def test_acceptance_rate_workload(cfg, space):
+    x = synth.config(cfg)
+    st, err = _alpha_case(x, space)
+    assert st == 0
+    report(f"alpha {cfg} {space}", {"max_abs_err": err})
+
+
+@pytest.mark.parametrize("seed,B,K,V,dtype,lam,T,ragged,ld,space", [
+    (41, 3, 4, 1000, "fp32", 0.0, 1.0, False, None, "prob"),
+    (42, 5, 3, 8200, "bf16", 0.3, 0.7, True, None, "prob"),
+    (43, 4, 2, 4097, "fp32", 0.5, 1.0, True, 4100, "logit"),
+    (44, 7, 1, 7, "fp32", 0.4, 1.0, False, 8, "logit"),
+    (45, 2, 64, 300, "fp32", 0.6, 1.0, False, None, "prob"),
+    (46, 6, 5, 33000, "bf16", 0.8, 1.5, True, None, "logit"),
+])
+def test_acceptance_rate_small(seed, B, K, V, dtype, lam, T, ragged, ld, space):
+    x = synth.make_chain(100 + seed, B, K, V, dtype, sigma_t=2.0, sigma_q=(0.3, 2.0),
+                         zipf=V > 16, lam=lam, temperature=T, ragged=ragged, k_min=0)
+    st, err = _alpha_case(x, space, ld)
+    assert st == 0
+    report(f"alpha small{seed}", {"max_abs_err": err})
+
+
+def test_acceptance_rate_identical_rows_and_lambda_one_are_one():
+    x = synth.make_chain(247, 4, 3, 5000, "bf16", lam=0.3)
+    x.draft = np.ascontiguousarray(x.target[:, :3, :])
+    _alpha_case(x)
+    alpha, _ = sv.chain_acceptance_rate(dev_logits(x.target, x.dtype), dev_logits(x.draft, x.dtype),
+                                        x.lam, x.temperature)
+    np.testing.assert_allclose(alpha.cpu().numpy(), 1.0, atol=ALPHA_TOL)
+    x = synth.make_chain(248, 3, 4, 2000, "fp32", lam=1.0, sigma_q=2.0)
+    alpha, _ = sv.chain_acceptance_rate(dev_logits(x.target, x.dtype), dev_logits(x.draft, x.dtype),
+                                        x.lam, x.temperature)
+    np.testing.assert_allclose(alpha.cpu().numpy(), 1.0, atol=ALPHA_TOL)
