@@ -4,4 +4,4 @@ from .verify import (FLAG_BAND, MIX_SPACES, BatchResult, ChainResult, GreedyResu
                      inverse_cdf,
                      mixture, pack_mask_rows, path_rows, residual_weights, softmax_T,
                      tree_attention_mask, tree_attention_mask_one, tree_greedy,
-                     tree_greedy_one, tree_path, tree_path_one)
+                     tree_greedy_one, tree_multi, tree_multi_one, tree_path, tree_path_one)

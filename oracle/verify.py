@@ -360,6 +360,103 @@ def pack_mask_rows(mask: np.ndarray, words: int) -> np.ndarray:
     return out
 
 
+@dataclasses.dataclass
+class MultiResult:
+    accepted: int              # depth of the deepest accepted node
+    tokens: List[int]          # accepted nodes' tokens + the final (residual or bonus) token
+    nodes: List[int]           # accepted node ids, root -> deepest
+    a: np.ndarray              # [N] acceptance probability of each tested node, -1 if untested
+    tested: List[int]          # node ids in the order they were tested
+    bonus: bool                # the walk ended at a node without (visible) children
+    fallback: bool             # a residual had zero mass; its current target was sampled instead
+    flagged: bool              # some draw lies within FLAG_BAND of its boundary
+
+
+def tree_multi_one(zt: np.ndarray, zq: np.ndarray, parent, node_token, u_acc, u_s: float,
+                   lam: float, T: float, space: str = "prob",
+                   Dmax: Optional[int] = None) -> MultiResult:
+    """Stochastic verification of a whole draft tree, retrying siblings.
+
+    [SD] "Tree Speculation": several candidates per position are verified
+    together, so when one branch is rejected another may still be accepted;
+    the pages give no rule for this.  Reading (the chain rule applied again
+    to what a rejection leaves): at node u with target r = p~ at row u (either
+    mixture space) and draft q at row u, the children are tested in node order;
+    child c with token x is accepted iff u_acc[c-1] < min(1, r(x) / q(x)) (the
+    chain test, same q(x) = 0 reading); after a rejection
+    r <- max(0, r - q) / sum max(0, r - q) (the chain's residual, now the
+    target of the next child).  The first accepted child becomes u; if every
+    child is rejected one token is drawn from the final r by inverse CDF with
+    u_s; at a node without children (or at depth Dmax) the bonus token is
+    drawn from the target's own softmax(z_t[u] / T).  When the children's
+    tokens are independent draws from q of their parent, every retry is a
+    fresh chain step aimed at the residual, so the emitted token follows p~
+    (the same argument as the chain's).  Zero residual mass (rounding only):
+    draw from the current r and report a fallback.
+    """
+    if space not in MIX_SPACES:
+        raise ValueError(f"unknown mixture space {space!r}")
+    lam = as_f32_scalar(lam)
+    T = as_f32_scalar(T)
+    u_s = float(np.float32(u_s))
+    zt = np.asarray(zt, dtype=np.float64)
+    zq = np.asarray(zq, dtype=np.float64)
+    N = len(parent)
+    V = zt.shape[1]
+    children = [[] for _ in range(N + 1)]
+    for i in range(1, N + 1):
+        p = int(parent[i - 1])
+        if not 0 <= p < i:
+            raise ValueError(f"parent of node {i} is {p}, not in [0, {i})")
+        children[p].append(i)
+    a_out = np.full(N, -1.0)
+    tested, nodes = [], []
+    flagged = fallback = False
+    u, depth = 0, 0
+    while True:
+        kids = children[u] if (Dmax is None or depth < Dmax) else []
+        if not kids:
+            tok, F_lo, F_hi = inverse_cdf(softmax_T(zt[u], T), u_s)
+            bonus = True
+            break
+        q = softmax_T(zq[u], T)
+        if space == "prob":
+            r = mixture(softmax_T(zt[u], T), q, lam)
+        else:
+            r = softmax_T(enhanced_logits(zt[u], zq[u], lam), T)
+        nxt = None
+        for c in kids:
+            x = int(node_token[c - 1])
+            if not 0 <= x < V:
+                raise ValueError(f"token {x} of node {c} outside [0, {V})")
+            a = accept_prob(r[x], q[x])
+            a_out[c - 1] = a
+            tested.append(c)
+            uc = float(np.float32(u_acc[c - 1]))
+            if a < 1.0 and abs(uc - a) < FLAG_BAND:
+                flagged = True
+            if uc < a:
+                nxt = c
+                break
+            w = residual_weights(r, q)
+            W = w.sum()
+            if not W > 0.0:
+                fallback = True
+                break
+            r = w / W
+        if nxt is not None:
+            nodes.append(nxt)
+            u, depth = nxt, depth + 1
+            continue
+        tok, F_lo, F_hi = inverse_cdf(r, u_s)
+        bonus = False
+        break
+    if (u_s - F_lo) < FLAG_BAND or (F_hi - u_s) < FLAG_BAND:
+        flagged = True
+    tokens = [int(node_token[c - 1]) for c in nodes] + [tok]
+    return MultiResult(len(nodes), tokens, nodes, a_out, tested, bonus, fallback, flagged)
+
+
 # ---------------------------------------------------------------------------
 # batches ([SD] "批量投机": every request is verified independently)
 # ---------------------------------------------------------------------------
@@ -443,3 +540,28 @@ def tree_attention_mask(parent, words: int):
         depth[b] = r.depth
         bad[b] = r.bad
     return mask, depth, bad
+
+
+def tree_multi(target, draft, parent, node_token, u_accept, u_sample, lam, T, Dmax: int,
+               space: str = "prob", requests=None):
+    """A batch of multi-branch tree verifications: (accepted, out_tokens [B, Dmax+1],
+    nodes [B, Dmax], accept_prob [B, N], flagged [B], details)."""
+    B, N = parent.shape
+    req = range(B) if requests is None else requests
+    acc = np.zeros(B, dtype=np.int32)
+    out = np.full((B, Dmax + 1), -1, dtype=np.int32)
+    nodes = np.full((B, Dmax), -1, dtype=np.int32)
+    ap = np.full((B, N), -1.0)
+    flag = np.zeros(B, dtype=bool)
+    det = [None] * B
+    for b in req:
+        r = tree_multi_one(target[b], draft[b], parent[b], node_token[b], u_accept[b],
+                           u_sample[b], lam, T, space, Dmax)
+        acc[b] = r.accepted
+        out[b, :len(r.tokens)] = r.tokens
+        nodes[b, :len(r.nodes)] = r.nodes
+        ap[b] = r.a
+        flag[b] = r.flagged
+        det[b] = r
+    return acc, out, nodes, ap, flag, det
+

@@ -17,7 +17,7 @@ import scipy.special
 import scipy.stats
 
 from oracle import (InvalidRow, chain_verify_one, inverse_cdf, pack_mask_rows, softmax_T,
-                    tree_attention_mask_one, tree_greedy_one, tree_path_one)
+                    tree_attention_mask_one, tree_greedy_one, tree_multi_one, tree_path_one)
 
 GRID = 2 ** 24          # the library's uniforms are fp32 multiples of 2^-24
 
@@ -575,4 +575,150 @@ def test_logit_mixture_identical_rows_accept_every_draft():
         r = chain_verify_one(zt, zq, rng.integers(0, 20, 3), rng.random(3, dtype=np.float32),
                              0.3, lam, 1.1, "logit")
         assert r.accepted == 3
+
+
+# ---------------------------------------------------------------------------
+# multi-branch stochastic tree verification (sibling retries)
+# ---------------------------------------------------------------------------
+
+
+def test_multi_on_a_chain_shaped_tree_is_the_chain():
+    rng = np.random.default_rng(51)
+    for _ in range(80):
+        N, V = int(rng.integers(1, 6)), int(rng.integers(2, 9))
+        lam, T = float(rng.choice([0.0, 0.3])), float(rng.uniform(0.7, 1.3))
+        space = str(rng.choice(["prob", "logit"]))
+        zt = rng.normal(0, 2, (N + 1, V))
+        zq = zt + rng.normal(0, 1, (N + 1, V))
+        tok = rng.integers(0, V, N)
+        ua, us = rng.random(N, dtype=np.float32), float(rng.random(dtype=np.float32))
+        m = tree_multi_one(zt, zq, np.arange(N), tok, ua, us, lam, T, space)
+        c = chain_verify_one(zt, zq[:N], tok, ua, us, lam, T, space)
+        assert (m.accepted, m.tokens) == (c.accepted, c.tokens)
+        k = len(m.tested)
+        np.testing.assert_array_equal(m.a[:k], c.a[:k])
+
+
+def test_multi_at_lambda_one_accepts_the_first_child():
+    rng = np.random.default_rng(52)
+    parent = [0, 0, 0, 1, 1, 2]
+    zt = rng.normal(0, 2, (7, 5))
+    zq = zt + rng.normal(0, 1, (7, 5))
+    for _ in range(20):
+        tok = rng.integers(0, 5, 6)
+        m = tree_multi_one(zt, zq, parent, tok, rng.random(6, dtype=np.float32), 0.5, 1.0, 1.0)
+        assert m.nodes[0] == 1 and m.tested[0] == 1 and m.a[0] == 1.0
+
+
+def _tree_rows(rng, parent, tok, V, table):
+    """Rows of a tree whose logits depend only on the token prefix of each node
+    (as a language model's would): table maps a prefix tuple to (z_t, z_q)."""
+    N = len(parent)
+    prefix = [()] + [None] * N
+    for i in range(1, N + 1):
+        prefix[i] = prefix[parent[i - 1]] + (int(tok[i - 1]),)
+    zt = np.stack([table(prefix[i])[0] for i in range(N + 1)])
+    zq = np.stack([table(prefix[i])[1] for i in range(N + 1)])
+    return zt, zq, prefix
+
+
+def _enumerate_tree(parent, V, table, lam, T, space):
+    """Exact law of the emitted token sequence, the oracle as a black box:
+    every assignment of node tokens (each child an independent draw from its
+    parent's q), every acceptance outcome (thresholds found by bisection over
+    the fp32 grid, the next tested node read from the oracle's trace) and the
+    final draw's CDF over the sampling uniform."""
+    N = len(parent)
+    law = {}
+
+    def q_of(prefix):
+        return sm(table(prefix)[1], T)
+
+    for toks in itertools.product(range(V), repeat=N):
+        zt, zq, prefix = _tree_rows(None, parent, toks, V, table)
+        w0 = 1.0
+        for i in range(1, N + 1):
+            w0 *= q_of(prefix[parent[i - 1]])[toks[i - 1]]
+        if w0 == 0.0:
+            continue
+
+        def run(fixed, us):
+            ua = np.zeros(N, dtype=np.float64)
+            for n, u in fixed.items():
+                ua[n - 1] = u
+            return tree_multi_one(zt, zq, parent, toks, ua, us, lam, T, space)
+
+        def explore(fixed, w):
+            r = run(fixed, 0.5)
+            nxt = [n for n in r.tested if n not in fixed]
+            if nxt:
+                n = nxt[0]
+                theta = _count_true(lambda u: n in run({**fixed, n: u}, 0.5).nodes)
+                if theta > 0:
+                    explore({**fixed, n: 0.0}, w * theta / GRID)
+                if theta < GRID:
+                    explore({**fixed, n: theta / GRID}, w * (GRID - theta) / GRID)
+                return
+            head = tuple(r.tokens[:-1])
+            prev = 0
+            for v in range(V):
+                cnt = _count_true(lambda u: run(fixed, u).tokens[-1] <= v)
+                if cnt > prev:
+                    key = head + (v,)
+                    law[key] = law.get(key, 0.0) + w * (cnt - prev) / GRID
+                prev = cnt
+
+        explore({}, w0)
+    return law
+
+
+def _check_conditional_laws(law, parent, table, lam, T, space, V):
+    depth = [0] * (len(parent) + 1)
+    for i in range(1, len(parent) + 1):
+        depth[i] = depth[parent[i - 1]] + 1
+    leaf_depth = max(depth)
+    lam32 = f32(lam)
+    assert sum(law.values()) == pytest.approx(1.0, abs=1e-6)
+    prefixes = {k[:j] for k in law for j in range(len(k))}
+    for s_ in prefixes:
+        mass = np.array([sum(p for k, p in law.items() if len(k) > len(s_) and k[:len(s_) + 1] == s_ + (v,))
+                         for v in range(V)])
+        tot = mass.sum()
+        if tot < 1e-9:
+            continue
+        zt_, zq_ = table(s_)
+        if len(s_) < leaf_depth:
+            if space == "prob":
+                want = (1 - lam32) * sm(zt_, T) + lam32 * sm(zq_, T)
+            else:
+                want = scipy.special.softmax(((1 - lam32) * zt_ + lam32 * zq_) / f32(T))
+        else:
+            want = sm(zt_, T)                      # the bonus at a leaf: the target alone
+        np.testing.assert_allclose(mass / tot, want, atol=2e-6 / tot)
+
+
+def _prefix_table(seed, V):
+    rng = np.random.default_rng(seed)
+    cache = {}
+
+    def table(prefix):
+        if prefix not in cache:
+            zt = rng.normal(0.0, 1.5, V)
+            cache[prefix] = (zt, zt + rng.normal(0.0, 1.2, V))
+        return cache[prefix]
+    return table
+
+
+@pytest.mark.parametrize("parent,V,lam,T,space,seed", [
+    ([0, 0, 0], 3, 0.0, 1.0, "prob", 61),            # a star: three sibling retries
+    ([0, 0, 0], 3, 0.4, 0.8, "logit", 62),
+    ([0, 0, 1, 1, 2, 2], 2, 0.3, 1.2, "prob", 63),   # two levels of two children
+])
+def test_multi_exact_enumeration_is_lossless(parent, V, lam, T, space, seed):
+    """Each emitted token, given the tokens before it, follows p~ of its prefix
+    (the target alone for the bonus after a leaf): the multi-branch walk keeps
+    the chain's lossless property ([SD] "修改的拒绝采样", [EAGLE] section 1)."""
+    table = _prefix_table(seed, V)
+    law = _enumerate_tree(parent, V, table, lam, T, space)
+    _check_conditional_laws(law, parent, table, lam, T, space, V)
 
