@@ -79,7 +79,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "c5mask"])
+    ap.add_argument("--workload", default="c4",
+                    choices=["c1", "c2", "c3", "c4", "c5", "c5mask", "c5multi"])
     ap.add_argument("--alpha", action="store_true",
                     help="chain workloads: time the acceptance-rate call instead of the verify call")
     ap.add_argument("--space", default="prob", choices=["prob", "logit"],
@@ -334,6 +335,83 @@ def bench_alpha(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_multi(args):
+    """Multi-branch stochastic verification of the c5 trees: one call per step."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sampling_spec_verify_amd import specverify as sv
+    from sampling_spec_verify_amd import synth
+
+    sv.lib()
+    x = synth.config("c5")
+    dev = "cuda:0"
+    R = max(2, min(512, math.ceil(ROTATE_BYTES / (x.target.nbytes + x.draft.nbytes))))
+    tgts = device_copies(x.target, x.dtype, R, torch)
+    drfs = device_copies(x.draft, x.dtype, R, torch)
+    par = torch.from_numpy(x.parent).to(dev)
+    tok = torch.from_numpy(x.node_token).to(dev)
+    un = torch.from_numpy(x.u_node).to(dev)
+    us = torch.from_numpy(x.u_sample).to(dev)
+    ws = torch.empty(int(sv.lib().sv_tree_multi_workspace_bytes(x.B, x.N, x.V)),
+                     dtype=torch.uint8, device=dev)
+
+    def call(i):
+        return sv.tree_verify_multi(tgts[i % R], drfs[i % R], par, tok, un, us, x.Dmax, x.lam,
+                                    x.temperature, args.space, workspace=ws)
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(K):
+        out = call(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    g = [o.cpu().numpy() for o in out]
+    cpu, parity = None, None
+    if args.cpu_seconds > 0:
+        t, d = x.widened(x.target), x.widened(x.draft)
+        done = nodes = mism = flagged = 0
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < args.cpu_seconds:
+            b = done % x.B
+            r = oracle.tree_multi_one(t[b], d[b], x.parent[b], x.node_token[b], x.u_node[b],
+                                      x.u_sample[b], x.lam, x.temperature, args.space, x.Dmax)
+            if done < x.B:
+                ref = np.full(x.Dmax + 1, -1, dtype=np.int32)
+                ref[:len(r.tokens)] = r.tokens
+                same = g[0][b] == r.accepted and np.array_equal(g[1][b], ref)
+                flagged += int(r.flagged)
+                mism += int(not same and not r.flagged)
+            nodes += x.N
+            done += 1
+        el = time.perf_counter() - t1
+        cpu = {"value": nodes / el, "unit": "tree nodes/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} oracle multi-branch tree walks cycling over the {x.B} trees, "
+                         f"fp64 numpy, one process", "seconds": round(el, 2)}
+        parity = {"requests_checked": min(done, x.B), "flagged": flagged,
+                  "unflagged_mismatches": mism}
+    line = {
+        "metric": "draft-tree nodes/sec through multi-branch stochastic verification",
+        "value": x.B * x.N * K / wall, "unit": "tree nodes/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / K, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"c5multi: {synth.CONFIGS['c5']}, per-node uniforms",
+                   "mixture_space": args.space, "lambda": x.lam, "buffer_sets_rotated": R},
+        "gpu_ms_per_step": ev0.elapsed_time(ev1) / K, "cpu_baseline": cpu,
+        "parity_sample": parity, "status_word": int(g[4][0]),
+        "accepted_depths": g[0].tolist(),
+        "note": "one 1024-thread block per tree walks it; bound by the walk's latency",
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -346,6 +424,9 @@ def main():
         return
     if args.workload == "c5mask":
         bench_mask(args)
+        return
+    if args.workload == "c5multi":
+        bench_multi(args)
         return
     if args.alpha:
         bench_alpha(args)

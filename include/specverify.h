@@ -350,6 +350,50 @@ sv_status sv_tree_verify_path_ex(const void *target_logits, int64_t ld_t,
                                  int32_t *status, void *workspace, size_t workspace_bytes,
                                  hipStream_t stream, int mix_space);
 
+/*
+ * Multi-branch stochastic verification of a whole draft tree ([SD] "Tree
+ * Speculation": when one branch is rejected another may still be accepted).
+ * The pages give no rule; the one used applies the chain rule again to what a
+ * rejection leaves.  At node u (starting at the root) the children are tested
+ * in node order against a target r, first p~ at row u (mix_space as in
+ * sv_chain_verify_ex) with the draft q at row u: child c with token x is
+ * accepted iff u_accept[b, c-1] < min(1, r(x) / q(x)) (q(x) = 0: accepted iff
+ * r(x) > 0); after a rejection r <- max(0, r - q) normalised, the next child's
+ * target.  The first accepted child becomes u.  If every child is rejected,
+ * one token is drawn from the last r by inverse CDF with u_sample[b]; at a
+ * node without children, or at depth Dmax, the bonus token is drawn from the
+ * target's own softmax(z_t/T) at that node.  When each child's token is an
+ * independent draw from its parent's q, the emitted tokens follow p~.
+ *
+ *  target_logits, draft_logits [B, N+1, V]; parent, node_token [B, N] as in
+ *  the tree calls; u_accept [B, N] one uniform per node; u_sample [B].
+ *  accepted [B] out: depth of the last accepted node (<= Dmax).
+ *  out_tokens [B, Dmax+1] out: the accepted nodes' tokens, then the drawn
+ *  token, then -1.  accepted_nodes [B, Dmax] out: node ids, -1 padded.
+ *  accept_prob [B, N] out or NULL: min(1, r(x)/q(x)) of every tested node,
+ *  -1 for nodes never tested.  Dmax in [0, SV_MAX_POSITIONS].
+ *  status: cleared, then SV_DATA_* bits (BAD_TREE: a node with an invalid
+ *  parent is never tested; BAD_TOKEN: rejected; ZERO_Q; FALLBACK: a residual
+ *  had zero mass and its current target was drawn from; BAD_ROW).
+ *  workspace: sv_tree_multi_workspace_bytes(B, N, V) bytes (two fp32
+ *  residual rows per request).
+ *
+ * One 1024-thread block per request walks its tree; every sum over the
+ * vocabulary is a pass of that block over the node's rows, so the call is
+ * bound by the walk's latency rather than by HBM bandwidth.
+ */
+size_t sv_tree_multi_workspace_bytes(int B, int N, int V);
+sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t,
+                               const void *draft_logits, int64_t ld_q,
+                               sv_dtype dtype, int B, int N, int V,
+                               const int32_t *parent, const int32_t *node_token,
+                               const float *u_accept, const float *u_sample,
+                               float lambda, float temperature, int mix_space,
+                               int32_t *accepted, int32_t *out_tokens,
+                               int32_t *accepted_nodes, float *accept_prob, int Dmax,
+                               int32_t *status, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

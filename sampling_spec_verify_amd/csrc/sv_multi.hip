@@ -1,0 +1,575 @@
+// Multi-branch stochastic verification of draft trees on gfx950.
+//
+// Method (cited by page title and section):
+//   "大模型推理的Speculative Decoding原理详解", "Tree Speculation": a tree of
+//     candidates is verified together, so a rejected branch may leave a
+//     sibling accepted (the page gives no rule).
+//   Same page, "修改的拒绝采样", and the EAGLE explainer, "1. 为什么无损": a
+//     draft x ~ q is kept with probability min(1, p(x)/q(x)), else the token
+//     is drawn from max(0, p - q) normalised.
+//   RAPID explainer (arXiv 2502.20330), "2) 推理时知识迁移" and
+//     "3) 候选验证机制（伪代码）": p is the mixture p~ (probability or logit
+//     space).
+//
+// Rule (applying the chain rule again to what a rejection leaves): at node u
+// the children are tested in node order against a target r, first p~ of
+// row u; after a rejection r <- max(0, r - q) / sum, the next child's
+// target.  The first accepted child becomes u; if every child is rejected one
+// token is drawn from the last residual; a node without children (or at depth
+// Dmax) emits the bonus token from the target's own softmax(z/T).
+//
+// One 1024-thread block per request walks its tree.  Each step that needs a
+// sum over the vocabulary is a pass of the whole block over the node's two
+// rows: the row statistics (as the chain's, integer shifts, fp64 sums), the
+// residual after a rejection (written to a ping-pong fp32 buffer of the
+// workspace with its fp64 mass), and a two-pass tiled inverse CDF (the first
+// pass forms the total with exactly the prefix sums the second one scans, so
+// the crossing is always found).  Acceptance of the first child uses the
+// gathered logits in fp64; later children read the stored residual.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <math.h>
+
+#include <algorithm>
+
+#include "sv_common.hpp"
+#include "sv_device.hpp"
+
+namespace sv {
+
+constexpr int kMB = 1024;                 // threads of a walk block
+constexpr int kMW = kMB / kWave;          // its waves
+constexpr int kMU = 2;                    // tiles of a pass in flight per thread
+constexpr int kMNodes = SV_MAX_TREE_NODES + 1;
+
+struct MultiArgs {
+    const char *tgt, *drf;
+    int64_t ld_t, ld_q;
+    int elem;
+    int B, N, V, Dmax;
+    const int32_t *parent, *node_token;
+    const float *u_accept, *u_sample;
+    float lam, c_hi, c_lo;
+    double c_d, al, be;                   // log2(e)/T; logit space: (1 - lambda) c, lambda c
+    int space;                            // 0 probability space, 1 logit space
+    int32_t *accepted, *out_tokens, *accepted_nodes;
+    float *accept_prob;                   // [B, N] or NULL
+    int32_t *status;
+    float *buf;                           // [B, 2, V] residual ping-pong
+};
+
+struct MultiShared {
+    int head[kMNodes];                    // first child of a node (node order), -1: none
+    int next[kMNodes];                    // next sibling, -1: none
+    int tok[kMNodes];
+    int path[SV_MAX_POSITIONS + 1];
+    double red[kMW];
+    float redf[kMW];
+    int redi[kMW];
+    double sA, SA, sB, SB;                // statistics of the two rows (A: target or mixed)
+    int flags, decision, token;
+};
+
+// ---- block reductions (every thread calls; results uniform) ---------------
+
+__device__ __forceinline__ float mblock_max(float v, MultiShared &sh) {
+    v = wave_max(v);
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) sh.redf[w] = v;
+    __syncthreads();
+    float r = sh.redf[0];
+    for (int i = 1; i < kMW; ++i) r = fmaxf(r, sh.redf[i]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ int mblock_max_i(int v, MultiShared &sh) {
+    v = -wave_min_i(-v);
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) sh.redi[w] = v;
+    __syncthreads();
+    int r = sh.redi[0];
+    for (int i = 1; i < kMW; ++i) r = max(r, sh.redi[i]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ double mblock_sum(double v, MultiShared &sh) {
+    v = wave_sum_d(v);
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) sh.red[w] = v;
+    __syncthreads();
+    double r = 0.0;
+    for (int i = 0; i < kMW; ++i) r += sh.red[i];
+    __syncthreads();
+    return r;
+}
+
+// Inclusive / exclusive scan of one double per thread in thread order,
+// offset by carry; every exclusive prefix is bitwise the previous thread's
+// inclusive one (the wave bases are formed by the same additions).
+__device__ __forceinline__ Scan mblock_scan(double v, double carry, MultiShared &sh) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const double x = wave_scan_d(v);
+    if (lane == kWave - 1) sh.red[w] = x;
+    __syncthreads();
+    double base = 0.0, tot = 0.0;
+    for (int i = 0; i < kMW; ++i) {
+        if (i == w) base = tot;
+        tot = tot + sh.red[i];
+    }
+    const double prev = dpp_shift_d<kDppWaveShr1, 0xF, 0xF>(x);
+    Scan s;
+    s.incl = carry + (base + x);
+    s.excl = carry + ((lane == 0) ? base : (base + prev));
+    s.total = carry + tot;
+    __syncthreads();
+    return s;
+}
+
+// ---- element values -----------------------------------------------------
+
+template <class DT>
+struct RowPair {
+    const char *t, *q;
+    int V;
+};
+
+// 2^(z c - s) with c = c_hi + c_lo
+__device__ __forceinline__ float m_pow2(float z, float c_hi, float c_lo, float s) {
+    return __builtin_amdgcn_exp2f(fmaf(z, c_lo, fmaf(z, c_hi, -s)));
+}
+__device__ __forceinline__ float m_pow2_mixed(float zt, float zq, double al, double be, float s) {
+    return __builtin_amdgcn_exp2f(static_cast<float>(
+        fma(static_cast<double>(zt), al, fma(static_cast<double>(zq), be, -static_cast<double>(s)))));
+}
+
+// p~(v) and q(v) of one element from its logits and the node's statistics
+template <class DT>
+__device__ __forceinline__ void m_probs(const MultiArgs &a, const MultiShared &sh, float zt, float zq,
+                                        double &pm, double &q) {
+    const double iA = 1.0 / sh.SA, iB = 1.0 / sh.SB;
+    q = static_cast<double>(m_pow2(zq, a.c_hi, a.c_lo, static_cast<float>(sh.sB))) * iB;
+    if (a.space == 1) {
+        pm = static_cast<double>(m_pow2_mixed(zt, zq, a.al, a.be, static_cast<float>(sh.sA))) * iA;
+    } else {
+        const double pt = static_cast<double>(m_pow2(zt, a.c_hi, a.c_lo, static_cast<float>(sh.sA))) * iA;
+        pm = (1.0 - static_cast<double>(a.lam)) * pt + static_cast<double>(a.lam) * q;
+    }
+}
+
+// ---- passes ----------------------------------------------------------------
+
+// Row statistics of the node's rows: A = target (probability space) or the
+// mixed logits (logit space), B = draft; with target_only, A alone (the bonus
+// row).  Per thread a running integer shift and fp64 sum, then block-wide.
+template <class DT>
+__device__ void pass_stats(const MultiArgs &a, MultiShared &sh, const char *row_t, const char *row_q,
+                           bool target_only) {
+    constexpr int VEC = DT::kVec;
+    const int V = a.V;
+    const int nvec = (V + VEC - 1) / VEC;
+    float sa = -INFINITY, sb = -INFINITY;
+    double aa = 0.0, ab = 0.0;
+    const bool mixed = !target_only && a.space == 1;
+    for (int g0 = 0; g0 < nvec; g0 += kMB * kMU) {
+        u32x4 dt[kMU], dq[kMU];
+#pragma unroll
+        for (int k = 0; k < kMU; ++k) {
+            const int gv = g0 + k * kMB + static_cast<int>(threadIdx.x);
+            dt[k] = load_row_vec<DT>(row_t, gv, V);
+            if (!target_only) dq[k] = load_row_vec<DT>(row_q, gv, V);
+        }
+#pragma unroll
+        for (int k = 0; k < kMU; ++k) {
+            float ft[VEC], fq[VEC];
+            DT::unpack(dt[k], ft);
+            float mt = -INFINITY, mq = -INFINITY;
+            for (int e = 0; e < VEC; ++e) mt = fmaxf(mt, ft[e]);
+            if (!target_only) {
+                DT::unpack(dq[k], fq);
+                for (int e = 0; e < VEC; ++e) mq = fmaxf(mq, fq[e]);
+            }
+            // row A
+            float cand;
+            if (mixed) {
+                cand = (mt == -INFINITY || mq == -INFINITY)
+                           ? -INFINITY
+                           : static_cast<float>(ceil(a.al * static_cast<double>(mt) + a.be * static_cast<double>(mq)));
+            } else {
+                cand = (mt == -INFINITY) ? -INFINITY : ceilf(mt * a.c_hi);
+            }
+            float sn = fmaxf(sa, cand);
+            aa *= pow2_shift_d(sa == -INFINITY ? 0.0 : static_cast<double>(sa) - static_cast<double>(sn));
+            sa = sn;
+            const float su = (sa == -INFINITY) ? 0.0f : sa;
+            float acc = 0.0f;
+            for (int e = 0; e < VEC; ++e)
+                acc += mixed ? m_pow2_mixed(ft[e], fq[e], a.al, a.be, su) : m_pow2(ft[e], a.c_hi, a.c_lo, su);
+            aa += static_cast<double>(acc);
+            if (!target_only) {
+                const float cq = (mq == -INFINITY) ? -INFINITY : ceilf(mq * a.c_hi);
+                sn = fmaxf(sb, cq);
+                ab *= pow2_shift_d(sb == -INFINITY ? 0.0 : static_cast<double>(sb) - static_cast<double>(sn));
+                sb = sn;
+                const float sq = (sb == -INFINITY) ? 0.0f : sb;
+                float accq = 0.0f;
+                for (int e = 0; e < VEC; ++e) accq += m_pow2(fq[e], a.c_hi, a.c_lo, sq);
+                ab += static_cast<double>(accq);
+            }
+        }
+    }
+    const float ma = mblock_max(sa, sh);
+    const double SA = mblock_sum(sa == -INFINITY ? 0.0 : aa * pow2_shift_d(static_cast<double>(sa) - static_cast<double>(ma)), sh);
+    double SB = 1.0;
+    float mb = 0.0f;
+    if (!target_only) {
+        mb = mblock_max(sb, sh);
+        SB = mblock_sum(sb == -INFINITY ? 0.0 : ab * pow2_shift_d(static_cast<double>(sb) - static_cast<double>(mb)), sh);
+    }
+    if (threadIdx.x == 0) {
+        sh.sA = ma;
+        sh.SA = SA;
+        sh.sB = mb;
+        sh.SB = SB;
+    }
+    __syncthreads();
+}
+
+// Residual after a rejection: w(v) = max(0, r(v) - q(v)) with r = p~ (first
+// rejection, from the logits) or the previous residual in[v] / Zin; w is
+// stored (fp32) in out and its fp64 sum returned.
+template <class DT>
+__device__ double pass_residual(const MultiArgs &a, MultiShared &sh, const char *row_t, const char *row_q,
+                                const float *in, double Zin, float *out) {
+    constexpr int VEC = DT::kVec;
+    const int V = a.V;
+    const int nvec = (V + VEC - 1) / VEC;
+    double tot = 0.0;
+    for (int gv = static_cast<int>(threadIdx.x); gv < nvec; gv += kMB) {
+        const u32x4 dt = load_row_vec<DT>(row_t, gv, V);
+        const u32x4 dq = load_row_vec<DT>(row_q, gv, V);
+        float ft[VEC], fq[VEC];
+        DT::unpack(dt, ft);
+        DT::unpack(dq, fq);
+        for (int e = 0; e < VEC; ++e) {
+            const int v = gv * VEC + e;
+            if (v >= V) break;
+            double pm, q;
+            m_probs<DT>(a, sh, ft[e], fq[e], pm, q);
+            const double r = (in == nullptr) ? pm : static_cast<double>(in[v]) / Zin;
+            const float w = static_cast<float>(fmax(0.0, r - q));
+            out[v] = w;
+            tot += static_cast<double>(w);
+        }
+    }
+    return mblock_sum(tot, sh);
+}
+
+enum MultiDraw { kDrawBonus = 0, kDrawBuffer = 1, kDrawMixture = 2 };
+
+// Weight of element v for a draw: the bonus 2^(z_t c - s) (unnormalised),
+// a stored residual, or p~ itself.
+template <class DT, int KIND>
+__device__ __forceinline__ double draw_weight(const MultiArgs &a, const MultiShared &sh, float zt,
+                                              float zq, const float *buf, int v) {
+    if (KIND == kDrawBonus) return static_cast<double>(m_pow2(zt, a.c_hi, a.c_lo, static_cast<float>(sh.sA)));
+    if (KIND == kDrawBuffer) return static_cast<double>(buf[v]);
+    double pm, q;
+    m_probs<DT>(a, sh, zt, zq, pm, q);
+    return pm;
+}
+
+// Inverse CDF in index order over tiles of kMB vectors: pass 0 returns the
+// total (the last carry), pass 1 the token min{v : F(v) > u * total}, with
+// the last positive weight when rounding leaves no crossing; -1 when the
+// total is not positive.
+template <class DT, int KIND>
+__device__ int pass_draw(const MultiArgs &a, MultiShared &sh, const char *row_t, const char *row_q,
+                         const float *buf, double u) {
+    constexpr int VEC = DT::kVec;
+    const int V = a.V;
+    const int nvec = (V + VEC - 1) / VEC;
+    double W = 0.0;
+    for (int pass = 0; pass < 2; ++pass) {
+        const double t = u * W;
+        double carry = 0.0;
+        int last = -1;
+        if (threadIdx.x == 0) sh.token = -1;
+        __syncthreads();
+        for (int g0 = 0; g0 < nvec; g0 += kMB) {
+            const int gv = g0 + static_cast<int>(threadIdx.x);
+            float ft[VEC], fq[VEC];
+            if (KIND != kDrawBuffer) {
+                const u32x4 dt = load_row_vec<DT>(row_t, gv, V);
+                DT::unpack(dt, ft);
+            }
+            if (KIND == kDrawMixture) {
+                const u32x4 dq = load_row_vec<DT>(row_q, gv, V);
+                DT::unpack(dq, fq);
+            }
+            double w[VEC];
+            double sum = 0.0;
+            for (int e = 0; e < VEC; ++e) {
+                const int v = gv * VEC + e;
+                w[e] = (v < V) ? draw_weight<DT, KIND>(a, sh, ft[e], fq[e], buf, v) : 0.0;
+                if (!(w[e] > 0.0)) w[e] = 0.0;
+                sum += w[e];
+                if (w[e] > 0.0) last = v;
+            }
+            const Scan s = mblock_scan(sum, carry, sh);
+            if (pass == 1 && s.excl <= t && t < s.incl) {
+                double cum = s.excl;
+                int pick = -1, lastpos = -1;
+                for (int e = 0; e < VEC; ++e) {
+                    if (w[e] > 0.0) {
+                        lastpos = gv * VEC + e;
+                        cum += w[e];
+                        if (pick < 0 && cum > t) pick = gv * VEC + e;
+                    }
+                }
+                sh.token = (pick >= 0) ? pick : lastpos;
+            }
+            carry = s.total;
+            __syncthreads();
+            if (pass == 1 && sh.token >= 0) break;
+        }
+        if (pass == 0) {
+            W = carry;
+            if (!(W > 0.0) || !isfinite(W)) return -1;
+        } else if (sh.token < 0) {
+            // t rounded to the very top: the last positive weight
+            return mblock_max_i(last, sh);
+        }
+    }
+    return sh.token;
+}
+
+// ---- the walk ----------------------------------------------------------------
+
+template <class DT>
+__global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
+    __shared__ MultiShared sh;
+    const int b = blockIdx.x;
+    const int t = threadIdx.x;
+    const int N = a.N, V = a.V;
+    for (int i = t; i <= N; i += kMB) {
+        sh.head[i] = -1;
+        sh.next[i] = -1;
+        sh.tok[i] = (i > 0) ? a.node_token[int64_t(b) * N + i - 1] : -1;
+    }
+    if (a.accept_prob != nullptr)
+        for (int i = t; i < N; i += kMB) a.accept_prob[int64_t(b) * N + i] = -1.0f;
+    if (t == 0) sh.flags = 0;
+    __syncthreads();
+    if (t == 0) {
+        // children lists in node order: link from the last node down
+        for (int i = N; i >= 1; --i) {
+            const int p = a.parent[int64_t(b) * N + i - 1];
+            if (p < 0 || p >= i) {
+                sh.flags |= SV_DATA_BAD_TREE;       // never tested
+                continue;
+            }
+            sh.next[i] = sh.head[p];
+            sh.head[p] = i;
+        }
+    }
+    __syncthreads();
+
+    const char *tb = a.tgt + int64_t(b) * (N + 1) * a.ld_t * a.elem;
+    const char *qb = a.drf + int64_t(b) * (N + 1) * a.ld_q * a.elem;
+    float *buf0 = a.buf + int64_t(b) * 2 * V;
+    float *buf1 = buf0 + V;
+    const double us = static_cast<double>(a.u_sample[b]);
+    int u = 0, depth = 0, tok = -1;
+    bool done = false;
+    while (!done) {
+        const char *rt = tb + int64_t(u) * a.ld_t * a.elem;
+        const char *rq = qb + int64_t(u) * a.ld_q * a.elem;
+        const int first = (depth < a.Dmax) ? sh.head[u] : -1;
+        if (first < 0) {
+            // bonus: the target's own softmax(z/T) at this node
+            pass_stats<DT>(a, sh, rt, rq, true);
+            tok = pass_draw<DT, kDrawBonus>(a, sh, rt, rq, nullptr, us);
+            if (tok < 0 && t == 0) sh.flags |= SV_DATA_BAD_ROW;
+            break;
+        }
+        pass_stats<DT>(a, sh, rt, rq, false);
+        if (!(sh.SA > 0.0) || !isfinite(sh.SA) || !(sh.SB > 0.0) || !isfinite(sh.SB) ||
+            !isfinite(sh.sA) || !isfinite(sh.sB)) {
+            if (t == 0) sh.flags |= SV_DATA_BAD_ROW;
+            tok = -1;
+            break;
+        }
+        // test the children in node order
+        float *cur = nullptr;            // stored residual (NULL: r = p~)
+        double Z = 1.0;
+        int c = first, nxt = -1;
+        bool drawn = false;
+        while (c >= 0) {
+            if (t == 0) {
+                const int x = sh.tok[c];
+                double acc_p = 0.0;
+                if (x < 0 || x >= V) {
+                    sh.flags |= SV_DATA_BAD_TOKEN;
+                } else {
+                    const float zt = DT::load1(rt, x);
+                    const float zq = DT::load1(rq, x);
+                    double q, r;
+                    if (cur == nullptr) {
+                        // fp64 from the gathered logits
+                        q = (zq == -INFINITY) ? 0.0
+                                              : exp2_d(static_cast<double>(zq) * a.c_d - sh.sB) / sh.SB;
+                        if (a.space == 1) {
+                            r = (zt == -INFINITY || zq == -INFINITY)
+                                    ? 0.0
+                                    : exp2_d(a.al * static_cast<double>(zt) + a.be * static_cast<double>(zq) - sh.sA) / sh.SA;
+                        } else {
+                            const double pt = (zt == -INFINITY) ? 0.0
+                                                                : exp2_d(static_cast<double>(zt) * a.c_d - sh.sA) / sh.SA;
+                            r = (1.0 - static_cast<double>(a.lam)) * pt + static_cast<double>(a.lam) * q;
+                        }
+                    } else {
+                        double pm;
+                        m_probs<DT>(a, sh, zt, zq, pm, q);
+                        r = static_cast<double>(cur[x]) / Z;
+                    }
+                    if (q == 0.0) {
+                        sh.flags |= SV_DATA_ZERO_Q;
+                        acc_p = (r > 0.0) ? 1.0 : 0.0;
+                    } else {
+                        acc_p = fmin(1.0, r / q);
+                    }
+                }
+                if (a.accept_prob != nullptr) a.accept_prob[int64_t(b) * N + c - 1] = static_cast<float>(acc_p);
+                const float uc = a.u_accept[int64_t(b) * N + c - 1];
+                sh.decision = (static_cast<double>(uc) < acc_p) ? 1 : 0;
+            }
+            __syncthreads();
+            if (sh.decision) {
+                nxt = c;
+                break;
+            }
+            // rejected: the residual becomes the next child's target
+            float *out = (cur == buf0) ? buf1 : buf0;
+            const double Zn = pass_residual<DT>(a, sh, rt, rq, cur, Z, out);
+            if (!(Zn > 0.0) || !isfinite(Zn)) {
+                // zero residual mass (rounding): draw from the current target
+                if (t == 0) sh.flags |= SV_DATA_FALLBACK;
+                tok = (cur == nullptr) ? pass_draw<DT, kDrawMixture>(a, sh, rt, rq, nullptr, us)
+                                       : pass_draw<DT, kDrawBuffer>(a, sh, rt, rq, cur, us);
+                drawn = true;
+                break;
+            }
+            cur = out;
+            Z = Zn;
+            c = sh.next[c];
+            __syncthreads();
+        }
+        if (drawn) break;
+        if (nxt >= 0) {
+            if (t == 0 && depth < SV_MAX_POSITIONS) sh.path[depth] = nxt;
+            u = nxt;
+            ++depth;
+            __syncthreads();
+            continue;
+        }
+        // every child rejected: draw from the last residual
+        tok = pass_draw<DT, kDrawBuffer>(a, sh, rt, rq, cur, us);
+        if (tok < 0 && t == 0) sh.flags |= SV_DATA_BAD_ROW;
+        done = true;
+    }
+    __syncthreads();
+    const int keep = min(depth, a.Dmax);
+    for (int i = t; i <= a.Dmax; i += kMB) {
+        int v = -1;
+        if (i < keep) v = sh.tok[sh.path[i]];
+        else if (i == keep) v = tok;
+        a.out_tokens[int64_t(b) * (a.Dmax + 1) + i] = v;
+        if (i < a.Dmax) a.accepted_nodes[int64_t(b) * a.Dmax + i] = (i < keep) ? sh.path[i] : -1;
+    }
+    if (t == 0) {
+        a.accepted[b] = keep;
+        if (sh.flags) atomicOr(a.status, sh.flags);
+    }
+}
+
+__global__ void k_multi_clear(int32_t *status) { *status = 0; }
+
+}  // namespace sv
+
+namespace {
+
+using namespace sv;
+
+int64_t multi_layout_total(int B, int V) { return 256 + align256(int64_t(B) * 2 * V * int64_t(sizeof(float))); }
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_tree_multi_workspace_bytes(int B, int N, int V) {
+    if (B < 0 || N < 0 || N > SV_MAX_TREE_NODES || V < 1) return 0;
+    return static_cast<size_t>(multi_layout_total(B, V));
+}
+
+sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const void *draft_logits,
+                               int64_t ld_q, sv_dtype dtype, int B, int N, int V,
+                               const int32_t *parent, const int32_t *node_token,
+                               const float *u_accept, const float *u_sample, float lambda,
+                               float temperature, int mix_space, int32_t *accepted,
+                               int32_t *out_tokens, int32_t *accepted_nodes, float *accept_prob,
+                               int Dmax, int32_t *status, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    if (mix_space != SV_MIX_PROB && mix_space != SV_MIX_LOGIT) return SV_EINVAL;
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return SV_EDTYPE;
+    if (B < 0 || N < 0 || N > SV_MAX_TREE_NODES || V < 1 || Dmax < 0 || Dmax > SV_MAX_POSITIONS ||
+        B > (1 << 30) || int64_t(V) > (int64_t(1) << 28))
+        return SV_EINVAL;
+    sv_status st = check_scalars(lambda, temperature);
+    if (st != SV_OK) return st;
+    if (B == 0) return SV_OK;
+    if (!u_sample || !accepted || !out_tokens || (Dmax > 0 && !accepted_nodes)) return SV_ENULL;
+    if (N > 0 && (!parent || !node_token || !u_accept)) return SV_ENULL;
+    if ((st = check_logits(target_logits, ld_t, V, eb)) != SV_OK) return st;
+    if ((st = check_logits(draft_logits, ld_q, V, eb)) != SV_OK) return st;
+    if (!workspace || !aligned16(workspace) ||
+        workspace_bytes < static_cast<size_t>(multi_layout_total(B, V)))
+        return SV_EWORKSPACE;
+    MultiArgs a;
+    a.tgt = static_cast<const char *>(target_logits);
+    a.drf = static_cast<const char *>(draft_logits);
+    a.ld_t = ld_t;
+    a.ld_q = ld_q;
+    a.elem = eb;
+    a.B = B;
+    a.N = N;
+    a.V = V;
+    a.Dmax = Dmax;
+    a.parent = parent;
+    a.node_token = node_token;
+    a.u_accept = u_accept;
+    a.u_sample = u_sample;
+    a.lam = lambda;
+    temperature_split(temperature, &a.c_hi, &a.c_lo, &a.c_d);
+    a.space = (mix_space == SV_MIX_LOGIT && lambda > 0.0f && lambda < 1.0f) ? 1 : 0;
+    a.al = (1.0 - static_cast<double>(lambda)) * a.c_d;
+    a.be = static_cast<double>(lambda) * a.c_d;
+    a.accepted = accepted;
+    a.out_tokens = out_tokens;
+    a.accepted_nodes = accepted_nodes;
+    a.accept_prob = accept_prob;
+    char *ws = static_cast<char *>(workspace);
+    a.status = status ? status : reinterpret_cast<int32_t *>(ws);
+    a.buf = reinterpret_cast<float *>(ws + 256);
+    hipLaunchKernelGGL(k_multi_clear, dim3(1), dim3(1), 0, stream, a.status);
+    if (dtype == SV_BF16)
+        hipLaunchKernelGGL(k_tree_multi<Bf16>, dim3(static_cast<unsigned>(B)), dim3(kMB), 0, stream, a);
+    else
+        hipLaunchKernelGGL(k_tree_multi<F32>, dim3(static_cast<unsigned>(B)), dim3(kMB), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+}  // extern "C"

@@ -56,6 +56,9 @@ SIGNATURES = {
     "sv_tree_row_argmax_timed": (_GREEDY_ARGS + [_P, _P], _I),
     "sv_tree_attention_mask": ([_P, _I, _I, _P, _I, _P, _P, _P], _I),
     "sv_tree_attention_mask_timed": ([_P, _I, _I, _P, _I, _P, _P, _P, _P, _P], _I),
+    "sv_tree_multi_workspace_bytes": ([_I, _I, _I], _S),
+    "sv_tree_verify_multi": ([_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _P, _P, _F, _F, _I, _P, _P,
+                              _P, _P, _I, _P, _P, _S, _P], _I),
     "sv_tree_verify_path": (_PATH_ARGS, _I),
     "sv_tree_verify_path_ex": (_PATH_ARGS + [_I], _I),
 }
@@ -471,3 +474,48 @@ def tree_verify_path(target, draft, node_token, path, u_accept, u_sample, lam: f
     else:
         _check(lib().sv_tree_verify_path_ex(*args, MIX_SPACES[space]), "sv_tree_verify_path_ex")
     return out
+
+
+class TreeMultiOut(NamedTuple):
+    accepted: object        # [B]
+    out_tokens: object      # [B, Dmax+1]
+    accepted_nodes: object  # [B, Dmax]
+    accept_prob: object     # [B, N], -1 for untested nodes
+    status: object          # [1]
+
+
+def tree_verify_multi(target, draft, parent, node_token, u_accept, u_sample, Dmax: int,
+                      lam: float = 0.0, temperature: float = 1.0, space: str = "prob",
+                      stream=None, workspace=None) -> TreeMultiOut:
+    """sv_tree_verify_multi: target / draft [B, N+1, V], parent / node_token [B, N],
+    u_accept [B, N] (one per node), u_sample [B]."""
+    torch = _torch()
+    if space not in MIX_SPACES:
+        raise ValueError(f"space must be one of {sorted(MIX_SPACES)}, got {space!r}")
+    B, N1, V = target.shape
+    N = N1 - 1
+    ld_t = _rows(target, B, N + 1, V, "target")
+    ld_q = _rows(draft, B, N + 1, V, "draft")
+    if draft.dtype != target.dtype:
+        raise TypeError("target and draft logits must share a dtype")
+    _i32(parent, (B, N), "parent")
+    _i32(node_token, (B, N), "node_token")
+    _f32(u_accept, (B, N), "u_accept")
+    _f32(u_sample, (B,), "u_sample")
+    dev = target.device
+    out = TreeMultiOut(torch.empty(B, dtype=torch.int32, device=dev),
+                       torch.empty(B, Dmax + 1, dtype=torch.int32, device=dev),
+                       torch.empty(B, max(Dmax, 0), dtype=torch.int32, device=dev),
+                       torch.empty(B, N, dtype=torch.float32, device=dev),
+                       torch.empty(1, dtype=torch.int32, device=dev))
+    ws = workspace if workspace is not None else torch.empty(
+        max(int(lib().sv_tree_multi_workspace_bytes(B, N, V)), 16), dtype=torch.uint8, device=dev)
+    code = lib().sv_tree_verify_multi(_ptr(target), ld_t, _ptr(draft), ld_q, _dtype_code(target), B,
+                                      N, V, _ptr(parent), _ptr(node_token), _ptr(u_accept),
+                                      _ptr(u_sample), float(lam), float(temperature),
+                                      MIX_SPACES[space], _ptr(out.accepted), _ptr(out.out_tokens),
+                                      _ptr(out.accepted_nodes), _ptr(out.accept_prob), int(Dmax),
+                                      _ptr(out.status), _ptr(ws), ws.numel(), _stream(stream))
+    _check(code, "sv_tree_verify_multi")
+    return out
+

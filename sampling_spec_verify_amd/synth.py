@@ -151,6 +151,7 @@ class TreeInputs:
     node_token [B, N] int32: token of node i+1
     path [B, Dmax] int32: root->leaf node ids (1-based), -1 terminated
     u_accept [B, Dmax], u_sample [B] fp32
+    u_node [B, N] fp32: one acceptance uniform per node (multi-branch walks)
     """
 
     name: str
@@ -164,6 +165,7 @@ class TreeInputs:
     u_sample: np.ndarray
     lam: float
     temperature: float
+    u_node: Optional[np.ndarray] = None
 
     @property
     def B(self) -> int:
@@ -189,8 +191,10 @@ class TreeInputs:
 # generic chain generator
 # ---------------------------------------------------------------------------
 
+# new streams go at the end: spawned children keep their index, so the
+# earlier streams (and every input drawn from them) stay as they were
 _STREAMS = ("target", "noise", "perm", "sigma_k", "draft_tok", "u_accept", "u_sample",
-            "tree_shape", "tree_path")
+            "tree_shape", "tree_path", "u_node")
 
 
 def _streams(seed: int):
@@ -345,7 +349,7 @@ def make_tree(seed: int, B: int, N: int, V: int, dtype: str = "bf16", *,
     u_acc = uniforms(s["u_accept"], (B, Dmax))
     u_smp = uniforms(s["u_sample"], (B,))
     return TreeInputs(name, dtype, t_arr, q_arr, parent, node_token, path, u_acc, u_smp,
-                      float(lam), float(temperature))
+                      float(lam), float(temperature), uniforms(s["u_node"], (B, N)))
 
 
 # ---------------------------------------------------------------------------
@@ -413,4 +417,4 @@ def make_random_tree(seed: int, B: int, N: int, V: int, dtype: str = "fp32", *,
     u_acc = uniforms(s["u_accept"], (B, Dmax))
     u_smp = uniforms(s["u_sample"], (B,))
     return TreeInputs(name, dtype, t_arr, q_arr, parent, node_token, path, u_acc, u_smp,
-                      float(lam), float(temperature))
+                      float(lam), float(temperature), uniforms(s["u_node"], (B, N)))

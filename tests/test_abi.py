@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
                             "sv_tree_row_argmax", "sv_tree_greedy_walk",
                             "sv_tree_row_argmax_timed", "sv_tree_attention_mask",
                             "sv_tree_attention_mask_timed", "sv_tree_verify_path",
-                            "sv_tree_verify_path_ex"])
+                            "sv_tree_verify_path_ex", "sv_tree_multi_workspace_bytes",
+                            "sv_tree_verify_multi"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -230,4 +231,28 @@ def test_acceptance_workspace_covers_the_chain_layout():
     for B, K, V in [(1, 8, 128256), (64, 8, 128256), (3, 0, 10)]:
         assert L.sv_chain_acceptance_workspace_bytes(B, K, V) >= L.sv_chain_workspace_bytes(B, K, V)
     assert L.sv_chain_acceptance_workspace_bytes(1, 65, 10) == 0
+
+
+def multi_call(**kw):
+    args = dict(t=FAKE, ld_t=128, d=FAKE, ld_q=128, dtype=sv.SV_BF16, B=2, N=5, V=128, par=FAKE,
+                tok=FAKE, ua=FAKE, us=FAKE, lam=0.2, T=1.0, space=sv.SV_MIX_PROB, acc=FAKE, out=FAKE,
+                nodes=FAKE, ap=None, Dmax=4, st=None, ws=FAKE, wsb=1 << 30, stream=None)
+    args.update(kw)
+    return sv.lib().sv_tree_verify_multi(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(space=2), sv.SV_EINVAL), (dict(dtype=4), sv.SV_EDTYPE), (dict(B=-1), sv.SV_EINVAL),
+    (dict(N=1025), sv.SV_EINVAL), (dict(V=0), sv.SV_EINVAL), (dict(Dmax=65), sv.SV_EINVAL),
+    (dict(Dmax=-1), sv.SV_EINVAL), (dict(T=-1.0), sv.SV_EINVAL), (dict(lam=1.5), sv.SV_EINVAL),
+    (dict(us=None), sv.SV_ENULL), (dict(acc=None), sv.SV_ENULL), (dict(out=None), sv.SV_ENULL),
+    (dict(nodes=None), sv.SV_ENULL), (dict(par=None), sv.SV_ENULL), (dict(tok=None), sv.SV_ENULL),
+    (dict(ua=None), sv.SV_ENULL), (dict(t=FAKE + 4), sv.SV_EALIGN), (dict(ld_q=127), sv.SV_EALIGN),
+    (dict(ws=None), sv.SV_EWORKSPACE), (dict(wsb="short"), sv.SV_EWORKSPACE),
+    (dict(B=0, t=None, acc=None), sv.SV_OK),
+])
+def test_multi_argument_errors(kw, code):
+    if kw.get("wsb") == "short":
+        kw = dict(wsb=sv.lib().sv_tree_multi_workspace_bytes(2, 5, 128) - 16)
+    assert multi_call(**kw) == code
 

@@ -14,7 +14,8 @@ import torch
 import oracle
 from sampling_spec_verify_amd import specverify as sv
 from sampling_spec_verify_amd import synth
-from tests.gpu_util import (chain_call, compare_chain, dev, dev_logits, oracle_chain, path_lengths,
+from tests.gpu_util import (ACCEPT_PROB_TOL, chain_call, compare_chain, dev, dev_logits,
+                            oracle_chain, path_lengths,
                             run_chain, run_greedy, run_path, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -506,3 +507,86 @@ def test_acceptance_rate_identical_rows_and_lambda_one_are_one():
     alpha, _ = sv.chain_acceptance_rate(dev_logits(x.target, x.dtype), dev_logits(x.draft, x.dtype),
                                         x.lam, x.temperature)
     np.testing.assert_allclose(alpha.cpu().numpy(), 1.0, atol=ALPHA_TOL)
+
+
+# ---------------------------------------------------------------------------
+# multi-branch stochastic tree verification (sibling retries)
+# ---------------------------------------------------------------------------
+
+
+def _multi_case(x, Dmax=None, space="prob", label="multi"):
+    Dmax = x.Dmax if Dmax is None else Dmax
+    g = sv.tree_verify_multi(dev_logits(x.target, x.dtype), dev_logits(x.draft, x.dtype),
+                             dev(x.parent), dev(x.node_token), dev(x.u_node), dev(x.u_sample), Dmax,
+                             x.lam, x.temperature, space)
+    g = to_host(g)
+    acc, out, nodes, ap, flag, det = oracle.tree_multi(
+        x.widened(x.target), x.widened(x.draft), x.parent, x.node_token, x.u_node, x.u_sample,
+        x.lam, x.temperature, Dmax, space)
+    stats = {"requests": x.B, "flagged": 0, "flagged_mismatch": 0, "max_a_err": 0.0,
+             "tested": 0}
+    for b in range(x.B):
+        tested = ap[b] >= 0.0
+        stats["tested"] += int(tested.sum())
+        same = (g.accepted[b] == acc[b] and np.array_equal(g.out_tokens[b], out[b])
+                and np.array_equal(g.accepted_nodes[b], nodes[b]))
+        if flag[b]:
+            stats["flagged"] += 1
+            stats["flagged_mismatch"] += int(not same)
+            continue
+        assert same, (f"request {b}: gpu {g.accepted[b]} {g.out_tokens[b].tolist()} "
+                      f"oracle {acc[b]} {out[b].tolist()}")
+        np.testing.assert_array_equal(g.accept_prob[b] >= 0.0, tested)
+        if tested.any():
+            err = float(np.abs(g.accept_prob[b][tested] - ap[b][tested]).max())
+            stats["max_a_err"] = max(stats["max_a_err"], err)
+            assert err <= ACCEPT_PROB_TOL, (b, err)
+    report(label, stats)
+    return g, stats
+
+
+@pytest.mark.parametrize("lam,space", [(0.0, "prob"), (0.3, "prob"), (0.3, "logit")])
+def test_multi_tree_workload(lam, space):
+    x = synth.config("c5")
+    x.lam = lam
+    g, stats = _multi_case(x, space=space, label=f"c5 multi {space} {lam}")
+    assert int(g.status[0]) == 0
+    assert stats["flagged"] <= 2
+
+
+@pytest.mark.parametrize("seed,B,N,V,dtype,lam,T,space,Dmax", [
+    (1, 6, 12, 3000, "fp32", 0.0, 1.0, "prob", None),
+    (2, 4, 40, 20000, "bf16", 0.3, 0.8, "prob", None),
+    (3, 3, 5, 17, "fp32", 0.5, 1.2, "logit", None),
+    (4, 5, 30, 9000, "bf16", 0.2, 1.0, "logit", 3),
+    (5, 2, 200, 500, "fp32", 0.0, 1.5, "prob", None),
+    (6, 4, 0, 700, "bf16", 0.0, 1.0, "prob", None),
+])
+def test_multi_random_trees(seed, B, N, V, dtype, lam, T, space, Dmax):
+    # loose draft rows (sigma 2) so that rejections and sibling retries are common
+    x = synth.make_random_tree(600 + seed, B, N, V, dtype, sharp=1.0, sigma_q=2.0, lam=lam,
+                               temperature=T)
+    g, _ = _multi_case(x, Dmax=Dmax, space=space, label=f"multi random {seed}")
+    assert int(g.status[0]) == 0
+
+
+def test_multi_on_chain_shaped_trees_matches_path_mode():
+    x = synth.make_random_tree(621, 5, 7, 4000, "fp32", sharp=1.0, sigma_q=1.5, lam=0.2)
+    x.parent[:] = np.arange(7)
+    x.path = np.tile(np.arange(1, 8, dtype=np.int32), (5, 1))
+    x.u_accept = x.u_node.copy()                # the same uniform per node in both calls
+    g, _ = _multi_case(x, Dmax=7)
+    p = run_path(x)
+    np.testing.assert_array_equal(g.accepted, p.accepted)
+    np.testing.assert_array_equal(g.out_tokens, p.out_tokens)
+
+
+def test_multi_bad_parent_and_token_are_reported():
+    x = synth.make_random_tree(622, 3, 10, 500, "fp32", sharp=1.0, sigma_q=2.0)
+    x.parent[0, 4] = 9                          # node 5's parent is not below it
+    x.node_token[1, :] = 600                    # tokens outside [0, V)
+    g = sv.tree_verify_multi(dev_logits(x.target, x.dtype), dev_logits(x.draft, x.dtype),
+                             dev(x.parent), dev(x.node_token), dev(x.u_node), dev(x.u_sample),
+                             x.Dmax)
+    flags = sv.decode_flags(int(to_host(g).status[0]))
+    assert "BAD_TREE" in flags and "BAD_TOKEN" in flags
