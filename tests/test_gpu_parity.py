@@ -590,3 +590,79 @@ def test_multi_bad_parent_and_token_are_reported():
                              x.Dmax)
     flags = sv.decode_flags(int(to_host(g).status[0]))
     assert "BAD_TREE" in flags and "BAD_TOKEN" in flags
+
+
+@pytest.mark.parametrize("space", ["prob", "logit"])
+def test_gpu_multi_output_law_monte_carlo(space):
+    """2 x 10^5 trees (root with three children, each with one child) whose rows
+    depend only on the token prefix and whose node tokens are independent
+    draws from the parent's q: the first emitted token follows p~ of the
+    root, the second p~ of its prefix, the bonus the target (chi-square
+    p > 0.01)."""
+    V, lam, T, n = 5, 0.3, 0.9, 200_000
+    parent = np.array([0, 0, 0, 1, 2, 3], dtype=np.int32)
+    rng = np.random.default_rng(78)
+    table = {(): (rng.normal(0, 1.5, V), None)}
+    for t1 in range(V):
+        table[(t1,)] = (rng.normal(0, 1.5, V), None)
+        for t2 in range(V):
+            table[(t1, t2)] = (rng.normal(0, 1.5, V), None)
+    for k in table:                                   # draft rows: target + noise
+        zt = table[k][0].astype(np.float32)
+        table[k] = (zt, (zt + rng.normal(0, 1.0, V)).astype(np.float32))
+    T32, l32 = float(np.float32(T)), float(np.float32(lam))
+
+    def q_of(k):
+        return scipy.special.softmax(table[k][1].astype(np.float64) / T32)
+
+    def pmix(k):
+        zt, zq = (a.astype(np.float64) for a in table[k])
+        if space == "prob":
+            return (1 - l32) * scipy.special.softmax(zt / T32) + l32 * scipy.special.softmax(zq / T32)
+        return scipy.special.softmax(((1 - l32) * zt + l32 * zq) / T32)
+
+    tok1 = np.stack([rng.choice(V, size=n, p=q_of(())) for _ in range(3)], axis=1)
+    tok2 = np.zeros_like(tok1)
+    for j in range(3):
+        for t in range(V):
+            sel = tok1[:, j] == t
+            tok2[sel, j] = rng.choice(V, size=int(sel.sum()), p=q_of((t,)))
+    node_token = np.concatenate([tok1, tok2], axis=1).astype(np.int32)
+    zt = np.zeros((n, 7, V), dtype=np.float32)
+    zq = np.zeros((n, 7, V), dtype=np.float32)
+    zt[:, 0], zq[:, 0] = table[()]
+    for t1 in range(V):
+        rows_t = np.stack([table[(t1,)][0]] + [table[(t1, t2)][0] for t2 in range(V)])
+        rows_q = np.stack([table[(t1,)][1]] + [table[(t1, t2)][1] for t2 in range(V)])
+        for j in range(3):
+            sel = tok1[:, j] == t1
+            zt[sel, 1 + j], zq[sel, 1 + j] = rows_t[0], rows_q[0]
+            zt[sel, 4 + j] = rows_t[1 + tok2[sel, j]]
+            zq[sel, 4 + j] = rows_q[1 + tok2[sel, j]]
+    u_node = rng.random((n, 6), dtype=np.float32)
+    u_s = rng.random(n, dtype=np.float32)
+    g = to_host(sv.tree_verify_multi(dev_logits(zt, "fp32", 8), dev_logits(zq, "fp32", 8),
+                                     dev(np.broadcast_to(parent, (n, 6)).copy()), dev(node_token),
+                                     dev(u_node), dev(u_s), 2, lam, T, space))
+    assert int(g.status[0]) == 0
+
+    def chisq(obs, prob):
+        keep = prob > 0
+        assert np.all(obs[~keep] == 0)
+        exp = prob[keep] / prob[keep].sum() * obs[keep].sum()
+        return scipy.stats.chisquare(obs[keep], exp).pvalue
+
+    pv = [chisq(np.bincount(g.out_tokens[:, 0], minlength=V), pmix(()))]
+    for t1 in range(V):
+        sel = (g.accepted >= 1) & (g.out_tokens[:, 0] == t1)
+        if sel.sum() > 2000:
+            pv.append(chisq(np.bincount(g.out_tokens[sel, 1], minlength=V), pmix((t1,))))
+        for t2 in range(V):
+            sel2 = (g.accepted == 2) & (g.out_tokens[:, 0] == t1) & (g.out_tokens[:, 1] == t2)
+            if sel2.sum() > 2000:
+                pbonus = scipy.special.softmax(table[(t1, t2)][0].astype(np.float64) / T32)
+                pv.append(chisq(np.bincount(g.out_tokens[sel2, 2], minlength=V), pbonus))
+    print(f"[parity] multi MC {space}: {len(pv)} laws, min p {min(pv):.4f}, "
+          f"depths {np.bincount(g.accepted).tolist()}", flush=True)
+    assert len(pv) >= 8
+    assert min(pv) > 0.01 / len(pv)            # Bonferroni over the tested laws
