@@ -405,6 +405,18 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
     const int b = pos / a.g.Pcap;
     if (!geo_position_valid(a.g, b, i)) return;            // uniform over the block
     const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    // the chunk's loads do not depend on the row statistics: issue them first
+    // so that they are in flight while waves 0 and 1 combine the partials
+    const int c = grp * kWaves + wv;
+    constexpr int VEC = DT::kVec;
+    const int V = a.g.V;
+    const int r = geo_row(a.g, b, i);
+    const char *row_t = row_ptr(a.g, 0, b, r);
+    const char *row_q = row_ptr(a.g, 1, b, r);
+    const int v0 = min(c, a.C1 - 1) * (kWave * NV);
+    u32x4 dt[NV], dq[NV];
+    load_chunk<DT, NV>(row_t, v0, lane, V, dt);
+    load_chunk<DT, NV>(row_q, v0, lane, V, dq);
     const Part *parts = a.part1 + (int64_t(b) * a.g.Pcap + i) * 2 * a.C1;
     if (wv < 2) {
         float s_, inv_;
@@ -420,17 +432,7 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
         }
     }
     __syncthreads();
-    const int c = grp * kWaves + wv;
     if (c >= a.C1) return;
-    constexpr int VEC = DT::kVec;
-    const int V = a.g.V;
-    const int r = geo_row(a.g, b, i);
-    const char *row_t = row_ptr(a.g, 0, b, r);
-    const char *row_q = row_ptr(a.g, 1, b, r);
-    const int v0 = c * (kWave * NV);
-    u32x4 dt[NV], dq[NV];
-    load_chunk<DT, NV>(row_t, v0, lane, V, dt);
-    load_chunk<DT, NV>(row_q, v0, lane, V, dq);
     const float c_hi = a.c_hi, c_lo = a.c_lo;
     const float ts = st_s, ti = st_i, qs = sq_s, qi = sq_i;
     const float w_t = 1.0f - a.lam, w_q = a.lam;

@@ -22,9 +22,8 @@
 // sum over the vocabulary is a pass of the whole block over the node's two
 // rows: the row statistics (as the chain's, integer shifts, fp64 sums), the
 // residual after a rejection (written to a ping-pong fp32 buffer of the
-// workspace with its fp64 mass), and a two-pass tiled inverse CDF (the first
-// pass forms the total with exactly the prefix sums the second one scans, so
-// the crossing is always found).  Acceptance of the first child uses the
+// workspace with its fp64 mass), and a tiled inverse CDF over the total an
+// earlier pass already summed (the residual mass or the bonus normaliser).  Acceptance of the first child uses the
 // gathered logits in fp64; later children read the stored residual.
 #include <hip/hip_runtime.h>
 #include <limits.h>
@@ -247,21 +246,30 @@ __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, const char 
     const int V = a.V;
     const int nvec = (V + VEC - 1) / VEC;
     double tot = 0.0;
-    for (int gv = static_cast<int>(threadIdx.x); gv < nvec; gv += kMB) {
-        const u32x4 dt = load_row_vec<DT>(row_t, gv, V);
-        const u32x4 dq = load_row_vec<DT>(row_q, gv, V);
-        float ft[VEC], fq[VEC];
-        DT::unpack(dt, ft);
-        DT::unpack(dq, fq);
-        for (int e = 0; e < VEC; ++e) {
-            const int v = gv * VEC + e;
-            if (v >= V) break;
-            double pm, q;
-            m_probs<DT>(a, sh, ft[e], fq[e], pm, q);
-            const double r = (in == nullptr) ? pm : static_cast<double>(in[v]) / Zin;
-            const float w = static_cast<float>(fmax(0.0, r - q));
-            out[v] = w;
-            tot += static_cast<double>(w);
+    for (int g0 = 0; g0 < nvec; g0 += kMB * kMU) {
+        u32x4 dt[kMU], dq[kMU];
+#pragma unroll
+        for (int k = 0; k < kMU; ++k) {
+            const int gv = g0 + k * kMB + static_cast<int>(threadIdx.x);
+            dt[k] = load_row_vec<DT>(row_t, gv, V);
+            dq[k] = load_row_vec<DT>(row_q, gv, V);
+        }
+#pragma unroll
+        for (int k = 0; k < kMU; ++k) {
+            const int gv = g0 + k * kMB + static_cast<int>(threadIdx.x);
+            float ft[VEC], fq[VEC];
+            DT::unpack(dt[k], ft);
+            DT::unpack(dq[k], fq);
+            for (int e = 0; e < VEC; ++e) {
+                const int v = gv * VEC + e;
+                if (v >= V) break;
+                double pm, q;
+                m_probs<DT>(a, sh, ft[e], fq[e], pm, q);
+                const double r = (in == nullptr) ? pm : static_cast<double>(in[v]) / Zin;
+                const float w = static_cast<float>(fmax(0.0, r - q));
+                out[v] = w;
+                tot += static_cast<double>(w);
+            }
         }
     }
     return mblock_sum(tot, sh);
@@ -281,18 +289,21 @@ __device__ __forceinline__ double draw_weight(const MultiArgs &a, const MultiSha
     return pm;
 }
 
-// Inverse CDF in index order over tiles of kMB vectors: pass 0 returns the
-// total (the last carry), pass 1 the token min{v : F(v) > u * total}, with
-// the last positive weight when rounding leaves no crossing; -1 when the
-// total is not positive.
+// Inverse CDF in index order over tiles of kMB vectors: the token
+// min{v : F(v) > u * W}, with the last positive weight when rounding leaves
+// no crossing; -1 when the total is not positive.  W_known > 0 is the total
+// as an earlier pass summed the same weights (the residual mass, the bonus
+// row's normaliser): then one scan suffices; otherwise a first scan forms
+// the total with exactly the prefix sums the second one walks.
 template <class DT, int KIND>
 __device__ int pass_draw(const MultiArgs &a, MultiShared &sh, const char *row_t, const char *row_q,
-                         const float *buf, double u) {
+                         const float *buf, double u, double W_known) {
     constexpr int VEC = DT::kVec;
     const int V = a.V;
     const int nvec = (V + VEC - 1) / VEC;
-    double W = 0.0;
-    for (int pass = 0; pass < 2; ++pass) {
+    double W = W_known;
+    const bool known = W_known > 0.0 && isfinite(W_known);
+    for (int pass = known ? 1 : 0; pass < 2; ++pass) {
         const double t = u * W;
         double carry = 0.0;
         int last = -1;
@@ -391,7 +402,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
         if (first < 0) {
             // bonus: the target's own softmax(z/T) at this node
             pass_stats<DT>(a, sh, rt, rq, true);
-            tok = pass_draw<DT, kDrawBonus>(a, sh, rt, rq, nullptr, us);
+            tok = pass_draw<DT, kDrawBonus>(a, sh, rt, rq, nullptr, us, sh.SA);
             if (tok < 0 && t == 0) sh.flags |= SV_DATA_BAD_ROW;
             break;
         }
@@ -457,8 +468,8 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
             if (!(Zn > 0.0) || !isfinite(Zn)) {
                 // zero residual mass (rounding): draw from the current target
                 if (t == 0) sh.flags |= SV_DATA_FALLBACK;
-                tok = (cur == nullptr) ? pass_draw<DT, kDrawMixture>(a, sh, rt, rq, nullptr, us)
-                                       : pass_draw<DT, kDrawBuffer>(a, sh, rt, rq, cur, us);
+                tok = (cur == nullptr) ? pass_draw<DT, kDrawMixture>(a, sh, rt, rq, nullptr, us, -1.0)
+                                       : pass_draw<DT, kDrawBuffer>(a, sh, rt, rq, cur, us, Z);
                 drawn = true;
                 break;
             }
@@ -476,7 +487,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
             continue;
         }
         // every child rejected: draw from the last residual
-        tok = pass_draw<DT, kDrawBuffer>(a, sh, rt, rq, cur, us);
+        tok = pass_draw<DT, kDrawBuffer>(a, sh, rt, rq, cur, us, Z);
         if (tok < 0 && t == 0) sh.flags |= SV_DATA_BAD_ROW;
         done = true;
     }
