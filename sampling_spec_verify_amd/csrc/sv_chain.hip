@@ -84,6 +84,52 @@ __device__ __forceinline__ int geo_token(const Geo &g, int b, int i) {
     return g.tokens[int64_t(b) * g.N + v - 1];
 }
 
+// Requests the packed order covers, kWave per draft_len load.
+constexpr int kPackChunks = 4;
+
+// The r-th drafted position of a ragged chain batch in (request, position)
+// order.  With it the jobs of drafted rows take the front of a statistics
+// launch and the undrafted remainder its tail, where whole blocks exit at
+// once, instead of idle waves sitting between busy ones in every block.
+// Called with r uniform over the wave; b and i come out uniform.  False past
+// the last drafted position.
+__device__ __forceinline__ bool packed_position(const Geo &g, int B, int r, int &b, int &i) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int k[kPackChunks];
+#pragma unroll
+    for (int t = 0; t < kPackChunks; ++t) {
+        const int req = t * kWave + lane;
+        k[t] = (req < B) ? min(max(g.draft_len[req], 0), g.P) : 0;
+    }
+    int base = 0;
+#pragma unroll
+    for (int t = 0; t < kPackChunks; ++t) {
+        const int incl = wave_scan_i(k[t]);
+        const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
+        if (r < base + tot) {
+            const int rr = r - base;
+            // requests before the owner end at or before rr; lanes past B carry
+            // the chunk total, which exceeds rr
+            const int owner = __popcll(__ballot(incl <= rr));
+            const int before = (owner > 0) ? __builtin_amdgcn_readlane(incl, owner - 1) : 0;
+            b = t * kWave + owner;
+            i = rr - before;
+            return true;
+        }
+        base += tot;
+    }
+    return false;
+}
+
+// (request, position) held by position slot r of a statistics launch; false
+// when the slot holds no drafted position.
+__device__ __forceinline__ bool slot_position(const ChainArgs &a, int r, int &b, int &i) {
+    if (a.packed) return packed_position(a.g, a.B, r, b, i);
+    i = r % a.g.Pcap;
+    b = r / a.g.Pcap;
+    return geo_position_valid(a.g, b, i);
+}
+
 __device__ __forceinline__ const char *row_ptr(const Geo &g, int tensor, int b, int r) {
     if (tensor == 0)
         return g.tgt + (int64_t(b) * g.req_t * g.ld_t + int64_t(r) * g.ld_t) * g.elem;
@@ -99,13 +145,10 @@ template <class DT, int NV>
 __device__ __forceinline__ void row_chunk_stats(const ChainArgs &a, unsigned job) {
     const unsigned C1 = static_cast<unsigned>(a.C1);
     const int c = static_cast<int>(job % C1);
-    unsigned rest = job / C1;
+    const unsigned rest = job / C1;
     const int tensor = static_cast<int>(rest & 1u);
-    rest >>= 1;
-    const unsigned Pc = static_cast<unsigned>(a.g.Pcap);
-    const int i = static_cast<int>(rest % Pc);
-    const int b = static_cast<int>(rest / Pc);
-    if (!geo_position_valid(a.g, b, i)) return;
+    int b, i;
+    if (!slot_position(a, static_cast<int>(rest >> 1), b, i)) return;
     const char *row = row_ptr(a.g, tensor, b, geo_row(a.g, b, i));
     // the wave whose chunk holds the drafted token also gathers its logit
     // no drafted tokens (the acceptance-rate call): nothing to gather
@@ -185,11 +228,8 @@ template <class DT, int NV>
 __device__ __forceinline__ void row_chunk_stats_logit(const ChainArgs &a, unsigned job) {
     const unsigned C1 = static_cast<unsigned>(a.C1);
     const int c = static_cast<int>(job % C1);
-    const unsigned rest = job / C1;
-    const unsigned Pc = static_cast<unsigned>(a.g.Pcap);
-    const int i = static_cast<int>(rest % Pc);
-    const int b = static_cast<int>(rest / Pc);
-    if (!geo_position_valid(a.g, b, i)) return;
+    int b, i;
+    if (!slot_position(a, static_cast<int>(job / C1), b, i)) return;
     const int r = geo_row(a.g, b, i);
     const char *row_t = row_ptr(a.g, 0, b, r);
     const char *row_q = row_ptr(a.g, 1, b, r);
@@ -400,10 +440,8 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
     const int groups = (a.C1 + kWaves - 1) / kWaves;
     const int job = blockIdx.x;
     const int grp = job % groups;
-    const int pos = job / groups;
-    const int i = pos % a.g.Pcap;
-    const int b = pos / a.g.Pcap;
-    if (!geo_position_valid(a.g, b, i)) return;            // uniform over the block
+    int b, i;
+    if (!slot_position(a, job / groups, b, i)) return;     // uniform over the block
     const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     // the chunk's loads do not depend on the row statistics: issue them first
     // so that they are in flight while waves 0 and 1 combine the partials
@@ -1081,6 +1119,7 @@ ChainArgs make_args(const ChainReq &q, int vec, int nv) {
     a.g.tokens = q.tokens;
     a.g.draft_len = q.path_mode ? nullptr : q.draft_len;
     a.g.path = q.path_mode ? q.path : nullptr;
+    a.packed = (a.g.draft_len != nullptr && q.B <= kPackChunks * kWave) ? 1 : 0;
     a.B = q.B;
     a.u_accept = q.u_accept;
     a.u_sample = q.u_sample;

@@ -79,6 +79,8 @@ struct ChainArgs {
     int NV2;                      // vectors per lane per sampling chunk (2, 4 or 8)
     int C2;                       // chunks per row in the sampling pass
     int rec_stride;               // doubles per chunk record: shift, pad, 16 * NV2 piece sums
+    int packed;                   // 1: position slots of the statistics launches follow the
+                                  // packed order of drafted positions (ragged chain, B <= 256)
     int space;                    // 0: probability-space mixture; 1: logit space (0 < lambda < 1)
     double alpha_c, beta_c;       // logit space: (1 - lambda) c and lambda c, c = log2(e)/T, fp64
     double *alpha_part;           // [B, Pcap, C1] workspace: per-chunk sum of min(p~, q)

@@ -226,6 +226,21 @@ __device__ __forceinline__ double wave_scan_d(double v) {
     return v;
 }
 
+// Inclusive scan of one int per lane, in lane order, by the same shift steps.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ int dpp_shift_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+__device__ __forceinline__ int wave_scan_i(int v) {
+    v += dpp_shift_i<kDppRowShr1, 0xF, 0xF>(v);
+    v += dpp_shift_i<kDppRowShr2, 0xF, 0xF>(v);
+    v += dpp_shift_i<kDppRowShr4, 0xF, 0xF>(v);
+    v += dpp_shift_i<kDppRowShr8, 0xF, 0xF>(v);
+    v += dpp_shift_i<kDppRowBcast15, 0xA, 0xF>(v);
+    v += dpp_shift_i<kDppRowBcast31, 0xC, 0xF>(v);
+    return v;
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
     v += dpp_d<kDppXor1>(v);
     v += dpp_d<kDppXor2>(v);
