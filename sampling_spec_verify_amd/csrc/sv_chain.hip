@@ -359,8 +359,8 @@ __device__ __forceinline__ int64_t piece_vec(int chunk, int wv, int n, int lane)
 
 template <class DT, int MODE>
 __device__ __forceinline__ void load_vec(const SampleCtx &S, int64_t gv, u32x4 &dt, u32x4 &dq) {
-    dt = load_row_vec<DT>(S.row_t, static_cast<int>(gv), S.V);
-    if (MODE != kBonus) dq = load_row_vec<DT>(S.row_q, static_cast<int>(gv), S.V);
+    dt = load_row_vec<DT, false>(S.row_t, static_cast<int>(gv), S.V);
+    if (MODE != kBonus) dq = load_row_vec<DT, false>(S.row_q, static_cast<int>(gv), S.V);
 }
 
 // Weights of one 16-byte vector; elements past V hold -inf logits and weigh 0.

@@ -58,19 +58,24 @@ struct F32 {
     }
 };
 
+// One 16-byte load.  NT marks it non-temporal: the single-use stream over the
+// drafted rows.  Reads of rows that were streamed just before (the sampling
+// row) or that the same block reads again (the tree walk) use ordinary loads.
+template <bool NT = true>
 __device__ __forceinline__ u32x4 load16(const char *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return *reinterpret_cast<const u32x4 *>(p);
 }
 
 // 16-byte vector gv (in units of DT::kVec elements) of a row of V elements:
 // vectors past the row read as -inf; in the one partial vector the elements
 // past V are set to -inf on the packed words.  The partial-vector test only
 // runs when V is not a multiple of kVec (a wave-uniform condition).
-template <class DT>
+template <class DT, bool NT = true>
 __device__ __forceinline__ u32x4 load_row_vec(const char *row, int gv, int V) {
     constexpr int VEC = DT::kVec;
     const int nvec = (V + VEC - 1) / VEC;
-    u32x4 d = (gv < nvec) ? load16(row + int64_t(gv) * 16)
+    u32x4 d = (gv < nvec) ? load16<NT>(row + int64_t(gv) * 16)
                           : u32x4{DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord};
     if ((V % VEC) != 0 && gv == nvec - 1) {
         const int valid = V - gv * VEC;             // 1 .. VEC-1 elements stay

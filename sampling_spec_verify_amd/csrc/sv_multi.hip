@@ -177,8 +177,8 @@ __device__ void pass_stats(const MultiArgs &a, MultiShared &sh, const char *row_
 #pragma unroll
         for (int k = 0; k < kMU; ++k) {
             const int gv = g0 + k * kMB + static_cast<int>(threadIdx.x);
-            dt[k] = load_row_vec<DT>(row_t, gv, V);
-            if (!target_only) dq[k] = load_row_vec<DT>(row_q, gv, V);
+            dt[k] = load_row_vec<DT, false>(row_t, gv, V);
+            if (!target_only) dq[k] = load_row_vec<DT, false>(row_q, gv, V);
         }
 #pragma unroll
         for (int k = 0; k < kMU; ++k) {
@@ -251,8 +251,8 @@ __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, const char 
 #pragma unroll
         for (int k = 0; k < kMU; ++k) {
             const int gv = g0 + k * kMB + static_cast<int>(threadIdx.x);
-            dt[k] = load_row_vec<DT>(row_t, gv, V);
-            dq[k] = load_row_vec<DT>(row_q, gv, V);
+            dt[k] = load_row_vec<DT, false>(row_t, gv, V);
+            dq[k] = load_row_vec<DT, false>(row_q, gv, V);
         }
 #pragma unroll
         for (int k = 0; k < kMU; ++k) {
@@ -313,11 +313,11 @@ __device__ int pass_draw(const MultiArgs &a, MultiShared &sh, const char *row_t,
             const int gv = g0 + static_cast<int>(threadIdx.x);
             float ft[VEC], fq[VEC];
             if (KIND != kDrawBuffer) {
-                const u32x4 dt = load_row_vec<DT>(row_t, gv, V);
+                const u32x4 dt = load_row_vec<DT, false>(row_t, gv, V);
                 DT::unpack(dt, ft);
             }
             if (KIND == kDrawMixture) {
-                const u32x4 dq = load_row_vec<DT>(row_q, gv, V);
+                const u32x4 dq = load_row_vec<DT, false>(row_q, gv, V);
                 DT::unpack(dq, fq);
             }
             double w[VEC];
