@@ -90,6 +90,14 @@ def parse():
                     help="bound on the oracle's CPU time for cpu_baseline (0 disables)")
     ap.add_argument("--time-every", type=int, default=4,
                     help="attach timing events to the dominant kernel of every n-th timed step")
+    ap.add_argument("--cpu-pool-seconds", type=float, default=6.0,
+                    help="bound on the all-cores oracle run (a fork pool over requests, taken "
+                         "before the GPU is touched); 0 disables")
+    ap.add_argument("--graph", type=int, default=0, metavar="REPLAYS",
+                    help="chain workloads: also time REPLAYS replays of a HIP graph holding one "
+                         "call per rotated buffer set (steady state without launch gaps)")
+    ap.add_argument("--no-stream-ceiling", action="store_true",
+                    help="skip the same-run read-stream ceiling measurement")
     ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
 
@@ -113,6 +121,141 @@ def device_copies(arr, dtype, R, torch):
     if dtype == "bf16":
         base = base.view(torch.bfloat16)
     return [base] + [base.clone() for _ in range(R - 1)]
+
+
+def read_stream_ceiling(nbytes, torch, sv, launches=60):
+    """Same-run practical read ceiling: ``sv_read_stream`` (the row streams' access
+    pattern, no arithmetic) over ``nbytes`` with buffer sets rotated past 1 GiB, and
+    over one 2 GiB buffer.  Launch-attached events, as for the verify kernels."""
+    import numpy as np
+
+    def timed(views, n, k):
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+        for i in range(5):
+            sv.read_stream(views[i % len(views)], n, sink)
+        timer = sv.KernelTimer(k)
+        for i in range(k):
+            sv.read_stream(views[i % len(views)], n, sink, timer.pair(i))
+        torch.cuda.synchronize()
+        ms = np.array([timer.elapsed_ms(i) for i in range(k)])
+        timer.close()
+        return ms
+
+    stride = (nbytes + 4095) // 4096 * 4096
+    R = max(2, math.ceil(ROTATE_BYTES / stride))
+    buf = torch.empty(R * stride, dtype=torch.uint8, device="cuda:0")
+    ms = timed([buf[i * stride:(i + 1) * stride] for i in range(R)], nbytes, launches)
+    del buf
+    big_n = 2 << 30
+    big = torch.empty(big_n, dtype=torch.uint8, device="cuda:0")
+    ms2 = timed([big], big_n, 20)
+    del big
+    torch.cuda.empty_cache()
+    med, med2 = float(np.median(ms)), float(np.median(ms2))
+    return {"kernel": "sv_read_stream", "bytes": nbytes, "buffer_sets_rotated": R,
+            "launches": launches, "ms_median": med, "gbs_median": nbytes / (med * 1e-3) / 1e9,
+            "gbs_2gib_median": big_n / (med2 * 1e-3) / 1e9}
+
+
+_POOL = {}
+
+
+def _pool_chain_worker(wid, nworkers, seconds):
+    import oracle
+    x, space, t, d = _POOL["x"], _POOL["space"], _POOL["t"], _POOL["d"]
+    lens = x.lengths()
+    done = pos = 0
+    t0 = time.perf_counter()
+    b = wid % x.B
+    while time.perf_counter() - t0 < seconds:
+        k = int(lens[b])
+        oracle.chain_verify_one(t[b, :k + 1], d[b, :k], x.tokens[b, :k], x.u_accept[b, :k],
+                                x.u_sample[b], x.lam, x.temperature, space)
+        pos += k
+        done += 1
+        b = (b + nworkers) % x.B
+    return done, pos
+
+
+def _pool_tree_worker(wid, nworkers, seconds):
+    import oracle
+    x, t = _POOL["x"], _POOL["t"]
+    done = 0
+    t0 = time.perf_counter()
+    b = wid % x.B
+    while time.perf_counter() - t0 < seconds:
+        oracle.tree_greedy_one(t[b], x.parent[b], x.node_token[b])
+        done += 1
+        b = (b + nworkers) % x.B
+    return done, done * x.N
+
+
+def cpu_pool_baseline(x, tree, seconds, space="prob", cores=None):
+    """The oracle on all of the host's cores: one forked worker per core (at most 16),
+    each cycling over its share of the batch's requests for ``seconds``.  Called before
+    anything touches the GPU, so the workers are plain copies of a CPU-only process."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    n = max(1, min(16, len(os.sched_getaffinity(0)))) if cores is None else cores
+    # widened once here, as in the one-core run; the workers share the arrays
+    _POOL.update(x=x, space=space, t=x.widened(x.target),
+                 d=None if tree else x.widened(x.draft))
+    fn = _pool_tree_worker if tree else _pool_chain_worker
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("fork")) as ex:
+        res = list(ex.map(fn, range(n), [n] * n, [seconds] * n))
+    wall = time.perf_counter() - t0
+    done = sum(r[0] for r in res)
+    units = sum(r[1] for r in res)
+    what = "greedy tree verifications" if tree else "request verifications"
+    return {"value": units / wall, "unit": UNIT, "cores": n, "kind": "oracle",
+            "sample": f"{done} oracle {what} on {n} forked workers (one per core, each cycling "
+                      f"over its share of the {x.B} requests of the same seeded batch), fp64 "
+                      f"numpy; wall time includes the pool start",
+            "seconds": round(wall, 2)}
+
+
+def graph_steady_state(x, tgts, drfs, tok, ua, us, dl, space, R, replays, torch, sv):
+    """One HIP graph holding one chain call per rotated buffer set, replayed
+    ``replays`` times; every replay's outputs are checked against an eager run."""
+    import numpy as np
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        calls = [sv.ChainCall(tgts[i], drfs[i], tok, ua, us, x.lam, x.temperature, dl,
+                              stream=s, space=space) for i in range(R)]
+        for c in calls:
+            c.run()
+    s.synchronize()
+    ref = [[o.cpu().numpy() for o in c.out] for c in calls]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for c in calls:
+            c.run()
+    match = True
+    for _ in range(3):
+        with torch.cuda.stream(s):
+            for c in calls:                 # eager work between replays: clobber the outputs
+                for o in c.out:
+                    o.fill_(-7)
+            g.replay()
+        s.synchronize()
+        for c, r in zip(calls, ref):
+            match &= all(np.array_equal(o.cpu().numpy(), e) for o, e in zip(c.out, r))
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        g.replay()
+        ev0.record()
+        for _ in range(replays):
+            g.replay()
+        ev1.record()
+    s.synchronize()
+    us_call = ev0.elapsed_time(ev1) * 1e3 / (replays * R)
+    return {"calls_per_graph": R, "replays": replays, "us_per_call": us_call,
+            "positions_per_s": x.positions() / (us_call * 1e-6),
+            "replays_match_eager": bool(match)}
 
 
 def cpu_baseline_chain(x, seconds, gpu_out, space="prob"):
@@ -432,16 +575,21 @@ def main():
         bench_alpha(args)
         return
 
+    from sampling_spec_verify_amd import synth
+
+    x = synth.config(args.workload)
+    tree = args.workload == "c5"
+    cpu_pool = None
+    if args.cpu_seconds > 0 and args.cpu_pool_seconds > 0:
+        cpu_pool = cpu_pool_baseline(x, tree, args.cpu_pool_seconds, args.space)
+
     import numpy as np
     import torch
 
     from sampling_spec_verify_amd import specverify as sv
-    from sampling_spec_verify_amd import synth
 
     sv.lib()
-    x = synth.config(args.workload)
     elem = 2 if x.dtype == "bf16" else 4
-    tree = args.workload == "c5"
     if tree:
         positions = x.B * x.N
         algo_bytes = x.B * (x.N + 1) * x.V * elem
@@ -516,6 +664,13 @@ def main():
     torch.cuda.synchronize()
     status = int(out.status[0].item())
     gpu_out = [o.cpu().numpy() for o in out]
+    graph = None
+    if args.graph > 0 and not tree:
+        graph = graph_steady_state(x, tgts, drfs, tok, ua, us, dl, args.space, R, args.graph,
+                                   torch, sv)
+    ceiling = None
+    if not args.no_stream_ceiling:
+        ceiling = read_stream_ceiling(algo_bytes, torch, sv)
 
     cpu = None
     parity = None
@@ -549,9 +704,15 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": kname, "algorithmic_bytes_per_launch": algo_bytes,
                      "kernel_ms_mean": kern_ms, "kernel_ms_median": float(np.median(first_ms)),
+                     "kernel_ms_p10": float(np.percentile(first_ms, 10)),
+                     "kernel_ms_p90": float(np.percentile(first_ms, 90)),
                      "kernel_timing": f"HIP events attached to the launch in every {every}-th timed "
-                                      f"step ({len(timed)} launches)"},
+                                      f"step ({len(timed)} launches)",
+                     "read_stream": ceiling,
+                     "frac_of_read_stream": (achieved / ceiling["gbs_median"]) if ceiling else None},
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_pool,
+        "graph_steady_state": graph,
         "step_hbm_gbps": algo_bytes * K / (wall * 1e9),
         "step_hbm_frac": algo_bytes * K / (wall * 1e9) / PEAK_HBM_GBS,
         "gpu_ms_per_step": gpu_ms / K,

@@ -394,6 +394,31 @@ sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t,
                                int32_t *status, void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement utility (not a step of the method)
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Read-stream calibration: reads bytes of device memory at buf once, with
+ * the access pattern of the row streams above (one wavefront per 8 KB job,
+ * 16-byte non-temporal loads, 256-thread blocks), and folds them with XOR;
+ * no other arithmetic.  Its duration over the same byte count as a verify
+ * kernel's stream is the practical read ceiling that kernel is compared with.
+ *
+ *  buf    device memory, 16-byte aligned, owned by the caller.
+ *  bytes  a positive multiple of 16.
+ *  sink   one device uint32 the kernel writes only when the fold equals a
+ *         fixed word (it keeps the loads from being elided); its value means
+ *         nothing.
+ *  kernel_start, kernel_stop  events recorded at the kernel's own begin and
+ *         end (hipExtLaunchKernelGGL), or NULL for an untimed launch.
+ * Returns SV_EINVAL (null pointer, bytes 0 or not a multiple of 16, buf not
+ * 16-byte aligned, more than 2^31 - 1 blocks) before any HIP call, SV_EHIP
+ * when the launch fails.
+ */
+sv_status sv_read_stream(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream,
+                         hipEvent_t kernel_start, hipEvent_t kernel_stop);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["sv_chain.hip", "sv_tree.hip", "sv_multi.hip"]
+SOURCES = ["sv_chain.hip", "sv_tree.hip", "sv_multi.hip", "sv_stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -61,6 +61,7 @@ SIGNATURES = {
                               _P, _P, _I, _P, _P, _S, _P], _I),
     "sv_tree_verify_path": (_PATH_ARGS, _I),
     "sv_tree_verify_path_ex": (_PATH_ARGS + [_I], _I),
+    "sv_read_stream": ([_P, _S, _P, _P, _P, _P], _I),
 }
 
 _lib = None
@@ -119,6 +120,19 @@ class KernelTimer:
         for ev in self.start + self.stop:
             self._hip.hipEventDestroy(ev)
         self.start, self.stop = [], []
+
+
+def read_stream(buf, nbytes: int, sink, events=None, stream=None):
+    """sv_read_stream over the first ``nbytes`` bytes of the GPU tensor ``buf``
+    (a calibration read, not a step of the method); ``sink`` is a device int32
+    tensor of at least one element, ``events`` an optional (start, stop) pair."""
+    if not buf.is_cuda or not sink.is_cuda:
+        raise ValueError("buf and sink must be GPU tensors")
+    if nbytes > buf.numel() * buf.element_size() or sink.numel() < 1:
+        raise ValueError("nbytes exceeds buf, or sink is empty")
+    ev = (None, None) if events is None else events
+    _check(lib().sv_read_stream(_ptr(buf), int(nbytes), _ptr(sink), _stream(stream), *ev),
+           "sv_read_stream")
 
 
 def status_string(code: int) -> str:

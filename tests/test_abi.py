@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
                             "sv_tree_row_argmax_timed", "sv_tree_attention_mask",
                             "sv_tree_attention_mask_timed", "sv_tree_verify_path",
                             "sv_tree_verify_path_ex", "sv_tree_multi_workspace_bytes",
-                            "sv_tree_verify_multi"])
+                            "sv_tree_verify_multi", "sv_read_stream"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -256,3 +256,13 @@ def test_multi_argument_errors(kw, code):
         kw = dict(wsb=sv.lib().sv_tree_multi_workspace_bytes(2, 5, 128) - 16)
     assert multi_call(**kw) == code
 
+
+def test_read_stream_rejects_bad_arguments():
+    L = sv.lib()
+    buf = ctypes.c_void_p(0x10000)      # never dereferenced: every call fails validation
+    sink = ctypes.c_void_p(0x20000)
+    assert L.sv_read_stream(None, 1024, sink, None, None, None) == sv.SV_EINVAL
+    assert L.sv_read_stream(buf, 1024, None, None, None, None) == sv.SV_EINVAL
+    assert L.sv_read_stream(buf, 0, sink, None, None, None) == sv.SV_EINVAL
+    assert L.sv_read_stream(buf, 1000, sink, None, None, None) == sv.SV_EINVAL
+    assert L.sv_read_stream(ctypes.c_void_p(0x10008), 1024, sink, None, None, None) == sv.SV_EINVAL
