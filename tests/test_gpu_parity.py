@@ -93,6 +93,14 @@ SMALL = [
     (9, 2, 64, 300, "fp32", 0.0, 1.0, False, None),
     (10, 9, 8, 20000, "fp32", 0.9, 2.0, True, None),
     (11, 40, 4, 2048, "bf16", 0.0, 1.0, True, None),
+    # ragged batches on either side of the packed job order's 256-request limit
+    (12, 256, 3, 1500, "fp32", 0.2, 0.8, True, None),
+    (13, 257, 3, 2000, "bf16", 0.0, 1.0, True, None),
+    (14, 300, 2, 1200, "bf16", 0.6, 1.1, True, None),
+    # the largest vocabularies the validator accepts (bf16 2^21, fp32 2^20): LDS
+    # staging is off, and the locate holds 16 piece masses per thread
+    (15, 2, 3, 1 << 21, "bf16", 0.0, 1.0, False, None),
+    (16, 2, 2, 1 << 20, "fp32", 0.3, 0.9, False, None),
 ]
 
 
@@ -189,6 +197,7 @@ def test_status_bad_row():
 @pytest.mark.parametrize("seed,B,N,V,dtype,ints", [
     (1, 6, 12, 50, "fp32", True), (2, 4, 30, 20000, "fp32", True), (3, 5, 20, 9000, "bf16", False),
     (4, 3, 1, 4, "fp32", True), (5, 2, 200, 100, "bf16", True), (6, 8, 0, 500, "fp32", False),
+    (7, 2, 1024, 300, "bf16", False),
 ])
 def test_greedy_random_trees(seed, B, N, V, dtype, ints):
     x = synth.make_random_tree(300 + seed, B, N, V, dtype, int_logits=ints)
@@ -387,6 +396,8 @@ LOGIT_SMALL = [
     (26, 6, 0, 5000, "bf16", 0.2, 0.8, False, None),
     (27, 2, 64, 300, "fp32", 0.6, 1.0, False, None),
     (28, 40, 4, 2048, "bf16", 0.95, 1.0, True, None),
+    (29, 300, 3, 1500, "bf16", 0.3, 1.0, True, None),
+    (30, 2, 2, 1 << 21, "bf16", 0.5, 1.0, False, None),
 ]
 
 
@@ -487,6 +498,8 @@ def test_acceptance_rate_workload(cfg, space):
     (44, 7, 1, 7, "fp32", 0.4, 1.0, False, 8, "logit"),
     (45, 2, 64, 300, "fp32", 0.6, 1.0, False, None, "prob"),
     (46, 6, 5, 33000, "bf16", 0.8, 1.5, True, None, "logit"),
+    (47, 300, 3, 1500, "bf16", 0.0, 1.0, True, None, "prob"),
+    (48, 2, 3, 1 << 21, "bf16", 0.3, 1.0, True, None, "logit"),
 ])
 def test_acceptance_rate_small(seed, B, K, V, dtype, lam, T, ragged, ld, space):
     x = synth.make_chain(100 + seed, B, K, V, dtype, sigma_t=2.0, sigma_q=(0.3, 2.0),
@@ -561,6 +574,7 @@ def test_multi_tree_workload(lam, space):
     (4, 5, 30, 9000, "bf16", 0.2, 1.0, "logit", 3),
     (5, 2, 200, 500, "fp32", 0.0, 1.5, "prob", None),
     (6, 4, 0, 700, "bf16", 0.0, 1.0, "prob", None),
+    (7, 1, 1024, 256, "fp32", 0.3, 1.0, "prob", None),
 ])
 def test_multi_random_trees(seed, B, N, V, dtype, lam, T, space, Dmax):
     # loose draft rows (sigma 2) so that rejections and sibling retries are common
