@@ -9,7 +9,7 @@
 //   "大模型推理的Speculative Decoding原理详解", "修改的拒绝采样", and the EAGLE
 //     explainer, "1. 为什么无损": the resample law is max(0, p - q), normalised.
 //
-// Three launches per call:
+// Two launches per call:
 //
 //  1. k_row_stats: one wavefront per (request, position, tensor, chunk) streams
 //     64 lanes x NV x 16 bytes of one drafted row with coalesced 16-byte loads
@@ -17,7 +17,8 @@
 //     s an integer, so partials combine by exact powers of two; the wave whose
 //     chunk holds the drafted token also records its logit.  Every
 //     drafted target and draft row is read exactly once.  Waves are
-//     independent (no LDS, no barrier); block 0 also clears the status word.
+//     independent (no LDS, no barrier); the launch also clears the status word
+//     and the per-request counters of launch 2.
 //
 //  2. k_resolve_mass: grid (B requests, C2 chunks) of 1024-thread blocks.
 //     Every block stages its request's row partials in LDS, combines them in
@@ -28,17 +29,22 @@
 //     reduces its chunk of the sampling row: the residual max(0, p_t - q) at
 //     row n (the same normalised law as max(0, p~ - q), since
 //     p~ - q = (1 - lambda)(p_t - q)), or the bonus softmax(z/T) at the
-//     request's last target row, to fp64 sums of its 16 * NV2 pieces.
-//
-//  3. k_locate: one block per request loads every piece mass in one round
-//     (up to kLocPP per thread, in registers), scales them to a common frame,
-//     finds the piece holding u * W with one monotone fp64 block scan over
+//     request's last target row, to fp64 sums of its 16 * NV2 pieces, and
+//     publishes them as agent-scope atomic stores.  The last of the request's
+//     C2 blocks to count itself done (one atomic counter per request) draws
+//     the token with its first 256 threads: it loads every piece mass in one
+//     round (up to kLocPP per thread), scales them to a common frame, finds
+//     the piece holding u * W with one monotone fp64 block scan over
 //     per-thread totals and a walk inside the owning thread, reloads that
 //     piece's 64 vectors and finds the token with a lane scan.
 //
-// Blocks never exchange data inside a launch, so no device-scope fences or
-// data atomics are needed; every reduction has a fixed order (bitwise
-// reproducible).
+// The only data that crosses blocks inside a launch are those piece masses:
+// written and read as relaxed agent-scope atomics (write-through stores,
+// coherent loads), drained before the counter is bumped, so no device-wide
+// cache writeback is needed.  A separate launch for the draw costs about as
+// much as the draw itself on this GPU (every kernel carries a fixed cost of
+// a few microseconds).  Every reduction has a fixed order (bitwise
+// reproducible): which block draws does not change the result.
 //
 // Path mode reuses both launches with a row indirection: position j of a
 // request uses target and draft row n_j of its draft tree (n_0 = root).
@@ -200,6 +206,14 @@ __device__ __forceinline__ void row_chunk_stats(const ChainArgs &a, unsigned job
     }
 }
 
+// Zeroes the per-request counters of the mass blocks (launch 2), so that
+// every call starts from zero whatever the workspace held.
+__device__ __forceinline__ void clear_counts(const ChainArgs &a) {
+    for (int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x); i < a.B;
+         i += static_cast<int>(gridDim.x * blockDim.x))
+        a.count[i] = 0;
+}
+
 // One wavefront per job; the job index is made wave-uniform so that its
 // decode runs as 32-bit scalar arithmetic.  Jobs of undrafted positions exit
 // after a few instructions.
@@ -211,6 +225,7 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(ChainArgs a, int n_jobs) {
     // cleared last: a store ahead of the job's reads would keep the compiler
     // from issuing them as scalar loads
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
+    clear_counts(a);
 }
 
 // Logit-space mixture (the RAPID pseudocode mixes logits, enhanced =
@@ -312,10 +327,11 @@ __global__ __launch_bounds__(kBlock) void k_row_stats_logit(ChainArgs a, int n_j
                                                    static_cast<int>(threadIdx.x) / kWave);
     if (job < n_jobs) row_chunk_stats_logit<DT, NV>(a, static_cast<unsigned>(job));
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
+    clear_counts(a);
 }
 
 // ---------------------------------------------------------------------------
-// launch 2: resolve + chunk masses; launch 3: inverse-CDF locate
+// launch 2: resolve + chunk masses, then the inverse-CDF draw in the last block
 // ---------------------------------------------------------------------------
 
 // kResidualLogit: the residual max(0, p~ - q) of the logit-space mixture,
@@ -683,6 +699,19 @@ __device__ __forceinline__ void resolve_request(const ChainArgs &a, int b, Resol
     __syncthreads();
 }
 
+// Hand-over of the chunk records between the mass blocks of one request,
+// which may run on different XCDs (each with its own L2): every record is
+// written and read as an agent-scope relaxed atomic (write-through stores and
+// coherent loads), and a writer drains its stores (s_waitcnt) before the
+// block counts itself done, so the last block sees every record without a
+// device-wide cache writeback.
+__device__ __forceinline__ void publish(double *p, double v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double collect(const double *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Sampling context of request b from its hand-over record.
 __device__ __forceinline__ SampleCtx sample_ctx(const ChainArgs &a, int b, const ReqRecord &r) {
     SampleCtx S;
@@ -737,59 +766,9 @@ __device__ __forceinline__ void chunk_pieces(const SampleCtx &S, int c, double *
         float w[VEC];
         vec_weights<DT, MODE>(S, dt[n], dq[n], piece_vec<NV2>(c, wv, n, lane) * VEC, s_use, w);
         const double ws = wave_sum_d(vec_sum<VEC>(w));
-        if (lane == 0) rec[2 + wv * NV2 + n] = ws;
+        if (lane == 0) publish(&rec[2 + wv * NV2 + n], ws);
     }
-    if (threadIdx.x == 0) rec[0] = static_cast<double>(s_rec);
-}
-
-template <class DT, int NV2>
-__global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int staged) {
-    __shared__ ResolveShared sh;
-    extern __shared__ double dyn[];
-    const int b = blockIdx.x;
-    const int c = blockIdx.y;
-    const int stage_n = staged ? 2 * a.g.Pcap * a.C1 : 0;
-    double *pS = dyn;
-    float *ps = reinterpret_cast<float *>(dyn + stage_n);
-    float *pz = ps + stage_n;
-    resolve_request<DT>(a, b, sh, ps, pS, pz, staged != 0);
-
-    const int n = sh.n, K = sh.K;
-    ReqRecord r;
-    r.n = n;
-    r.st = r.sq = r.it = r.iq = 0.0f;
-    if (n < K) {
-        r.mode = (a.space == 1) ? kResidualLogit : kResidual;
-        r.row = sh.rowi[n];
-        r.rows_ok = !sh.row_bad[2 * n] && !sh.row_bad[2 * n + 1];
-        // p(v) = 2^(z c - s) / S
-        r.st = sh.s[2 * n];
-        r.sq = sh.s[2 * n + 1];
-        r.it = static_cast<float>(1.0 / sh.S[2 * n]);
-        r.iq = static_cast<float>(1.0 / sh.S[2 * n + 1]);
-    } else {
-        r.mode = kBonus;
-        r.row = sh.rowi[K];
-        r.rows_ok = 1;
-    }
-    if (c == 0) {
-        // every output but the sampled token
-        const int P = a.g.P;
-        const int t = threadIdx.x;
-        if (t <= P && t != n) a.out_tokens[int64_t(b) * (P + 1) + t] = (t < n) ? sh.x[t] : -1;
-        if (a.accept_prob != nullptr && t < P)
-            a.accept_prob[int64_t(b) * P + t] = (t < K) ? static_cast<float>(sh.a[t]) : 0.0f;
-        if (t == 0) {
-            a.accepted[b] = n;
-            a.rec[b] = r;
-            if (sh.flags) atomicOr(a.status, sh.flags);
-        }
-    }
-    const SampleCtx S = sample_ctx(a, b, r);
-    double *cr = a.chunks + (int64_t(b) * a.C2 + c) * a.rec_stride;
-    if (r.mode == kResidual) chunk_pieces<DT, kResidual, NV2>(S, c, cr, sh.f);
-    else if (r.mode == kResidualLogit) chunk_pieces<DT, kResidualLogit, NV2>(S, c, cr, sh.f);
-    else chunk_pieces<DT, kBonus, NV2>(S, c, cr, sh.f);
+    if (threadIdx.x == 0) publish(&rec[0], static_cast<double>(s_rec));
 }
 
 struct LocateShared {
@@ -822,8 +801,8 @@ __device__ __forceinline__ void load_pieces(const ChainArgs &a, int b, int pp, L
             const int p = p0 + j;
             if (p < np) {
                 const double *rc = cr + int64_t(p / kPieces) * a.rec_stride;
-                P.m[j] = rc[2 + p % kPieces];
-                P.s[j] = static_cast<float>(rc[0]);
+                P.m[j] = collect(&rc[2 + p % kPieces]);
+                P.s[j] = static_cast<float>(collect(&rc[0]));
             }
         }
     }
@@ -995,15 +974,15 @@ __device__ __forceinline__ int sample_mixture(const SampleCtx &S, double u, Loca
     return L.tok;
 }
 
+// The sampled (corrected or bonus) token of request b from its chunk records,
+// written at position r.n.  Run by threads 0 .. kBlock-1 of the request's last
+// mass block (the block's other waves have ended).
 template <class DT, int NV2>
-__global__ __launch_bounds__(kBlock) void k_locate(ChainArgs a) {
-    __shared__ LocateShared L;
-    const int b = blockIdx.x;
+__device__ __forceinline__ void draw_request(const ChainArgs &a, int b, const ReqRecord &r,
+                                             const SampleCtx &S, LocateShared &L) {
     const int pp = (a.C2 * kWaves2 * NV2 + kBlock - 1) / kBlock;
     LocatePieces P;
     load_pieces<NV2>(a, b, pp, P);
-    const ReqRecord r = a.rec[b];
-    const SampleCtx S = sample_ctx(a, b, r);
     const double u = static_cast<double>(a.u_sample[b]);
     int flags = 0;
     // At lambda = 1, p~ = q and the residual max(0, p~ - q) is identically
@@ -1028,6 +1007,68 @@ __global__ __launch_bounds__(kBlock) void k_locate(ChainArgs a) {
         a.out_tokens[int64_t(b) * (a.g.P + 1) + r.n] = tok;
         if (flags) atomicOr(a.status, flags);
     }
+}
+
+
+template <class DT, int NV2>
+__global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int staged) {
+    __shared__ ResolveShared sh;
+    __shared__ LocateShared L;
+    __shared__ int last;
+    extern __shared__ double dyn[];
+    const int b = blockIdx.x;
+    const int c = blockIdx.y;
+    const int stage_n = staged ? 2 * a.g.Pcap * a.C1 : 0;
+    double *pS = dyn;
+    float *ps = reinterpret_cast<float *>(dyn + stage_n);
+    float *pz = ps + stage_n;
+    resolve_request<DT>(a, b, sh, ps, pS, pz, staged != 0);
+
+    const int n = sh.n, K = sh.K;
+    ReqRecord r;
+    r.n = n;
+    r.st = r.sq = r.it = r.iq = 0.0f;
+    if (n < K) {
+        r.mode = (a.space == 1) ? kResidualLogit : kResidual;
+        r.row = sh.rowi[n];
+        r.rows_ok = !sh.row_bad[2 * n] && !sh.row_bad[2 * n + 1];
+        // p(v) = 2^(z c - s) / S
+        r.st = sh.s[2 * n];
+        r.sq = sh.s[2 * n + 1];
+        r.it = static_cast<float>(1.0 / sh.S[2 * n]);
+        r.iq = static_cast<float>(1.0 / sh.S[2 * n + 1]);
+    } else {
+        r.mode = kBonus;
+        r.row = sh.rowi[K];
+        r.rows_ok = 1;
+    }
+    if (c == 0) {
+        // every output but the sampled token
+        const int P = a.g.P;
+        const int t = threadIdx.x;
+        if (t <= P && t != n) a.out_tokens[int64_t(b) * (P + 1) + t] = (t < n) ? sh.x[t] : -1;
+        if (a.accept_prob != nullptr && t < P)
+            a.accept_prob[int64_t(b) * P + t] = (t < K) ? static_cast<float>(sh.a[t]) : 0.0f;
+        if (t == 0) {
+            a.accepted[b] = n;
+            if (sh.flags) atomicOr(a.status, sh.flags);
+        }
+    }
+    const SampleCtx S = sample_ctx(a, b, r);
+    double *cr = a.chunks + (int64_t(b) * a.C2 + c) * a.rec_stride;
+    if (r.mode == kResidual) chunk_pieces<DT, kResidual, NV2>(S, c, cr, sh.f);
+    else if (r.mode == kResidualLogit) chunk_pieces<DT, kResidualLogit, NV2>(S, c, cr, sh.f);
+    else chunk_pieces<DT, kBonus, NV2>(S, c, cr, sh.f);
+
+    // the last of the request's C2 blocks to finish draws the token
+    __builtin_amdgcn_s_waitcnt(0);          // this thread's record stores are done
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last = __hip_atomic_fetch_add(&a.count[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               a.C2 - 1;
+    __syncthreads();
+    if (!last || threadIdx.x >= kBlock) return;   // uniform, then whole waves
+    draw_request<DT, NV2>(a, b, r, S, L);
 }
 
 }  // namespace sv
@@ -1130,7 +1171,7 @@ ChainArgs make_args(const ChainReq &q, int vec, int nv) {
     a.accept_prob = q.accept_prob;
     a.status = q.status ? q.status : reinterpret_cast<int32_t *>(ws + L.status);
     a.part1 = reinterpret_cast<Part *>(ws + L.part1);
-    a.rec = reinterpret_cast<ReqRecord *>(ws + L.rec);
+    a.count = reinterpret_cast<int *>(ws + L.count);
     a.chunks = reinterpret_cast<double *>(ws + L.chunks);
     a.C1 = c1_for(q.V, nv, vec);
     a.ch1 = 64 * nv * vec;
@@ -1174,16 +1215,12 @@ sv_status run_typed(const ChainReq &q, int which) {
         const int staged = stage_n <= kStageMax ? 1 : 0;
         const size_t lds = staged ? static_cast<size_t>(stage_n) * (sizeof(double) + 2 * sizeof(float)) : 0;
         const dim3 grid(static_cast<unsigned>(q.B), static_cast<unsigned>(a.C2));
-        const dim3 gridB(static_cast<unsigned>(q.B));
         if (a.NV2 == 8) {
             hipLaunchKernelGGL((k_resolve_mass<DT, 8>), grid, dim3(kBlock2), lds, q.stream, a, staged);
-            hipLaunchKernelGGL((k_locate<DT, 8>), gridB, dim3(kBlock), 0, q.stream, a);
         } else if (a.NV2 == 4) {
             hipLaunchKernelGGL((k_resolve_mass<DT, 4>), grid, dim3(kBlock2), lds, q.stream, a, staged);
-            hipLaunchKernelGGL((k_locate<DT, 4>), gridB, dim3(kBlock), 0, q.stream, a);
         } else {
             hipLaunchKernelGGL((k_resolve_mass<DT, 2>), grid, dim3(kBlock2), lds, q.stream, a, staged);
-            hipLaunchKernelGGL((k_locate<DT, 2>), gridB, dim3(kBlock), 0, q.stream, a);
         }
         if (hipGetLastError() != hipSuccess) return SV_EHIP;
     }

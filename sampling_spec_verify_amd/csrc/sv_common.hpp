@@ -32,7 +32,8 @@ struct alignas(16) ArgPart {
     int pad;
 };
 
-// Per-request hand-over from launch 2 to launch 3 of a chain call.
+// Per-request record of launch 2 of a chain call: the accepted count and the
+// sampling row with its statistics.
 struct alignas(16) ReqRecord {
     int n;          // accepted drafts
     int mode;       // residual (0) or bonus (1)
@@ -72,7 +73,7 @@ struct ChainArgs {
     float *accept_prob;           // [B, P] or NULL
     int32_t *status;              // [1]
     Part *part1;                  // [B, Pcap, 2, C1] workspace: row partials
-    ReqRecord *rec;               // [B] workspace: per-request hand-over
+    int *count;                   // [B] workspace: mass blocks of the request done (cleared by launch 1)
     double *chunks;               // [B, C2, rec_stride] workspace: sampling-chunk records
     int C1;                       // wave-chunks per row in the row-stats pass
     int ch1;                      // elements per row-stats chunk
@@ -156,15 +157,15 @@ inline int64_t chunk_bytes(int B, int V) {
 }
 
 struct ChainLayout {
-    int64_t status, rec, chunks, part1, total;
+    int64_t status, count, chunks, part1, total;
 };
 
 inline ChainLayout chain_layout(int B, int P, int V) {
     ChainLayout L;
     const int64_t c1max = c1_for(V, kMinNV, kMinVec);
     L.status = 0;
-    L.rec = 256;
-    L.chunks = L.rec + align256(int64_t(B) * int64_t(sizeof(ReqRecord)));
+    L.count = 256;
+    L.chunks = L.count + align256(int64_t(B) * int64_t(sizeof(int)));
     L.part1 = L.chunks + align256(chunk_bytes(B, V));
     L.total = L.part1 + align256(int64_t(B) * P * 2 * c1max * int64_t(sizeof(Part)));
     return L;

@@ -680,3 +680,40 @@ def test_gpu_multi_output_law_monte_carlo(space):
           f"depths {np.bincount(g.accepted).tolist()}", flush=True)
     assert len(pv) >= 8
     assert min(pv) > 0.01 / len(pv)            # Bonferroni over the tested laws
+
+
+# ---------------------------------------------------------------------------
+# the hand-over of chunk records between the mass blocks of a request
+# ---------------------------------------------------------------------------
+
+
+def test_handover_between_mass_blocks_under_alternating_inputs():
+    """Two batches alternate 300 times on one workspace.  Each request's four
+    mass blocks land on different XCDs (B = 7 is not a multiple of 8), and a
+    record read before its writer's store landed would carry the other batch's
+    value, so any such read changes an output token."""
+    B, K, V = 7, 4, 50000
+    xs = [synth.make_chain(seed, B, K, V, "bf16", sigma_t=2.0, sigma_q=(0.3, 2.0), lam=lam,
+                           temperature=T, ragged=True)
+          for seed, lam, T in ((705, 0.0, 1.0), (709, 0.3, 0.8))]
+    ws = torch.empty(sv.chain_workspace_bytes(B, K, V), dtype=torch.uint8, device="cuda:0")
+    calls = [sv.ChainCall(dev_logits(x.target, x.dtype), dev_logits(x.draft, x.dtype), dev(x.tokens),
+                          dev(x.u_accept), dev(x.u_sample), x.lam, x.temperature, dev(x.draft_len),
+                          workspace=ws) for x in xs]
+    refs = [oracle_chain(x) for x in xs]
+    reps = 300
+    hist = [torch.empty((reps, B, K + 1), dtype=torch.int32, device="cuda:0") for _ in xs]
+    acc = [torch.empty((reps, B), dtype=torch.int32, device="cuda:0") for _ in xs]
+    for i in range(reps):
+        for j, c in enumerate(calls):
+            out = c.run()
+            hist[j][i].copy_(out.out_tokens)
+            acc[j][i].copy_(out.accepted)
+    torch.cuda.synchronize()
+    for j, (x, ref) in enumerate(zip(xs, refs)):
+        assert not ref.flagged.any()
+        assert int(calls[j].out.status[0]) == 0
+        h, a = hist[j].cpu().numpy(), acc[j].cpu().numpy()
+        assert (a == ref.accepted[None, :]).all(), np.argwhere(a != ref.accepted[None, :])[:5]
+        assert (h == ref.out_tokens[None]).all(), np.argwhere(h != ref.out_tokens[None])[:5]
+    report("handover", {"calls": 2 * reps, "requests": B})
