@@ -429,7 +429,10 @@ __device__ __forceinline__ double vec_sum(const float *w) {
 // Row statistics (shift s, 1 / S) of one row from its C1 chunk partials, by
 // one wavefront, in fp64 and in a fixed order; S = 0 or non-finite marks the
 // row bad (1 / S is then NaN).
-__device__ __forceinline__ void combine_row(const Part *p, int C1, float &s_out, float &inv_out) {
+// Row statistics from the chunk partials: the shift s and 1 / S, and also
+// off = s + log2 S, so that log2 p(v) = z c - off (NaN for a bad row).
+__device__ __forceinline__ void combine_row(const Part *p, int C1, float &s_out, float &inv_out,
+                                            float &off_out) {
     const int lane = threadIdx.x & (kWave - 1);
     float smax = -INFINITY;
     for (int c = lane; c < C1; c += kWave) smax = fmaxf(smax, p[c].s);
@@ -441,7 +444,9 @@ __device__ __forceinline__ void combine_row(const Part *p, int C1, float &s_out,
     }
     S = wave_sum_d(S);
     s_out = smax;
-    inv_out = (S > 0.0 && isfinite(S) && isfinite(smax)) ? static_cast<float>(1.0 / S) : NAN;
+    const bool ok = S > 0.0 && isfinite(S) && isfinite(smax);
+    inv_out = ok ? static_cast<float>(1.0 / S) : NAN;
+    off_out = ok ? static_cast<float>(static_cast<double>(smax) + log2(S)) : NAN;
 }
 
 // One block per (request, position, group of 4 chunks): wave 0 combines the
@@ -450,9 +455,14 @@ __device__ __forceinline__ void combine_row(const Part *p, int C1, float &s_out,
 // min(p~(v), q(v)) over its elements.  Per element (probability space)
 // p~ = (1 - lambda) p_t + lambda q with p(v) = 2^(z c - s) / S; in logit
 // space p~(v) = 2^(alpha z_t + beta z_q - s_e) / S_e.
-template <class DT, int NV, int LOGIT>
+//
+// MODE 0 (probability space, lambda > 0) forms both probabilities.  Where p~
+// is itself one softmax (MODE 1: logit space; MODE 2: lambda = 0, p~ = p_t),
+// min(p~, q) = 2^min(log2 p~, log2 q) with log2 p(v) = z c - (s + log2 S):
+// one exponential per element instead of two.
+template <class DT, int NV, int MODE>
 __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
-    __shared__ float st_s, st_i, sq_s, sq_i;
+    __shared__ float st_s, st_i, sq_s, sq_i, st_o, sq_o;
     const int groups = (a.C1 + kWaves - 1) / kWaves;
     const int job = blockIdx.x;
     const int grp = job % groups;
@@ -473,15 +483,17 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
     load_chunk<DT, NV>(row_q, v0, lane, V, dq);
     const Part *parts = a.part1 + (int64_t(b) * a.g.Pcap + i) * 2 * a.C1;
     if (wv < 2) {
-        float s_, inv_;
-        combine_row(parts + wv * a.C1, a.C1, s_, inv_);
+        float s_, inv_, off_;
+        combine_row(parts + wv * a.C1, a.C1, s_, inv_, off_);
         if (lane == 0) {
             if (wv == 0) {
                 st_s = s_;
                 st_i = inv_;
+                st_o = off_;
             } else {
                 sq_s = s_;
                 sq_i = inv_;
+                sq_o = off_;
             }
         }
     }
@@ -493,6 +505,7 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+    const float ot = st_o, oq = sq_o;
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
         float ft[VEC], fq[VEC];
@@ -500,14 +513,25 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
         DT::unpack(dq[n], fq);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const float q = pow2_logit(fq[e], c_hi, c_lo, qs) * qi;
-            float pm;
-            if (LOGIT) pm = pow2_mixed(ft[e], fq[e], a.alpha_c, a.beta_c, ts) * ti;
-            else pm = fmaf(w_t, pow2_logit(ft[e], c_hi, c_lo, ts) * ti, w_q * q);
-            acc[e] += fminf(pm, q);
+            if (MODE == 0) {
+                const float q = pow2_logit(fq[e], c_hi, c_lo, qs) * qi;
+                const float pm = fmaf(w_t, pow2_logit(ft[e], c_hi, c_lo, ts) * ti, w_q * q);
+                acc[e] += fminf(pm, q);
+            } else {
+                const float yq = fmaf(fq[e], c_lo, fmaf(fq[e], c_hi, -oq));
+                const float yp =
+                    (MODE == 1) ? static_cast<float>(fma(static_cast<double>(ft[e]), a.alpha_c,
+                                                         fma(static_cast<double>(fq[e]), a.beta_c,
+                                                             -static_cast<double>(ot))))
+                                : fmaf(ft[e], c_lo, fmaf(ft[e], c_hi, -ot));
+                acc[e] += __builtin_amdgcn_exp2f(fminf(yp, yq));
+            }
         }
     }
-    const double tot = wave_sum_d(vec_sum<VEC>(acc));
+    double tot = wave_sum_d(vec_sum<VEC>(acc));
+    // a bad row (its statistics are NaN) makes alpha NaN; fminf alone would
+    // drop a NaN probability in favour of the other one
+    if (!(ti == ti && qi == qi)) tot = NAN;
     if (lane == 0) a.alpha_part[(int64_t(b) * a.g.Pcap + i) * a.C1 + c] = tot;
 }
 
@@ -1233,6 +1257,8 @@ void launch_alpha(const ChainArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(int64_t(a.B) * a.g.Pcap * groups));
     if (a.space == 1)
         hipLaunchKernelGGL((k_alpha_mass<DT, NV, 1>), grid, dim3(kBlock), 0, stream, a);
+    else if (a.lam == 0.0f)
+        hipLaunchKernelGGL((k_alpha_mass<DT, NV, 2>), grid, dim3(kBlock), 0, stream, a);
     else
         hipLaunchKernelGGL((k_alpha_mass<DT, NV, 0>), grid, dim3(kBlock), 0, stream, a);
 }

@@ -509,6 +509,32 @@ def test_acceptance_rate_small(seed, B, K, V, dtype, lam, T, ragged, ld, space):
     report(f"alpha small{seed}", {"max_abs_err": err})
 
 
+@pytest.mark.parametrize("lam,space", [(0.0, "prob"), (0.3, "prob"), (0.4, "logit")])
+def test_acceptance_rate_bad_row_is_nan_and_flagged(lam, space):
+    """A NaN in a drafted target or draft row makes that position's alpha NaN and
+    sets SV_DATA_BAD_ROW; the other positions keep the oracle's values (each of
+    the kernel's three forms of the sum: two probabilities, and the single
+    exponential of the logit space and of lambda = 0)."""
+    x = synth.make_chain(261, 3, 3, 3000, "fp32", lam=lam)
+    x.target[0, 1, 17] = np.nan
+    x.draft[2, 0, 2999] = np.nan
+    alpha, status = sv.chain_acceptance_rate(dev_logits(x.target, x.dtype),
+                                             dev_logits(x.draft, x.dtype), x.lam, x.temperature,
+                                             space=space)
+    torch.cuda.synchronize()
+    g = alpha.cpu().numpy()
+    assert int(status[0].item()) & 0x02
+    assert np.isnan(g[0, 1]) and np.isnan(g[2, 0])
+    good = np.isfinite(g)
+    assert good.sum() == g.size - 2
+    y = synth.make_chain(261, 3, 3, 3000, "fp32", lam=lam)
+    ref = oracle_chain(y, space=space)
+    for b in range(3):
+        for i in range(3):
+            if good[b, i]:
+                assert abs(g[b, i] - ref.details[b].alpha[i]) <= ALPHA_TOL
+
+
 def test_acceptance_rate_identical_rows_and_lambda_one_are_one():
     x = synth.make_chain(247, 4, 3, 5000, "bf16", lam=0.3)
     x.draft = np.ascontiguousarray(x.target[:, :3, :])
