@@ -136,6 +136,14 @@ __device__ __forceinline__ bool slot_position(const ChainArgs &a, int r, int &b,
     return geo_position_valid(a.g, b, i);
 }
 
+// alpha z_t + beta z_q - s in fp32 with alpha = m[0] + m[1], beta = m[2] + m[3]
+// (the hi + lo splits): the large products first, each fma rounding once,
+// then the two small corrections.  Near the largest mixed logit (the terms
+// that carry the mass) the result is within about 1e-7 of the exact value.
+__device__ __forceinline__ float mixed_expo(float zt, float zq, const float (&m)[4], float s) {
+    return fmaf(zq, m[3], fmaf(zt, m[1], fmaf(zq, m[2], fmaf(zt, m[0], -s))));
+}
+
 __device__ __forceinline__ const char *row_ptr(const Geo &g, int tensor, int b, int r) {
     if (tensor == 0)
         return g.tgt + (int64_t(b) * g.req_t * g.ld_t + int64_t(r) * g.ld_t) * g.elem;
@@ -274,6 +282,7 @@ __device__ __forceinline__ void row_chunk_stats_logit(const ChainArgs &a, unsign
         }
     const float c_hi = a.c_hi, c_lo = a.c_lo;
     const double al = a.alpha_c, be = a.beta_c;
+    const float mx[4] = {a.al_hi, a.al_lo, a.be_hi, a.be_lo};
     // draft row, as in probability space
     const float sq_lane = (mq == -INFINITY) ? -INFINITY : ceilf(mq * c_hi);
     const float sq_use = (mq == -INFINITY) ? 0.0f : sq_lane;
@@ -291,9 +300,7 @@ __device__ __forceinline__ void row_chunk_stats_logit(const ChainArgs &a, unsign
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             accq[e] += __builtin_amdgcn_exp2f(fmaf(fq[n][e], c_lo, fmaf(fq[n][e], c_hi, -sq_use)));
-            const double y = fma(static_cast<double>(ft[n][e]), al,
-                                 fma(static_cast<double>(fq[n][e]), be, -se_use));
-            acce[e] += __builtin_amdgcn_exp2f(static_cast<float>(y));
+            acce[e] += __builtin_amdgcn_exp2f(mixed_expo(ft[n][e], fq[n][e], mx, static_cast<float>(se_use)));
         }
     float Sq_lane = 0.0f, Se_lane = 0.0f;
 #pragma unroll
@@ -346,7 +353,7 @@ struct SampleCtx {
     float st, it;           // target row: p_t(v) = 2^(z c - st) * it
     float sq, iq;           // draft row:  q(v)   = 2^(z c - sq) * iq
     float w_t, w_q;         // mixture weights (1 - lambda, lambda)
-    double al, be;          // logit space: (1 - lambda) c, lambda c
+    float mx[4];            // logit space: (1 - lambda) c and lambda c, each as hi + lo
     int logit;              // the target-slot statistics are those of the mixed logits
     int V;
 };
@@ -356,10 +363,9 @@ __device__ __forceinline__ float pow2_logit(float z, float c_hi, float c_lo, flo
     return __builtin_amdgcn_exp2f(fmaf(z, c_lo, fmaf(z, c_hi, -s)));
 }
 
-// 2^(alpha z_t + beta z_q - s) of the logit-space mixture, the argument in fp64
-__device__ __forceinline__ float pow2_mixed(float zt, float zq, double al, double be, float s) {
-    return __builtin_amdgcn_exp2f(static_cast<float>(
-        fma(static_cast<double>(zt), al, fma(static_cast<double>(zq), be, -static_cast<double>(s)))));
+// 2^(alpha z_t + beta z_q - s) of the logit-space mixture
+__device__ __forceinline__ float pow2_mixed(float zt, float zq, const float (&m)[4], float s) {
+    return __builtin_amdgcn_exp2f(mixed_expo(zt, zq, m, s));
 }
 
 // The sampling row is cut into chunks of kBlock2 lanes x NV2 vectors, one
@@ -394,7 +400,7 @@ __device__ __forceinline__ void vec_weights(const SampleCtx &S, const u32x4 &dt,
         if (MODE == kBonus) {
             w[e] = pow2_logit(ft[e], S.c_hi, S.c_lo, s_use);
         } else if (MODE == kResidualLogit) {
-            const float pe = pow2_mixed(ft[e], fq[e], S.al, S.be, S.st) * S.it;
+            const float pe = pow2_mixed(ft[e], fq[e], S.mx, S.st) * S.it;
             const float pq = pow2_logit(fq[e], S.c_hi, S.c_lo, S.sq) * S.iq;
             w[e] = fmaxf(pe - pq, 0.0f);
         } else {
@@ -506,6 +512,7 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
     const float ot = st_o, oq = sq_o;
+    const float mx[4] = {a.al_hi, a.al_lo, a.be_hi, a.be_lo};
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
         float ft[VEC], fq[VEC];
@@ -519,11 +526,8 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
                 acc[e] += fminf(pm, q);
             } else {
                 const float yq = fmaf(fq[e], c_lo, fmaf(fq[e], c_hi, -oq));
-                const float yp =
-                    (MODE == 1) ? static_cast<float>(fma(static_cast<double>(ft[e]), a.alpha_c,
-                                                         fma(static_cast<double>(fq[e]), a.beta_c,
-                                                             -static_cast<double>(ot))))
-                                : fmaf(ft[e], c_lo, fmaf(ft[e], c_hi, -ot));
+                const float yp = (MODE == 1) ? mixed_expo(ft[e], fq[e], mx, ot)
+                                             : fmaf(ft[e], c_lo, fmaf(ft[e], c_hi, -ot));
                 acc[e] += __builtin_amdgcn_exp2f(fminf(yp, yq));
             }
         }
@@ -744,8 +748,10 @@ __device__ __forceinline__ SampleCtx sample_ctx(const ChainArgs &a, int b, const
     S.c_lo = a.c_lo;
     S.w_t = 1.0f - a.lam;
     S.w_q = a.lam;
-    S.al = a.alpha_c;
-    S.be = a.beta_c;
+    S.mx[0] = a.al_hi;
+    S.mx[1] = a.al_lo;
+    S.mx[2] = a.be_hi;
+    S.mx[3] = a.be_lo;
     S.logit = a.space;
     S.row_t = row_ptr(a.g, 0, b, r.row);
     S.row_q = (r.mode != kBonus) ? row_ptr(a.g, 1, b, r.row) : nullptr;
@@ -963,7 +969,7 @@ __device__ __forceinline__ int sample_mixture(const SampleCtx &S, double u, Loca
         if (v >= V) return 0.0f;
         const float zt = DT::load1(S.row_t, v);
         const float zq = DT::load1(S.row_q, v);
-        if (S.logit) return pow2_mixed(zt, zq, S.al, S.be, S.st) * S.it;   // p~ itself
+        if (S.logit) return pow2_mixed(zt, zq, S.mx, S.st) * S.it;   // p~ itself
         const float pt = pow2_logit(zt, S.c_hi, S.c_lo, S.st) * S.it;
         const float pq = pow2_logit(zq, S.c_hi, S.c_lo, S.sq) * S.iq;
         return fmaf(S.w_t, pt, S.w_q * pq);
@@ -1205,6 +1211,8 @@ ChainArgs make_args(const ChainReq &q, int vec, int nv) {
     a.space = q.space;
     a.alpha_c = (1.0 - static_cast<double>(q.lam)) * a.c_d;
     a.beta_c = static_cast<double>(q.lam) * a.c_d;
+    split_positive(a.alpha_c, &a.al_hi, &a.al_lo);
+    split_positive(a.beta_c, &a.be_hi, &a.be_lo);
     return a;
 }
 

@@ -84,6 +84,7 @@ struct ChainArgs {
                                   // packed order of drafted positions (ragged chain, B <= 256)
     int space;                    // 0: probability-space mixture; 1: logit space (0 < lambda < 1)
     double alpha_c, beta_c;       // logit space: (1 - lambda) c and lambda c, c = log2(e)/T, fp64
+    float al_hi, al_lo, be_hi, be_lo;   // the same split as hi + lo, each part > 0 (fp32 exponents)
     double *alpha_part;           // [B, Pcap, C1] workspace: per-chunk sum of min(p~, q)
     float *alpha;                 // [B, P] out: expected acceptance of each drafted position
 };
@@ -205,6 +206,20 @@ inline bool temperature_split(float T, float *c_hi, float *c_lo, double *c_d) {
     *c_lo = lo;
     *c_d = static_cast<double>(hi) + static_cast<double>(lo);
     return true;
+}
+
+// x > 0 as hi + lo in fp32 with hi < x the largest float below it and lo > 0,
+// so that (-inf) * hi + (-inf) * lo stays -inf.  x = 0 gives 0 + 0.
+inline void split_positive(double x, float *hi, float *lo) {
+    if (!(x > 0.0)) {
+        *hi = 0.0f;
+        *lo = 0.0f;
+        return;
+    }
+    float h = static_cast<float>(x);
+    if (static_cast<double>(h) >= x) h = nextafterf(h, 0.0f);
+    *hi = h;
+    *lo = static_cast<float>(x - static_cast<double>(h));
 }
 
 // Launches `kernel` on `stream`; when either event is given, the launch
