@@ -241,9 +241,9 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(ChainArgs a, int n_jobs) {
 // c of drafted position i with its target and draft chunks together, so each
 // drafted row is still read once.  Slot 0 of the position receives the
 // enhanced row's partial: its exponent y = alpha z_t + beta z_q - s
-// (alpha = (1 - lambda) c, beta = lambda c) is formed in fp64, since a mixed
-// logit is not exact in fp32 while bf16 / fp32 logits times fp64 constants
-// are; the lane shift ceil(alpha m_t + beta m_q) bounds the lane's largest
+// (alpha = (1 - lambda) c, beta = lambda c) comes from mixed_expo, four fp32
+// fmas of the split constants; the lane shift ceil(alpha m_t + beta m_q),
+// formed in fp64 once per lane, bounds the lane's largest
 // alpha z_t + beta z_q from above (alpha, beta >= 0), and the slot carries the
 // drafted token's target logit.  Slot 1 receives the draft row's partial
 // exactly as in probability space.
