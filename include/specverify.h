@@ -89,6 +89,9 @@ typedef enum { SV_MIX_PROB = 0, SV_MIX_LOGIT = 1 } sv_mix_space;
 #define SV_DATA_BAD_TREE    0x10 /* parent or path entry invalid: node never accepted / path cut */
 #define SV_DATA_FALLBACK    0x20 /* residual mass was zero after a rejection: sampled p~ instead */
 #define SV_DATA_DEPTH       0x40 /* accepted tree path deeper than Dmax: cut at Dmax nodes */
+#define SV_DATA_SYNC        0x80 /* sv_tree_verify_multi: a block of a tree gave up waiting for the
+                                    tree's other blocks (not expected: they are launched resident
+                                    together); that tree's outputs are invalid */
 
 /* Human-readable name of a status code (static storage, host memory). */
 const char *sv_status_string(sv_status s);
@@ -378,9 +381,12 @@ sv_status sv_tree_verify_path_ex(const void *target_logits, int64_t ld_t,
  *  workspace: sv_tree_multi_workspace_bytes(B, N, V) bytes (two fp32
  *  residual rows per request).
  *
- * One 1024-thread block per request walks its tree; every sum over the
- * vocabulary is a pass of that block over the node's rows, so the call is
- * bound by the walk's latency rather than by HBM bandwidth.
+ * Each tree is walked by G cooperating 1024-thread blocks (G up to 16, so
+ * that B * G blocks fit the GPU at once; the launch is cooperative), each
+ * owning a slice of the vocabulary: every sum over the vocabulary is a pass of
+ * the blocks over their slices, combined at a barrier of the tree's blocks.
+ * The call is bound by that chain of passes rather than by HBM bandwidth.
+ * SV_DATA_SYNC reports a block that stopped waiting at such a barrier.
  */
 size_t sv_tree_multi_workspace_bytes(int B, int N, int V);
 sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t,

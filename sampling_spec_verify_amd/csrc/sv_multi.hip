@@ -18,12 +18,15 @@
 // token is drawn from the last residual; a node without children (or at depth
 // Dmax) emits the bonus token from the target's own softmax(z/T).
 //
-// One 1024-thread block per request walks its tree.  Each step that needs a
-// sum over the vocabulary is a pass of the whole block over the node's two
-// rows: the row statistics (as the chain's, integer shifts, fp64 sums), the
+// G cooperating 1024-thread blocks walk each tree (G up to 16, as many as fit
+// the GPU with the other trees' blocks), block g owning vocabulary slice g.
+// Every block takes every decision of the walk from the same combined values;
+// each step that needs a sum over the vocabulary is a pass of every block over
+// its slice of the node's two rows, combined at a barrier of the tree's
+// blocks: the row statistics (as the chain's, integer shifts, fp64 sums), the
 // residual after a rejection (written to a ping-pong fp32 buffer of the
-// workspace with its fp64 mass), and a tiled inverse CDF over the total an
-// earlier pass already summed (the residual mass or the bonus normaliser).  Acceptance of the first child uses the
+// workspace with its fp64 mass), and an inverse CDF over slice totals, then
+// within the slice holding the draw.  Acceptance of the first child uses the
 // gathered logits in fp64; later children read the stored residual.
 #include <hip/hip_runtime.h>
 #include <limits.h>
@@ -40,6 +43,9 @@ constexpr int kMB = 1024;                 // threads of a walk block
 constexpr int kMW = kMB / kWave;          // its waves
 constexpr int kMU = 2;                    // tiles of a pass in flight per thread
 constexpr int kMNodes = SV_MAX_TREE_NODES + 1;
+constexpr int kMaxG = 16;                 // blocks per tree at most
+constexpr int kSlot = 4;                  // doubles a block publishes per barrier
+constexpr int kSpinLimit = 1 << 15;       // polls of a barrier before it is given up
 
 struct MultiArgs {
     const char *tgt, *drf;
@@ -55,6 +61,9 @@ struct MultiArgs {
     float *accept_prob;                   // [B, N] or NULL
     int32_t *status;
     float *buf;                           // [B, 2, V] residual ping-pong
+    int G;                                // blocks per tree; block g owns vocabulary slice g
+    int *bar;                             // [B] barrier arrivals, cleared by k_multi_clear
+    double *pub;                          // [B, G, 2, kSlot] values published at a barrier
 };
 
 struct MultiShared {
@@ -66,7 +75,9 @@ struct MultiShared {
     float redf[kMW];
     int redi[kMW];
     double sA, SA, sB, SB;                // statistics of the two rows (A: target or mixed)
-    int flags, decision, token;
+    double iA, iB;                        // 1 / SA, 1 / SB
+    double gath[kMaxG][kSlot];            // every block's published values after a barrier
+    int flags, decision, token, broken;
 };
 
 // ---- block reductions (every thread calls; results uniform) ---------------
@@ -127,6 +138,78 @@ __device__ __forceinline__ Scan mblock_scan(double v, double carry, MultiShared 
     return s;
 }
 
+// ---- the blocks of one tree -------------------------------------------------
+//
+// Block g of a tree owns the contiguous vocabulary slice g (whole 16-byte
+// vectors, in index order) for every pass.  The blocks take the same
+// decisions from the same combined values, so they meet the same barriers.
+// Values cross blocks only through agent-scope relaxed atomics (write-through
+// stores, coherent loads): a block publishes, drains its stores, arrives at
+// the tree's counter and polls it until all G blocks have arrived; published
+// slots alternate with the barrier's parity, so a slot is rewritten only after
+// every block has read it.  The launch is cooperative (all blocks resident),
+// and a poll gives up after kSpinLimit rounds, marking the block broken, so
+// every wave ends.
+
+struct Slice {
+    int lo, hi;                            // vectors [lo, hi)
+};
+
+__device__ __forceinline__ Slice my_slice(const MultiArgs &a, int nvec) {
+    const int g = static_cast<int>(blockIdx.x) % a.G;
+    const int per = (nvec + a.G - 1) / a.G;
+    Slice s;
+    s.lo = min(g * per, nvec);
+    s.hi = min(s.lo + per, nvec);
+    return s;
+}
+
+__device__ __forceinline__ double *pub_slot(const MultiArgs &a, int g, int phase) {
+    const int b = static_cast<int>(blockIdx.x) / a.G;
+    return a.pub + ((int64_t(b) * a.G + g) * 2 + (phase & 1)) * kSlot;
+}
+
+// Thread 0 publishes v[0..n) for the barrier that ends phase + 1.
+__device__ __forceinline__ void publish_vals(const MultiArgs &a, int phase, const double *v, int n) {
+    if (threadIdx.x != 0) return;
+    double *p = pub_slot(a, static_cast<int>(blockIdx.x) % a.G, phase + 1);
+    for (int j = 0; j < n; ++j) __hip_atomic_store(&p[j], v[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The tree's barrier; then sh.gath holds every block's published values.
+// Every thread calls it with the same phase count, which it advances.
+__device__ void tree_barrier(const MultiArgs &a, MultiShared &sh, int &phase, int n) {
+    __builtin_amdgcn_s_waitcnt(0);        // this thread's published stores are done
+    __syncthreads();
+    ++phase;
+    if (threadIdx.x == 0 && a.G > 1 && !sh.broken) {
+        int *cnt = a.bar + static_cast<int>(blockIdx.x) / a.G;
+        __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int target = phase * a.G;
+        int polls = 0;
+        while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++polls > kSpinLimit) {
+                sh.broken = 1;
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    if (static_cast<int>(threadIdx.x) < a.G * n) {
+        const int g = static_cast<int>(threadIdx.x) / n, j = static_cast<int>(threadIdx.x) % n;
+        sh.gath[g][j] = __hip_atomic_load(&pub_slot(a, g, phase)[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---- element values -----------------------------------------------------
 
 template <class DT>
@@ -148,7 +231,7 @@ __device__ __forceinline__ float m_pow2_mixed(float zt, float zq, double al, dou
 template <class DT>
 __device__ __forceinline__ void m_probs(const MultiArgs &a, const MultiShared &sh, float zt, float zq,
                                         double &pm, double &q) {
-    const double iA = 1.0 / sh.SA, iB = 1.0 / sh.SB;
+    const double iA = sh.iA, iB = sh.iB;
     q = static_cast<double>(m_pow2(zq, a.c_hi, a.c_lo, static_cast<float>(sh.sB))) * iB;
     if (a.space == 1) {
         pm = static_cast<double>(m_pow2_mixed(zt, zq, a.al, a.be, static_cast<float>(sh.sA))) * iA;
@@ -164,21 +247,23 @@ __device__ __forceinline__ void m_probs(const MultiArgs &a, const MultiShared &s
 // mixed logits (logit space), B = draft; with target_only, A alone (the bonus
 // row).  Per thread a running integer shift and fp64 sum, then block-wide.
 template <class DT>
-__device__ void pass_stats(const MultiArgs &a, MultiShared &sh, const char *row_t, const char *row_q,
-                           bool target_only) {
+__device__ void pass_stats(const MultiArgs &a, MultiShared &sh, int &phase, const char *row_t,
+                           const char *row_q, bool target_only) {
     constexpr int VEC = DT::kVec;
     const int V = a.V;
     const int nvec = (V + VEC - 1) / VEC;
+    const Slice sl = my_slice(a, nvec);
     float sa = -INFINITY, sb = -INFINITY;
     double aa = 0.0, ab = 0.0;
     const bool mixed = !target_only && a.space == 1;
-    for (int g0 = 0; g0 < nvec; g0 += kMB * kMU) {
+    for (int g0 = sl.lo; g0 < sl.hi; g0 += kMB * kMU) {
         u32x4 dt[kMU], dq[kMU];
 #pragma unroll
         for (int k = 0; k < kMU; ++k) {
+            // vectors past the slice read as -inf (their weights are 0)
             const int gv = g0 + k * kMB + static_cast<int>(threadIdx.x);
-            dt[k] = load_row_vec<DT, false>(row_t, gv, V);
-            if (!target_only) dq[k] = load_row_vec<DT, false>(row_q, gv, V);
+            dt[k] = load_row_vec<DT, false>(row_t, gv < sl.hi ? gv : nvec, V);
+            if (!target_only) dq[k] = load_row_vec<DT, false>(row_q, gv < sl.hi ? gv : nvec, V);
         }
 #pragma unroll
         for (int k = 0; k < kMU; ++k) {
@@ -227,36 +312,55 @@ __device__ void pass_stats(const MultiArgs &a, MultiShared &sh, const char *row_
         mb = mblock_max(sb, sh);
         SB = mblock_sum(sb == -INFINITY ? 0.0 : ab * pow2_shift_d(static_cast<double>(sb) - static_cast<double>(mb)), sh);
     }
+    // the tree's rows: combine the blocks' (shift, sum) pairs in slice order
+    const double mine[kSlot] = {static_cast<double>(ma), SA, static_cast<double>(mb), SB};
+    publish_vals(a, phase, mine, 4);
+    tree_barrier(a, sh, phase, 4);
+    double tA = -INFINITY, tB = -INFINITY;
+    for (int g = 0; g < a.G; ++g) {
+        tA = fmax(tA, sh.gath[g][0]);
+        tB = fmax(tB, sh.gath[g][2]);
+    }
+    double SAt = 0.0, SBt = 0.0;
+    for (int g = 0; g < a.G; ++g) {
+        if (sh.gath[g][0] != -INFINITY) SAt += sh.gath[g][1] * pow2_shift_d(sh.gath[g][0] - tA);
+        if (sh.gath[g][2] != -INFINITY) SBt += sh.gath[g][3] * pow2_shift_d(sh.gath[g][2] - tB);
+    }
     if (threadIdx.x == 0) {
-        sh.sA = ma;
-        sh.SA = SA;
-        sh.sB = mb;
-        sh.SB = SB;
+        sh.sA = tA;
+        sh.SA = SAt;
+        sh.sB = target_only ? 0.0 : tB;
+        sh.SB = target_only ? 1.0 : SBt;
+        sh.iA = 1.0 / SAt;
+        sh.iB = target_only ? 1.0 : 1.0 / SBt;
     }
     __syncthreads();
 }
 
 // Residual after a rejection: w(v) = max(0, r(v) - q(v)) with r = p~ (first
 // rejection, from the logits) or the previous residual in[v] / Zin; w is
-// stored (fp32) in out and its fp64 sum returned.
+// stored (fp32, coherent stores: the child tests of every block read it) in
+// out, and its fp64 sum over the tree's slices returned.
 template <class DT>
-__device__ double pass_residual(const MultiArgs &a, MultiShared &sh, const char *row_t, const char *row_q,
-                                const float *in, double Zin, float *out) {
+__device__ double pass_residual(const MultiArgs &a, MultiShared &sh, int &phase, const char *row_t,
+                                const char *row_q, const float *in, double Zin, float *out) {
     constexpr int VEC = DT::kVec;
     const int V = a.V;
     const int nvec = (V + VEC - 1) / VEC;
+    const Slice sl = my_slice(a, nvec);
     double tot = 0.0;
-    for (int g0 = 0; g0 < nvec; g0 += kMB * kMU) {
+    for (int g0 = sl.lo; g0 < sl.hi; g0 += kMB * kMU) {
         u32x4 dt[kMU], dq[kMU];
 #pragma unroll
         for (int k = 0; k < kMU; ++k) {
             const int gv = g0 + k * kMB + static_cast<int>(threadIdx.x);
-            dt[k] = load_row_vec<DT, false>(row_t, gv, V);
-            dq[k] = load_row_vec<DT, false>(row_q, gv, V);
+            dt[k] = load_row_vec<DT, false>(row_t, gv < sl.hi ? gv : nvec, V);
+            dq[k] = load_row_vec<DT, false>(row_q, gv < sl.hi ? gv : nvec, V);
         }
 #pragma unroll
         for (int k = 0; k < kMU; ++k) {
             const int gv = g0 + k * kMB + static_cast<int>(threadIdx.x);
+            if (gv >= sl.hi) continue;
             float ft[VEC], fq[VEC];
             DT::unpack(dt[k], ft);
             DT::unpack(dq[k], fq);
@@ -265,14 +369,19 @@ __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, const char 
                 if (v >= V) break;
                 double pm, q;
                 m_probs<DT>(a, sh, ft[e], fq[e], pm, q);
-                const double r = (in == nullptr) ? pm : static_cast<double>(in[v]) / Zin;
+                const double r = (in == nullptr) ? pm : static_cast<double>(load_coherent(&in[v])) / Zin;
                 const float w = static_cast<float>(fmax(0.0, r - q));
-                out[v] = w;
+                store_coherent(&out[v], w);
                 tot += static_cast<double>(w);
             }
         }
     }
-    return mblock_sum(tot, sh);
+    const double mine[kSlot] = {mblock_sum(tot, sh), 0.0, 0.0, 0.0};
+    publish_vals(a, phase, mine, 1);
+    tree_barrier(a, sh, phase, 1);
+    double Z = 0.0;
+    for (int g = 0; g < a.G; ++g) Z += sh.gath[g][0];
+    return Z;
 }
 
 enum MultiDraw { kDrawBonus = 0, kDrawBuffer = 1, kDrawMixture = 2 };
@@ -283,54 +392,83 @@ template <class DT, int KIND>
 __device__ __forceinline__ double draw_weight(const MultiArgs &a, const MultiShared &sh, float zt,
                                               float zq, const float *buf, int v) {
     if (KIND == kDrawBonus) return static_cast<double>(m_pow2(zt, a.c_hi, a.c_lo, static_cast<float>(sh.sA)));
-    if (KIND == kDrawBuffer) return static_cast<double>(buf[v]);
+    if (KIND == kDrawBuffer) return static_cast<double>(load_coherent(&buf[v]));
     double pm, q;
     m_probs<DT>(a, sh, zt, zq, pm, q);
     return pm;
 }
 
-// Inverse CDF in index order over tiles of kMB vectors: the token
-// min{v : F(v) > u * W}, with the last positive weight when rounding leaves
-// no crossing; -1 when the total is not positive.  W_known > 0 is the total
-// as an earlier pass summed the same weights (the residual mass, the bonus
-// row's normaliser): then one scan suffices; otherwise a first scan forms
-// the total with exactly the prefix sums the second one walks.
+// Weights of vector gv of the slice ending at vector hi (0 past it), their
+// sum in element order, and the last element with a positive weight.
 template <class DT, int KIND>
-__device__ int pass_draw(const MultiArgs &a, MultiShared &sh, const char *row_t, const char *row_q,
-                         const float *buf, double u, double W_known) {
+__device__ __forceinline__ double tile_weights(const MultiArgs &a, const MultiShared &sh, const char *row_t,
+                                              const char *row_q, const float *buf, int gv, int hi,
+                                              double (&w)[DT::kVec], int &last) {
     constexpr int VEC = DT::kVec;
     const int V = a.V;
-    const int nvec = (V + VEC - 1) / VEC;
-    double W = W_known;
-    const bool known = W_known > 0.0 && isfinite(W_known);
-    for (int pass = known ? 1 : 0; pass < 2; ++pass) {
-        const double t = u * W;
-        double carry = 0.0;
-        int last = -1;
+    const int gl = (gv < hi) ? gv : (V + VEC - 1) / VEC;      // past the slice: a -inf vector
+    float ft[VEC], fq[VEC];
+    if (KIND != kDrawBuffer) DT::unpack(load_row_vec<DT, false>(row_t, gl, V), ft);
+    if (KIND == kDrawMixture) DT::unpack(load_row_vec<DT, false>(row_q, gl, V), fq);
+    double sum = 0.0;
+    for (int e = 0; e < VEC; ++e) {
+        const int v = gv * VEC + e;
+        w[e] = (gv < hi && v < V) ? draw_weight<DT, KIND>(a, sh, ft[e], fq[e], buf, v) : 0.0;
+        if (!(w[e] > 0.0)) w[e] = 0.0;
+        sum += w[e];
+        if (w[e] > 0.0) last = v;
+    }
+    return sum;
+}
+
+// Inverse CDF in index order: the token min{v : F(v) > u * W}, with the last
+// positive weight when rounding leaves no crossing; -1 when the total is not
+// positive.  Every block first sums its slice in tiles of kMB vectors (a
+// block scan per tile) and publishes the total; the slice totals in slice
+// order give each slice its base and W.  The block whose [base, base + total)
+// holds u * W walks its slice again with the same tile scans from base and
+// publishes the token.
+template <class DT, int KIND>
+__device__ int pass_draw(const MultiArgs &a, MultiShared &sh, int &phase, const char *row_t,
+                         const char *row_q, const float *buf, double u) {
+    constexpr int VEC = DT::kVec;
+    const int nvec = (a.V + VEC - 1) / VEC;
+    const Slice sl = my_slice(a, nvec);
+    const int g = static_cast<int>(blockIdx.x) % a.G;
+    double carry = 0.0;
+    int last = -1;
+    for (int g0 = sl.lo; g0 < sl.hi; g0 += kMB) {
+        double w[VEC];
+        const double sum = tile_weights<DT, KIND>(a, sh, row_t, row_q, buf, g0 + static_cast<int>(threadIdx.x),
+                                                  sl.hi, w, last);
+        carry = mblock_scan(sum, carry, sh).total;
+    }
+    last = mblock_max_i(last, sh);
+    const double mine[kSlot] = {carry, static_cast<double>(last), 0.0, 0.0};
+    publish_vals(a, phase, mine, 2);
+    tree_barrier(a, sh, phase, 2);
+    double base = 0.0, W = 0.0;
+    int glast = -1;
+    for (int i = 0; i < a.G; ++i) {
+        if (i == g) base = W;
+        W += sh.gath[i][0];
+        glast = max(glast, static_cast<int>(sh.gath[i][1]));
+    }
+    const double mytot = sh.gath[g][0];
+    if (!(W > 0.0) || !isfinite(W)) return -1;                 // the same in every block
+    const double t = u * W;
+    int mytok = -1;
+    if (mytot > 0.0 && base <= t && t < base + mytot) {        // uniform over the block
         if (threadIdx.x == 0) sh.token = -1;
         __syncthreads();
-        for (int g0 = 0; g0 < nvec; g0 += kMB) {
+        double c2 = base;
+        for (int g0 = sl.lo; g0 < sl.hi; g0 += kMB) {
             const int gv = g0 + static_cast<int>(threadIdx.x);
-            float ft[VEC], fq[VEC];
-            if (KIND != kDrawBuffer) {
-                const u32x4 dt = load_row_vec<DT, false>(row_t, gv, V);
-                DT::unpack(dt, ft);
-            }
-            if (KIND == kDrawMixture) {
-                const u32x4 dq = load_row_vec<DT, false>(row_q, gv, V);
-                DT::unpack(dq, fq);
-            }
             double w[VEC];
-            double sum = 0.0;
-            for (int e = 0; e < VEC; ++e) {
-                const int v = gv * VEC + e;
-                w[e] = (v < V) ? draw_weight<DT, KIND>(a, sh, ft[e], fq[e], buf, v) : 0.0;
-                if (!(w[e] > 0.0)) w[e] = 0.0;
-                sum += w[e];
-                if (w[e] > 0.0) last = v;
-            }
-            const Scan s = mblock_scan(sum, carry, sh);
-            if (pass == 1 && s.excl <= t && t < s.incl) {
+            int dummy = -1;
+            const double sum = tile_weights<DT, KIND>(a, sh, row_t, row_q, buf, gv, sl.hi, w, dummy);
+            const Scan s = mblock_scan(sum, c2, sh);
+            if (s.excl <= t && t < s.incl) {
                 double cum = s.excl;
                 int pick = -1, lastpos = -1;
                 for (int e = 0; e < VEC; ++e) {
@@ -342,19 +480,20 @@ __device__ int pass_draw(const MultiArgs &a, MultiShared &sh, const char *row_t,
                 }
                 sh.token = (pick >= 0) ? pick : lastpos;
             }
-            carry = s.total;
+            c2 = s.total;
             __syncthreads();
-            if (pass == 1 && sh.token >= 0) break;
+            if (sh.token >= 0) break;
         }
-        if (pass == 0) {
-            W = carry;
-            if (!(W > 0.0) || !isfinite(W)) return -1;
-        } else if (sh.token < 0) {
-            // t rounded to the very top: the last positive weight
-            return mblock_max_i(last, sh);
-        }
+        // t rounded past this slice's last prefix: its last positive weight
+        mytok = (sh.token >= 0) ? sh.token : static_cast<int>(sh.gath[g][1]);
+        __syncthreads();
     }
-    return sh.token;
+    const double mt[kSlot] = {static_cast<double>(mytok), 0.0, 0.0, 0.0};
+    publish_vals(a, phase, mt, 1);
+    tree_barrier(a, sh, phase, 1);
+    int tok = -1;
+    for (int i = 0; i < a.G; ++i) tok = max(tok, static_cast<int>(sh.gath[i][0]));
+    return (tok >= 0) ? tok : glast;        // t rounded to the very top: the last positive weight
 }
 
 // ---- the walk ----------------------------------------------------------------
@@ -362,17 +501,22 @@ __device__ int pass_draw(const MultiArgs &a, MultiShared &sh, const char *row_t,
 template <class DT>
 __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
     __shared__ MultiShared sh;
-    const int b = blockIdx.x;
+    const int b = static_cast<int>(blockIdx.x) / a.G;
+    const int g = static_cast<int>(blockIdx.x) % a.G;     // block 0 of the tree writes the outputs
     const int t = threadIdx.x;
+    int phase = 0;
     const int N = a.N, V = a.V;
     for (int i = t; i <= N; i += kMB) {
         sh.head[i] = -1;
         sh.next[i] = -1;
         sh.tok[i] = (i > 0) ? a.node_token[int64_t(b) * N + i - 1] : -1;
     }
-    if (a.accept_prob != nullptr)
+    if (a.accept_prob != nullptr && g == 0)
         for (int i = t; i < N; i += kMB) a.accept_prob[int64_t(b) * N + i] = -1.0f;
-    if (t == 0) sh.flags = 0;
+    if (t == 0) {
+        sh.flags = 0;
+        sh.broken = 0;
+    }
     __syncthreads();
     if (t == 0) {
         // children lists in node order: link from the last node down
@@ -401,12 +545,12 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
         const int first = (depth < a.Dmax) ? sh.head[u] : -1;
         if (first < 0) {
             // bonus: the target's own softmax(z/T) at this node
-            pass_stats<DT>(a, sh, rt, rq, true);
-            tok = pass_draw<DT, kDrawBonus>(a, sh, rt, rq, nullptr, us, sh.SA);
+            pass_stats<DT>(a, sh, phase, rt, rq, true);
+            tok = pass_draw<DT, kDrawBonus>(a, sh, phase, rt, rq, nullptr, us);
             if (tok < 0 && t == 0) sh.flags |= SV_DATA_BAD_ROW;
             break;
         }
-        pass_stats<DT>(a, sh, rt, rq, false);
+        pass_stats<DT>(a, sh, phase, rt, rq, false);
         if (!(sh.SA > 0.0) || !isfinite(sh.SA) || !(sh.SB > 0.0) || !isfinite(sh.SB) ||
             !isfinite(sh.sA) || !isfinite(sh.sB)) {
             if (t == 0) sh.flags |= SV_DATA_BAD_ROW;
@@ -444,7 +588,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
                     } else {
                         double pm;
                         m_probs<DT>(a, sh, zt, zq, pm, q);
-                        r = static_cast<double>(cur[x]) / Z;
+                        r = static_cast<double>(load_coherent(&cur[x])) / Z;
                     }
                     if (q == 0.0) {
                         sh.flags |= SV_DATA_ZERO_Q;
@@ -453,7 +597,8 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
                         acc_p = fmin(1.0, r / q);
                     }
                 }
-                if (a.accept_prob != nullptr) a.accept_prob[int64_t(b) * N + c - 1] = static_cast<float>(acc_p);
+                if (a.accept_prob != nullptr && g == 0)
+                    a.accept_prob[int64_t(b) * N + c - 1] = static_cast<float>(acc_p);
                 const float uc = a.u_accept[int64_t(b) * N + c - 1];
                 sh.decision = (static_cast<double>(uc) < acc_p) ? 1 : 0;
             }
@@ -464,12 +609,12 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
             }
             // rejected: the residual becomes the next child's target
             float *out = (cur == buf0) ? buf1 : buf0;
-            const double Zn = pass_residual<DT>(a, sh, rt, rq, cur, Z, out);
+            const double Zn = pass_residual<DT>(a, sh, phase, rt, rq, cur, Z, out);
             if (!(Zn > 0.0) || !isfinite(Zn)) {
                 // zero residual mass (rounding): draw from the current target
                 if (t == 0) sh.flags |= SV_DATA_FALLBACK;
-                tok = (cur == nullptr) ? pass_draw<DT, kDrawMixture>(a, sh, rt, rq, nullptr, us, -1.0)
-                                       : pass_draw<DT, kDrawBuffer>(a, sh, rt, rq, cur, us, Z);
+                tok = (cur == nullptr) ? pass_draw<DT, kDrawMixture>(a, sh, phase, rt, rq, nullptr, us)
+                                       : pass_draw<DT, kDrawBuffer>(a, sh, phase, rt, rq, cur, us);
                 drawn = true;
                 break;
             }
@@ -487,11 +632,13 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
             continue;
         }
         // every child rejected: draw from the last residual
-        tok = pass_draw<DT, kDrawBuffer>(a, sh, rt, rq, cur, us, Z);
+        tok = pass_draw<DT, kDrawBuffer>(a, sh, phase, rt, rq, cur, us);
         if (tok < 0 && t == 0) sh.flags |= SV_DATA_BAD_ROW;
         done = true;
     }
     __syncthreads();
+    if (t == 0 && sh.broken) atomicOr(a.status, SV_DATA_SYNC);
+    if (g != 0) return;
     const int keep = min(depth, a.Dmax);
     for (int i = t; i <= a.Dmax; i += kMB) {
         int v = -1;
@@ -506,7 +653,13 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
     }
 }
 
-__global__ void k_multi_clear(int32_t *status) { *status = 0; }
+// Clears the status word and the trees' barrier counters.
+__global__ void k_multi_clear(int32_t *status, int *bar, int B) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
+    for (int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x); i < B;
+         i += static_cast<int>(gridDim.x * blockDim.x))
+        bar[i] = 0;
+}
 
 }  // namespace sv
 
@@ -514,7 +667,23 @@ namespace {
 
 using namespace sv;
 
-int64_t multi_layout_total(int B, int V) { return 256 + align256(int64_t(B) * 2 * V * int64_t(sizeof(float))); }
+// status word, barrier counters [B], published slots [B, kMaxG, 2, kSlot], residual rows [B, 2, V]
+int64_t multi_layout_bar() { return 256; }
+int64_t multi_layout_pub(int B) { return multi_layout_bar() + align256(int64_t(B) * int64_t(sizeof(int))); }
+int64_t multi_layout_buf(int B) {
+    return multi_layout_pub(B) + align256(int64_t(B) * kMaxG * 2 * kSlot * int64_t(sizeof(double)));
+}
+int64_t multi_layout_total(int B, int V) {
+    return multi_layout_buf(B) + align256(int64_t(B) * 2 * V * int64_t(sizeof(float)));
+}
+
+// Blocks per tree: the trees share the GPU's compute units (one 1024-thread
+// block fits a unit), each block keeping at least one tile of the row.
+int choose_g(int B, int V, int vec, int units) {
+    const int nvec = (V + vec - 1) / vec;
+    int G = std::max(1, std::min({kMaxG, units / std::max(B, 1), (nvec + kMB - 1) / kMB}));
+    return G;
+}
 
 }  // namespace
 
@@ -574,12 +743,31 @@ sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const vo
     a.accept_prob = accept_prob;
     char *ws = static_cast<char *>(workspace);
     a.status = status ? status : reinterpret_cast<int32_t *>(ws);
-    a.buf = reinterpret_cast<float *>(ws + 256);
-    hipLaunchKernelGGL(k_multi_clear, dim3(1), dim3(1), 0, stream, a.status);
-    if (dtype == SV_BF16)
-        hipLaunchKernelGGL(k_tree_multi<Bf16>, dim3(static_cast<unsigned>(B)), dim3(kMB), 0, stream, a);
-    else
-        hipLaunchKernelGGL(k_tree_multi<F32>, dim3(static_cast<unsigned>(B)), dim3(kMB), 0, stream, a);
+    a.bar = reinterpret_cast<int *>(ws + multi_layout_bar());
+    a.pub = reinterpret_cast<double *>(ws + multi_layout_pub(B));
+    a.buf = reinterpret_cast<float *>(ws + multi_layout_buf(B));
+    // co-resident blocks: all of a tree's blocks must run at once (they wait
+    // for one another), so G comes from the resident capacity and the launch
+    // is cooperative
+    const void *kern = dtype == SV_BF16 ? reinterpret_cast<const void *>(k_tree_multi<Bf16>)
+                                        : reinterpret_cast<const void *>(k_tree_multi<F32>);
+    int dev = 0, units = 0, per_unit = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&units, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, kern, kMB, 0) != hipSuccess)
+        return SV_EHIP;
+    a.G = choose_g(B, V, 16 / eb, units * std::max(per_unit, 0));
+    hipLaunchKernelGGL(k_multi_clear, dim3(static_cast<unsigned>(std::min<int64_t>(cdiv(B, 256), 1024))),
+                       dim3(256), 0, stream, a.status, a.bar, B);
+    const dim3 grid(static_cast<unsigned>(int64_t(B) * a.G));
+    if (a.G > 1) {
+        void *args[] = {&a};
+        if (hipLaunchCooperativeKernel(kern, grid, dim3(kMB), args, 0, stream) != hipSuccess) return SV_EHIP;
+    } else if (dtype == SV_BF16) {
+        hipLaunchKernelGGL(k_tree_multi<Bf16>, grid, dim3(kMB), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(k_tree_multi<F32>, grid, dim3(kMB), 0, stream, a);
+    }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
