@@ -90,8 +90,8 @@ typedef enum { SV_MIX_PROB = 0, SV_MIX_LOGIT = 1 } sv_mix_space;
 #define SV_DATA_FALLBACK    0x20 /* residual mass was zero after a rejection: sampled p~ instead */
 #define SV_DATA_DEPTH       0x40 /* accepted tree path deeper than Dmax: cut at Dmax nodes */
 #define SV_DATA_SYNC        0x80 /* sv_tree_verify_multi: a block of a tree gave up waiting for the
-                                    tree's other blocks (not expected: they are launched resident
-                                    together); that tree's outputs are invalid */
+                                    tree's other blocks (other work held the GPU's compute units);
+                                    the call's outputs are invalid */
 
 /* Human-readable name of a status code (static storage, host memory). */
 const char *sv_status_string(sv_status s);
@@ -382,11 +382,13 @@ sv_status sv_tree_verify_path_ex(const void *target_logits, int64_t ld_t,
  *  residual rows per request).
  *
  * Each tree is walked by G cooperating 1024-thread blocks (G up to 16, so
- * that B * G blocks fit the GPU at once; the launch is cooperative), each
- * owning a slice of the vocabulary: every sum over the vocabulary is a pass of
- * the blocks over their slices, combined at a barrier of the tree's blocks.
- * The call is bound by that chain of passes rather than by HBM bandwidth.
- * SV_DATA_SYNC reports a block that stopped waiting at such a barrier.
+ * that B * G blocks fit the GPU at once), each owning a slice of the
+ * vocabulary: every sum over the vocabulary is a pass of the blocks over their
+ * slices, combined at a barrier of the tree's blocks.  The call is bound by
+ * that chain of passes rather than by HBM bandwidth.  A tree's blocks wait
+ * for one another: if other work on the GPU keeps some of them from starting
+ * for about a second, the waiting blocks give up and SV_DATA_SYNC marks the
+ * call's outputs invalid (rerun it when the GPU is free).
  */
 size_t sv_tree_multi_workspace_bytes(int B, int N, int V);
 sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t,

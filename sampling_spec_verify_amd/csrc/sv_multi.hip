@@ -45,7 +45,7 @@ constexpr int kMU = 2;                    // tiles of a pass in flight per threa
 constexpr int kMNodes = SV_MAX_TREE_NODES + 1;
 constexpr int kMaxG = 16;                 // blocks per tree at most
 constexpr int kSlot = 4;                  // doubles a block publishes per barrier
-constexpr int kSpinLimit = 1 << 15;       // polls of a barrier before it is given up
+constexpr int kSpinLimit = 1 << 20;       // polls of a barrier before it is given up (about 1 s)
 
 struct MultiArgs {
     const char *tgt, *drf;
@@ -147,9 +147,10 @@ __device__ __forceinline__ Scan mblock_scan(double v, double carry, MultiShared 
 // stores, coherent loads): a block publishes, drains its stores, arrives at
 // the tree's counter and polls it until all G blocks have arrived; published
 // slots alternate with the barrier's parity, so a slot is rewritten only after
-// every block has read it.  The launch is cooperative (all blocks resident),
-// and a poll gives up after kSpinLimit rounds, marking the block broken, so
-// every wave ends.
+// every block has read it.  The grid is sized to the GPU's resident capacity
+// (one 1024-thread block per compute unit), so on a GPU without other work
+// every block runs at once; a poll gives up after kSpinLimit rounds, marking
+// the block broken (SV_DATA_SYNC), so every wave ends in any case.
 
 struct Slice {
     int lo, hi;                            // vectors [lo, hi)
@@ -746,9 +747,9 @@ sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const vo
     a.bar = reinterpret_cast<int *>(ws + multi_layout_bar());
     a.pub = reinterpret_cast<double *>(ws + multi_layout_pub(B));
     a.buf = reinterpret_cast<float *>(ws + multi_layout_buf(B));
-    // co-resident blocks: all of a tree's blocks must run at once (they wait
-    // for one another), so G comes from the resident capacity and the launch
-    // is cooperative
+    // all of a tree's blocks must run at once (they wait for one another), so
+    // B * G stays within the resident capacity.  An ordinary launch: a
+    // cooperative one guarantees residency but costs about 20 us per call here
     const void *kern = dtype == SV_BF16 ? reinterpret_cast<const void *>(k_tree_multi<Bf16>)
                                         : reinterpret_cast<const void *>(k_tree_multi<F32>);
     int dev = 0, units = 0, per_unit = 0;
@@ -760,10 +761,7 @@ sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const vo
     hipLaunchKernelGGL(k_multi_clear, dim3(static_cast<unsigned>(std::min<int64_t>(cdiv(B, 256), 1024))),
                        dim3(256), 0, stream, a.status, a.bar, B);
     const dim3 grid(static_cast<unsigned>(int64_t(B) * a.G));
-    if (a.G > 1) {
-        void *args[] = {&a};
-        if (hipLaunchCooperativeKernel(kern, grid, dim3(kMB), args, 0, stream) != hipSuccess) return SV_EHIP;
-    } else if (dtype == SV_BF16) {
+    if (dtype == SV_BF16) {
         hipLaunchKernelGGL(k_tree_multi<Bf16>, grid, dim3(kMB), 0, stream, a);
     } else {
         hipLaunchKernelGGL(k_tree_multi<F32>, grid, dim3(kMB), 0, stream, a);
