@@ -266,3 +266,16 @@ def test_read_stream_rejects_bad_arguments():
     assert L.sv_read_stream(buf, 0, sink, None, None, None) == sv.SV_EINVAL
     assert L.sv_read_stream(buf, 1000, sink, None, None, None) == sv.SV_EINVAL
     assert L.sv_read_stream(ctypes.c_void_p(0x10008), 1024, sink, None, None, None) == sv.SV_EINVAL
+
+
+def test_data_flags_match_the_header():
+    text = open(HEADER).read()
+    macros = {int(v, 16): n for n, v in re.findall(r"#define SV_DATA_([A-Z_]+)\s+(0x[0-9a-fA-F]+)", text)}
+    assert macros == sv.DATA_FLAGS
+    assert sv.decode_flags(0x82) == ["BAD_ROW", "SYNC"]
+
+
+def test_header_constants_match_the_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define SV_MAX_POSITIONS\s+(\d+)", text).group(1)) == sv.SV_MAX_POSITIONS
+    assert int(re.search(r"#define SV_MAX_TREE_NODES\s+(\d+)", text).group(1)) == sv.SV_MAX_TREE_NODES
