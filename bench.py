@@ -94,8 +94,9 @@ def parse():
                     help="bound on the all-cores oracle run (a fork pool over requests, taken "
                          "before the GPU is touched); 0 disables")
     ap.add_argument("--graph", type=int, default=0, metavar="REPLAYS",
-                    help="chain workloads: also time REPLAYS replays of a HIP graph holding one "
-                         "call per rotated buffer set (steady state without launch gaps)")
+                    help="chain, greedy tree and mask workloads: also time REPLAYS replays of a "
+                         "HIP graph holding one call per rotated buffer set (64 mask calls) - "
+                         "the steady state without host launch gaps")
     ap.add_argument("--no-stream-ceiling", action="store_true",
                     help="skip the same-run read-stream ceiling measurement")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -216,15 +217,15 @@ def cpu_pool_baseline(x, tree, seconds, space="prob", cores=None):
             "seconds": round(wall, 2)}
 
 
-def graph_steady_state(x, tgts, drfs, tok, ua, us, dl, space, R, replays, torch, sv):
-    """One HIP graph holding one chain call per rotated buffer set, replayed
-    ``replays`` times; every replay's outputs are checked against an eager run."""
+def graph_replay(calls, stream, replays, units, torch, launches_per_call=1):
+    """One HIP graph holding every call of ``calls`` (bound to ``stream``) in order,
+    replayed ``replays`` times; before timing, three replays are each checked
+    against an eager run, with the outputs overwritten between replays.
+    ``units`` counts the positions (or nodes) one call verifies."""
     import numpy as np
 
-    s = torch.cuda.Stream()
+    s = stream
     with torch.cuda.stream(s):
-        calls = [sv.ChainCall(tgts[i], drfs[i], tok, ua, us, x.lam, x.temperature, dl,
-                              stream=s, space=space) for i in range(R)]
         for c in calls:
             c.run()
     s.synchronize()
@@ -237,8 +238,9 @@ def graph_steady_state(x, tgts, drfs, tok, ua, us, dl, space, R, replays, torch,
     for _ in range(3):
         with torch.cuda.stream(s):
             for c in calls:                 # eager work between replays: clobber the outputs
-                for o in c.out:
-                    o.fill_(-7)
+                for name, o in zip(c.out._fields, c.out):
+                    if name != "status":    # the mask call ORs into its status word
+                        o.fill_(-7)
             g.replay()
         s.synchronize()
         for c, r in zip(calls, ref):
@@ -252,10 +254,9 @@ def graph_steady_state(x, tgts, drfs, tok, ua, us, dl, space, R, replays, torch,
             g.replay()
         ev1.record()
     s.synchronize()
-    us_call = ev0.elapsed_time(ev1) * 1e3 / (replays * R)
-    return {"calls_per_graph": R, "replays": replays, "us_per_call": us_call,
-            "positions_per_s": x.positions() / (us_call * 1e-6),
-            "replays_match_eager": bool(match)}
+    us_call = ev0.elapsed_time(ev1) * 1e3 / (replays * len(calls))
+    return {"calls_per_graph": len(calls), "replays": replays, "us_per_call": us_call,
+            "units_per_s": units / (us_call * 1e-6), "replays_match_eager": bool(match)}
 
 
 def cpu_baseline_chain(x, seconds, gpu_out, space="prob"):
@@ -362,6 +363,12 @@ def bench_mask(args):
     par = torch.from_numpy(x.parent).to("cuda:0")
     call = sv.TreeMaskCall(par, x.N)
     W = call.out.mask.shape[2]
+    graph = None
+    if args.graph > 0:
+        gs = torch.cuda.Stream()
+        with torch.cuda.stream(gs):
+            gcall = sv.TreeMaskCall(par, x.N, stream=gs)
+        graph = graph_replay([gcall] * 64, gs, args.graph, x.B * x.N, torch)
     algo_bytes = 4 * (x.B * x.N + x.B * (x.N + 1) * W + x.B * (x.N + 1))
     for _ in range(args.warmup):
         call.run()
@@ -402,6 +409,7 @@ def bench_mask(args):
                                       f"timed step ({len(kern)} launches)",
                      "note": "launch-latency bound: a few KB per call"},
         "cpu_baseline": cpu, "gpu_ms_per_step": ev0.elapsed_time(ev1) / K,
+        "graph_steady_state": graph,
         "status_word": int(call.out.status[0].item()), "parity_sample": parity,
     }
     print(json.dumps(line), flush=True)
@@ -665,9 +673,15 @@ def main():
     status = int(out.status[0].item())
     gpu_out = [o.cpu().numpy() for o in out]
     graph = None
-    if args.graph > 0 and not tree:
-        graph = graph_steady_state(x, tgts, drfs, tok, ua, us, dl, args.space, R, args.graph,
-                                   torch, sv)
+    if args.graph > 0:
+        gs = torch.cuda.Stream()
+        with torch.cuda.stream(gs):
+            if tree:
+                gcalls = [sv.TreeGreedyCall(tgts[i], par, ntok, x.Dmax, stream=gs) for i in range(R)]
+            else:
+                gcalls = [sv.ChainCall(tgts[i], drfs[i], tok, ua, us, x.lam, x.temperature, dl,
+                                       stream=gs, space=args.space) for i in range(R)]
+        graph = graph_replay(gcalls, gs, args.graph, positions, torch)
     ceiling = None
     if not args.no_stream_ceiling:
         ceiling = read_stream_ceiling(algo_bytes, torch, sv)
