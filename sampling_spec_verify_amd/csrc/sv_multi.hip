@@ -27,7 +27,9 @@
 // residual after a rejection (written to a ping-pong fp32 buffer of the
 // workspace with its fp64 mass), and an inverse CDF over slice totals, then
 // within the slice holding the draw.  Acceptance of the first child uses the
-// gathered logits in fp64; later children read the stored residual.
+// gathered logits in fp64; a later child forms the residual at its token again
+// with the residual pass's own operations (bitwise the stored value), so no
+// block reads another block's slice of the residual.
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <math.h>
@@ -70,6 +72,7 @@ struct MultiShared {
     int head[kMNodes];                    // first child of a node (node order), -1: none
     int next[kMNodes];                    // next sibling, -1: none
     int tok[kMNodes];
+    double zs[kMNodes];                   // residual masses of the current node, in order
     int path[SV_MAX_POSITIONS + 1];
     double red[kMW];
     float redf[kMW];
@@ -204,13 +207,6 @@ __device__ void tree_barrier(const MultiArgs &a, MultiShared &sh, int &phase, in
     __syncthreads();
 }
 
-__device__ __forceinline__ float load_coherent(const float *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_coherent(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ---- element values -----------------------------------------------------
 
 template <class DT>
@@ -340,8 +336,9 @@ __device__ void pass_stats(const MultiArgs &a, MultiShared &sh, int &phase, cons
 
 // Residual after a rejection: w(v) = max(0, r(v) - q(v)) with r = p~ (first
 // rejection, from the logits) or the previous residual in[v] / Zin; w is
-// stored (fp32, coherent stores: the child tests of every block read it) in
-// out, and its fp64 sum over the tree's slices returned.
+// stored (fp32) in out, where only this block reads it again (its slice), and
+// its fp64 sum over the tree's slices returned.  The child tests form w at a
+// child's token again from the same values and operations.
 template <class DT>
 __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, int &phase, const char *row_t,
                                 const char *row_q, const float *in, double Zin, float *out) {
@@ -370,9 +367,9 @@ __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, int &phase,
                 if (v >= V) break;
                 double pm, q;
                 m_probs<DT>(a, sh, ft[e], fq[e], pm, q);
-                const double r = (in == nullptr) ? pm : static_cast<double>(load_coherent(&in[v])) / Zin;
+                const double r = (in == nullptr) ? pm : static_cast<double>(in[v]) / Zin;
                 const float w = static_cast<float>(fmax(0.0, r - q));
-                store_coherent(&out[v], w);
+                out[v] = w;
                 tot += static_cast<double>(w);
             }
         }
@@ -393,7 +390,7 @@ template <class DT, int KIND>
 __device__ __forceinline__ double draw_weight(const MultiArgs &a, const MultiShared &sh, float zt,
                                               float zq, const float *buf, int v) {
     if (KIND == kDrawBonus) return static_cast<double>(m_pow2(zt, a.c_hi, a.c_lo, static_cast<float>(sh.sA)));
-    if (KIND == kDrawBuffer) return static_cast<double>(load_coherent(&buf[v]));
+    if (KIND == kDrawBuffer) return static_cast<double>(buf[v]);
     double pm, q;
     m_probs<DT>(a, sh, zt, zq, pm, q);
     return pm;
@@ -561,6 +558,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
         // test the children in node order
         float *cur = nullptr;            // stored residual (NULL: r = p~)
         double Z = 1.0;
+        int nrej = 0;                    // residuals formed at this node; their masses in sh.zs
         int c = first, nxt = -1;
         bool drawn = false;
         while (c >= 0) {
@@ -587,9 +585,13 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
                             r = (1.0 - static_cast<double>(a.lam)) * pt + static_cast<double>(a.lam) * q;
                         }
                     } else {
+                        // the stored residual at x, formed again with the residual
+                        // pass's own operations from p~(x), q(x) and the masses
                         double pm;
                         m_probs<DT>(a, sh, zt, zq, pm, q);
-                        r = static_cast<double>(load_coherent(&cur[x])) / Z;
+                        r = pm;
+                        for (int j = 1; j <= nrej; ++j)
+                            r = static_cast<double>(static_cast<float>(fmax(0.0, r - q))) / sh.zs[j];
                     }
                     if (q == 0.0) {
                         sh.flags |= SV_DATA_ZERO_Q;
@@ -621,6 +623,8 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
             }
             cur = out;
             Z = Zn;
+            ++nrej;
+            if (t == 0) sh.zs[nrej] = Zn;
             c = sh.next[c];
             __syncthreads();
         }
