@@ -97,6 +97,8 @@ SMALL = [
     (12, 256, 3, 1500, "fp32", 0.2, 0.8, True, None),
     (13, 257, 3, 2000, "bf16", 0.0, 1.0, True, None),
     (14, 300, 2, 1200, "bf16", 0.6, 1.1, True, None),
+    # a large batch: thousands of blocks in every launch, the unpacked job order
+    (17, 4096, 4, 1000, "fp32", 0.2, 0.9, True, None),
     # the largest vocabularies the validator accepts (bf16 2^21, fp32 2^20): LDS
     # staging is off, and the locate holds 16 piece masses per thread
     (15, 2, 3, 1 << 21, "bf16", 0.0, 1.0, False, None),
@@ -198,6 +200,7 @@ def test_status_bad_row():
     (1, 6, 12, 50, "fp32", True), (2, 4, 30, 20000, "fp32", True), (3, 5, 20, 9000, "bf16", False),
     (4, 3, 1, 4, "fp32", True), (5, 2, 200, 100, "bf16", True), (6, 8, 0, 500, "fp32", False),
     (7, 2, 1024, 300, "bf16", False),
+    (8, 2048, 12, 500, "bf16", False),
 ])
 def test_greedy_random_trees(seed, B, N, V, dtype, ints):
     x = synth.make_random_tree(300 + seed, B, N, V, dtype, int_logits=ints)
