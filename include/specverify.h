@@ -138,7 +138,8 @@ sv_status sv_chain_verify(const void *target_logits, int64_t ld_t,
  * interleave them.  Same arguments and meaning; sv_chain_row_stats streams the
  * drafted rows once and reduces each to (max, sum of exponentials);
  * sv_chain_accept_resample must follow it on the same stream with the same
- * workspace and resolves acceptance, resamples and writes the outputs.
+ * workspace and resolves acceptance, resamples and writes the outputs; it
+ * may be repeated on the same statistics (for instance with new uniforms).
  */
 sv_status sv_chain_row_stats(const void *target_logits, int64_t ld_t,
                              const void *draft_logits, int64_t ld_q,

@@ -1097,9 +1097,13 @@ __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int stage
     // the last of the request's C2 blocks to finish draws the token
     __builtin_amdgcn_s_waitcnt(0);          // this thread's record stores are done
     __syncthreads();
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         last = __hip_atomic_fetch_add(&a.count[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                a.C2 - 1;
+        // every block of the request has counted: zero again, so that this
+        // launch may be repeated on the same statistics (new uniforms)
+        if (last) __hip_atomic_store(&a.count[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
     if (!last || threadIdx.x >= kBlock) return;   // uniform, then whole waves
     draw_request<DT, NV2>(a, b, r, S, L);

@@ -152,6 +152,24 @@ def test_stage_calls_equal_full_call():
         np.testing.assert_array_equal(a, b)
 
 
+def test_resample_stage_repeats_on_the_same_statistics():
+    """One row-statistics launch, then the accept / resample launch twice with
+    different uniforms written in place: each run matches the oracle for its
+    own uniforms (the hand-over counters of the draw reset themselves)."""
+    x = synth.make_chain(206, 7, 4, 30000, "bf16", ragged=True, lam=0.2, sigma_q=(0.3, 2.0))
+    call = chain_call(x)
+    call.row_stats()
+    rng = np.random.default_rng(207)
+    for rep in range(3):
+        if rep:
+            x.u_accept = rng.random(x.u_accept.shape, dtype=np.float32)
+            x.u_sample = rng.random(x.u_sample.shape, dtype=np.float32)
+            call.inputs[4].copy_(torch.from_numpy(x.u_accept).to(call.inputs[4].device))
+            call.inputs[5].copy_(torch.from_numpy(x.u_sample).to(call.inputs[5].device))
+        g = to_host(call.accept_resample())
+        report(f"repeat{rep}", compare_chain(x, g, oracle_chain(x)))
+
+
 def test_bitwise_deterministic():
     x = synth.make_chain(205, 16, 8, 50000, "bf16", ragged=True, lam=0.3)
     a = run_chain(x)
