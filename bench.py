@@ -80,7 +80,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="c4",
-                    choices=["c1", "c2", "c3", "c4", "c5", "c5mask", "c5multi"])
+                    choices=["c1", "c2", "c3", "c4", "c5", "c5path", "c5mask", "c5multi"])
     ap.add_argument("--alpha", action="store_true",
                     help="chain workloads: time the acceptance-rate call instead of the verify call")
     ap.add_argument("--space", default="prob", choices=["prob", "logit"],
@@ -558,7 +558,97 @@ def bench_multi(args):
         "gpu_ms_per_step": ev0.elapsed_time(ev1) / K, "cpu_baseline": cpu,
         "parity_sample": parity, "status_word": int(g[4][0]),
         "accepted_depths": g[0].tolist(),
-        "note": "one 1024-thread block per tree walks it; bound by the walk's latency",
+        "note": "up to 16 cooperating 1024-thread blocks walk each tree; bound by the chain "
+                "of barriers between the walk's vocabulary passes",
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_path(args):
+    """Path mode on the c5 trees: chain acceptance along each tree's seeded root-to-leaf
+    path (target rows [0, n_1..n_d], draft rows [0, n_1..n_{d-1}]); one call per step."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sampling_spec_verify_amd import specverify as sv
+    from sampling_spec_verify_amd import synth
+
+    sv.lib()
+    x = synth.config("c5")
+    dev = "cuda:0"
+    elem = 2 if x.dtype == "bf16" else 4
+    # drafted positions of each path: its node ids up to the -1 terminator
+    dlen = np.array([int(np.argmax(np.append(p, -1) < 1)) for p in x.path])
+    positions = int(dlen.sum())
+    algo_bytes = 2 * x.V * elem * positions          # the row-statistics stream
+    R = max(2, min(512, math.ceil(ROTATE_BYTES / (x.target.nbytes + x.draft.nbytes))))
+    tgts = device_copies(x.target, x.dtype, R, torch)
+    drfs = device_copies(x.draft, x.dtype, R, torch)
+    tok = torch.from_numpy(x.node_token).to(dev)
+    path = torch.from_numpy(x.path).to(dev)
+    ua = torch.from_numpy(x.u_accept).to(dev)
+    us = torch.from_numpy(x.u_sample).to(dev)
+    calls = [sv.TreePathCall(tgts[i], drfs[i], tok, path, ua, us, x.lam, x.temperature,
+                             space=args.space) for i in range(R)]
+    for i in range(args.warmup):
+        calls[i % R].run()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(K):
+        calls[i % R].run()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    g = [o.cpu().numpy() for o in calls[0].out]
+    graph = None
+    if args.graph > 0:
+        gs = torch.cuda.Stream()
+        with torch.cuda.stream(gs):
+            gcalls = [sv.TreePathCall(tgts[i], drfs[i], tok, path, ua, us, x.lam, x.temperature,
+                                      stream=gs, space=args.space) for i in range(R)]
+        graph = graph_replay(gcalls, gs, args.graph, positions, torch)
+    cpu, parity = None, None
+    if args.cpu_seconds > 0:
+        t, d = x.widened(x.target), x.widened(x.draft)
+        done = pos = mism = flagged = 0
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < args.cpu_seconds:
+            b = done % x.B
+            r = oracle.tree_path_one(t[b], d[b], x.node_token[b], x.path[b], x.u_accept[b],
+                                     x.u_sample[b], x.lam, x.temperature, args.space)
+            if done < x.B:
+                ref = np.full(x.path.shape[1] + 1, -1, dtype=np.int32)
+                ref[:len(r.tokens)] = r.tokens
+                same = g[0][b] == r.accepted and np.array_equal(g[1][b], ref)
+                flagged += int(r.flagged)
+                mism += int(not same and not r.flagged)
+            pos += int(dlen[b])
+            done += 1
+        el = time.perf_counter() - t1
+        cpu = {"value": pos / el, "unit": UNIT, "cores": 1, "kind": "oracle",
+               "sample": f"{done} oracle path verifications ({pos} drafted positions) cycling "
+                         f"over the {x.B} trees, fp64 numpy, one process",
+               "seconds": round(el, 2)}
+        parity = {"requests_checked": min(done, x.B), "flagged": flagged,
+                  "unflagged_mismatches": mism}
+    line = {
+        "metric": "verified path positions/sec through path-mode tree verification",
+        "value": positions * K / wall, "unit": UNIT, "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / K, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"c5path: {synth.CONFIGS['c5']}, seeded root-to-leaf paths",
+                   "path_lengths": dlen.tolist(), "mixture_space": args.space,
+                   "lambda": x.lam, "temperature": x.temperature, "buffer_sets_rotated": R},
+        "step_hbm_gbps": algo_bytes * K / (wall * 1e9),
+        "step_hbm_frac": algo_bytes * K / (wall * 1e9) / PEAK_HBM_GBS,
+        "algorithmic_bytes_per_step": algo_bytes, "gpu_ms_per_step": ev0.elapsed_time(ev1) / K,
+        "graph_steady_state": graph, "cpu_baseline": cpu, "parity_sample": parity,
+        "status_word": int(g[3][0]),
     }
     print(json.dumps(line), flush=True)
 
@@ -578,6 +668,9 @@ def main():
         return
     if args.workload == "c5multi":
         bench_multi(args)
+        return
+    if args.workload == "c5path":
+        bench_path(args)
         return
     if args.alpha:
         bench_alpha(args)

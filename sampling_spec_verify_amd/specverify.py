@@ -454,40 +454,57 @@ def tree_attention_mask(parent, N: Optional[int] = None, mask_words: Optional[in
     return TreeMaskCall(parent, N, mask_words, stream, status).run()
 
 
+class TreePathCall:
+    """A path-mode call (chain acceptance along one root->leaf path of each
+    tree) with its outputs and workspace bound once (see ChainCall)."""
+
+    def __init__(self, target, draft, node_token, path, u_accept, u_sample, lam: float = 0.0,
+                 temperature: float = 1.0, stream=None, workspace=None, space: str = "prob"):
+        torch = _torch()
+        B, N1, V = target.shape
+        N = N1 - 1
+        Dmax = path.shape[1]
+        ld_t = _rows(target, B, N + 1, V, "target")
+        ld_q = _rows(draft, B, N + 1, V, "draft")
+        if draft.dtype != target.dtype:
+            raise TypeError("target and draft logits must share a dtype")
+        _i32(node_token, (B, N), "node_token")
+        _i32(path, (B, Dmax), "path")
+        _f32(u_accept, (B, Dmax), "u_accept")
+        _f32(u_sample, (B,), "u_sample")
+        if space not in MIX_SPACES:
+            raise ValueError(f"space must be one of {sorted(MIX_SPACES)}, got {space!r}")
+        self.space = space
+        dev = target.device
+        self.out = ChainOut(torch.empty(B, dtype=torch.int32, device=dev),
+                            torch.empty(B, Dmax + 1, dtype=torch.int32, device=dev),
+                            torch.empty(B, Dmax, dtype=torch.float32, device=dev),
+                            torch.empty(1, dtype=torch.int32, device=dev))
+        self.workspace = workspace if workspace is not None else torch.empty(
+            max(tree_workspace_bytes(B, N, V), 16), dtype=torch.uint8, device=dev)
+        self.inputs = (target, draft, node_token, path, u_accept, u_sample)
+        o = self.out
+        self._cached = (_ptr(target), ld_t, _ptr(draft), ld_q, _dtype_code(target), B, N, V,
+                        _ptr(node_token), _ptr(path), Dmax, _ptr(u_accept), _ptr(u_sample),
+                        float(lam), float(temperature), _ptr(o.accepted), _ptr(o.out_tokens),
+                        _ptr(o.accept_prob), _ptr(o.status), _ptr(self.workspace),
+                        self.workspace.numel(), _stream(stream))
+
+    def run(self) -> ChainOut:
+        if self.space == "prob":
+            _check(lib().sv_tree_verify_path(*self._cached), "sv_tree_verify_path")
+        else:
+            _check(lib().sv_tree_verify_path_ex(*self._cached, MIX_SPACES[self.space]),
+                   "sv_tree_verify_path_ex")
+        return self.out
+
+
 def tree_verify_path(target, draft, node_token, path, u_accept, u_sample, lam: float = 0.0,
                      temperature: float = 1.0, stream=None, workspace=None,
                      space: str = "prob") -> ChainOut:
     """sv_tree_verify_path: target / draft [B, N+1, V], path [B, Dmax] (-1 terminated)."""
-    torch = _torch()
-    B, N1, V = target.shape
-    N = N1 - 1
-    Dmax = path.shape[1]
-    ld_t = _rows(target, B, N + 1, V, "target")
-    ld_q = _rows(draft, B, N + 1, V, "draft")
-    if draft.dtype != target.dtype:
-        raise TypeError("target and draft logits must share a dtype")
-    _i32(node_token, (B, N), "node_token")
-    _i32(path, (B, Dmax), "path")
-    _f32(u_accept, (B, Dmax), "u_accept")
-    _f32(u_sample, (B,), "u_sample")
-    dev = target.device
-    out = ChainOut(torch.empty(B, dtype=torch.int32, device=dev),
-                   torch.empty(B, Dmax + 1, dtype=torch.int32, device=dev),
-                   torch.empty(B, Dmax, dtype=torch.float32, device=dev),
-                   torch.empty(1, dtype=torch.int32, device=dev))
-    ws = workspace if workspace is not None else torch.empty(
-        max(tree_workspace_bytes(B, N, V), 16), dtype=torch.uint8, device=dev)
-    if space not in MIX_SPACES:
-        raise ValueError(f"space must be one of {sorted(MIX_SPACES)}, got {space!r}")
-    args = (_ptr(target), ld_t, _ptr(draft), ld_q, _dtype_code(target), B, N, V, _ptr(node_token),
-            _ptr(path), Dmax, _ptr(u_accept), _ptr(u_sample), float(lam), float(temperature),
-            _ptr(out.accepted), _ptr(out.out_tokens), _ptr(out.accept_prob), _ptr(out.status),
-            _ptr(ws), ws.numel(), _stream(stream))
-    if space == "prob":
-        _check(lib().sv_tree_verify_path(*args), "sv_tree_verify_path")
-    else:
-        _check(lib().sv_tree_verify_path_ex(*args, MIX_SPACES[space]), "sv_tree_verify_path_ex")
-    return out
+    return TreePathCall(target, draft, node_token, path, u_accept, u_sample, lam, temperature,
+                        stream, workspace, space).run()
 
 
 class TreeMultiOut(NamedTuple):
