@@ -939,10 +939,9 @@ __device__ __forceinline__ int locate(const SampleCtx &S, const LocatePieces &P,
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
             if (w[e] > 0.0f) last = e;
-        if (last >= 0) atomicMax(&L.lastpos, static_cast<int>(gv * VEC + last));
+        int pick = -1;
         if (excl <= tp && tp < x) {
             double cum = excl;
-            int pick = -1;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 if (w[e] > 0.0f) {
@@ -951,7 +950,24 @@ __device__ __forceinline__ int locate(const SampleCtx &S, const LocatePieces &P,
                 }
             }
             if (pick < 0) pick = last;
-            if (pick >= 0) atomicMin(&L.tok, static_cast<int>(gv * VEC + pick));
+        }
+        // The lanes hold the piece's vectors in index order.  The token is
+        // the pick of the lowest lane whose interval holds tp (the intervals
+        // tile the piece, so there is at most one such lane); the fallback is
+        // the last positive weight of the highest lane that has one.  Ballots
+        // and lane reads, not LDS atomics: an atomic from every lane runs as
+        // a serial loop over the lanes.
+        const int base = static_cast<int>(gv * VEC);
+        const int tok_v = base + pick, last_v = base + last;
+        const unsigned long long own = __ballot(pick >= 0);
+        const unsigned long long pos = __ballot(last >= 0);
+        const int tok_l = own ? __builtin_amdgcn_readlane(tok_v, __ffsll(static_cast<long long>(own)) - 1)
+                              : INT_MAX;
+        const int last_l = pos ? __builtin_amdgcn_readlane(last_v, 63 - __clzll(static_cast<long long>(pos)))
+                               : -1;
+        if (lane == 0) {
+            L.tok = tok_l;
+            L.lastpos = last_l;
         }
     }
     __syncthreads();
