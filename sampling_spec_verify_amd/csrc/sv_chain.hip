@@ -30,21 +30,22 @@
 //     row n (the same normalised law as max(0, p~ - q), since
 //     p~ - q = (1 - lambda)(p_t - q)), or the bonus softmax(z/T) at the
 //     request's last target row, to fp64 sums of its 16 * NV2 pieces, and
-//     publishes them as agent-scope atomic stores.  The last of the request's
-//     C2 blocks to count itself done (one atomic counter per request) draws
-//     the token with its first 256 threads: it loads every piece mass in one
-//     round (up to kLocPP per thread), scales them to a common frame, finds
-//     the piece holding u * W with one monotone fp64 block scan over
-//     per-thread totals and a walk inside the owning thread, reloads that
-//     piece's 64 vectors and finds the token with a lane scan.
+//     publishes them as agent-scope atomic stores.  Every block then counts
+//     itself done (one atomic counter per request); wave 0 of the last of
+//     the request's C2 blocks draws the token alone: it loads every piece
+//     mass in one round (runs of consecutive pieces per lane, staged in LDS),
+//     scales them to a common frame, finds the run and then the piece holding
+//     u * W with two fp64 wave scans, reloads that piece's 64 vectors and
+//     finds the token with a third.
 //
 // The only data that crosses blocks inside a launch are those piece masses:
 // written and read as relaxed agent-scope atomics (write-through stores,
 // coherent loads), drained before the counter is bumped, so no device-wide
 // cache writeback is needed.  A separate launch for the draw costs about as
 // much as the draw itself on this GPU (every kernel carries a fixed cost of
-// a few microseconds).  Every reduction has a fixed order (bitwise
-// reproducible): which block draws does not change the result.
+// a few microseconds).  The draw itself is all wave-level scans, ballots and
+// lane reads, with no block barrier.  Every reduction has a fixed order
+// (bitwise reproducible): which block draws does not change the result.
 //
 // Path mode reuses both launches with a row indirection: position j of a
 // request uses target and draft row n_j of its draft tree (n_0 = root).
@@ -721,8 +722,7 @@ __device__ __forceinline__ void resolve_request(const ChainArgs &a, int b, Resol
             rej = !(static_cast<double>(sh.u[i]) < acc_p);
         }
         const unsigned long long mask = __ballot(rej);
-        int fl_all = fl;
-        for (int off = 1; off < kWave; off <<= 1) fl_all |= __shfl_xor(fl_all, off, kWave);
+        const int fl_all = wave_or8(fl);
         if (lane == 0) {
             sh.n = mask ? (__ffsll(static_cast<long long>(mask)) - 1) : K;
             sh.flags |= fl_all;
@@ -805,234 +805,222 @@ __device__ __forceinline__ void chunk_pieces(const SampleCtx &S, int c, double *
     if (threadIdx.x == 0) publish(&rec[0], static_cast<double>(s_rec));
 }
 
-struct LocateShared {
-    double d4[kWaves];
-    float f4[kWaves];
-    int pstar, tok, lastpos;
-    float spick;
-    double excl, scale;
-};
+// The draw runs on one wavefront: wave 0 of the block that counts its
+// request's mass blocks complete.  Every step below is a wave-level scan, ballot or lane
+// read; the only memory round trips are the piece masses (coherent loads)
+// and the reload of the chosen piece.
+//
+// Intervals: the pieces of the sampling row, in index order, are cut into
+// 64 runs of pp consecutive pieces, one run per lane.  The lanes' run masses
+// are scanned in lane order, so the lane intervals [excl, incl) tile [0, W);
+// inside the run that holds t = u * W the pieces are scanned again, one per
+// lane, from the run's lower bound, and the run's last piece ends at the
+// run's upper bound, so the piece intervals tile the run.  Rounding can still
+// leave t past the last piece's lower bound with no owner: then the run's
+// last positive piece is taken.  Every sum has a fixed order, so the draw is
+// bitwise reproducible.
 
-// Pieces of the request held by one locate thread (thread t owns the
-// contiguous pieces [t * pp, (t + 1) * pp), pp = ceil(np / kBlock) <= kLocPP).
-struct LocatePieces {
-    double m[kLocPP];       // piece mass in its chunk's frame
-    float s[kLocPP];        // the chunk's shift
-};
-
-// One load round: every piece mass this thread owns and its chunk's shift.
-template <int NV2>
-__device__ __forceinline__ void load_pieces(const ChainArgs &a, int b, int pp, LocatePieces &P) {
-    constexpr int kPieces = kWaves2 * NV2;
-    const double *cr = a.chunks + int64_t(b) * a.C2 * a.rec_stride;
-    const int np = a.C2 * kPieces;
-    const int p0 = threadIdx.x * pp;
-#pragma unroll
-    for (int j = 0; j < kLocPP; ++j) {
-        P.m[j] = 0.0;
-        P.s[j] = -INFINITY;
-        if (j < pp) {                        // pp is uniform: whole iterations are skipped
-            const int p = p0 + j;
-            if (p < np) {
-                const double *rc = cr + int64_t(p / kPieces) * a.rec_stride;
-                P.m[j] = collect(&rc[2 + p % kPieces]);
-                P.s[j] = static_cast<float>(collect(&rc[0]));
-            }
-        }
-    }
-}
-
-// Inverse CDF over the request's pieces: scale every chunk to the common
-// frame 2^(-max shift) (bonus rows only; residual chunks share shift 0), one
-// fp64 block scan over per-thread totals, a sequential walk inside the owning
-// thread, then a lane scan inside the chosen piece.  The interval of a piece
-// is [prefix before it, prefix after it); the first and last boundary of each
-// thread are the block scan's, so the intervals tile [0, W) and the owner is
-// unique.  Every thread must call this; returns -1 when the row carries no
-// positive mass.
+// Wave-level inverse CDF over the request's piece masses (staged in LDS:
+// np doubles, then np floats of chunk shifts for the bonus row), then over
+// the chosen piece's 64 vectors.  Returns -1 when the row has no positive
+// mass.  All lanes of the wave must call this; the result is wave-uniform.
 template <class DT, int MODE, int NV2>
-__device__ __forceinline__ int locate(const SampleCtx &S, const LocatePieces &P, int pp, double u,
-                                      LocateShared &L) {
+__device__ __forceinline__ int locate_wave(const ChainArgs &a, int b, const SampleCtx &S, double u,
+                                           double *stage) {
     constexpr int VEC = DT::kVec;
     constexpr int kPieces = kWaves2 * NV2;
+    const int lane = threadIdx.x & (kWave - 1);
+    const double *cr = a.chunks + int64_t(b) * a.C2 * a.rec_stride;
+    const int np = a.C2 * kPieces;
+    const int pp = (np + kWave - 1) / kWave;        // pieces per lane run, <= kMaxPieces / 64
+    float *sstage = reinterpret_cast<float *>(stage + np);
+    const int p0 = lane * pp;
+    // 1. this lane's run: piece masses (and, for the bonus row, chunk shifts)
+    double tot = 0.0;
+    float sm = -INFINITY;
+#pragma unroll 16
+    for (int j = 0; j < pp; ++j) {
+        const int p = p0 + j;
+        if (p < np) {
+            const double *rc = cr + int64_t(p / kPieces) * a.rec_stride;
+            const double m = collect(&rc[2 + p % kPieces]);
+            stage[p] = m;
+            if (MODE == kBonus) {
+                const float sp = static_cast<float>(collect(&rc[0]));
+                sstage[p] = sp;
+                sm = fmaxf(sm, sp);
+            } else {
+                tot += m;                            // residual chunks share shift 0
+            }
+        }
+    }
+    // 2. bonus row: every piece to the common frame 2^(-largest chunk shift)
     float smax = 0.0f;
     if (MODE == kBonus) {
-        float sm = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < kLocPP; ++j)
-            if (j < pp) sm = fmaxf(sm, P.s[j]);
-        smax = block_max(sm, L.f4);
-    }
-    double sc[kLocPP];
-    double tot = 0.0;
-#pragma unroll
-    for (int j = 0; j < kLocPP; ++j) {
-        sc[j] = 1.0;
-        if (j < pp) {
-            if (MODE == kBonus)
-                sc[j] = (P.s[j] == -INFINITY) ? 0.0 : pow2_shift_d(static_cast<double>(P.s[j]) - static_cast<double>(smax));
-            tot += P.m[j] * sc[j];
+        smax = wave_max(sm);
+#pragma unroll 4
+        for (int j = 0; j < pp; ++j) {
+            const int p = p0 + j;
+            if (p < np) {
+                const float sp = sstage[p];
+                const double sc = (sp == -INFINITY) ? 0.0 : pow2_shift_d(static_cast<double>(sp) - static_cast<double>(smax));
+                const double m = stage[p] * sc;
+                stage[p] = m;
+                tot += m;
+            }
         }
     }
-    if (threadIdx.x == 0) {
-        L.pstar = -1;
-        L.tok = INT_MAX;
-        L.lastpos = -1;
-    }
-    const Scan s = block_scan_d(tot, 0.0, L.d4);
-    const double W = s.total;
+    // 3. the run holding t
+    const double incl = wave_scan_d(tot);
+    const double excl = dpp_shift_d<kDppWaveShr1, 0xF, 0xF>(incl);   // 0 at lane 0
+    const double W = readlane_d(incl, kWave - 1);
     if (!(W > 0.0) || !isfinite(W)) return -1;
     const double t = u * W;
-    if (s.excl <= t && t < s.incl) {
-        // walk this thread's pieces; the last interval ends at s.incl
-        double lo = s.excl;
-        int pick = -1, last = -1;
-        double pick_lo = lo, last_lo = lo;
-#pragma unroll
-        for (int j = 0; j < kLocPP; ++j) {
-            const double mj = P.m[j] * sc[j];
-            if (j < pp && mj > 0.0) {
-                last = j;
-                last_lo = lo;
-                const double hi = (j == pp - 1) ? s.incl : lo + mj;
-                if (pick < 0 && t < hi) {
-                    pick = j;
-                    pick_lo = lo;
-                }
-                lo = hi;
-            }
-        }
-        if (pick < 0) {                     // t rounded past the walk: the last positive piece
-            pick = last;
-            pick_lo = last_lo;
-        }
-        L.pstar = threadIdx.x * pp + pick;
-        L.excl = pick_lo;
-        double scp = 1.0;
-        float spk = 0.0f;
-#pragma unroll
-        for (int j = 0; j < kLocPP; ++j)
-            if (j == pick) {
-                scp = sc[j];
-                spk = P.s[j];
-            }
-        L.scale = scp;
-        L.spick = spk;
-    }
-    __syncthreads();
-    const int ps = L.pstar;
-    if (ps < 0) return -1;
+    const unsigned long long run = __ballot(excl <= t && t < incl);
+    if (run == 0ull) return -1;                       // t outside [0, W): u outside [0, 1)
+    const int ol = __ffsll(static_cast<long long>(run)) - 1;
+    const double run_lo = readlane_d(excl, ol), run_hi = readlane_d(incl, ol);
+    // 4. the piece holding t inside that run, one piece per lane (the run's
+    // masses were written by lane ol: order the wave's LDS accesses)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int q = ol * pp + lane;
+    const double mj = (lane < pp && q < np) ? stage[q] : 0.0;
+    const double x2 = wave_scan_d(mj);
+    const double lo = run_lo + dpp_shift_d<kDppWaveShr1, 0xF, 0xF>(x2);
+    const double hi = (lane == pp - 1) ? run_hi : run_lo + x2;
+    const unsigned long long hit = __ballot(mj > 0.0 && lo <= t && t < hi);
+    const unsigned long long posm = __ballot(mj > 0.0);
+    if (posm == 0ull) return -1;                      // not reached: the run has positive mass
+    const int js = hit ? (__ffsll(static_cast<long long>(hit)) - 1)
+                       : (63 - __clzll(static_cast<long long>(posm)));
+    const int ps = ol * pp + js;
+    const double lo_s = readlane_d(lo, js);
     const int cs = ps / kPieces, wsv = (ps % kPieces) / NV2, ns = ps % NV2;
-    const double tp = (t - L.excl) / L.scale;        // target inside the piece, chunk frame
+    float spick = 0.0f;
+    double scale = 1.0;
+    if (MODE == kBonus) {
+        spick = sstage[ps];
+        scale = (spick == -INFINITY) ? 0.0 : pow2_shift_d(static_cast<double>(spick) - static_cast<double>(smax));
+    }
+    const double tp = (t - lo_s) / scale;            // target inside the piece, chunk frame
     // the chosen piece's own chunk shift, as the mass kernel used it
-    const float s_use = (MODE == kBonus && L.spick != -INFINITY) ? L.spick : 0.0f;
-    if (threadIdx.x < kWave) {
-        const int lane = threadIdx.x;
-        const int64_t gv = piece_vec<NV2>(cs, wsv, ns, lane);
-        u32x4 dt, dq;
-        load_vec<DT, MODE>(S, gv, dt, dq);
+    const float s_use = (MODE == kBonus && spick != -INFINITY) ? spick : 0.0f;
+    // 5. the token inside the piece: its 64 vectors, one per lane
+    const int64_t gv = piece_vec<NV2>(cs, wsv, ns, lane);
+    u32x4 dt, dq;
+    load_vec<DT, MODE>(S, gv, dt, dq);
+    float w[VEC];
+    vec_weights<DT, MODE>(S, dt, dq, gv * VEC, s_use, w);
+    const double x = wave_scan_d(vec_sum<VEC>(w));
+    const double ex = dpp_shift_d<kDppWaveShr1, 0xF, 0xF>(x);     // 0 at lane 0
+    int last = -1;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        if (w[e] > 0.0f) last = e;
+    int pick = -1;
+    if (ex <= tp && tp < x) {
+        double cum = ex;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if (w[e] > 0.0f) {
+                cum += static_cast<double>(w[e]);
+                if (pick < 0 && cum > tp) pick = e;
+            }
+        }
+        if (pick < 0) pick = last;
+    }
+    // The lanes hold the piece's vectors in index order.  The token is the
+    // pick of the lowest lane whose interval holds tp (the intervals tile the
+    // piece, so there is at most one such lane); rounding can hide the
+    // crossing, and then the last positive weight of the highest lane that
+    // has one is taken.  Ballots and lane reads, not LDS atomics: an atomic
+    // from every lane runs as a serial loop over the lanes.
+    const int base = static_cast<int>(gv * VEC);
+    const unsigned long long own = __ballot(pick >= 0);
+    const unsigned long long pos = __ballot(last >= 0);
+    if (own) return __builtin_amdgcn_readlane(base + pick, __ffsll(static_cast<long long>(own)) - 1);
+    if (pos) return __builtin_amdgcn_readlane(base + last, 63 - __clzll(static_cast<long long>(pos)));
+    return -1;
+}
+
+// Zero residual mass after a rejection (reachable only through rounding):
+// draw from p~ = (1 - lambda) p_t + lambda q at that row instead.  Two passes
+// over the row in pages of 64 vectors (one per lane) in index order, the
+// first for the total W, the second for the page, lane and element where the
+// running sum first exceeds u * W (rare path: small code rather than speed).
+// All lanes must call this; the result is wave-uniform.
+template <class DT>
+__device__ __forceinline__ int sample_mixture_wave(const SampleCtx &S, double u) {
+    constexpr int VEC = DT::kVec;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int V = S.V;
+    const int nvec = (V + VEC - 1) / VEC;
+    auto weights = [&](int gv, float (&w)[VEC]) {
+        float ft[VEC], fq[VEC];
+        DT::unpack(load_row_vec<DT, false>(S.row_t, gv, V), ft);
+        DT::unpack(load_row_vec<DT, false>(S.row_q, gv, V), fq);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if (S.logit) {
+                w[e] = pow2_mixed(ft[e], fq[e], S.mx, S.st) * S.it;          // p~ itself
+            } else {
+                const float pt = pow2_logit(ft[e], S.c_hi, S.c_lo, S.st) * S.it;
+                const float pq = pow2_logit(fq[e], S.c_hi, S.c_lo, S.sq) * S.iq;
+                w[e] = fmaf(S.w_t, pt, S.w_q * pq);
+            }
+        }
+    };
+    double carry = 0.0;
+#pragma unroll 1
+    for (int base = 0; base < nvec; base += kWave) {
         float w[VEC];
-        vec_weights<DT, MODE>(S, dt, dq, gv * VEC, s_use, w);
+        weights(base + lane, w);                      // vectors past the row read as -inf: weight 0
+        carry += readlane_d(wave_scan_d(vec_sum<VEC>(w)), kWave - 1);
+    }
+    const double W = carry;
+    if (!(W > 0.0) || !isfinite(W)) return -1;
+    const double t = u * W;
+    carry = 0.0;
+    int last_tok = -1;
+#pragma unroll 1
+    for (int base = 0; base < nvec; base += kWave) {
+        float w[VEC];
+        weights(base + lane, w);
         const double x = wave_scan_d(vec_sum<VEC>(w));
-        const double excl = dpp_shift_d<kDppWaveShr1, 0xF, 0xF>(x);   // 0 at lane 0
+        const double lo = carry + dpp_shift_d<kDppWaveShr1, 0xF, 0xF>(x);
+        const double hi = carry + x;
         int last = -1;
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
             if (w[e] > 0.0f) last = e;
         int pick = -1;
-        if (excl <= tp && tp < x) {
-            double cum = excl;
+        if (lo <= t && t < hi) {                      // this lane's interval of the page holds t
+            double cum = lo;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 if (w[e] > 0.0f) {
                     cum += static_cast<double>(w[e]);
-                    if (pick < 0 && cum > tp) pick = e;
+                    if (pick < 0 && cum > t) pick = e;
                 }
             }
             if (pick < 0) pick = last;
         }
-        // The lanes hold the piece's vectors in index order.  The token is
-        // the pick of the lowest lane whose interval holds tp (the intervals
-        // tile the piece, so there is at most one such lane); the fallback is
-        // the last positive weight of the highest lane that has one.  Ballots
-        // and lane reads, not LDS atomics: an atomic from every lane runs as
-        // a serial loop over the lanes.
-        const int base = static_cast<int>(gv * VEC);
-        const int tok_v = base + pick, last_v = base + last;
         const unsigned long long own = __ballot(pick >= 0);
+        if (own) return __builtin_amdgcn_readlane((base + lane) * VEC + pick, __ffsll(static_cast<long long>(own)) - 1);
         const unsigned long long pos = __ballot(last >= 0);
-        const int tok_l = own ? __builtin_amdgcn_readlane(tok_v, __ffsll(static_cast<long long>(own)) - 1)
-                              : INT_MAX;
-        const int last_l = pos ? __builtin_amdgcn_readlane(last_v, 63 - __clzll(static_cast<long long>(pos)))
-                               : -1;
-        if (lane == 0) {
-            L.tok = tok_l;
-            L.lastpos = last_l;
-        }
+        if (pos) last_tok = __builtin_amdgcn_readlane((base + lane) * VEC + last, 63 - __clzll(static_cast<long long>(pos)));
+        carry += readlane_d(x, kWave - 1);
     }
-    __syncthreads();
-    // rounding can hide the crossing inside the piece: then its last positive
-    // weight is taken
-    const int tok = (L.tok != INT_MAX) ? L.tok : L.lastpos;
-    __syncthreads();
-    return tok;
+    return last_tok;                                  // t at the very top by rounding: last positive weight
 }
 
-// Zero residual mass after a rejection (reachable only through rounding):
-// draw from p~ = (1 - lambda) p_t + lambda q at that row instead.  A compact
-// two-pass scan over 256-element pages in index order (rare path: small code
-// rather than speed).
-template <class DT>
-__device__ __forceinline__ int sample_mixture(const SampleCtx &S, double u, LocateShared &L) {
-    const int V = S.V;
-    auto weight = [&](int v) -> float {
-        if (v >= V) return 0.0f;
-        const float zt = DT::load1(S.row_t, v);
-        const float zq = DT::load1(S.row_q, v);
-        if (S.logit) return pow2_mixed(zt, zq, S.mx, S.st) * S.it;   // p~ itself
-        const float pt = pow2_logit(zt, S.c_hi, S.c_lo, S.st) * S.it;
-        const float pq = pow2_logit(zq, S.c_hi, S.c_lo, S.sq) * S.iq;
-        return fmaf(S.w_t, pt, S.w_q * pq);
-    };
-    double carry = 0.0;
-#pragma unroll 1
-    for (int base = 0; base < V; base += kBlock)
-        carry = block_scan_d(static_cast<double>(weight(base + threadIdx.x)), carry, L.d4).total;
-    const double W = carry;
-    if (!(W > 0.0) || !isfinite(W)) return -1;
-    const double t = u * W;
-    if (threadIdx.x == 0) L.tok = -1;
-    __syncthreads();
-    carry = 0.0;
-#pragma unroll 1
-    for (int base = 0; base < V; base += kBlock) {
-        const float w = weight(base + threadIdx.x);
-        const Scan sc = block_scan_d(static_cast<double>(w), carry, L.d4);
-        if (w > 0.0f && sc.excl <= t && t < sc.incl) L.tok = base + threadIdx.x;
-        carry = sc.total;
-        __syncthreads();
-        if (L.tok >= 0) break;
-    }
-    if (L.tok < 0 && threadIdx.x == 0) {   // t at the very top by rounding: last positive weight
-        for (int v = V - 1; v >= 0; --v)
-            if (weight(v) > 0.0f) {
-                L.tok = v;
-                break;
-            }
-    }
-    __syncthreads();
-    return L.tok;
-}
-
-// The sampled (corrected or bonus) token of request b from its chunk records,
-// written at position r.n.  Run by threads 0 .. kBlock-1 of the request's last
-// mass block (the block's other waves have ended).
+// The sampled (corrected or bonus) token of request b, written at position
+// r.n by wave 0 of the block that completed the request's mass blocks.
 template <class DT, int NV2>
 __device__ __forceinline__ void draw_request(const ChainArgs &a, int b, const ReqRecord &r,
-                                             const SampleCtx &S, LocateShared &L) {
-    const int pp = (a.C2 * kWaves2 * NV2 + kBlock - 1) / kBlock;
-    LocatePieces P;
-    load_pieces<NV2>(a, b, pp, P);
+                                             const SampleCtx &S, double *stage) {
     const double u = static_cast<double>(a.u_sample[b]);
     int flags = 0;
     // At lambda = 1, p~ = q and the residual max(0, p~ - q) is identically
@@ -1040,20 +1028,20 @@ __device__ __forceinline__ void draw_request(const ChainArgs &a, int b, const Re
     // The chunk records hold max(0, p_t - q), which is no longer the same law.
     int tok;
     if (r.mode == kResidual)
-        tok = (a.lam >= 1.0f) ? -1 : locate<DT, kResidual, NV2>(S, P, pp, u, L);
+        tok = (a.lam >= 1.0f) ? -1 : locate_wave<DT, kResidual, NV2>(a, b, S, u, stage);
     else if (r.mode == kResidualLogit)
-        tok = locate<DT, kResidualLogit, NV2>(S, P, pp, u, L);
+        tok = locate_wave<DT, kResidualLogit, NV2>(a, b, S, u, stage);
     else
-        tok = locate<DT, kBonus, NV2>(S, P, pp, u, L);
+        tok = locate_wave<DT, kBonus, NV2>(a, b, S, u, stage);
     if (tok < 0 && r.mode != kBonus && r.rows_ok) {
         flags |= SV_DATA_FALLBACK;
-        tok = sample_mixture<DT>(S, u, L);
+        tok = sample_mixture_wave<DT>(S, u);
     }
     if (tok < 0) {
         tok = -1;
         flags |= SV_DATA_BAD_ROW;
     }
-    if (threadIdx.x == 0) {
+    if ((threadIdx.x & (kWave - 1)) == 0) {
         a.out_tokens[int64_t(b) * (a.g.P + 1) + r.n] = tok;
         if (flags) atomicOr(a.status, flags);
     }
@@ -1063,7 +1051,6 @@ __device__ __forceinline__ void draw_request(const ChainArgs &a, int b, const Re
 template <class DT, int NV2>
 __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int staged) {
     __shared__ ResolveShared sh;
-    __shared__ LocateShared L;
     __shared__ int last;
     extern __shared__ double dyn[];
     const int b = blockIdx.x;
@@ -1110,8 +1097,12 @@ __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int stage
     else if (r.mode == kResidualLogit) chunk_pieces<DT, kResidualLogit, NV2>(S, c, cr, sh.f);
     else chunk_pieces<DT, kBonus, NV2>(S, c, cr, sh.f);
 
-    // the last of the request's C2 blocks to finish draws the token
-    __builtin_amdgcn_s_waitcnt(0);          // this thread's record stores are done
+    // The block counts itself done once every thread's record stores have
+    // drained (one atomic per block: an atomic per wave on the request's one
+    // counter serialises, 30 against 15 us on the c4 batch); wave 0 of the
+    // block that brings the count to C2 sees every record of the request and
+    // draws the token alone.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
         last = __hip_atomic_fetch_add(&a.count[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -1121,8 +1112,9 @@ __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int stage
         if (last) __hip_atomic_store(&a.count[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    if (!last || threadIdx.x >= kBlock) return;   // uniform, then whole waves
-    draw_request<DT, NV2>(a, b, r, S, L);
+    if (!last || threadIdx.x >= kWave) return;     // uniform, then whole waves
+    // the resolve staging area is free again: it holds the piece masses
+    draw_request<DT, NV2>(a, b, r, S, dyn);
 }
 
 }  // namespace sv
@@ -1244,9 +1236,10 @@ template <class DT>
 sv_status run_typed(const ChainReq &q, int which) {
     const int nv = choose_nv_mode(q, DT::kVec);
     const ChainArgs a = make_args(q, DT::kVec, nv);
-    // every locate thread holds at most kLocPP piece masses (always true for
+    // the draw stages at most kMaxPieces piece masses in LDS (always true for
     // the vocabularies validate() accepts; checked before any launch)
-    if (int64_t(a.C2) * kWaves2 * a.NV2 > int64_t(kBlock) * kLocPP) return SV_EINVAL;
+    const int64_t n_pieces = int64_t(a.C2) * kWaves2 * a.NV2;
+    if (n_pieces > kMaxPieces) return SV_EINVAL;
     if ((which & 1) && a.space == 1) {
         const int jobs = static_cast<int>(int64_t(q.B) * a.g.Pcap * a.C1);
         const dim3 grid(static_cast<unsigned>(jobs > 0 ? cdiv(jobs, kWaves) : 1));
@@ -1270,7 +1263,10 @@ sv_status run_typed(const ChainReq &q, int which) {
     if (which & 2) {
         const int64_t stage_n = int64_t(2) * a.g.Pcap * a.C1;
         const int staged = stage_n <= kStageMax ? 1 : 0;
-        const size_t lds = staged ? static_cast<size_t>(stage_n) * (sizeof(double) + 2 * sizeof(float)) : 0;
+        // the resolve staging area, reused by the draw for the piece masses
+        // (a double and a float each)
+        const size_t lds = std::max(staged ? static_cast<size_t>(stage_n) * (sizeof(double) + 2 * sizeof(float)) : 0,
+                                    static_cast<size_t>(n_pieces) * (sizeof(double) + sizeof(float)));
         const dim3 grid(static_cast<unsigned>(q.B), static_cast<unsigned>(a.C2));
         if (a.NV2 == 8) {
             hipLaunchKernelGGL((k_resolve_mass<DT, 8>), grid, dim3(kBlock2), lds, q.stream, a, staged);

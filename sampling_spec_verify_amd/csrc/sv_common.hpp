@@ -113,7 +113,7 @@ constexpr int kMaxC2 = 128;                   // sampling chunks per row at NV2 
 constexpr int kMinVec = 4;                    // fp32: 4 elements per 16-byte vector
 constexpr int kMinNV = 2;                     // smallest row-stats vectors per lane
 constexpr int kStageMax = 2048;               // row partials staged in LDS per request
-constexpr int kLocPP = 16;                   // piece masses per locate thread (np <= 256 * 16)
+constexpr int kMaxPieces = 4096;             // piece masses of one sampling row (staged in LDS by the draw)
 constexpr int kGreedyStageMax = 2048;         // argmax partials staged in LDS per tree
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -246,6 +246,16 @@ __device__ __forceinline__ int wave_scan_i(int v) {
     return v;
 }
 
+// OR of an 8-bit flag word over the wave, one ballot per bit (a shuffle
+// butterfly would take six LDS round trips).
+__device__ __forceinline__ int wave_or8(int v) {
+    int r = 0;
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit)
+        if (__ballot((v >> bit) & 1)) r |= 1 << bit;
+    return r;
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
     v += dpp_d<kDppXor1>(v);
     v += dpp_d<kDppXor2>(v);

@@ -224,8 +224,7 @@ __global__ __launch_bounds__(kBlock2) void k_greedy_walk(TreeArgs a, int staged)
     const unsigned long long fl_mask = __ballot(flags != 0);
     if (lane == 0) wkey[wv] = key;
     if (fl_mask) {
-        int fl_all = flags;
-        for (int off = 1; off < kWave; off <<= 1) fl_all |= __shfl_xor(fl_all, off, kWave);
+        const int fl_all = wave_or8(flags);
         if (lane == 0) atomicOr(&sh_flags, fl_all);
     }
     __syncthreads();
