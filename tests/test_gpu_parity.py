@@ -465,17 +465,25 @@ def test_logit_mixture_path_mode():
     report("path logit", compare_chain(x, g, ref, lengths=path_lengths(x)))
 
 
-def test_lambda_one_with_unreachable_draft_samples_the_draft():
+@pytest.mark.parametrize("dtype,V,space", [("fp32", 3000, "prob"), ("bf16", 3001, "prob"),
+                                           ("bf16", 3001, "logit"), ("fp32", 70001, "logit")])
+def test_lambda_one_with_unreachable_draft_samples_the_draft(dtype, V, space):
     """lambda = 1 and q(x) = 0: the draft is rejected and, the residual
-    max(0, p~ - q) being zero, the token is drawn from p~ = q."""
-    x = synth.make_chain(234, 6, 3, 3000, "fp32", lam=1.0, sigma_q=2.0)
-    for b in range(x.B):
-        x.draft[b, 1, x.tokens[b, 1]] = -np.inf      # position 1's draft cannot produce x
-    g = run_chain(x)
+    max(0, p~ - q) being zero, the token is drawn from p~ = q by the
+    fallback scan (both mixture spaces, a partial last vector, and a row of
+    several pages)."""
+    x = synth.make_chain(234, 6, 3, V, dtype, lam=1.0, sigma_q=2.0)
+    neg_inf = np.float32(-np.inf)
+    for b in range(x.B):                             # position 1's draft cannot produce x
+        if dtype == "bf16":
+            x.draft[b, 1, x.tokens[b, 1]] = 0xFF80
+        else:
+            x.draft[b, 1, x.tokens[b, 1]] = neg_inf
+    g = run_chain(x, space=space)
     flags = sv.decode_flags(int(g.status[0]))
     assert "ZERO_Q" in flags and "FALLBACK" in flags
     assert np.all(g.accepted == 1)
-    report("lambda=1 q(x)=0", compare_chain(x, g, oracle_chain(x)))
+    report(f"lambda=1 q(x)=0 {dtype} {space}", compare_chain(x, g, oracle_chain(x, space=space)))
 
 
 # ---------------------------------------------------------------------------
