@@ -65,7 +65,6 @@ typedef enum {
 
 typedef enum { SV_BF16 = 0, SV_F32 = 1 } sv_dtype;
 
-/* Largest number of drafted positions per request (chain K, tree path Dmax). */
 /* Where the target and draft models are mixed ([RAPID]): SV_MIX_PROB is the
  * mixture equation of section "2) 推理时知识迁移", p~ = (1 - lambda) p_t +
  * lambda q; SV_MIX_LOGIT is the form of the section-3 pseudocode, p~ =
@@ -76,9 +75,16 @@ typedef enum { SV_BF16 = 0, SV_F32 = 1 } sv_dtype;
  * coincide. */
 typedef enum { SV_MIX_PROB = 0, SV_MIX_LOGIT = 1 } sv_mix_space;
 
+/* Largest number of drafted positions per request (chain K, tree path Dmax). */
 #define SV_MAX_POSITIONS 64
 /* Largest number of non-root nodes of a draft tree. */
 #define SV_MAX_TREE_NODES 1024
+/* Largest vocabulary of the chain and path calls, by dtype (their draw
+ * stages at most 4096 piece masses of a sampling row in LDS); a larger V
+ * returns SV_EINVAL.  The acceptance-rate, greedy and multi-branch calls
+ * accept larger vocabularies. */
+#define SV_MAX_VOCAB_BF16 2097152
+#define SV_MAX_VOCAB_F32 1048576
 
 /* Bits of the device-side status word. */
 #define SV_DATA_BAD_TOKEN   0x01 /* a drafted or node token outside [0, V): that draft is rejected */

@@ -279,3 +279,16 @@ def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define SV_MAX_POSITIONS\s+(\d+)", text).group(1)) == sv.SV_MAX_POSITIONS
     assert int(re.search(r"#define SV_MAX_TREE_NODES\s+(\d+)", text).group(1)) == sv.SV_MAX_TREE_NODES
+    assert int(re.search(r"#define SV_MAX_VOCAB_BF16\s+(\d+)", text).group(1)) == sv.SV_MAX_VOCAB_BF16
+    assert int(re.search(r"#define SV_MAX_VOCAB_F32\s+(\d+)", text).group(1)) == sv.SV_MAX_VOCAB_F32
+
+
+@pytest.mark.parametrize("fn", ["sv_chain_verify", "sv_chain_row_stats", "sv_chain_accept_resample",
+                                "sv_chain_verify_ex"])
+@pytest.mark.parametrize("dtype,per", [(sv.SV_BF16, 8), (sv.SV_F32, 4)])
+def test_chain_vocabulary_limit(fn, dtype, per):
+    """One element past the largest vocabulary is refused before any launch."""
+    vmax = sv.SV_MAX_VOCAB_BF16 if dtype == sv.SV_BF16 else sv.SV_MAX_VOCAB_F32
+    ld = vmax + per
+    assert chain_call(fn, dtype=dtype, V=vmax + 1, ld_t=ld, ld_q=ld) == sv.SV_EINVAL
+    assert sv.lib().sv_chain_workspace_bytes(2, 4, vmax) > 0
