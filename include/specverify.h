@@ -388,7 +388,7 @@ sv_status sv_tree_verify_path_ex(const void *target_logits, int64_t ld_t,
  *  workspace: sv_tree_multi_workspace_bytes(B, N, V) bytes (two fp32
  *  residual rows per request).
  *
- * Each tree is walked by G cooperating 1024-thread blocks (G up to 16, so
+ * Each tree is walked by G cooperating 512-thread blocks (G up to 16, so
  * that B * G blocks fit the GPU at once), each owning a slice of the
  * vocabulary: every sum over the vocabulary is a pass of the blocks over their
  * slices, combined at a barrier of the tree's blocks.  The call is bound by

@@ -18,7 +18,7 @@
 // token is drawn from the last residual; a node without children (or at depth
 // Dmax) emits the bonus token from the target's own softmax(z/T).
 //
-// G cooperating 1024-thread blocks walk each tree (G up to 16, as many as fit
+// G cooperating 512-thread blocks walk each tree (G up to 16, as many as fit
 // the GPU with the other trees' blocks), block g owning vocabulary slice g.
 // Every block takes every decision of the walk from the same combined values;
 // each step that needs a sum over the vocabulary is a pass of every block over
@@ -41,7 +41,7 @@
 
 namespace sv {
 
-constexpr int kMB = 1024;                 // threads of a walk block
+constexpr int kMB = 512;                  // threads of a walk block (1024 spilled registers)
 constexpr int kMW = kMB / kWave;          // its waves
 constexpr int kMU = 2;                    // tiles of a pass in flight per thread
 constexpr int kMNodes = SV_MAX_TREE_NODES + 1;
@@ -151,7 +151,7 @@ __device__ __forceinline__ Scan mblock_scan(double v, double carry, MultiShared 
 // the tree's counter and polls it until all G blocks have arrived; published
 // slots alternate with the barrier's parity, so a slot is rewritten only after
 // every block has read it.  The grid is sized to the GPU's resident capacity
-// (one 1024-thread block per compute unit), so on a GPU without other work
+// (as many walk blocks as the compute units hold), so on a GPU without other work
 // every block runs at once; a poll gives up after kSpinLimit rounds, marking
 // the block broken (SV_DATA_SYNC), so every wave ends in any case.
 
@@ -682,8 +682,8 @@ int64_t multi_layout_total(int B, int V) {
     return multi_layout_buf(B) + align256(int64_t(B) * 2 * V * int64_t(sizeof(float)));
 }
 
-// Blocks per tree: the trees share the GPU's compute units (one 1024-thread
-// block fits a unit), each block keeping at least one tile of the row.
+// Blocks per tree: the trees share the GPU's resident walk blocks, each block
+// keeping at least one tile of the row.
 int choose_g(int B, int V, int vec, int units) {
     const int nvec = (V + vec - 1) / vec;
     int G = std::max(1, std::min({kMaxG, units / std::max(B, 1), (nvec + kMB - 1) / kMB}));
