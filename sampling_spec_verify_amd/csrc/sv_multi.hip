@@ -69,10 +69,12 @@ struct MultiArgs {
 };
 
 struct MultiShared {
+    int par[kMNodes];                     // parent of each node (as given)
     int head[kMNodes];                    // first child of a node (node order), -1: none
     int next[kMNodes];                    // next sibling, -1: none
     int tok[kMNodes];
     double zs[kMNodes];                   // residual masses of the current node, in order
+    float czt[kMNodes], czq[kMNodes];     // target / draft logit of each child's token at its parent's rows
     int path[SV_MAX_POSITIONS + 1];
     double red[kMW];
     float redf[kMW];
@@ -508,6 +510,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
         sh.head[i] = -1;
         sh.next[i] = -1;
         sh.tok[i] = (i > 0) ? a.node_token[int64_t(b) * N + i - 1] : -1;
+        sh.par[i] = (i > 0) ? a.parent[int64_t(b) * N + i - 1] : -1;
     }
     if (a.accept_prob != nullptr && g == 0)
         for (int i = t; i < N; i += kMB) a.accept_prob[int64_t(b) * N + i] = -1.0f;
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
     if (t == 0) {
         // children lists in node order: link from the last node down
         for (int i = N; i >= 1; --i) {
-            const int p = a.parent[int64_t(b) * N + i - 1];
+            const int p = sh.par[i];
             if (p < 0 || p >= i) {
                 sh.flags |= SV_DATA_BAD_TREE;       // never tested
                 continue;
@@ -548,7 +551,32 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
             if (tok < 0 && t == 0) sh.flags |= SV_DATA_BAD_ROW;
             break;
         }
+        // the children's two logits, loaded by the threads of their node ids
+        // while the statistics pass runs, for thread 0's child tests
+        constexpr int kPre = (kMNodes + kMB - 1) / kMB;
+        float pzt[kPre], pzq[kPre];
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) {
+            const int i = t + k * kMB;
+            pzt[k] = pzq[k] = 0.0f;
+            if (i >= 1 && i <= N && sh.par[i] == u) {
+                const int x = sh.tok[i];
+                if (x >= 0 && x < V) {
+                    pzt[k] = DT::load1(rt, x);
+                    pzq[k] = DT::load1(rq, x);
+                }
+            }
+        }
         pass_stats<DT>(a, sh, phase, rt, rq, false);
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) {
+            const int i = t + k * kMB;
+            if (i >= 1 && i <= N && sh.par[i] == u) {
+                sh.czt[i] = pzt[k];
+                sh.czq[i] = pzq[k];
+            }
+        }
+        __syncthreads();
         if (!(sh.SA > 0.0) || !isfinite(sh.SA) || !(sh.SB > 0.0) || !isfinite(sh.SB) ||
             !isfinite(sh.sA) || !isfinite(sh.sB)) {
             if (t == 0) sh.flags |= SV_DATA_BAD_ROW;
@@ -568,8 +596,8 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
                 if (x < 0 || x >= V) {
                     sh.flags |= SV_DATA_BAD_TOKEN;
                 } else {
-                    const float zt = DT::load1(rt, x);
-                    const float zq = DT::load1(rq, x);
+                    const float zt = sh.czt[c];
+                    const float zq = sh.czq[c];
                     double q, r;
                     if (cur == nullptr) {
                         // fp64 from the gathered logits
