@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kBlock) void k_row_stats_logit(ChainArgs a, int n_j
 // kResidualLogit: the residual max(0, p~ - q) of the logit-space mixture,
 // p~ = softmax of the mixed logits (the target slot of the record holds its
 // shift and 1 / sum).
-enum SampleMode { kResidual = 0, kBonus = 1, kMixture = 2, kResidualLogit = 3 };
+enum SampleMode { kResidual = 0, kBonus = 1, kResidualLogit = 2 };
 
 struct SampleCtx {
     const char *row_t;      // target row of the sampling position
@@ -394,9 +394,8 @@ __device__ __forceinline__ void load_vec(const SampleCtx &S, int64_t gv, u32x4 &
 // `s_use` is the bonus shift.
 template <class DT, int MODE>
 __device__ __forceinline__ void vec_weights(const SampleCtx &S, const u32x4 &dt, const u32x4 &dq,
-                                            int64_t e0, float s_use, float *w) {
+                                            float s_use, float *w) {
     constexpr int VEC = DT::kVec;
-    (void)e0;
     float ft[VEC], fq[VEC];
     DT::unpack(dt, ft);
     if (MODE != kBonus) DT::unpack(dq, fq);
@@ -411,8 +410,7 @@ __device__ __forceinline__ void vec_weights(const SampleCtx &S, const u32x4 &dt,
         } else {
             const float et = pow2_logit(ft[e], S.c_hi, S.c_lo, S.st);
             const float pq = pow2_logit(fq[e], S.c_hi, S.c_lo, S.sq) * S.iq;
-            w[e] = (MODE == kResidual) ? fmaxf(fmaf(et, S.it, -pq), 0.0f)
-                                       : fmaf(S.w_t, et * S.it, S.w_q * pq);
+            w[e] = fmaxf(fmaf(et, S.it, -pq), 0.0f);
         }
     }
 }
@@ -798,7 +796,7 @@ __device__ __forceinline__ void chunk_pieces(const SampleCtx &S, int c, double *
 #pragma unroll
     for (int n = 0; n < NV2; ++n) {
         float w[VEC];
-        vec_weights<DT, MODE>(S, dt[n], dq[n], piece_vec<NV2>(c, wv, n, lane) * VEC, s_use, w);
+        vec_weights<DT, MODE>(S, dt[n], dq[n], s_use, w);
         const double ws = wave_sum_d(vec_sum<VEC>(w));
         if (lane == 0) publish(&rec[2 + wv * NV2 + n], ws);
     }
@@ -912,7 +910,7 @@ __device__ __forceinline__ int locate_wave(const ChainArgs &a, int b, const Samp
     u32x4 dt, dq;
     load_vec<DT, MODE>(S, gv, dt, dq);
     float w[VEC];
-    vec_weights<DT, MODE>(S, dt, dq, gv * VEC, s_use, w);
+    vec_weights<DT, MODE>(S, dt, dq, s_use, w);
     const double x = wave_scan_d(vec_sum<VEC>(w));
     const double ex = dpp_shift_d<kDppWaveShr1, 0xF, 0xF>(x);     // 0 at lane 0
     int last = -1;

@@ -36,7 +36,7 @@ struct alignas(16) ArgPart {
 // sampling row with its statistics.
 struct alignas(16) ReqRecord {
     int n;          // accepted drafts
-    int mode;       // residual (0) or bonus (1)
+    int mode;       // the sampling row's law: residual, logit-space residual or bonus
     int row;        // request row of the sampling position
     int rows_ok;    // the residual rows have valid statistics
     float st, sq;   // integer shifts of the target and draft rows: p(v) = 2^(z c - s) / S
