@@ -64,8 +64,7 @@ struct MultiArgs {
     int32_t *status;
     float *buf;                           // [B, 2, V] residual ping-pong
     int G;                                // blocks per tree; block g owns vocabulary slice g
-    int *bar;                             // [B] barrier arrivals, cleared by k_multi_clear
-    double *pub;                          // [B, G, 2, kSlot] values published at a barrier
+    unsigned long long *pub;              // [B, G, 3, kSlot] values published at a barrier (bit patterns)
 };
 
 struct MultiShared {
@@ -149,10 +148,16 @@ __device__ __forceinline__ Scan mblock_scan(double v, double carry, MultiShared 
 // vectors, in index order) for every pass.  The blocks take the same
 // decisions from the same combined values, so they meet the same barriers.
 // Values cross blocks only through agent-scope relaxed atomics (write-through
-// stores, coherent loads): a block publishes, drains its stores, arrives at
-// the tree's counter and polls it until all G blocks have arrived; published
-// slots alternate with the barrier's parity, so a slot is rewritten only after
-// every block has read it.  The grid is sized to the GPU's resident capacity
+// stores, coherent loads), and every published value marks its own arrival:
+// a block's slot reads as an empty marker (a signalling-NaN bit pattern that
+// no arithmetic produces) until the block writes the value, and the readers
+// poll the values themselves, one thread per value, so a barrier costs one
+// store and one load round trip.  Slots rotate over three barriers: after
+// barrier k a block empties the slot it filled for barrier k - 1 (every
+// reader has consumed it, since each reader published for barrier k after
+// reading it) for use at barrier k + 2, and it drains that store before it
+// publishes for barrier k + 1, so a reader that has passed barrier k + 1
+// finds the slot empty or holding the barrier-(k + 2) value.  The grid is sized to the GPU's resident capacity
 // (as many walk blocks as the compute units hold), so on a GPU without other work
 // every block runs at once; a poll gives up after kSpinLimit rounds, marking
 // the block broken (SV_DATA_SYNC), so every wave ends in any case.
@@ -170,43 +175,51 @@ __device__ __forceinline__ Slice my_slice(const MultiArgs &a, int nvec) {
     return s;
 }
 
-__device__ __forceinline__ double *pub_slot(const MultiArgs &a, int g, int phase) {
+constexpr unsigned long long kEmpty = 0x7FF0DEAD5EED1234ull;   // an empty slot (a signalling NaN)
+constexpr int kRot = 3;                                            // slots per block, used in rotation
+
+__device__ __forceinline__ unsigned long long *pub_slot(const MultiArgs &a, int g, int phase) {
     const int b = static_cast<int>(blockIdx.x) / a.G;
-    return a.pub + ((int64_t(b) * a.G + g) * 2 + (phase & 1)) * kSlot;
+    return a.pub + ((int64_t(b) * a.G + g) * kRot + (phase % kRot)) * kSlot;
 }
 
-// Thread 0 publishes v[0..n) for the barrier that ends phase + 1.
+// Thread 0 publishes v[0..n) for the barrier that ends phase + 1, once its
+// earlier stores (the emptying of this slot) have drained.
 __device__ __forceinline__ void publish_vals(const MultiArgs &a, int phase, const double *v, int n) {
     if (threadIdx.x != 0) return;
-    double *p = pub_slot(a, static_cast<int>(blockIdx.x) % a.G, phase + 1);
-    for (int j = 0; j < n; ++j) __hip_atomic_store(&p[j], v[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long *p = pub_slot(a, static_cast<int>(blockIdx.x) % a.G, phase + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int j = 0; j < n; ++j)
+        __hip_atomic_store(&p[j], static_cast<unsigned long long>(__double_as_longlong(v[j])), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The tree's barrier; then sh.gath holds every block's published values.
 // Every thread calls it with the same phase count, which it advances.
 __device__ void tree_barrier(const MultiArgs &a, MultiShared &sh, int &phase, int n) {
-    __builtin_amdgcn_s_waitcnt(0);        // this thread's published stores are done
-    __syncthreads();
     ++phase;
-    if (threadIdx.x == 0 && a.G > 1 && !sh.broken) {
-        int *cnt = a.bar + static_cast<int>(blockIdx.x) / a.G;
-        __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int target = phase * a.G;
+    if (static_cast<int>(threadIdx.x) < a.G * n) {
+        const int g = static_cast<int>(threadIdx.x) / n, j = static_cast<int>(threadIdx.x) % n;
+        const unsigned long long *p = &pub_slot(a, g, phase)[j];
+        unsigned long long w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         int polls = 0;
-        while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        while (w == kEmpty && !sh.broken) {
             __builtin_amdgcn_s_sleep(1);
             if (++polls > kSpinLimit) {
                 sh.broken = 1;
                 break;
             }
+            w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        sh.gath[g][j] = __longlong_as_double(static_cast<long long>(w));
     }
     __syncthreads();
-    if (static_cast<int>(threadIdx.x) < a.G * n) {
-        const int g = static_cast<int>(threadIdx.x) / n, j = static_cast<int>(threadIdx.x) % n;
-        sh.gath[g][j] = __hip_atomic_load(&pub_slot(a, g, phase)[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every block has read this block's slot of the barrier before this one:
+    // empty it for the barrier after the next
+    if (threadIdx.x == 0) {
+        unsigned long long *mine = pub_slot(a, static_cast<int>(blockIdx.x) % a.G, phase + 2);
+        for (int j = 0; j < kSlot; ++j) __hip_atomic_store(&mine[j], kEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();
 }
 
 // ---- element values -----------------------------------------------------
@@ -686,12 +699,11 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
     }
 }
 
-// Clears the status word and the trees' barrier counters.
-__global__ void k_multi_clear(int32_t *status, int *bar, int B) {
+// Clears the status word and empties every published slot of the trees.
+__global__ void k_multi_clear(int32_t *status, unsigned long long *pub, int64_t n) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
-    for (int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x); i < B;
-         i += static_cast<int>(gridDim.x * blockDim.x))
-        bar[i] = 0;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+        pub[i] = kEmpty;
 }
 
 }  // namespace sv
@@ -700,11 +712,10 @@ namespace {
 
 using namespace sv;
 
-// status word, barrier counters [B], published slots [B, kMaxG, 2, kSlot], residual rows [B, 2, V]
-int64_t multi_layout_bar() { return 256; }
-int64_t multi_layout_pub(int B) { return multi_layout_bar() + align256(int64_t(B) * int64_t(sizeof(int))); }
+// status word (when the caller passes none), published slots [B, kMaxG, 3, kSlot], residual rows [B, 2, V]
+int64_t multi_layout_pub() { return 256; }
 int64_t multi_layout_buf(int B) {
-    return multi_layout_pub(B) + align256(int64_t(B) * kMaxG * 2 * kSlot * int64_t(sizeof(double)));
+    return multi_layout_pub() + align256(int64_t(B) * kMaxG * kRot * kSlot * int64_t(sizeof(double)));
 }
 int64_t multi_layout_total(int B, int V) {
     return multi_layout_buf(B) + align256(int64_t(B) * 2 * V * int64_t(sizeof(float)));
@@ -776,8 +787,7 @@ sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const vo
     a.accept_prob = accept_prob;
     char *ws = static_cast<char *>(workspace);
     a.status = status ? status : reinterpret_cast<int32_t *>(ws);
-    a.bar = reinterpret_cast<int *>(ws + multi_layout_bar());
-    a.pub = reinterpret_cast<double *>(ws + multi_layout_pub(B));
+    a.pub = reinterpret_cast<unsigned long long *>(ws + multi_layout_pub());
     a.buf = reinterpret_cast<float *>(ws + multi_layout_buf(B));
     // all of a tree's blocks must run at once (they wait for one another), so
     // B * G stays within the resident capacity.  An ordinary launch: a
@@ -790,8 +800,9 @@ sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const vo
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, kern, kMB, 0) != hipSuccess)
         return SV_EHIP;
     a.G = choose_g(B, V, 16 / eb, units * std::max(per_unit, 0));
-    hipLaunchKernelGGL(k_multi_clear, dim3(static_cast<unsigned>(std::min<int64_t>(cdiv(B, 256), 1024))),
-                       dim3(256), 0, stream, a.status, a.bar, B);
+    const int64_t n_slots = int64_t(B) * a.G * kRot * kSlot;
+    hipLaunchKernelGGL(k_multi_clear, dim3(static_cast<unsigned>(std::min<int64_t>(cdiv(n_slots, 256), 1024))),
+                       dim3(256), 0, stream, a.status, a.pub, n_slots);
     const dim3 grid(static_cast<unsigned>(int64_t(B) * a.G));
     if (dtype == SV_BF16) {
         hipLaunchKernelGGL(k_tree_multi<Bf16>, grid, dim3(kMB), 0, stream, a);

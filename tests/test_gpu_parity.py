@@ -639,6 +639,40 @@ def test_multi_random_trees(seed, B, N, V, dtype, lam, T, space, Dmax):
     assert int(g.status[0]) == 0
 
 
+def test_multi_barrier_slots_under_alternating_batches():
+    """Two batches of trees alternate 60 times on one workspace.  The blocks of
+    a tree exchange values through rotating slots that each call starts empty;
+    a value read from the previous call or from an earlier barrier of the same
+    call would change an output, and a slot never filled would raise
+    SV_DATA_SYNC.  B = 3 puts a tree's blocks on different XCDs."""
+    xs = [synth.make_random_tree(seed, 3, 30, 20000, "bf16", sharp=1.0, sigma_q=2.0, lam=lam,
+                                 temperature=T) for seed, lam, T in ((631, 0.0, 1.0), (637, 0.3, 0.8))]
+    B, N, V = 3, 30, 20000
+    ws = torch.empty(int(sv.lib().sv_tree_multi_workspace_bytes(B, N, V)), dtype=torch.uint8,
+                     device="cuda:0")
+    refs = [oracle.tree_multi(x.widened(x.target), x.widened(x.draft), x.parent, x.node_token,
+                              x.u_node, x.u_sample, x.lam, x.temperature, x.Dmax, "prob") for x in xs]
+    args = [(dev_logits(x.target, x.dtype), dev_logits(x.draft, x.dtype), dev(x.parent),
+             dev(x.node_token), dev(x.u_node), dev(x.u_sample), x.Dmax, x.lam, x.temperature, "prob")
+            for x in xs]
+    reps = 60
+    hist = [[] for _ in xs]
+    for _ in range(reps):
+        for j in range(len(xs)):
+            out = sv.tree_verify_multi(*args[j], workspace=ws)
+            hist[j].append((out.status.clone(), out.accepted.clone(), out.out_tokens.clone()))
+    torch.cuda.synchronize()
+    for j, ref in enumerate(refs):
+        acc, toks, flag = ref[0], ref[1], ref[4]
+        for st, a, o in hist[j]:
+            assert int(st[0]) & 0x80 == 0
+            a, o = a.cpu().numpy(), o.cpu().numpy()
+            for b in range(B):
+                if not flag[b]:
+                    assert a[b] == acc[b] and np.array_equal(o[b], toks[b])
+    report("multi slots", {"calls": 2 * reps, "trees": B})
+
+
 def test_multi_on_chain_shaped_trees_matches_path_mode():
     x = synth.make_random_tree(621, 5, 7, 4000, "fp32", sharp=1.0, sigma_q=1.5, lam=0.2)
     x.parent[:] = np.arange(7)
