@@ -20,8 +20,8 @@ from tests.test_gpu_parity import _alpha_case, _mask_case, _multi_case, report
 
 pytestmark = pytest.mark.gpu
 
-N_CHAIN = 24
-N_TREE = 12
+N_CHAIN = 40
+N_TREE = 20
 
 
 @pytest.fixture(scope="module", autouse=True)
