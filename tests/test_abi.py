@@ -4,6 +4,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 from sampling_spec_verify_amd import specverify as sv
@@ -292,3 +294,23 @@ def test_chain_vocabulary_limit(fn, dtype, per):
     ld = vmax + per
     assert chain_call(fn, dtype=dtype, V=vmax + 1, ld_t=ld, ld_q=ld) == sv.SV_EINVAL
     assert sv.lib().sv_chain_workspace_bytes(2, 4, vmax) > 0
+
+
+def test_multi_empty_slot_marker_cannot_be_a_published_value():
+    """The multi-branch walk's barrier reads a slot as empty while it holds a
+    fixed signalling-NaN bit pattern.  A published value is an fp64 result of
+    arithmetic (a quiet NaN at worst), an fp32 value widened (low 29 bits
+    zero), or an integer converted to fp64 (never NaN): none can carry it."""
+    text = open(os.path.join(ROOT, "sampling_spec_verify_amd", "csrc", "sv_multi.hip")).read()
+    marker = int(re.search(r"kEmpty = (0x[0-9A-Fa-f]+)ull", text).group(1), 16)
+    exp, frac = (marker >> 52) & 0x7FF, marker & ((1 << 52) - 1)
+    assert exp == 0x7FF and frac != 0              # a NaN ...
+    assert not (frac >> 51) & 1                     # ... with the quiet bit clear
+    assert marker & ((1 << 29) - 1) != 0            # not a widened fp32 value
+    # every fp32 NaN pattern (quiet and signalling, both signs), widened
+    payload = np.arange(1, 1 << 23, dtype=np.uint32)
+    for sign in (0, 1):
+        bits = (np.uint32(sign << 31) | np.uint32(0xFF << 23) | payload).view(np.float32)
+        with np.errstate(invalid="ignore"):
+            wide = bits.astype(np.float64).view(np.uint64)
+        assert not (wide == np.uint64(marker)).any()
