@@ -5,7 +5,6 @@ import os
 import re
 
 import numpy as np
-
 import pytest
 
 from sampling_spec_verify_amd import specverify as sv
