@@ -225,9 +225,10 @@ __device__ __forceinline__ void clear_counts(const ChainArgs &a) {
 
 // One wavefront per job; the job index is made wave-uniform so that its
 // decode runs as 32-bit scalar arithmetic.  Jobs of undrafted positions exit
-// after a few instructions.  Two waves per block: on a ragged batch the last
-// busy blocks finish sooner than with four (26.1-26.3 against 26.5-27.0 us on
-// the c4 batch; level on a full one).
+// after a few instructions.  Two waves per block in both row-statistics
+// kernels: on a ragged batch the last busy blocks finish sooner than with
+// four (26.1-26.3 against 26.5-27.0 us on the c4 batch), and the logit-space
+// kernel gains a little on a full one (17.3 against 17.6 us on c3).
 constexpr int kStatsWaves = 2;
 
 template <class DT, int NV>
@@ -334,8 +335,8 @@ __device__ __forceinline__ void row_chunk_stats_logit(const ChainArgs &a, unsign
 }
 
 template <class DT, int NV>
-__global__ __launch_bounds__(kBlock) void k_row_stats_logit(ChainArgs a, int n_jobs) {
-    const int job = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves +
+__global__ __launch_bounds__(kStatsWaves * kWave) void k_row_stats_logit(ChainArgs a, int n_jobs) {
+    const int job = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kStatsWaves +
                                                    static_cast<int>(threadIdx.x) / kWave);
     if (job < n_jobs) row_chunk_stats_logit<DT, NV>(a, static_cast<unsigned>(job));
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
@@ -1240,11 +1241,12 @@ sv_status run_typed(const ChainReq &q, int which) {
     if (n_pieces > kMaxPieces) return SV_EINVAL;
     if ((which & 1) && a.space == 1) {
         const int jobs = static_cast<int>(int64_t(q.B) * a.g.Pcap * a.C1);
-        const dim3 grid(static_cast<unsigned>(jobs > 0 ? cdiv(jobs, kWaves) : 1));
+        const dim3 grid(static_cast<unsigned>(jobs > 0 ? cdiv(jobs, kStatsWaves) : 1));
+        const dim3 block(kStatsWaves * kWave);
         if (nv == 4)
-            launch_timed(k_row_stats_logit<DT, 4>, grid, dim3(kBlock), 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
+            launch_timed(k_row_stats_logit<DT, 4>, grid, block, 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
         else
-            launch_timed(k_row_stats_logit<DT, 2>, grid, dim3(kBlock), 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
+            launch_timed(k_row_stats_logit<DT, 2>, grid, block, 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
         if (hipGetLastError() != hipSuccess) return SV_EHIP;
     } else if (which & 1) {
         const int jobs = static_cast<int>(int64_t(q.B) * a.g.Pcap * 2 * a.C1);
