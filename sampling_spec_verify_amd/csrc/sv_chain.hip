@@ -177,6 +177,8 @@ __device__ __forceinline__ void row_chunk_stats(const ChainArgs &a, unsigned job
 
     u32x4 d[NV];
     load_chunk<DT, NV>(row, v0, lane, V, d);
+    // the loads are out: back to the base issue priority for the fold
+    __builtin_amdgcn_s_setprio(0);
     float f[NV][VEC];
 #pragma unroll
     for (int n = 0; n < NV; ++n) DT::unpack(d[n], f[n]);
@@ -231,8 +233,18 @@ __device__ __forceinline__ void clear_counts(const ChainArgs &a) {
 // kernel gains a little on a full one (17.3 against 17.6 us on c3).
 constexpr int kStatsWaves = 2;
 
-template <class DT, int NV>
+// Issue priority for a long row stream: when the grid spans at least two
+// rounds of resident waves (256 CUs x 28 waves of this kernel), a wave starts
+// at raised priority, so that a newly started wave decodes its job and issues
+// its loads ahead of the folds of the waves already resident, and drops back
+// once its loads are out.  On the c4 batch (64 requests, 32,768 jobs) this
+// took the kernel from 26.1-26.3 to 25.1-25.2 us; on c3 (9,728 jobs, 1.4
+// rounds) it cost 1.2 us, so shorter grids keep one priority.
+constexpr int kPrioJobs = 2 * 256 * 28;
+
+template <class DT, int NV, bool PRIO>
 __global__ __launch_bounds__(kStatsWaves * kWave) void k_row_stats(ChainArgs a, int n_jobs) {
+    if (PRIO) __builtin_amdgcn_s_setprio(3);
     const int job = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kStatsWaves +
                                                    static_cast<int>(threadIdx.x) / kWave);
     if (job < n_jobs) row_chunk_stats<DT, NV>(a, static_cast<unsigned>(job));
@@ -1252,12 +1264,14 @@ sv_status run_typed(const ChainReq &q, int which) {
         const int jobs = static_cast<int>(int64_t(q.B) * a.g.Pcap * 2 * a.C1);
         const dim3 grid(static_cast<unsigned>(jobs > 0 ? cdiv(jobs, kStatsWaves) : 1));
         const dim3 block(kStatsWaves * kWave);
-        if (nv == 8)
-            launch_timed(k_row_stats<DT, 8>, grid, block, 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
+        if (nv == 8 && jobs >= kPrioJobs)
+            launch_timed(k_row_stats<DT, 8, true>, grid, block, 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
+        else if (nv == 8)
+            launch_timed(k_row_stats<DT, 8, false>, grid, block, 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
         else if (nv == 4)
-            launch_timed(k_row_stats<DT, 4>, grid, block, 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
+            launch_timed(k_row_stats<DT, 4, false>, grid, block, 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
         else
-            launch_timed(k_row_stats<DT, 2>, grid, block, 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
+            launch_timed(k_row_stats<DT, 2, false>, grid, block, 0, q.stream, q.ev_start, q.ev_stop, a, jobs);
         if (hipGetLastError() != hipSuccess) return SV_EHIP;
     }
     if (which & 2) {
