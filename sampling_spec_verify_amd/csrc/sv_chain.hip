@@ -229,17 +229,19 @@ __device__ __forceinline__ void clear_counts(const ChainArgs &a) {
 // decode runs as 32-bit scalar arithmetic.  Jobs of undrafted positions exit
 // after a few instructions.  Two waves per block in both row-statistics
 // kernels: on a ragged batch the last busy blocks finish sooner than with
-// four (26.1-26.3 against 26.5-27.0 us on the c4 batch), and the logit-space
-// kernel gains a little on a full one (17.3 against 17.6 us on c3).
+// four (26.1-26.3 against 26.5-27.0 us on a ragged batch of 64 requests of
+// 1-8 positions at V = 128256), and the logit-space kernel gains a little on a
+// full one (17.3 against 17.6 us on 16 requests of 8 positions at V = 151936).
 constexpr int kStatsWaves = 2;
 
 // Issue priority for a long row stream: when the grid spans at least two
 // rounds of resident waves (256 CUs x 28 waves of this kernel), a wave starts
 // at raised priority, so that a newly started wave decodes its job and issues
 // its loads ahead of the folds of the waves already resident, and drops back
-// once its loads are out.  On the c4 batch (64 requests, 32,768 jobs) this
-// took the kernel from 26.1-26.3 to 25.1-25.2 us; on c3 (9,728 jobs, 1.4
-// rounds) it cost 1.2 us, so shorter grids keep one priority.
+// once its loads are out.  On the ragged 64-request batch (32,768 jobs) this
+// took the kernel from 26.1-26.3 to 25.1-25.2 us; on the full 16-request
+// batch at V = 151936 (9,728 jobs, 1.4 rounds) it cost 1.2 us, so shorter
+// grids keep one priority.
 constexpr int kPrioJobs = 2 * 256 * 28;
 
 template <class DT, int NV, bool PRIO>
@@ -1110,7 +1112,7 @@ __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int stage
 
     // The block counts itself done once every thread's record stores have
     // drained (one atomic per block: an atomic per wave on the request's one
-    // counter serialises, 30 against 15 us on the c4 batch); wave 0 of the
+    // counter serialises, 30 against 15 us on the ragged 64-request batch); wave 0 of the
     // block that brings the count to C2 sees every record of the request and
     // draws the token alone.
     __builtin_amdgcn_s_waitcnt(0);
