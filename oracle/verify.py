@@ -24,8 +24,10 @@ Readings where the pages are silent or disagree (temperature, bonus token,
 uniform layout, tie rules, the tree encoding) are listed in the design notes;
 each is marked "reading" below.
 
-All functions are pinned by ``tests/test_oracle_pins.py``; none is
-"parity unpinned".
+All functions are pinned by ``tests/test_oracle_pins.py``; the boundary-band
+predicate that decides which requests a parity comparison may excuse, the
+q(x) = 0 reading and the zero-residual fallback are pinned by
+``tests/test_oracle_excusal.py``.  None is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -78,13 +80,27 @@ def mixture(p_t: np.ndarray, q: np.ndarray, lam: float) -> np.ndarray:
     return (1.0 - lam) * p_t + lam * q
 
 
+def mixture_excess(p_t: np.ndarray, q: np.ndarray, lam: float) -> np.ndarray:
+    """p~ - q of the probability-space mixture, written as (1 - lam)(p_t - q).
+
+    [RAPID] section "2) 推理时知识迁移": p~ = (1 - lam) p_t + lam q, so
+    p~ - q = (1 - lam)(p_t - q) exactly.  This form is exactly zero wherever
+    p_t == q, as the mathematics says; the expanded form leaves rounding
+    residue there, which a normalisation would turn into a spurious law.
+    """
+    return (1.0 - lam) * (p_t - q)
+
+
 def enhanced_logits(zt: np.ndarray, zq: np.ndarray, lam: float) -> np.ndarray:
     """The RAPID pseudocode's logit-space mixture: (1 - lam) z_t + lam z_q.
 
     [RAPID] "3) 候选验证机制（伪代码）": ``enhanced_target = (1 - λ) *
     target_logits + λ * draft_logits``, then a softmax per position.  At
     lam = 0 and lam = 1 the other model's logits carry weight 0 and are left
-    out (so a -inf there does not turn into NaN).
+    out (so a -inf there does not turn into NaN).  Where both logits are
+    finite it is evaluated as z_q + (1 - lam)(z_t - z_q), the same number,
+    which equals z_q exactly when z_t == z_q (the mixture of a model with
+    itself is that model); elsewhere the expression as written.
     """
     zt = np.asarray(zt, dtype=np.float64)
     zq = np.asarray(zq, dtype=np.float64)
@@ -92,7 +108,9 @@ def enhanced_logits(zt: np.ndarray, zq: np.ndarray, lam: float) -> np.ndarray:
         return zt.copy()
     if lam == 1.0:
         return zq.copy()
-    return (1.0 - lam) * zt + lam * zq
+    fin = np.isfinite(zt) & np.isfinite(zq)
+    with np.errstate(invalid="ignore"):
+        return np.where(fin, zq + (1.0 - lam) * (zt - zq), (1.0 - lam) * zt + lam * zq)
 
 
 def accept_prob(p_mix_x: float, q_x: float) -> float:
@@ -108,14 +126,15 @@ def accept_prob(p_mix_x: float, q_x: float) -> float:
     return min(1.0, p_mix_x / q_x)
 
 
-def residual_weights(p_mix: np.ndarray, q: np.ndarray) -> np.ndarray:
+def residual_weights(p_mix: np.ndarray, q: np.ndarray, excess: Optional[np.ndarray] = None) -> np.ndarray:
     """Unnormalised law resampled after a rejection: max(0, p~ - q).
 
     [EAGLE] section 1 (resample from max(0, p - q)); [SD] "修改的拒绝采样"
     calls it the (p - q) distribution; the RAPID pseudocode's ``p_t - p_q`` is
-    read as the same clipped difference, with p~ in place of p.
+    read as the same clipped difference, with p~ in place of p.  ``excess``,
+    when given, is p~ - q already formed (``mixture_excess``).
     """
-    return np.maximum(0.0, p_mix - q)
+    return np.maximum(0.0, p_mix - q if excess is None else excess)
 
 
 def inverse_cdf(w: np.ndarray, u: float):
@@ -196,20 +215,23 @@ def chain_verify_one(zt: np.ndarray, zq: np.ndarray, x, u_acc, u_s: float,
     V = zt.shape[1]
     a = np.zeros(k)
     alpha = np.zeros(k)
-    p_mix_rows, q_rows = [], []
+    p_mix_rows, excess_rows = [], []
     for i in range(k):
         xi = int(x[i])
         if not 0 <= xi < V:
             raise ValueError(f"drafted token {xi} outside [0, {V})")
         q = softmax_T(zq[i], T)
         if space == "prob":
-            p_mix = mixture(softmax_T(zt[i], T), q, lam)
+            p_t = softmax_T(zt[i], T)
+            p_mix = mixture(p_t, q, lam)
+            excess = mixture_excess(p_t, q, lam)
         else:
             p_mix = softmax_T(enhanced_logits(zt[i], zq[i], lam), T)
+            excess = p_mix - q
         a[i] = accept_prob(p_mix[xi], q[xi])
         alpha[i] = np.minimum(p_mix, q).sum()
         p_mix_rows.append(p_mix)
-        q_rows.append(q)
+        excess_rows.append(excess)
 
     n = k
     for i in range(k):
@@ -219,7 +241,7 @@ def chain_verify_one(zt: np.ndarray, zq: np.ndarray, x, u_acc, u_s: float,
 
     fallback = False
     if n < k:
-        w = residual_weights(p_mix_rows[n], q_rows[n])
+        w = residual_weights(None, None, excess_rows[n])
         if not w.sum() > 0.0:                # reading: zero residual mass -> draw from p~
             w = p_mix_rows[n]
             fallback = True
@@ -421,9 +443,12 @@ def tree_multi_one(zt: np.ndarray, zq: np.ndarray, parent, node_token, u_acc, u_
             break
         q = softmax_T(zq[u], T)
         if space == "prob":
-            r = mixture(softmax_T(zt[u], T), q, lam)
+            p_t = softmax_T(zt[u], T)
+            r = mixture(p_t, q, lam)
+            excess = mixture_excess(p_t, q, lam)        # r - q while r is p~
         else:
             r = softmax_T(enhanced_logits(zt[u], zq[u], lam), T)
+            excess = r - q
         nxt = None
         for c in kids:
             x = int(node_token[c - 1])
@@ -438,7 +463,8 @@ def tree_multi_one(zt: np.ndarray, zq: np.ndarray, parent, node_token, u_acc, u_
             if uc < a:
                 nxt = c
                 break
-            w = residual_weights(r, q)
+            w = residual_weights(r, q, excess)
+            excess = None                               # later residuals: r - q itself
             W = w.sum()
             if not W > 0.0:
                 fallback = True
