@@ -6,16 +6,19 @@
 One step is one full verify call on one batch of seeded synthetic logits that
 already sit in HBM: for a chain workload ``sv_chain_verify`` (row statistics,
 then accept / first rejection / residual-or-bonus resample / emit); for ``c5``
-``sv_tree_verify_greedy``.  On every n-th step the same kernels run through
-the two stage calls instead, the first of them timed.  ``R`` copies of the inputs (at least 1 GiB in all, four
-times the 256 MB Infinity Cache) are rotated so that every step reads HBM.
+``sv_tree_verify_greedy``.  ``R`` copies of the inputs (at least 1 GiB in all,
+four times the 256 MB Infinity Cache) are rotated so that every step reads HBM.
 
 Prints one JSON line.  ``roofline`` rates the row-statistics kernel (the
 dominant one) on its algorithmic bytes, 2 * V * bytes_per_logit per drafted
-position, over its average duration in the timed steps.  That duration comes
-from HIP events attached to each of its launches (``sv_chain_row_stats_timed``
-/ ``sv_tree_row_argmax_timed``): the dispatch's own begin and end timestamps,
-the interval rocprofv3's kernel trace reports.  ``traffic`` comes from the
+position, over its median duration in a leg of ``--kernel-reps`` full calls
+(100 by default, independent of ``--steps``) run after the timed steps
+through the two stage calls.  Each duration comes from HIP events attached to
+the launch itself (``sv_chain_row_stats_timed`` / ``sv_tree_row_argmax_timed``
+/ ``sv_chain_verify_ex``): the dispatch's own begin and end timestamps, the
+interval rocprofv3's kernel trace reports.  ``mass_kernel`` does the same for
+the chain's accept / resample kernel, on the bytes of the rows it samples from
+(two rows per rejecting request, the bonus row otherwise).  ``traffic`` comes from the
 rocprofv3 FETCH_SIZE / WRITE_SIZE summary under ``profiles/`` when it was taken
 on the current kernel source, else null.
 ``cpu_baseline`` times the fp64 oracle on the same host arrays.
@@ -40,6 +43,7 @@ if ROOT not in sys.path:
 METRIC = "verified draft positions/sec + achieved HBM GB/s (% of peak) at V=128256 bf16"
 UNIT = "verified positions/s"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+POOL_CAP = 16                  # oracle worker processes at most
 ROTATE_BYTES = 1 << 30
 _CSRC = "sampling_spec_verify_amd/csrc/"
 KERNEL_SOURCES = {
@@ -88,8 +92,13 @@ def parse():
                          "mixture equation) or logit space (the pseudocode's form)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU time for cpu_baseline (0 disables)")
-    ap.add_argument("--time-every", type=int, default=4,
-                    help="attach timing events to the dominant kernel of every n-th timed step")
+    ap.add_argument("--time-every", type=int, default=0,
+                    help="also attach timing events to the dominant kernel of every n-th timed "
+                         "step (0: none; the roofline comes from the --kernel-reps leg)")
+    ap.add_argument("--kernel-reps", type=int, default=100,
+                    help="launch-attached timings of the dominant kernel (and of the chain's "
+                         "accept / resample kernel) in a leg of their own after the timed steps; "
+                         "the roofline uses their median")
     ap.add_argument("--cpu-pool-seconds", type=float, default=6.0,
                     help="bound on the all-cores oracle run (a fork pool over requests, taken "
                          "before the GPU is touched); 0 disables")
@@ -198,7 +207,8 @@ def cpu_pool_baseline(x, tree, seconds, space="prob", cores=None):
     import multiprocessing as mp
     from concurrent.futures import ProcessPoolExecutor
 
-    n = max(1, min(16, len(os.sched_getaffinity(0)))) if cores is None else cores
+    host = len(os.sched_getaffinity(0))
+    n = max(1, min(POOL_CAP, host)) if cores is None else cores
     # widened once here, as in the one-core run; the workers share the arrays
     _POOL.update(x=x, space=space, t=x.widened(x.target),
                  d=None if tree else x.widened(x.draft))
@@ -211,6 +221,8 @@ def cpu_pool_baseline(x, tree, seconds, space="prob", cores=None):
     units = sum(r[1] for r in res)
     what = "greedy tree verifications" if tree else "request verifications"
     return {"value": units / wall, "unit": UNIT, "cores": n, "kind": "oracle",
+            "host_cores_visible": host,
+            "worker_cap": f"{POOL_CAP} (the host's CPU share per GPU on the GPU boxes)",
             "sample": f"{done} oracle {what} on {n} forked workers (one per core, each cycling "
                       f"over its share of the {x.B} requests of the same seeded batch), fp64 "
                       f"numpy; wall time includes the pool start",
@@ -374,7 +386,7 @@ def bench_mask(args):
         call.run()
     torch.cuda.synchronize()
     K = args.steps
-    every = max(1, args.time_every)
+    every = args.time_every if args.time_every > 0 else 4
     timer = sv.KernelTimer(len(range(0, K, every)))
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -737,27 +749,26 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    every = max(1, args.time_every)
-    timed = list(range(0, K, every))
-    timer = sv.KernelTimer(len(timed))
+    every = args.time_every
+    timed = list(range(0, K, every)) if every > 0 else []
+    timer = sv.KernelTimer(len(timed)) if timed else None
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for i in range(K):
-        step(i, timer.pair(i // every) if i % every == 0 else None)
+        step(i, timer.pair(i // every) if timed and i % every == 0 else None)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     gpu_ms = ev0.elapsed_time(ev1)
-    first_ms = np.array([timer.elapsed_ms(j) for j in range(len(timed))])
-    timer.close()
+    in_loop_ms = np.array([timer.elapsed_ms(j) for j in range(len(timed))]) if timed else None
+    if timer:
+        timer.close()
     ms_per_step = wall * 1e3 / K
     value = positions * K / wall
-    kern_ms = float(first_ms.mean())
-    achieved = algo_bytes / (kern_ms * 1e-3) / 1e9
     kname = "row_argmax" if tree else "row_stats"
     traffic = load_traffic(kname, args.workload)
 
@@ -765,6 +776,43 @@ def main():
     torch.cuda.synchronize()
     status = int(out.status[0].item())
     gpu_out = [o.cpu().numpy() for o in out]
+
+    # the dominant kernel (and the chain's accept / resample kernel) over
+    # launch-attached events, in a leg of its own: one full call per rep through
+    # the two stage calls, buffer sets rotated as in the timed steps
+    reps = max(1, args.kernel_reps)
+    kt = sv.KernelTimer(reps)
+    mt = None if tree else sv.KernelTimer(reps)
+    for i in range(reps):
+        c = calls[i % R]
+        if tree:
+            c.row_argmax(kt.pair(i))
+            c.walk()
+        else:
+            c.row_stats(kt.pair(i))
+            c.accept_resample(mt.pair(i))
+    torch.cuda.synchronize()
+    first_ms = np.array([kt.elapsed_ms(i) for i in range(reps)])
+    kt.close()
+    kern_ms = float(np.median(first_ms))
+    achieved = algo_bytes / (kern_ms * 1e-3) / 1e9
+    mass = None
+    if mt is not None:
+        mass_ms = np.array([mt.elapsed_ms(i) for i in range(reps)])
+        mt.close()
+        lens = x.lengths()
+        # the sampling row(s) each request reads: target and draft row at a
+        # rejection, the target's bonus row when every draft is accepted
+        mass_bytes = int(sum((2 if gpu_out[0][b] < lens[b] else 1) * x.V * elem
+                             for b in range(x.B)))
+        mm = float(np.median(mass_ms))
+        mass = {"kernel": "resolve_mass", "bound": "hbm",
+                "algorithmic_bytes_per_launch": mass_bytes,
+                "rejected_requests": int(sum(gpu_out[0][b] < lens[b] for b in range(x.B))),
+                "kernel_ms_median": mm, "kernel_ms_p10": float(np.percentile(mass_ms, 10)),
+                "kernel_ms_p90": float(np.percentile(mass_ms, 90)),
+                "achieved": mass_bytes / (mm * 1e-3) / 1e9,
+                "frac": mass_bytes / (mm * 1e-3) / 1e9 / PEAK_HBM_GBS}
     graph = None
     if args.graph > 0:
         gs = torch.cuda.Stream()
@@ -810,13 +858,16 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": kname, "algorithmic_bytes_per_launch": algo_bytes,
-                     "kernel_ms_mean": kern_ms, "kernel_ms_median": float(np.median(first_ms)),
+                     "kernel_ms_median": kern_ms, "kernel_ms_mean": float(first_ms.mean()),
                      "kernel_ms_p10": float(np.percentile(first_ms, 10)),
                      "kernel_ms_p90": float(np.percentile(first_ms, 90)),
-                     "kernel_timing": f"HIP events attached to the launch in every {every}-th timed "
-                                      f"step ({len(timed)} launches)",
+                     "kernel_timing": f"median of {reps} launch-attached HIP event pairs, one per "
+                                      f"full call in a leg after the timed steps",
+                     "in_loop_kernel_ms_median": (float(np.median(in_loop_ms))
+                                                  if in_loop_ms is not None else None),
                      "read_stream": ceiling,
                      "frac_of_read_stream": (achieved / ceiling["gbs_median"]) if ceiling else None},
+        "mass_kernel": mass,
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_pool,
         "graph_steady_state": graph,

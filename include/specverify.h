@@ -191,8 +191,9 @@ sv_status sv_chain_row_stats_timed(const void *target_logits, int64_t ld_t,
  * and the launches selected: stages = 1 runs the row-statistics launch,
  * 2 the accept / resample launches (after a stage-1 call of the same
  * arguments on the same stream and workspace), 3 both.  kernel_start /
- * kernel_stop (either may be NULL) time the row-statistics kernel as in
- * sv_chain_row_stats_timed.  In logit space a row-statistics job reads the
+ * kernel_stop (either may be NULL) time the call's first launch as in
+ * sv_chain_row_stats_timed: the row-statistics kernel for stages 1 and 3,
+ * the accept / resample kernel for stages = 2.  In logit space a row-statistics job reads the
  * target and draft chunks of a position together, so each drafted row is
  * still read once.  SV_EINVAL also for an unknown mix_space or stages.
  */

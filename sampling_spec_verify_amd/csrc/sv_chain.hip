@@ -374,6 +374,8 @@ struct SampleCtx {
     float sq, iq;           // draft row:  q(v)   = 2^(z c - sq) * iq
     float w_t, w_q;         // mixture weights (1 - lambda, lambda)
     float mx[4];            // logit space: (1 - lambda) c and lambda c, each as hi + lo
+    float d_hi, d_lo;       // residual: q(v) / p(v) = 2^((z_q - z_t) (d_hi + d_lo) + k0)
+    float k0;               //   (d = c, or (1 - lambda) c in logit space)
     int logit;              // the target-slot statistics are those of the mixed logits
     int V;
 };
@@ -407,6 +409,15 @@ __device__ __forceinline__ void load_vec(const SampleCtx &S, int64_t gv, u32x4 &
 
 // Weights of one 16-byte vector; elements past V hold -inf logits and weigh 0.
 // `s_use` is the bonus shift.
+//
+// Residual: max(0, p(v) - q(v)) = p(v) max(0, 1 - q(v) / p(v)), with p = p_t
+// (or the logit-space p~) and q(v) / p(v) = 2^e(v),
+// e(v) = (z_q(v) - z_t(v)) d + k0, k0 = (s_p - s_q) + log2(S_p / S_q) formed in
+// fp64 once per request.  Every factor carries a few fp32 ulps of error
+// relative to the weight itself, however close p and q are: subtracting the
+// two probabilities would leave an error relative to p instead, which grows
+// without bound relative to the residual mass as the draft approaches the
+// target.  The common factor 1 / S_p is left out (the law is normalised).
 template <class DT, int MODE>
 __device__ __forceinline__ void vec_weights(const SampleCtx &S, const u32x4 &dt, const u32x4 &dq,
                                             float s_use, float *w) {
@@ -418,32 +429,27 @@ __device__ __forceinline__ void vec_weights(const SampleCtx &S, const u32x4 &dt,
     for (int e = 0; e < VEC; ++e) {
         if (MODE == kBonus) {
             w[e] = pow2_logit(ft[e], S.c_hi, S.c_lo, s_use);
-        } else if (MODE == kResidualLogit) {
-            const float pe = pow2_mixed(ft[e], fq[e], S.mx, S.st) * S.it;
-            const float pq = pow2_logit(fq[e], S.c_hi, S.c_lo, S.sq) * S.iq;
-            w[e] = fmaxf(pe - pq, 0.0f);
         } else {
-            const float et = pow2_logit(ft[e], S.c_hi, S.c_lo, S.st);
-            const float pq = pow2_logit(fq[e], S.c_hi, S.c_lo, S.sq) * S.iq;
-            w[e] = fmaxf(fmaf(et, S.it, -pq), 0.0f);
+            const float ep = (MODE == kResidualLogit) ? pow2_mixed(ft[e], fq[e], S.mx, S.st)
+                                                      : pow2_logit(ft[e], S.c_hi, S.c_lo, S.st);
+            const float d = fq[e] - ft[e];
+            w[e] = ep * one_minus_exp2(fmaf(d, S.d_hi, fmaf(d, S.d_lo, S.k0)));
         }
     }
 }
 
-// Sum of one vector's weights: a pairwise fp32 tree (adjacent pairs first),
-// widened once.  Its relative error stays below 3 * 2^-24 of the vector's
-// mass, so every inverse-CDF boundary built from these sums moves by less
-// than 2e-7 of the total.
+// Sum of one vector's weights in fp64 (adjacent pairs first): the fp32
+// weights add without rounding error that matters (below 2^-50 of the sum).
 template <int VEC>
 __device__ __forceinline__ double vec_sum(const float *w) {
-    float p[VEC];
+    double p[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) p[e] = w[e];
+    for (int e = 0; e < VEC; ++e) p[e] = static_cast<double>(w[e]);
 #pragma unroll
     for (int h = 1; h < VEC; h *= 2)
 #pragma unroll
         for (int e = 0; e + h < VEC; e += 2 * h) p[e] = p[e] + p[e + h];
-    return static_cast<double>(p[0]);
+    return p[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -770,6 +776,9 @@ __device__ __forceinline__ SampleCtx sample_ctx(const ChainArgs &a, int b, const
     S.mx[2] = a.be_hi;
     S.mx[3] = a.be_lo;
     S.logit = a.space;
+    S.d_hi = a.space ? a.al_hi : a.c_hi;
+    S.d_lo = a.space ? a.al_lo : a.c_lo;
+    S.k0 = r.k0;
     S.row_t = row_ptr(a.g, 0, b, r.row);
     S.row_q = (r.mode != kBonus) ? row_ptr(a.g, 1, b, r.row) : nullptr;
     S.st = r.st;
@@ -1077,7 +1086,7 @@ __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int stage
     const int n = sh.n, K = sh.K;
     ReqRecord r;
     r.n = n;
-    r.st = r.sq = r.it = r.iq = 0.0f;
+    r.st = r.sq = r.it = r.iq = r.k0 = 0.0f;
     if (n < K) {
         r.mode = (a.space == 1) ? kResidualLogit : kResidual;
         r.row = sh.rowi[n];
@@ -1087,6 +1096,10 @@ __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int stage
         r.sq = sh.s[2 * n + 1];
         r.it = static_cast<float>(1.0 / sh.S[2 * n]);
         r.iq = static_cast<float>(1.0 / sh.S[2 * n + 1]);
+        // q(v) / p(v) = 2^((z_q - z_t) d + k0): the shifts are integers, the
+        // sums fp64; 0 exactly for two identical rows
+        r.k0 = static_cast<float>((static_cast<double>(sh.s[2 * n]) - static_cast<double>(sh.s[2 * n + 1])) +
+                                  log2(sh.S[2 * n] / sh.S[2 * n + 1]));
     } else {
         r.mode = kBonus;
         r.row = sh.rowi[K];
@@ -1284,12 +1297,15 @@ sv_status run_typed(const ChainReq &q, int which) {
         const size_t lds = std::max(staged ? static_cast<size_t>(stage_n) * (sizeof(double) + 2 * sizeof(float)) : 0,
                                     static_cast<size_t>(n_pieces) * (sizeof(double) + sizeof(float)));
         const dim3 grid(static_cast<unsigned>(q.B), static_cast<unsigned>(a.C2));
+        // the events time the call's first launch: this one when it runs alone
+        hipEvent_t e0 = (which & 1) ? nullptr : q.ev_start, e1 = (which & 1) ? nullptr : q.ev_stop;
+        const uint32_t ldsb = static_cast<uint32_t>(lds);
         if (a.NV2 == 8) {
-            hipLaunchKernelGGL((k_resolve_mass<DT, 8>), grid, dim3(kBlock2), lds, q.stream, a, staged);
+            launch_timed(k_resolve_mass<DT, 8>, grid, dim3(kBlock2), ldsb, q.stream, e0, e1, a, staged);
         } else if (a.NV2 == 4) {
-            hipLaunchKernelGGL((k_resolve_mass<DT, 4>), grid, dim3(kBlock2), lds, q.stream, a, staged);
+            launch_timed(k_resolve_mass<DT, 4>, grid, dim3(kBlock2), ldsb, q.stream, e0, e1, a, staged);
         } else {
-            hipLaunchKernelGGL((k_resolve_mass<DT, 2>), grid, dim3(kBlock2), lds, q.stream, a, staged);
+            launch_timed(k_resolve_mass<DT, 2>, grid, dim3(kBlock2), ldsb, q.stream, e0, e1, a, staged);
         }
         if (hipGetLastError() != hipSuccess) return SV_EHIP;
     }

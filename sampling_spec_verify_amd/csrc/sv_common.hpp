@@ -41,6 +41,7 @@ struct alignas(16) ReqRecord {
     int rows_ok;    // the residual rows have valid statistics
     float st, sq;   // integer shifts of the target and draft rows: p(v) = 2^(z c - s) / S
     float it, iq;   // 1 / S of the target and draft rows
+    float k0;       // residual: q(v) / p(v) = 2^((z_q(v) - z_t(v)) d + k0)
 };
 
 // Request geometry of the chain and path calls.

@@ -143,6 +143,28 @@ __device__ __forceinline__ double exp2_d(double x) {
     return ldexp(1.41421356237309504880 * p, static_cast<int>(k));
 }
 
+// max(0, 1 - 2^e) in fp32 with an error of a few ulps relative to the result
+// itself, also where 2^e is close to 1 (the residual weight of an element whose
+// two probabilities nearly agree).  0 for e >= 0 and for NaN.  For -1 <= e < 0
+// it is -expm1(y), y = e ln 2 in [-0.694, 0), by its Taylor series
+// y + y^2/2! + ... + y^9/9! (truncation below 1.1e-8 relative); below -1 it is
+// 1 - 2^e, where 2^e < 1/2 and the subtraction loses at most one bit.
+__device__ __forceinline__ float one_minus_exp2(float e) {
+    const float y = e * 0.693147180559945309f;
+    float p = 1.0f / 362880.0f;                     // 1/9!: the series of expm1(y)/y
+    p = fmaf(p, y, 1.0f / 40320.0f);
+    p = fmaf(p, y, 1.0f / 5040.0f);
+    p = fmaf(p, y, 1.0f / 720.0f);
+    p = fmaf(p, y, 1.0f / 120.0f);
+    p = fmaf(p, y, 1.0f / 24.0f);
+    p = fmaf(p, y, 1.0f / 6.0f);
+    p = fmaf(p, y, 0.5f);
+    p = fmaf(p, y, 1.0f);
+    const float small = -y * p;
+    const float large = 1.0f - __builtin_amdgcn_exp2f(e);
+    return (e < -1.0f) ? large : ((e < 0.0f) ? small : 0.0f);
+}
+
 // ---------------------------------------------------------------------------
 // lane moves
 // ---------------------------------------------------------------------------

@@ -58,6 +58,7 @@ struct MultiArgs {
     const float *u_accept, *u_sample;
     float lam, c_hi, c_lo;
     double c_d, al, be;                   // log2(e)/T; logit space: (1 - lambda) c, lambda c
+    float d_hi, d_lo;                     // c (or (1 - lambda) c in logit space) as hi + lo
     int space;                            // 0 probability space, 1 logit space
     int32_t *accepted, *out_tokens, *accepted_nodes;
     float *accept_prob;                   // [B, N] or NULL
@@ -80,6 +81,7 @@ struct MultiShared {
     int redi[kMW];
     double sA, SA, sB, SB;                // statistics of the two rows (A: target or mixed)
     double iA, iB;                        // 1 / SA, 1 / SB
+    float k0;                             // q(v) / A(v) = 2^((z_q - z_t) d + k0)
     double gath[kMaxG][kSlot];            // every block's published values after a barrier
     int flags, decision, token, broken;
 };
@@ -195,8 +197,11 @@ __device__ __forceinline__ void publish_vals(const MultiArgs &a, int phase, cons
 }
 
 // The tree's barrier; then sh.gath holds every block's published values.
-// Every thread calls it with the same phase count, which it advances.
+// Every thread calls it with the same phase count, which it advances.  It
+// starts with a block barrier: the polling threads overwrite sh.gath, which
+// other waves of the block may still be reading from the barrier before.
 __device__ void tree_barrier(const MultiArgs &a, MultiShared &sh, int &phase, int n) {
+    __syncthreads();
     ++phase;
     if (static_cast<int>(threadIdx.x) < a.G * n) {
         const int g = static_cast<int>(threadIdx.x) / n, j = static_cast<int>(threadIdx.x) % n;
@@ -251,6 +256,22 @@ __device__ __forceinline__ void m_probs(const MultiArgs &a, const MultiShared &s
         const double pt = static_cast<double>(m_pow2(zt, a.c_hi, a.c_lo, static_cast<float>(sh.sA))) * iA;
         pm = (1.0 - static_cast<double>(a.lam)) * pt + static_cast<double>(a.lam) * q;
     }
+}
+
+// The first residual at a node, max(0, p~(v) - q(v)), as an fp32 weight:
+// (1 - lambda) p_t(v) max(0, 1 - q(v)/p_t(v)) in probability space (the
+// mixture equation gives p~ - q = (1 - lambda)(p_t - q)), p~(v) max(0,
+// 1 - q(v)/p~(v)) in logit space, with the ratio 2^e, e = (z_q - z_t) d + k0
+// (sv_device one_minus_exp2: error relative to the weight, however close the
+// rows are).  The residual pass and the child tests both form it here.
+__device__ __forceinline__ float first_residual(const MultiArgs &a, const MultiShared &sh, float zt, float zq) {
+    const float d = zq - zt;
+    const float g = one_minus_exp2(fmaf(d, a.d_hi, fmaf(d, a.d_lo, sh.k0)));
+    if (a.space == 1)
+        return static_cast<float>(static_cast<double>(m_pow2_mixed(zt, zq, a.al, a.be, static_cast<float>(sh.sA))) *
+                                  sh.iA * static_cast<double>(g));
+    const double pt = static_cast<double>(m_pow2(zt, a.c_hi, a.c_lo, static_cast<float>(sh.sA))) * sh.iA;
+    return static_cast<float>((1.0 - static_cast<double>(a.lam)) * pt * static_cast<double>(g));
 }
 
 // ---- passes ----------------------------------------------------------------
@@ -345,12 +366,14 @@ __device__ void pass_stats(const MultiArgs &a, MultiShared &sh, int &phase, cons
         sh.SB = target_only ? 1.0 : SBt;
         sh.iA = 1.0 / SAt;
         sh.iB = target_only ? 1.0 : 1.0 / SBt;
+        sh.k0 = target_only ? 0.0f : static_cast<float>((tA - tB) + log2(SAt / SBt));
     }
     __syncthreads();
 }
 
 // Residual after a rejection: w(v) = max(0, r(v) - q(v)) with r = p~ (first
-// rejection, from the logits) or the previous residual in[v] / Zin; w is
+// rejection, from the logits: first_residual) or the previous residual
+// in[v] / Zin; w is
 // stored (fp32) in out, where only this block reads it again (its slice), and
 // its fp64 sum over the tree's slices returned.  The child tests form w at a
 // child's token again from the same values and operations.
@@ -380,10 +403,14 @@ __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, int &phase,
             for (int e = 0; e < VEC; ++e) {
                 const int v = gv * VEC + e;
                 if (v >= V) break;
-                double pm, q;
-                m_probs<DT>(a, sh, ft[e], fq[e], pm, q);
-                const double r = (in == nullptr) ? pm : static_cast<double>(in[v]) / Zin;
-                const float w = static_cast<float>(fmax(0.0, r - q));
+                float w;
+                if (in == nullptr) {
+                    w = first_residual(a, sh, ft[e], fq[e]);
+                } else {
+                    double pm, q;
+                    m_probs<DT>(a, sh, ft[e], fq[e], pm, q);
+                    w = static_cast<float>(fmax(0.0, static_cast<double>(in[v]) / Zin - q));
+                }
                 out[v] = w;
                 tot += static_cast<double>(w);
             }
@@ -627,11 +654,11 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
                         }
                     } else {
                         // the stored residual at x, formed again with the residual
-                        // pass's own operations from p~(x), q(x) and the masses
+                        // pass's own operations from the logits, q(x) and the masses
                         double pm;
                         m_probs<DT>(a, sh, zt, zq, pm, q);
-                        r = pm;
-                        for (int j = 1; j <= nrej; ++j)
+                        r = static_cast<double>(first_residual(a, sh, zt, zq)) / sh.zs[1];
+                        for (int j = 2; j <= nrej; ++j)
                             r = static_cast<double>(static_cast<float>(fmax(0.0, r - q))) / sh.zs[j];
                     }
                     if (q == 0.0) {
@@ -781,6 +808,12 @@ sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const vo
     a.space = (mix_space == SV_MIX_LOGIT && lambda > 0.0f && lambda < 1.0f) ? 1 : 0;
     a.al = (1.0 - static_cast<double>(lambda)) * a.c_d;
     a.be = static_cast<double>(lambda) * a.c_d;
+    if (a.space == 1) {
+        split_positive(a.al, &a.d_hi, &a.d_lo);
+    } else {
+        a.d_hi = a.c_hi;
+        a.d_lo = a.c_lo;
+    }
     a.accepted = accepted;
     a.out_tokens = out_tokens;
     a.accepted_nodes = accepted_nodes;

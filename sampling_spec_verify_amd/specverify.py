@@ -297,9 +297,10 @@ class ChainCall:
             _check(lib().sv_chain_row_stats_timed(*self._cached, *events),
                    "sv_chain_row_stats_timed")
 
-    def accept_resample(self) -> ChainOut:
-        if self.space != SV_MIX_PROB:
-            self._ex(2)
+    def accept_resample(self, events=None) -> ChainOut:
+        """Launch the accept / resample kernel; ``events`` = (start, stop) times it."""
+        if self.space != SV_MIX_PROB or events is not None:
+            self._ex(2, events)
         else:
             _check(lib().sv_chain_accept_resample(*self._cached), "sv_chain_accept_resample")
         return self.out

@@ -69,6 +69,16 @@ def uniforms(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.random(shape, dtype=np.float32)
 
 
+def raise_uniforms(u: np.ndarray, eps: float) -> np.ndarray:
+    """Map grid uniforms u in [0, 1) onto the top of the interval, [1 - eps, 1):
+    1 - m 2^-24 with m = max(1, round(eps (1 - u) 2^24)), still on the grid.
+    Acceptance uniforms this high reject most drafts whose ratio is below one,
+    which makes a close draft produce residual draws."""
+    k = np.rint((1.0 - np.asarray(u, dtype=np.float64)) * 2.0 ** 24)
+    m = np.maximum(1.0, np.rint(eps * k))
+    return (1.0 - m * 2.0 ** -24).astype(np.float32)
+
+
 def zipf_bias(rng: np.random.Generator, rows: int, V: int, slope: float = 1.1) -> np.ndarray:
     """[rows, V] fp32: rank r (1-based) of a fresh permutation gets -slope*ln(r)."""
     ranks = -slope * np.log(np.arange(1, V + 1, dtype=np.float64))

@@ -55,10 +55,13 @@ def oracle_chain(x: ChainInputs, requests=None, space: str = "prob"):
 
 
 def flag_limit(requests: int) -> int:
-    """Most boundary-flagged requests a comparison may excuse.  A request makes
-    at most 65 draws, each within the 1e-6 band of its boundary with probability
-    at most 2e-6, so even 5000 requests expect fewer than one flagged request."""
-    return 2 + requests // 5000
+    """Most boundary-flagged requests a comparison may excuse: 1 + requests / 16.
+    An acceptance draw falls in the 1e-6 band of its ratio with probability
+    2e-6; a sampling draw falls in the band of some CDF boundary with
+    probability up to 2e-6 per token of the law's support (about 1 % at
+    V = 1500, more where many tokens carry under 2e-6 of mass each).  A band of
+    1e-3, or an inverted test, would flag nearly every request."""
+    return 1 + requests // 16
 
 
 def compare_chain(x: ChainInputs, g, ref, requests=None, lengths=None):

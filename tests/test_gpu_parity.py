@@ -45,6 +45,8 @@ def test_chain_workload(cfg):
     assert int(g.status[0]) == 0, sv.decode_flags(int(g.status[0]))
     stats = compare_chain(x, g, oracle_chain(x))
     report(cfg, stats)
+    if x.B == 1:                     # a single request is checked outright, never excused
+        assert stats["flagged"] == 0
 
 
 def test_tree_workload_greedy():
@@ -73,6 +75,7 @@ def test_c2_more_seeds(seed_offset):
     x = synth.config("c2", seed_offset)
     stats = compare_chain(x, run_chain(x), oracle_chain(x))
     report(f"c2/{seed_offset}", stats)
+    assert stats["flagged"] == 0
 
 
 # ---------------------------------------------------------------------------
