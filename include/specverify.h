@@ -39,7 +39,9 @@
  *  - `workspace` is caller-owned device scratch of at least the size the
  *    matching *_workspace_bytes() reports, 16-byte aligned, and not shared by
  *    calls that may run concurrently.  Its contents need no initialisation.
- *  - The library keeps no state and is thread-safe.
+ *  - The library keeps no state and is thread-safe, apart from the per-device
+ *    address of the fixed scratch array of sv_chain_verify_noalloc, looked up
+ *    once per device under a lock.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -60,7 +62,8 @@ typedef enum {
     SV_EALIGN = 3,      /* a logits pointer or row stride is not 16-byte aligned, or ld < V */
     SV_EWORKSPACE = 4,  /* workspace NULL, misaligned or smaller than required */
     SV_EDTYPE = 5,      /* unknown sv_dtype */
-    SV_EHIP = 6         /* a kernel launch failed */
+    SV_EHIP = 6,        /* a kernel launch failed */
+    SV_ETOOBIG = 7      /* sv_chain_verify_noalloc: the sizes need more than its fixed scratch */
 } sv_status;
 
 typedef enum { SV_BF16 = 0, SV_F32 = 1 } sv_dtype;
@@ -138,6 +141,33 @@ sv_status sv_chain_verify(const void *target_logits, int64_t ld_t,
                           int32_t *accepted, int32_t *out_tokens, float *accept_prob,
                           int32_t *status, void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/* Bytes of the device scratch array that sv_chain_verify_noalloc uses in
+ * place of a workspace (one array per GPU, held until the process ends). */
+#define SV_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * sv_chain_verify for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as sv_chain_verify, without the workspace: the
+ * call uses a file-scope device array of SV_NOALLOC_SCRATCH_BYTES bytes,
+ * whose address on the current device it looks up once (hipGetSymbolAddress)
+ * on its first call there.  It calls no hipMalloc, hipFree or other
+ * allocating routine.  Sizes whose workspace (sv_chain_workspace_bytes)
+ * exceeds that array return SV_ETOOBIG before any HIP call; other argument
+ * errors as sv_chain_verify.  Every call on one GPU shares that GPU's array
+ * and nothing in it needs to start cleared (each call re-initialises what it
+ * reads); calls that may overlap on one GPU (other streams, other host
+ * threads) race on it and must be serialised by the caller.
+ */
+sv_status sv_chain_verify_noalloc(const void *target_logits, int64_t ld_t,
+                                  const void *draft_logits, int64_t ld_q,
+                                  sv_dtype dtype, int B, int K, int V,
+                                  const int32_t *draft_tokens, const int32_t *draft_len,
+                                  const float *u_accept, const float *u_sample,
+                                  float lambda, float temperature,
+                                  int32_t *accepted, int32_t *out_tokens, float *accept_prob,
+                                  int32_t *status, hipStream_t stream);
 
 /*
  * The two launches sv_chain_verify makes, exposed so that a caller can time or

@@ -54,6 +54,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "sv_common.hpp"
 #include "sv_device.hpp"
@@ -1188,7 +1189,8 @@ int choose_nv_mode(const ChainReq &q, int vec) {
     return choose_nv(q.B, pcap(q), q.V, vec);
 }
 
-sv_status validate(const ChainReq &q) {
+// Everything but the workspace.
+sv_status validate_args(const ChainReq &q) {
     const int eb = elem_bytes(q.dtype);
     if (eb == 0) return SV_EDTYPE;
     if (q.B < 0 || q.P < 0 || q.P > SV_MAX_POSITIONS || q.V < 1 || q.N < 0 ||
@@ -1209,6 +1211,12 @@ sv_status validate(const ChainReq &q) {
         }
     }
     if (int64_t(q.B) * pcap(q) * 2 * c1_for(q.V, kMinNV, kMinVec) >= (int64_t(1) << 31)) return SV_EINVAL;
+    return SV_OK;
+}
+
+sv_status validate(const ChainReq &q) {
+    const sv_status st = validate_args(q);
+    if (st != SV_OK || q.B == 0) return st;
     const ChainLayout L = chain_layout(q.B, pcap(q), q.V);
     if (!q.ws || !aligned16(q.ws) || q.ws_bytes < static_cast<size_t>(L.total)) return SV_EWORKSPACE;
     return SV_OK;
@@ -1389,6 +1397,35 @@ ChainReq chain_req(const void *t, int64_t ld_t, const void *d, int64_t ld_q, sv_
 
 }  // namespace
 
+// Workspace of sv_chain_verify_noalloc: one copy per GPU, held until the
+// process ends.  Its name is a host-side stand-in in host code; the kernels
+// get the device address that hipGetSymbolAddress returns for the current
+// device.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];      // device address of `scratch`, per device, once looked up
+
+// The current device's copy of `scratch`, looked up on the first call made
+// with that device current.
+sv_status scratch_for_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SV_EHIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return SV_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *sv_status_string(sv_status s) {
@@ -1400,6 +1437,7 @@ const char *sv_status_string(sv_status s) {
         case SV_EWORKSPACE: return "SV_EWORKSPACE: workspace missing, misaligned or too small";
         case SV_EDTYPE: return "SV_EDTYPE: unknown dtype";
         case SV_EHIP: return "SV_EHIP: kernel launch failed";
+        case SV_ETOOBIG: return "SV_ETOOBIG: the call needs more scratch than sv_chain_verify_noalloc holds";
     }
     return "unknown sv_status";
 }
@@ -1421,6 +1459,24 @@ sv_status sv_chain_verify(const void *target_logits, int64_t ld_t, const void *d
                                accepted, out_tokens, accept_prob, status, workspace,
                                workspace_bytes, stream),
                      3);
+}
+
+sv_status sv_chain_verify_noalloc(const void *target_logits, int64_t ld_t, const void *draft_logits,
+                                  int64_t ld_q, sv_dtype dtype, int B, int K, int V,
+                                  const int32_t *draft_tokens, const int32_t *draft_len,
+                                  const float *u_accept, const float *u_sample, float lambda,
+                                  float temperature, int32_t *accepted, int32_t *out_tokens,
+                                  float *accept_prob, int32_t *status, hipStream_t stream) {
+    ChainReq q = chain_req(target_logits, ld_t, draft_logits, ld_q, dtype, B, K, V, draft_tokens,
+                           draft_len, u_accept, u_sample, lambda, temperature, accepted,
+                           out_tokens, accept_prob, status, nullptr, 0, stream);
+    sv_status st = validate_args(q);
+    if (st != SV_OK || q.B == 0) return st;
+    if (chain_layout(q.B, pcap(q), q.V).total > static_cast<int64_t>(SV_NOALLOC_SCRATCH_BYTES))
+        return SV_ETOOBIG;
+    if ((st = scratch_for_current_device(&q.ws)) != SV_OK) return st;
+    q.ws_bytes = SV_NOALLOC_SCRATCH_BYTES;
+    return q.dtype == SV_BF16 ? run_typed<Bf16>(q, 3) : run_typed<F32>(q, 3);
 }
 
 sv_status sv_chain_row_stats(const void *target_logits, int64_t ld_t, const void *draft_logits,

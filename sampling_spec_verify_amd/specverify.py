@@ -16,7 +16,8 @@ from typing import NamedTuple, Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
-SV_OK, SV_EINVAL, SV_ENULL, SV_EALIGN, SV_EWORKSPACE, SV_EDTYPE, SV_EHIP = range(7)
+SV_OK, SV_EINVAL, SV_ENULL, SV_EALIGN, SV_EWORKSPACE, SV_EDTYPE, SV_EHIP, SV_ETOOBIG = range(8)
+SV_NOALLOC_SCRATCH_BYTES = 16 << 20
 SV_BF16, SV_F32 = 0, 1
 SV_MIX_PROB, SV_MIX_LOGIT = 0, 1
 MIX_SPACES = {"prob": SV_MIX_PROB, "logit": SV_MIX_LOGIT}
@@ -44,6 +45,7 @@ SIGNATURES = {
     "sv_status_string": ([_I], ctypes.c_char_p),
     "sv_chain_workspace_bytes": ([_I, _I, _I], _S),
     "sv_chain_verify": (_CHAIN_ARGS, _I),
+    "sv_chain_verify_noalloc": (_CHAIN_ARGS[:18] + [_P], _I),
     "sv_chain_row_stats": (_CHAIN_ARGS, _I),
     "sv_chain_accept_resample": (_CHAIN_ARGS, _I),
     "sv_chain_row_stats_timed": (_CHAIN_ARGS + [_P, _P], _I),
@@ -304,6 +306,16 @@ class ChainCall:
         else:
             _check(lib().sv_chain_accept_resample(*self._cached), "sv_chain_accept_resample")
         return self.out
+
+
+def chain_verify_noalloc(call: "ChainCall") -> ChainOut:
+    """sv_chain_verify_noalloc on the inputs and outputs bound to ``call`` (its
+    workspace is not used: the library's own per-GPU scratch array is)."""
+    if call.space != SV_MIX_PROB:
+        raise ValueError("sv_chain_verify_noalloc mixes in probability space")
+    args = call._cached
+    _check(lib().sv_chain_verify_noalloc(*args[:18], args[20]), "sv_chain_verify_noalloc")
+    return call.out
 
 
 def chain_verify(target, draft, tokens, u_accept, u_sample, lam: float = 0.0,

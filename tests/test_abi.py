@@ -22,6 +22,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["sv_status_string", "sv_chain_workspace_bytes", "sv_chain_verify",
+                            "sv_chain_verify_noalloc",
                             "sv_chain_acceptance_workspace_bytes", "sv_chain_acceptance_rate",
                             "sv_chain_row_stats", "sv_chain_accept_resample",
                             "sv_chain_row_stats_timed", "sv_chain_verify_ex",
@@ -41,10 +42,48 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         s = sv.status_string(code)
         assert s.startswith("SV_")
     assert "unknown" in sv.status_string(99)
+
+
+def _header_enum(name):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef enum \{([^}]*)\} " + name + ";", text).group(1)
+    return {k: int(v) for k, v in re.findall(r"(SV_[A-Z0-9_]+)\s*=\s*(\d+)", body)}
+
+
+def test_status_codes_and_data_bits():
+    """The return codes and data-status bits the header fixes.  Against the
+    survey's sketch of the boundary they differ on purpose: SV_ESHAPE is not
+    used (shape errors are SV_EINVAL), SV_ENULL, SV_EALIGN and SV_ETOOBIG are
+    added, so the codes are renumbered; data errors are OR-ed bits of one
+    status word rather than a first-error code."""
+    codes = _header_enum("sv_status")
+    assert codes == {"SV_OK": 0, "SV_EINVAL": 1, "SV_ENULL": 2, "SV_EALIGN": 3,
+                     "SV_EWORKSPACE": 4, "SV_EDTYPE": 5, "SV_EHIP": 6, "SV_ETOOBIG": 7}
+    for k, v in codes.items():
+        assert getattr(sv, k) == v, k
+        assert sv.status_string(v).startswith(k + ":"), k
+    bits = dict(re.findall(r"#define (SV_DATA_[A-Z_]+)\s+(0x[0-9a-fA-F]+)", open(HEADER).read()))
+    assert {k[8:]: int(v, 16) for k, v in bits.items()} == {n: b for b, n in sv.DATA_FLAGS.items()}
+    vals = sorted(int(v, 16) for v in bits.values())
+    assert vals == [1 << i for i in range(len(vals))]          # one bit each: they OR together
+
+
+def test_noalloc_rejects_oversize_before_any_hip_call():
+    B, K, V = 2048, 64, 128256
+    assert sv.chain_workspace_bytes(B, K, V) > sv.SV_NOALLOC_SCRATCH_BYTES
+    p = ctypes.c_void_p(16)
+    code = sv.lib().sv_chain_verify_noalloc(p, V, p, V, sv.SV_BF16, B, K, V, p, None, p, p, 0.0,
+                                            1.0, p, p, None, None, None)
+    assert code == sv.SV_ETOOBIG
+    # argument errors still come first
+    assert sv.lib().sv_chain_verify_noalloc(p, V, p, V, sv.SV_BF16, B, K, V, p, None, p, p, 2.0,
+                                            1.0, p, p, None, None, None) == sv.SV_EINVAL
+    assert sv.lib().sv_chain_verify_noalloc(p, V, p, V, 9, B, K, V, p, None, p, p, 0.0,
+                                            1.0, p, p, None, None, None) == sv.SV_EDTYPE
 
 
 def test_workspace_sizes():
