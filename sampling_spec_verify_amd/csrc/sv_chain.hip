@@ -219,10 +219,13 @@ __device__ __forceinline__ void row_chunk_stats(const ChainArgs &a, unsigned job
 }
 
 // Zeroes the per-request counters of the mass blocks (launch 2), so that
-// every call starts from zero whatever the workspace held.
+// every call starts from zero whatever the workspace held.  The block size is
+// the compile-time THREADS: reading blockDim would cost every wave a load
+// from the dispatch packet before it can retire.
+template <int THREADS>
 __device__ __forceinline__ void clear_counts(const ChainArgs &a) {
-    for (int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x); i < a.B;
-         i += static_cast<int>(gridDim.x * blockDim.x))
+    for (int i = static_cast<int>(blockIdx.x) * THREADS + static_cast<int>(threadIdx.x); i < a.B;
+         i += static_cast<int>(gridDim.x) * THREADS)
         a.count[i] = 0;
 }
 
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(kStatsWaves * kWave) void k_row_stats(ChainArgs a, 
     // cleared last: a store ahead of the job's reads would keep the compiler
     // from issuing them as scalar loads
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
-    clear_counts(a);
+    clear_counts<kStatsWaves * kWave>(a);
 }
 
 // Logit-space mixture (the RAPID pseudocode mixes logits, enhanced =
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(kStatsWaves * kWave) void k_row_stats_logit(ChainAr
                                                    static_cast<int>(threadIdx.x) / kWave);
     if (job < n_jobs) row_chunk_stats_logit<DT, NV>(a, static_cast<unsigned>(job));
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
-    clear_counts(a);
+    clear_counts<kStatsWaves * kWave>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -439,18 +442,19 @@ __device__ __forceinline__ void vec_weights(const SampleCtx &S, const u32x4 &dt,
     }
 }
 
-// Sum of one vector's weights in fp64 (adjacent pairs first): the fp32
-// weights add without rounding error that matters (below 2^-50 of the sum).
+// Sum of one vector's weights: a pairwise fp32 tree (adjacent pairs first),
+// widened once.  The weights are non-negative, so its relative error stays
+// below 3 * 2^-24 of the vector's own mass.
 template <int VEC>
 __device__ __forceinline__ double vec_sum(const float *w) {
-    double p[VEC];
+    float p[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) p[e] = static_cast<double>(w[e]);
+    for (int e = 0; e < VEC; ++e) p[e] = w[e];
 #pragma unroll
     for (int h = 1; h < VEC; h *= 2)
 #pragma unroll
         for (int e = 0; e + h < VEC; e += 2 * h) p[e] = p[e] + p[e + h];
-    return p[0];
+    return static_cast<double>(p[0]);
 }
 
 // ---------------------------------------------------------------------------

@@ -145,24 +145,22 @@ __device__ __forceinline__ double exp2_d(double x) {
 
 // max(0, 1 - 2^e) in fp32 with an error of a few ulps relative to the result
 // itself, also where 2^e is close to 1 (the residual weight of an element whose
-// two probabilities nearly agree).  0 for e >= 0 and for NaN.  For -1 <= e < 0
-// it is -expm1(y), y = e ln 2 in [-0.694, 0), by its Taylor series
-// y + y^2/2! + ... + y^9/9! (truncation below 1.1e-8 relative); below -1 it is
-// 1 - 2^e, where 2^e < 1/2 and the subtraction loses at most one bit.
+// two probabilities nearly agree).  0 for e >= 0 and for NaN.  For
+// -1/2 <= e < 0 it is -expm1(e ln 2) by its Taylor series c1 e + ... + c7 e^7,
+// c_k = (ln 2)^k / k! (truncation below 1.6e-8 relative; 2 ulps in all, as
+// measured against fp64 over the interval); below -1/2 it is 1 - 2^e, where
+// 2^e < 0.71 and the subtraction loses under two bits.
 __device__ __forceinline__ float one_minus_exp2(float e) {
-    const float y = e * 0.693147180559945309f;
-    float p = 1.0f / 362880.0f;                     // 1/9!: the series of expm1(y)/y
-    p = fmaf(p, y, 1.0f / 40320.0f);
-    p = fmaf(p, y, 1.0f / 5040.0f);
-    p = fmaf(p, y, 1.0f / 720.0f);
-    p = fmaf(p, y, 1.0f / 120.0f);
-    p = fmaf(p, y, 1.0f / 24.0f);
-    p = fmaf(p, y, 1.0f / 6.0f);
-    p = fmaf(p, y, 0.5f);
-    p = fmaf(p, y, 1.0f);
-    const float small = -y * p;
+    float p = 1.5252733804059841e-05f;              // (ln 2)^7 / 7!
+    p = fmaf(p, e, 1.5403530393381608e-04f);
+    p = fmaf(p, e, 1.3333558146428443e-03f);
+    p = fmaf(p, e, 9.6181291076284772e-03f);
+    p = fmaf(p, e, 5.5504108664821580e-02f);
+    p = fmaf(p, e, 2.4022650695910071e-01f);
+    p = fmaf(p, e, 6.9314718055994531e-01f);        // ln 2
+    const float small = -e * p;
     const float large = 1.0f - __builtin_amdgcn_exp2f(e);
-    return (e < -1.0f) ? large : ((e < 0.0f) ? small : 0.0f);
+    return fmaxf((e < -0.5f) ? large : small, 0.0f);  // e >= 0 gives small <= 0; NaN gives 0
 }
 
 // ---------------------------------------------------------------------------
@@ -177,9 +175,11 @@ constexpr int kDppMirror = 0x140;
 // ds_swizzle bitmask mode: and 0x1f, or 0, xor 0x10 -> lane ^ 16 within 32
 constexpr int kSwzXor16 = 0x401F;
 
+// Lane permutations whose every lane has a source lane (quad perms and
+// mirrors), so no lane keeps an old value.
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v) {
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
 }
 __device__ __forceinline__ int swz16(int v) { return __builtin_amdgcn_ds_swizzle(v, kSwzXor16); }
 
@@ -207,14 +207,26 @@ __device__ __forceinline__ double readlane_d(double v, int lane) {
 // wavefront reductions (result is wave-uniform)
 // ---------------------------------------------------------------------------
 
+__device__ __forceinline__ int wave_max_i(int v);
+
+// Maximum over the wave of non-NaN floats, through integer keys: the key
+// flips the magnitude bits of negative values, so signed integer order is
+// float order (-0 and +0 map to -1 and 0 and come back unchanged).  Integer
+// maxima fuse with the lane moves, where a float maximum would first
+// canonicalise every moved value.
 __device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, f_of(dpp<kDppXor1>(i_of(v))));
-    v = fmaxf(v, f_of(dpp<kDppXor2>(i_of(v))));
-    v = fmaxf(v, f_of(dpp<kDppHalfMirror>(i_of(v))));
-    v = fmaxf(v, f_of(dpp<kDppMirror>(i_of(v))));
-    v = fmaxf(v, f_of(swz16(i_of(v))));
-    return fmaxf(f_of(__builtin_amdgcn_readlane(i_of(v), 0)),
-                 f_of(__builtin_amdgcn_readlane(i_of(v), 32)));
+    const int b = i_of(v);
+    const int k = wave_max_i(b ^ ((b >> 31) & 0x7fffffff));
+    return f_of(k ^ ((k >> 31) & 0x7fffffff));
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+    v = max(v, dpp<kDppXor1>(v));
+    v = max(v, dpp<kDppXor2>(v));
+    v = max(v, dpp<kDppHalfMirror>(v));
+    v = max(v, dpp<kDppMirror>(v));
+    v = max(v, swz16(v));
+    return max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
 }
 
 __device__ __forceinline__ int wave_min_i(int v) {

@@ -35,7 +35,7 @@ namespace sv {
 // equal to it (a lane's vectors, and the elements inside one, are in index
 // order).  The lane maxima use the NaN-propagating maximum (v_maximum3_f32),
 // so a NaN anywhere in a lane shows up in that lane's maximum and marks the
-// whole row bad; the wave maximum then ignores such lanes.  Signed zeros
+// whole row bad (the chunk's maximum and index then do not matter).  Signed zeros
 // compare equal in the position search, as in the first-maximum rule.
 // Elements past V read as -inf and sit above every valid index, so they never
 // win a tie.
