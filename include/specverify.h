@@ -419,14 +419,21 @@ sv_status sv_tree_verify_path_ex(const void *target_logits, int64_t ld_t,
  *  workspace: sv_tree_multi_workspace_bytes(B, N, V) bytes (two fp32
  *  residual rows per request).
  *
- * Each tree is walked by G cooperating 512-thread blocks (G up to 16, so
- * that B * G blocks fit the GPU at once), each owning a slice of the
- * vocabulary: every sum over the vocabulary is a pass of the blocks over their
- * slices, combined at a barrier of the tree's blocks.  The call is bound by
- * that chain of passes rather than by HBM bandwidth.  A tree's blocks wait
- * for one another: if other work on the GPU keeps some of them from starting
- * for about a second, the waiting blocks give up and SV_DATA_SYNC marks the
- * call's outputs invalid (rerun it when the GPU is free).
+ * Each tree is walked by G cooperating 512-thread blocks (G up to 16; by
+ * default as many as let all B * G blocks fit the GPU at once), each owning a
+ * slice of the vocabulary: every sum over the vocabulary is a pass of the
+ * blocks over their slices, combined at a barrier of the tree's blocks.  The
+ * call is bound by that chain of passes rather than by HBM bandwidth.
+ *
+ * Residency contract.  A tree's blocks wait for one another.  Each block takes
+ * its tree and slice from a start-order ticket, so a block only ever waits for
+ * blocks of a tree whose earlier blocks are already running: the call
+ * progresses whenever G of its blocks fit on the GPU at once (one per compute
+ * unit), whatever else runs there, and a grid wider than the GPU runs its
+ * trees in rounds.  SV_DATA_SYNC (outputs invalid; rerun the call) is set only
+ * if other work keeps a started tree's remaining blocks from starting for
+ * about a second.  G = 1 (sv_tree_verify_multi_ex) has no waits between
+ * blocks at all, at the cost of one compute unit's speed per tree.
  */
 size_t sv_tree_multi_workspace_bytes(int B, int N, int V);
 sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t,
@@ -439,6 +446,23 @@ sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t,
                                int32_t *accepted_nodes, float *accept_prob, int Dmax,
                                int32_t *status, void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
+
+/* sv_tree_verify_multi with the number of blocks per tree chosen by the
+ * caller: blocks_per_tree 0 is the automatic choice above, 1..16 asks for that
+ * many (fewer when the row has fewer 512-vector tiles than that); outside
+ * 0..16 returns SV_EINVAL.  Outputs follow the same rule for every choice; the
+ * acceptance values may differ in the last bits, since the per-slice sums are
+ * combined in another grouping. */
+sv_status sv_tree_verify_multi_ex(const void *target_logits, int64_t ld_t,
+                                  const void *draft_logits, int64_t ld_q,
+                                  sv_dtype dtype, int B, int N, int V,
+                                  const int32_t *parent, const int32_t *node_token,
+                                  const float *u_accept, const float *u_sample,
+                                  float lambda, float temperature, int mix_space,
+                                  int32_t *accepted, int32_t *out_tokens,
+                                  int32_t *accepted_nodes, float *accept_prob, int Dmax,
+                                  int32_t *status, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream, int blocks_per_tree);
 
 /* ------------------------------------------------------------------------
  * Measurement utility (not a step of the method)

@@ -66,6 +66,7 @@ struct MultiArgs {
     float *buf;                           // [B, 2, V] residual ping-pong
     int G;                                // blocks per tree; block g owns vocabulary slice g
     unsigned long long *pub;              // [B, G, 3, kSlot] values published at a barrier (bit patterns)
+    unsigned *ticket;                     // start-order counter that assigns each block its (tree, slice)
 };
 
 struct MultiShared {
@@ -84,6 +85,7 @@ struct MultiShared {
     float k0;                             // q(v) / A(v) = 2^((z_q - z_t) d + k0)
     double gath[kMaxG][kSlot];            // every block's published values after a barrier
     int flags, decision, token, broken;
+    int tree, slice;                      // this block's role, from its start-order ticket
 };
 
 // ---- block reductions (every thread calls; results uniform) ---------------
@@ -159,17 +161,25 @@ __device__ __forceinline__ Scan mblock_scan(double v, double carry, MultiShared 
 // reader has consumed it, since each reader published for barrier k after
 // reading it) for use at barrier k + 2, and it drains that store before it
 // publishes for barrier k + 1, so a reader that has passed barrier k + 1
-// finds the slot empty or holding the barrier-(k + 2) value.  The grid is sized to the GPU's resident capacity
-// (as many walk blocks as the compute units hold), so on a GPU without other work
-// every block runs at once; a poll gives up after kSpinLimit rounds, marking
-// the block broken (SV_DATA_SYNC), so every wave ends in any case.
+// finds the slot empty or holding the barrier-(k + 2) value.
+//
+// A block's role (tree, slice) is not its grid index but the ticket it takes
+// from a counter when it starts: ticket k is tree k / G, slice k % G.  Only
+// running blocks hold tickets and tickets are handed out in order, so every
+// tree below the newest ticket's has all its blocks running or done, and at
+// most one tree is still missing blocks.  The complete trees finish and free
+// their compute units, and the next blocks to start complete the last tree:
+// the walk progresses whenever G blocks fit on the GPU beside other work,
+// whatever the grid size (a grid wider than the GPU runs its trees in
+// rounds).  A poll still gives up after kSpinLimit rounds, marking the block
+// broken (SV_DATA_SYNC), so every wave ends in any case.
 
 struct Slice {
     int lo, hi;                            // vectors [lo, hi)
 };
 
-__device__ __forceinline__ Slice my_slice(const MultiArgs &a, int nvec) {
-    const int g = static_cast<int>(blockIdx.x) % a.G;
+__device__ __forceinline__ Slice my_slice(const MultiArgs &a, const MultiShared &sh, int nvec) {
+    const int g = sh.slice;
     const int per = (nvec + a.G - 1) / a.G;
     Slice s;
     s.lo = min(g * per, nvec);
@@ -180,16 +190,18 @@ __device__ __forceinline__ Slice my_slice(const MultiArgs &a, int nvec) {
 constexpr unsigned long long kEmpty = 0x7FF0DEAD5EED1234ull;   // an empty slot (a signalling NaN)
 constexpr int kRot = 3;                                            // slots per block, used in rotation
 
-__device__ __forceinline__ unsigned long long *pub_slot(const MultiArgs &a, int g, int phase) {
-    const int b = static_cast<int>(blockIdx.x) / a.G;
+__device__ __forceinline__ unsigned long long *pub_slot(const MultiArgs &a, const MultiShared &sh, int g,
+                                                        int phase) {
+    const int b = sh.tree;
     return a.pub + ((int64_t(b) * a.G + g) * kRot + (phase % kRot)) * kSlot;
 }
 
 // Thread 0 publishes v[0..n) for the barrier that ends phase + 1, once its
 // earlier stores (the emptying of this slot) have drained.
-__device__ __forceinline__ void publish_vals(const MultiArgs &a, int phase, const double *v, int n) {
+__device__ __forceinline__ void publish_vals(const MultiArgs &a, const MultiShared &sh, int phase, const double *v,
+                                             int n) {
     if (threadIdx.x != 0) return;
-    unsigned long long *p = pub_slot(a, static_cast<int>(blockIdx.x) % a.G, phase + 1);
+    unsigned long long *p = pub_slot(a, sh, sh.slice, phase + 1);
     __builtin_amdgcn_s_waitcnt(0);
     for (int j = 0; j < n; ++j)
         __hip_atomic_store(&p[j], static_cast<unsigned long long>(__double_as_longlong(v[j])), __ATOMIC_RELAXED,
@@ -205,7 +217,7 @@ __device__ void tree_barrier(const MultiArgs &a, MultiShared &sh, int &phase, in
     ++phase;
     if (static_cast<int>(threadIdx.x) < a.G * n) {
         const int g = static_cast<int>(threadIdx.x) / n, j = static_cast<int>(threadIdx.x) % n;
-        const unsigned long long *p = &pub_slot(a, g, phase)[j];
+        const unsigned long long *p = &pub_slot(a, sh, g, phase)[j];
         unsigned long long w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         int polls = 0;
         while (w == kEmpty && !sh.broken) {
@@ -222,7 +234,7 @@ __device__ void tree_barrier(const MultiArgs &a, MultiShared &sh, int &phase, in
     // every block has read this block's slot of the barrier before this one:
     // empty it for the barrier after the next
     if (threadIdx.x == 0) {
-        unsigned long long *mine = pub_slot(a, static_cast<int>(blockIdx.x) % a.G, phase + 2);
+        unsigned long long *mine = pub_slot(a, sh, sh.slice, phase + 2);
         for (int j = 0; j < kSlot; ++j) __hip_atomic_store(&mine[j], kEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -285,7 +297,7 @@ __device__ void pass_stats(const MultiArgs &a, MultiShared &sh, int &phase, cons
     constexpr int VEC = DT::kVec;
     const int V = a.V;
     const int nvec = (V + VEC - 1) / VEC;
-    const Slice sl = my_slice(a, nvec);
+    const Slice sl = my_slice(a, sh, nvec);
     float sa = -INFINITY, sb = -INFINITY;
     double aa = 0.0, ab = 0.0;
     const bool mixed = !target_only && a.space == 1;
@@ -347,7 +359,7 @@ __device__ void pass_stats(const MultiArgs &a, MultiShared &sh, int &phase, cons
     }
     // the tree's rows: combine the blocks' (shift, sum) pairs in slice order
     const double mine[kSlot] = {static_cast<double>(ma), SA, static_cast<double>(mb), SB};
-    publish_vals(a, phase, mine, 4);
+    publish_vals(a, sh, phase, mine, 4);
     tree_barrier(a, sh, phase, 4);
     double tA = -INFINITY, tB = -INFINITY;
     for (int g = 0; g < a.G; ++g) {
@@ -383,7 +395,7 @@ __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, int &phase,
     constexpr int VEC = DT::kVec;
     const int V = a.V;
     const int nvec = (V + VEC - 1) / VEC;
-    const Slice sl = my_slice(a, nvec);
+    const Slice sl = my_slice(a, sh, nvec);
     double tot = 0.0;
     for (int g0 = sl.lo; g0 < sl.hi; g0 += kMB * kMU) {
         u32x4 dt[kMU], dq[kMU];
@@ -417,7 +429,7 @@ __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, int &phase,
         }
     }
     const double mine[kSlot] = {mblock_sum(tot, sh), 0.0, 0.0, 0.0};
-    publish_vals(a, phase, mine, 1);
+    publish_vals(a, sh, phase, mine, 1);
     tree_barrier(a, sh, phase, 1);
     double Z = 0.0;
     for (int g = 0; g < a.G; ++g) Z += sh.gath[g][0];
@@ -473,8 +485,8 @@ __device__ int pass_draw(const MultiArgs &a, MultiShared &sh, int &phase, const 
                          const char *row_q, const float *buf, double u) {
     constexpr int VEC = DT::kVec;
     const int nvec = (a.V + VEC - 1) / VEC;
-    const Slice sl = my_slice(a, nvec);
-    const int g = static_cast<int>(blockIdx.x) % a.G;
+    const Slice sl = my_slice(a, sh, nvec);
+    const int g = sh.slice;
     double carry = 0.0;
     int last = -1;
     for (int g0 = sl.lo; g0 < sl.hi; g0 += kMB) {
@@ -485,7 +497,7 @@ __device__ int pass_draw(const MultiArgs &a, MultiShared &sh, int &phase, const 
     }
     last = mblock_max_i(last, sh);
     const double mine[kSlot] = {carry, static_cast<double>(last), 0.0, 0.0};
-    publish_vals(a, phase, mine, 2);
+    publish_vals(a, sh, phase, mine, 2);
     tree_barrier(a, sh, phase, 2);
     double base = 0.0, W = 0.0;
     int glast = -1;
@@ -529,7 +541,7 @@ __device__ int pass_draw(const MultiArgs &a, MultiShared &sh, int &phase, const 
         __syncthreads();
     }
     const double mt[kSlot] = {static_cast<double>(mytok), 0.0, 0.0, 0.0};
-    publish_vals(a, phase, mt, 1);
+    publish_vals(a, sh, phase, mt, 1);
     tree_barrier(a, sh, phase, 1);
     int tok = -1;
     for (int i = 0; i < a.G; ++i) tok = max(tok, static_cast<int>(sh.gath[i][0]));
@@ -541,9 +553,15 @@ __device__ int pass_draw(const MultiArgs &a, MultiShared &sh, int &phase, const 
 template <class DT>
 __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
     __shared__ MultiShared sh;
-    const int b = static_cast<int>(blockIdx.x) / a.G;
-    const int g = static_cast<int>(blockIdx.x) % a.G;     // block 0 of the tree writes the outputs
     const int t = threadIdx.x;
+    if (t == 0) {
+        const unsigned k = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh.tree = static_cast<int>(k / static_cast<unsigned>(a.G));
+        sh.slice = static_cast<int>(k % static_cast<unsigned>(a.G));
+    }
+    __syncthreads();
+    const int b = sh.tree;
+    const int g = sh.slice;     // block 0 of the tree writes the outputs
     int phase = 0;
     const int N = a.N, V = a.V;
     for (int i = t; i <= N; i += kMB) {
@@ -726,9 +744,13 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
     }
 }
 
-// Clears the status word and empties every published slot of the trees.
-__global__ void k_multi_clear(int32_t *status, unsigned long long *pub, int64_t n) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
+// Clears the status word and the ticket counter and empties every published
+// slot of the trees.
+__global__ void k_multi_clear(int32_t *status, unsigned *ticket, unsigned long long *pub, int64_t n) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *status = 0;
+        *ticket = 0u;
+    }
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
         pub[i] = kEmpty;
 }
@@ -739,7 +761,9 @@ namespace {
 
 using namespace sv;
 
-// status word (when the caller passes none), published slots [B, kMaxG, 3, kSlot], residual rows [B, 2, V]
+// status word (when the caller passes none) at 0 and the ticket counter at 64,
+// published slots [B, kMaxG, 3, kSlot], residual rows [B, 2, V]
+constexpr int64_t kTicketOffset = 64;
 int64_t multi_layout_pub() { return 256; }
 int64_t multi_layout_buf(int B) {
     return multi_layout_pub() + align256(int64_t(B) * kMaxG * kRot * kSlot * int64_t(sizeof(double)));
@@ -748,32 +772,23 @@ int64_t multi_layout_total(int B, int V) {
     return multi_layout_buf(B) + align256(int64_t(B) * 2 * V * int64_t(sizeof(float)));
 }
 
-// Blocks per tree: the trees share the GPU's resident walk blocks, each block
-// keeping at least one tile of the row.
-int choose_g(int B, int V, int vec, int units) {
+// Blocks per tree: each block keeps at least one tile of the row; by default
+// the trees share the GPU's resident walk blocks, so that every tree runs in
+// the first round; `want` in 1..kMaxG asks for that many.
+int choose_g(int B, int V, int vec, int units, int want) {
     const int nvec = (V + vec - 1) / vec;
-    int G = std::max(1, std::min({kMaxG, units / std::max(B, 1), (nvec + kMB - 1) / kMB}));
-    return G;
+    const int cap = (want > 0) ? want : units / std::max(B, 1);
+    return std::max(1, std::min({kMaxG, cap, (nvec + kMB - 1) / kMB}));
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t sv_tree_multi_workspace_bytes(int B, int N, int V) {
-    if (B < 0 || N < 0 || N > SV_MAX_TREE_NODES || V < 1) return 0;
-    return static_cast<size_t>(multi_layout_total(B, V));
-}
-
-sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const void *draft_logits,
-                               int64_t ld_q, sv_dtype dtype, int B, int N, int V,
-                               const int32_t *parent, const int32_t *node_token,
-                               const float *u_accept, const float *u_sample, float lambda,
-                               float temperature, int mix_space, int32_t *accepted,
-                               int32_t *out_tokens, int32_t *accepted_nodes, float *accept_prob,
-                               int Dmax, int32_t *status, void *workspace, size_t workspace_bytes,
-                               hipStream_t stream) {
+sv_status verify_multi(const void *target_logits, int64_t ld_t, const void *draft_logits, int64_t ld_q,
+                       sv_dtype dtype, int B, int N, int V, const int32_t *parent, const int32_t *node_token,
+                       const float *u_accept, const float *u_sample, float lambda, float temperature,
+                       int mix_space, int32_t *accepted, int32_t *out_tokens, int32_t *accepted_nodes,
+                       float *accept_prob, int Dmax, int32_t *status, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream, int blocks_per_tree) {
     if (mix_space != SV_MIX_PROB && mix_space != SV_MIX_LOGIT) return SV_EINVAL;
+    if (blocks_per_tree < 0 || blocks_per_tree > kMaxG) return SV_EINVAL;
     const int eb = elem_bytes(dtype);
     if (eb == 0) return SV_EDTYPE;
     if (B < 0 || N < 0 || N > SV_MAX_TREE_NODES || V < 1 || Dmax < 0 || Dmax > SV_MAX_POSITIONS ||
@@ -822,9 +837,11 @@ sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const vo
     a.status = status ? status : reinterpret_cast<int32_t *>(ws);
     a.pub = reinterpret_cast<unsigned long long *>(ws + multi_layout_pub());
     a.buf = reinterpret_cast<float *>(ws + multi_layout_buf(B));
-    // all of a tree's blocks must run at once (they wait for one another), so
-    // B * G stays within the resident capacity.  An ordinary launch: a
-    // cooperative one guarantees residency but costs about 20 us per call here
+    a.ticket = reinterpret_cast<unsigned *>(ws + kTicketOffset);
+    // A tree's blocks wait for one another; the start-order tickets make any
+    // grid progress as long as G blocks fit at once.  By default B * G stays
+    // within the resident capacity, so every tree runs in the first round.  An
+    // ordinary launch: a cooperative one costs about 20 us per call here
     const void *kern = dtype == SV_BF16 ? reinterpret_cast<const void *>(k_tree_multi<Bf16>)
                                         : reinterpret_cast<const void *>(k_tree_multi<F32>);
     int dev = 0, units = 0, per_unit = 0;
@@ -832,10 +849,10 @@ sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const vo
         hipDeviceGetAttribute(&units, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, kern, kMB, 0) != hipSuccess)
         return SV_EHIP;
-    a.G = choose_g(B, V, 16 / eb, units * std::max(per_unit, 0));
+    a.G = choose_g(B, V, 16 / eb, units * std::max(per_unit, 0), blocks_per_tree);
     const int64_t n_slots = int64_t(B) * a.G * kRot * kSlot;
     hipLaunchKernelGGL(k_multi_clear, dim3(static_cast<unsigned>(std::min<int64_t>(cdiv(n_slots, 256), 1024))),
-                       dim3(256), 0, stream, a.status, a.pub, n_slots);
+                       dim3(256), 0, stream, a.status, a.ticket, a.pub, n_slots);
     const dim3 grid(static_cast<unsigned>(int64_t(B) * a.G));
     if (dtype == SV_BF16) {
         hipLaunchKernelGGL(k_tree_multi<Bf16>, grid, dim3(kMB), 0, stream, a);
@@ -843,6 +860,41 @@ sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const vo
         hipLaunchKernelGGL(k_tree_multi<F32>, grid, dim3(kMB), 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_tree_multi_workspace_bytes(int B, int N, int V) {
+    if (B < 0 || N < 0 || N > SV_MAX_TREE_NODES || V < 1) return 0;
+    return static_cast<size_t>(multi_layout_total(B, V));
+}
+
+sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const void *draft_logits,
+                               int64_t ld_q, sv_dtype dtype, int B, int N, int V,
+                               const int32_t *parent, const int32_t *node_token,
+                               const float *u_accept, const float *u_sample, float lambda,
+                               float temperature, int mix_space, int32_t *accepted,
+                               int32_t *out_tokens, int32_t *accepted_nodes, float *accept_prob,
+                               int Dmax, int32_t *status, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    return verify_multi(target_logits, ld_t, draft_logits, ld_q, dtype, B, N, V, parent, node_token, u_accept,
+                        u_sample, lambda, temperature, mix_space, accepted, out_tokens, accepted_nodes,
+                        accept_prob, Dmax, status, workspace, workspace_bytes, stream, 0);
+}
+
+sv_status sv_tree_verify_multi_ex(const void *target_logits, int64_t ld_t, const void *draft_logits,
+                                  int64_t ld_q, sv_dtype dtype, int B, int N, int V,
+                                  const int32_t *parent, const int32_t *node_token,
+                                  const float *u_accept, const float *u_sample, float lambda,
+                                  float temperature, int mix_space, int32_t *accepted,
+                                  int32_t *out_tokens, int32_t *accepted_nodes, float *accept_prob,
+                                  int Dmax, int32_t *status, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream, int blocks_per_tree) {
+    return verify_multi(target_logits, ld_t, draft_logits, ld_q, dtype, B, N, V, parent, node_token, u_accept,
+                        u_sample, lambda, temperature, mix_space, accepted, out_tokens, accepted_nodes,
+                        accept_prob, Dmax, status, workspace, workspace_bytes, stream, blocks_per_tree);
 }
 
 }  // extern "C"

@@ -40,6 +40,8 @@ _CHAIN_ARGS = [_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _P, _P, _F, _F, _P, _P, _
 _GREEDY_ARGS = [_P, _L, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _S, _P]
 _PATH_ARGS = [_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _I, _P, _P, _F, _F, _P, _P, _P, _P, _P, _S,
               _P]
+_MULTI_ARGS = [_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _P, _P, _F, _F, _I, _P, _P, _P, _P, _I, _P,
+               _P, _S, _P]
 
 SIGNATURES = {
     "sv_status_string": ([_I], ctypes.c_char_p),
@@ -61,8 +63,8 @@ SIGNATURES = {
     "sv_tree_attention_mask": ([_P, _I, _I, _P, _I, _P, _P, _P], _I),
     "sv_tree_attention_mask_timed": ([_P, _I, _I, _P, _I, _P, _P, _P, _P, _P], _I),
     "sv_tree_multi_workspace_bytes": ([_I, _I, _I], _S),
-    "sv_tree_verify_multi": ([_P, _L, _P, _L, _I, _I, _I, _I, _P, _P, _P, _P, _F, _F, _I, _P, _P,
-                              _P, _P, _I, _P, _P, _S, _P], _I),
+    "sv_tree_verify_multi": (_MULTI_ARGS, _I),
+    "sv_tree_verify_multi_ex": (_MULTI_ARGS + [_I], _I),
     "sv_tree_verify_path": (_PATH_ARGS, _I),
     "sv_tree_verify_path_ex": (_PATH_ARGS + [_I], _I),
     "sv_read_stream": ([_P, _S, _P, _P, _P, _P], _I),
@@ -532,9 +534,10 @@ class TreeMultiOut(NamedTuple):
 
 def tree_verify_multi(target, draft, parent, node_token, u_accept, u_sample, Dmax: int,
                       lam: float = 0.0, temperature: float = 1.0, space: str = "prob",
-                      stream=None, workspace=None) -> TreeMultiOut:
+                      stream=None, workspace=None, blocks_per_tree: int = 0) -> TreeMultiOut:
     """sv_tree_verify_multi: target / draft [B, N+1, V], parent / node_token [B, N],
-    u_accept [B, N] (one per node), u_sample [B]."""
+    u_accept [B, N] (one per node), u_sample [B].  blocks_per_tree other than 0
+    calls sv_tree_verify_multi_ex with it."""
     torch = _torch()
     if space not in MIX_SPACES:
         raise ValueError(f"space must be one of {sorted(MIX_SPACES)}, got {space!r}")
@@ -556,12 +559,13 @@ def tree_verify_multi(target, draft, parent, node_token, u_accept, u_sample, Dma
                        torch.empty(1, dtype=torch.int32, device=dev))
     ws = workspace if workspace is not None else torch.empty(
         max(int(lib().sv_tree_multi_workspace_bytes(B, N, V)), 16), dtype=torch.uint8, device=dev)
-    code = lib().sv_tree_verify_multi(_ptr(target), ld_t, _ptr(draft), ld_q, _dtype_code(target), B,
-                                      N, V, _ptr(parent), _ptr(node_token), _ptr(u_accept),
-                                      _ptr(u_sample), float(lam), float(temperature),
-                                      MIX_SPACES[space], _ptr(out.accepted), _ptr(out.out_tokens),
-                                      _ptr(out.accepted_nodes), _ptr(out.accept_prob), int(Dmax),
-                                      _ptr(out.status), _ptr(ws), ws.numel(), _stream(stream))
-    _check(code, "sv_tree_verify_multi")
+    args = [_ptr(target), ld_t, _ptr(draft), ld_q, _dtype_code(target), B, N, V, _ptr(parent),
+            _ptr(node_token), _ptr(u_accept), _ptr(u_sample), float(lam), float(temperature),
+            MIX_SPACES[space], _ptr(out.accepted), _ptr(out.out_tokens), _ptr(out.accepted_nodes),
+            _ptr(out.accept_prob), int(Dmax), _ptr(out.status), _ptr(ws), ws.numel(), _stream(stream)]
+    if blocks_per_tree:
+        _check(lib().sv_tree_verify_multi_ex(*args, int(blocks_per_tree)), "sv_tree_verify_multi_ex")
+    else:
+        _check(lib().sv_tree_verify_multi(*args), "sv_tree_verify_multi")
     return out
 

@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
                             "sv_tree_row_argmax_timed", "sv_tree_attention_mask",
                             "sv_tree_attention_mask_timed", "sv_tree_verify_path",
                             "sv_tree_verify_path_ex", "sv_tree_multi_workspace_bytes",
-                            "sv_tree_verify_multi", "sv_read_stream"])
+                            "sv_tree_verify_multi", "sv_tree_verify_multi_ex",
+                            "sv_read_stream"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -277,8 +278,11 @@ def multi_call(**kw):
     args = dict(t=FAKE, ld_t=128, d=FAKE, ld_q=128, dtype=sv.SV_BF16, B=2, N=5, V=128, par=FAKE,
                 tok=FAKE, ua=FAKE, us=FAKE, lam=0.2, T=1.0, space=sv.SV_MIX_PROB, acc=FAKE, out=FAKE,
                 nodes=FAKE, ap=None, Dmax=4, st=None, ws=FAKE, wsb=1 << 30, stream=None)
+    ex = kw.pop("ex", None)
     args.update(kw)
-    return sv.lib().sv_tree_verify_multi(*args.values())
+    if ex is None:
+        return sv.lib().sv_tree_verify_multi(*args.values())
+    return sv.lib().sv_tree_verify_multi_ex(*args.values(), ex)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -295,6 +299,14 @@ def test_multi_argument_errors(kw, code):
     if kw.get("wsb") == "short":
         kw = dict(wsb=sv.lib().sv_tree_multi_workspace_bytes(2, 5, 128) - 16)
     assert multi_call(**kw) == code
+    for g in (0, 1, 16):
+        assert multi_call(ex=g, **kw) == code
+
+
+@pytest.mark.parametrize("g", [-1, 17, 1 << 20])
+def test_multi_ex_rejects_block_counts_outside_0_to_16(g):
+    assert multi_call(ex=g) == sv.SV_EINVAL
+    assert multi_call(ex=g, B=0, t=None, acc=None) == sv.SV_EINVAL
 
 
 def test_read_stream_rejects_bad_arguments():

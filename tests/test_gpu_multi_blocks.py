@@ -1,0 +1,62 @@
+"""The multi-branch walk at every number of blocks per tree, and on a grid
+wider than the GPU.
+
+A tree's blocks wait for one another at its barriers.  Each block takes its
+(tree, slice) role from a start-order ticket, so the walk needs only one
+tree's blocks on the GPU at once: a grid of more blocks than the compute units
+hold runs its trees in rounds.  These cases check that every choice of blocks
+per tree, that wide grid included, gives the oracle's walk ([SD] "Tree
+Speculation", the chain rule of [EAGLE] section 1 applied to what a rejection
+leaves) with the status word clear.
+"""
+import numpy as np
+import pytest
+import torch
+
+from sampling_spec_verify_amd import specverify as sv
+from sampling_spec_verify_amd import synth
+from tests.test_gpu_parity import _multi_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    sv.lib()
+
+
+@pytest.mark.parametrize("blocks", [1, 2, 5, 16])
+def test_multi_every_block_count_matches_the_oracle(blocks):
+    x = synth.config("c5")
+    x.lam = 0.3
+    print(f"[multi blocks] c5 trees, lam 0.3, {blocks} blocks per tree", flush=True)
+    g, stats = _multi_case(x, label=f"c5 multi, {blocks} blocks per tree", blocks_per_tree=blocks)
+    assert int(g.status[0]) == 0
+
+
+def test_multi_grid_wider_than_the_gpu():
+    """64 trees at 16 blocks each: 1024 walk blocks, four times what the
+    compute units hold at once (one 512-thread walk block per unit)."""
+    props = torch.cuda.get_device_properties(0)
+    x = synth.make_tree(9100, 64, 26, 65536, "bf16", lam=0.2)
+    assert 64 * 16 > props.multi_processor_count
+    print(f"[multi blocks] 64 trees x 16 blocks on {props.multi_processor_count} units", flush=True)
+    for space in ("prob", "logit"):
+        g, stats = _multi_case(x, space=space, label=f"64 trees x 16 blocks, {space}", blocks_per_tree=16)
+        assert int(g.status[0]) == 0, sv.decode_flags(int(g.status[0]))
+
+
+def test_multi_block_counts_agree_with_each_other():
+    """The walk's decisions do not depend on the block count: the same trees at
+    1 and 16 blocks emit the same tokens outside draws near a boundary."""
+    x = synth.make_tree(9200, 12, 40, 128256, "bf16", lam=0.0)
+    g1, s1 = _multi_case(x, label="12 trees, 1 block", blocks_per_tree=1)
+    g16, s16 = _multi_case(x, label="12 trees, 16 blocks", blocks_per_tree=16)
+    if s1["flagged"] == 0 and s16["flagged"] == 0:
+        np.testing.assert_array_equal(g1.out_tokens, g16.out_tokens)
+        np.testing.assert_array_equal(g1.accepted_nodes, g16.accepted_nodes)
+    tested = g1.accept_prob >= 0
+    np.testing.assert_array_equal(tested, g16.accept_prob >= 0)
+    assert float(np.abs(g1.accept_prob[tested] - g16.accept_prob[tested]).max(initial=0.0)) <= 1e-6

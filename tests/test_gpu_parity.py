@@ -583,11 +583,11 @@ def test_acceptance_rate_identical_rows_and_lambda_one_are_one():
 # ---------------------------------------------------------------------------
 
 
-def _multi_case(x, Dmax=None, space="prob", label="multi"):
+def _multi_case(x, Dmax=None, space="prob", label="multi", blocks_per_tree=0):
     Dmax = x.Dmax if Dmax is None else Dmax
     g = sv.tree_verify_multi(dev_logits(x.target, x.dtype), dev_logits(x.draft, x.dtype),
                              dev(x.parent), dev(x.node_token), dev(x.u_node), dev(x.u_sample), Dmax,
-                             x.lam, x.temperature, space)
+                             x.lam, x.temperature, space, blocks_per_tree=blocks_per_tree)
     g = to_host(g)
     acc, out, nodes, ap, flag, det = oracle.tree_multi(
         x.widened(x.target), x.widened(x.draft), x.parent, x.node_token, x.u_node, x.u_sample,
