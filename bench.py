@@ -6,17 +6,21 @@
 One step is one full verify call on one batch of seeded synthetic logits that
 already sit in HBM: for a chain workload ``sv_chain_verify`` (row statistics,
 then accept / first rejection / residual-or-bonus resample / emit); for ``c5``
-``sv_tree_verify_greedy``.  ``R`` copies of the inputs (at least 1 GiB in all,
+``sv_tree_verify_greedy`` (one launch for its 27-node trees: row argmax, with
+each tree walked by the wave of its last chunk).  ``R`` copies of the inputs (at least 1 GiB in all,
 four times the 256 MB Infinity Cache) are rotated so that every step reads HBM.
 
-Prints one JSON line.  ``roofline`` rates the row-statistics kernel (the
-dominant one) on its algorithmic bytes, 2 * V * bytes_per_logit per drafted
-position, over its median duration in a leg of ``--kernel-reps`` full calls
-(100 by default, independent of ``--steps``) run after the timed steps
-through the two stage calls.  Each duration comes from HIP events attached to
-the launch itself (``sv_chain_row_stats_timed`` / ``sv_tree_row_argmax_timed``
+Prints one JSON line.  ``roofline`` rates the dominant kernel (the chain's
+row-statistics kernel; the greedy call's one launch) on its algorithmic bytes,
+2 * V * bytes_per_logit per drafted position (V * bytes_per_logit per tree
+row), over its median duration in a leg of ``--kernel-reps`` full calls (100
+by default, independent of ``--steps``) run after the timed steps, the chain
+through its two stage calls.  Each duration comes from HIP events attached to
+the launch itself (``sv_chain_row_stats_timed`` / ``sv_tree_verify_greedy_timed``
 / ``sv_chain_verify_ex``): the dispatch's own begin and end timestamps, the
-interval rocprofv3's kernel trace reports.  ``mass_kernel`` does the same for
+interval rocprofv3's kernel trace reports.  For the greedy call,
+``argmax_only`` times the two-launch form's row-argmax kernel (the same
+stream without the walks) beside it.  ``mass_kernel`` does the same for
 the chain's accept / resample kernel, on the bytes of the rows it samples from
 (two rows per rejecting request, the bonus row otherwise).  ``traffic`` comes from the
 rocprofv3 FETCH_SIZE / WRITE_SIZE summary under ``profiles/`` when it was taken
@@ -49,6 +53,7 @@ _CSRC = "sampling_spec_verify_amd/csrc/"
 KERNEL_SOURCES = {
     "row_stats": [_CSRC + "sv_chain.hip", _CSRC + "sv_device.hpp", _CSRC + "sv_common.hpp"],
     "row_argmax": [_CSRC + "sv_tree.hip", _CSRC + "sv_device.hpp", _CSRC + "sv_common.hpp"],
+    "greedy_fold": [_CSRC + "sv_tree.hip", _CSRC + "sv_device.hpp", _CSRC + "sv_common.hpp"],
 }
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_{kernel}_{workload}.md")
 
@@ -570,7 +575,7 @@ def bench_multi(args):
         "gpu_ms_per_step": ev0.elapsed_time(ev1) / K, "cpu_baseline": cpu,
         "parity_sample": parity, "status_word": int(g[4][0]),
         "accepted_depths": g[0].tolist(),
-        "note": "up to 16 cooperating 1024-thread blocks walk each tree; bound by the chain "
+        "note": "up to 16 cooperating 512-thread blocks walk each tree; bound by the chain "
                 "of barriers between the walk's vocabulary passes",
     }
     print(json.dumps(line), flush=True)
@@ -721,12 +726,7 @@ def main():
         calls = [sv.TreeGreedyCall(tgts[i], par, ntok, x.Dmax) for i in range(R)]
 
         def step(i, events=None):
-            c = calls[i % R]
-            if events is None:
-                c.run()
-            else:
-                c.row_argmax(events)
-                c.walk()
+            calls[i % R].run(events)
     else:
         drfs = device_copies(x.draft, x.dtype, R, torch)
         tok = torch.from_numpy(x.tokens).to(dev)
@@ -769,7 +769,9 @@ def main():
         timer.close()
     ms_per_step = wall * 1e3 / K
     value = positions * K / wall
-    kname = "row_argmax" if tree else "row_stats"
+    # the greedy call's one launch covers trees of at most 64 nodes, 1024 trees
+    fold = tree and x.N + 1 <= 64 and x.B <= 1024
+    kname = ("greedy_fold" if fold else "row_argmax") if tree else "row_stats"
     traffic = load_traffic(kname, args.workload)
 
     out = calls[0].out
@@ -786,8 +788,7 @@ def main():
     for i in range(reps):
         c = calls[i % R]
         if tree:
-            c.row_argmax(kt.pair(i))
-            c.walk()
+            c.run(kt.pair(i))
         else:
             c.row_stats(kt.pair(i))
             c.accept_resample(mt.pair(i))
@@ -813,6 +814,23 @@ def main():
                 "kernel_ms_p90": float(np.percentile(mass_ms, 90)),
                 "achieved": mass_bytes / (mm * 1e-3) / 1e9,
                 "frac": mass_bytes / (mm * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    argmax_only = None
+    if fold:
+        at = sv.KernelTimer(reps)
+        for i in range(reps):
+            c = calls[i % R]
+            c.row_argmax(at.pair(i))
+            c.walk()
+        torch.cuda.synchronize()
+        am_ms = np.array([at.elapsed_ms(i) for i in range(reps)])
+        at.close()
+        amm = float(np.median(am_ms))
+        argmax_only = {"kernel": "row_argmax", "note": "the two-launch form's first kernel: the same "
+                       "row stream and chunk argmax, without the walks",
+                       "kernel_ms_median": amm, "kernel_ms_p10": float(np.percentile(am_ms, 10)),
+                       "kernel_ms_p90": float(np.percentile(am_ms, 90)),
+                       "achieved": algo_bytes / (amm * 1e-3) / 1e9,
+                       "frac": algo_bytes / (amm * 1e-3) / 1e9 / PEAK_HBM_GBS}
     graph = None
     if args.graph > 0:
         gs = torch.cuda.Stream()
@@ -868,6 +886,7 @@ def main():
                      "read_stream": ceiling,
                      "frac_of_read_stream": (achieved / ceiling["gbs_median"]) if ceiling else None},
         "mass_kernel": mass,
+        "argmax_only": argmax_only,
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_pool,
         "graph_steady_state": graph,

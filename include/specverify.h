@@ -98,9 +98,9 @@ typedef enum { SV_MIX_PROB = 0, SV_MIX_LOGIT = 1 } sv_mix_space;
 #define SV_DATA_BAD_TREE    0x10 /* parent or path entry invalid: node never accepted / path cut */
 #define SV_DATA_FALLBACK    0x20 /* residual mass was zero after a rejection: sampled p~ instead */
 #define SV_DATA_DEPTH       0x40 /* accepted tree path deeper than Dmax: cut at Dmax nodes */
-#define SV_DATA_SYNC        0x80 /* sv_tree_verify_multi: a block of a tree gave up waiting for the
-                                    tree's other blocks (other work held the GPU's compute units);
-                                    the call's outputs are invalid */
+#define SV_DATA_SYNC        0x80 /* sv_tree_verify_multi, one-launch sv_tree_verify_greedy: a wait
+                                    for another block's or wave's values gave up (other work held
+                                    the GPU's compute units); the call's outputs are invalid */
 
 /* Human-readable name of a status code (static storage, host memory). */
 const char *sv_status_string(sv_status s);
@@ -284,6 +284,15 @@ size_t sv_tree_workspace_bytes(int B, int N, int V);
  *                 then the argmax of the winning node's row, then -1.
  *  accepted_nodes [B, Dmax] out: accepted node ids root->leaf, then -1.
  *  lambda and temperature do not enter (argmax is temperature-free).
+ *
+ * Launches.  Trees of at most 64 nodes (N <= 63, the root included) in
+ * batches of at most 1024 trees take one launch: the wave that streams a
+ * tree's last row chunk walks that tree once the tree's other chunk and row
+ * records (tagged with the call, write-through) are in; it waits only for
+ * waves of earlier jobs, dispatched before it.  The status word is stored once,
+ * by the last tree to finish.  Other sizes take the two launches below.  In
+ * the one-launch form every wait is bounded (about a second): a wave that
+ * gives up sets SV_DATA_SYNC, and the call's outputs are then invalid.
  */
 sv_status sv_tree_verify_greedy(const void *target_logits, int64_t ld_t, sv_dtype dtype,
                                 int B, int N, int V,
@@ -293,8 +302,9 @@ sv_status sv_tree_verify_greedy(const void *target_logits, int64_t ld_t, sv_dtyp
                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
- * The two launches sv_tree_verify_greedy makes, exposed so that a caller can
- * time or interleave them.  Same arguments and meaning; sv_tree_row_argmax
+ * The two launches sv_tree_verify_greedy makes for larger trees, exposed so
+ * that a caller can time or interleave them (at any size).  Same arguments
+ * and meaning; sv_tree_row_argmax
  * streams every target row once and reduces it to per-chunk (max, lowest
  * index) partials; sv_tree_greedy_walk must follow it on the same stream with
  * the same workspace, combines the partials into row argmaxes, walks the
@@ -312,6 +322,19 @@ sv_status sv_tree_greedy_walk(const void *target_logits, int64_t ld_t, sv_dtype 
                               int32_t *accepted, int32_t *out_tokens, int32_t *accepted_nodes,
                               int Dmax, int32_t *status, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sv_tree_verify_greedy with its first launch (the one launch, for the trees
+ * it covers; else the row argmax) timed by kernel_start / kernel_stop, events
+ * attached to the launch itself as in sv_chain_row_stats_timed.
+ */
+sv_status sv_tree_verify_greedy_timed(const void *target_logits, int64_t ld_t, sv_dtype dtype,
+                                      int B, int N, int V,
+                                      const int32_t *parent, const int32_t *node_token,
+                                      int32_t *accepted, int32_t *out_tokens,
+                                      int32_t *accepted_nodes, int Dmax, int32_t *status,
+                                      void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                      hipEvent_t kernel_start, hipEvent_t kernel_stop);
 
 /*
  * sv_tree_row_argmax with the row-argmax kernel timed by kernel_start /

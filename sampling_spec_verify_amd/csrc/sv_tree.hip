@@ -8,20 +8,24 @@
 //   "大模型推理的Speculative Decoding原理详解", "Tree Speculation": several
 //     candidate branches per position, verified together.
 //
-// Two launches:
-//  1. k_row_argmax: one wavefront per (request, row, chunk) streams 64 lanes x
-//     NV x 16 bytes of a target row and keeps the largest value with its
-//     lowest index (no exponentials: argmax is temperature-free).
-//  2. k_greedy_walk: one 1024-thread block per request combines the chunk partials into
-//     the argmax of each row, then walks the parent array in node order:
-//     ok[i] = ok[parent[i]] and token[i] == argmax[parent[i]]; the deepest ok
-//     node (lowest id on ties) and its root path are emitted, followed by the
-//     argmax of its row as the bonus token.
+// Row argmax: one wavefront per (request, row, chunk) streams 64 lanes x NV x
+// 16 bytes of a target row and keeps the largest value with its lowest index
+// (no exponentials: argmax is temperature-free).  Walk: the chunk results give
+// the argmax of each row, then ok[i] = ok[parent[i]] and token[i] ==
+// argmax[parent[i]]; the deepest ok node (lowest id on ties) and its root path
+// are emitted, followed by the argmax of its row as the bonus token.
+//
+// Trees of at most 64 nodes (the root included) take one launch,
+// k_greedy_fold: the wave of each tree's last job walks that tree in
+// registers, one lane per node, once the tree's chunk records are in.  Larger
+// trees take two: k_row_argmax, then k_greedy_walk, one 1024-thread block per
+// tree.
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "sv_common.hpp"
 #include "sv_device.hpp"
@@ -39,8 +43,14 @@ namespace sv {
 // compare equal in the position search, as in the first-maximum rule.
 // Elements past V read as -inf and sit above every valid index, so they never
 // win a tie.
+struct ChunkMax {
+    float val;      // the chunk's largest value
+    int idx;        // its lowest index (INT_MAX: none)
+    bool nan;       // a NaN in the chunk
+};
+
 template <class DT, int NV>
-__device__ __forceinline__ void row_chunk_argmax(const TreeArgs &a, unsigned job) {
+__device__ __forceinline__ ChunkMax chunk_argmax(const TreeArgs &a, unsigned job) {
     const int c = static_cast<int>(job % static_cast<unsigned>(a.C1));
     const int64_t row_id = job / static_cast<unsigned>(a.C1);   // b * (N+1) + r
     const char *row = a.tgt + row_id * a.ld_t * a.elem;
@@ -85,15 +95,23 @@ __device__ __forceinline__ void row_chunk_argmax(const TreeArgs &a, unsigned job
             if (f[e] == wm) esel = e;
         idx = (v0 + nsel * kWave + lane) * VEC + esel;
     }
-    const int widx = wave_min_i(idx);
-    const bool wnan = __ballot(nan) != 0ull;
-    if (lane == 0) {
+    ChunkMax r;
+    r.val = wm;
+    r.idx = wave_min_i(idx);
+    r.nan = __ballot(nan) != 0ull;
+    return r;
+}
+
+template <class DT, int NV>
+__device__ __forceinline__ void row_chunk_argmax(const TreeArgs &a, unsigned job) {
+    const ChunkMax r = chunk_argmax<DT, NV>(a, job);
+    if ((threadIdx.x & (kWave - 1)) == 0) {
         ArgPart p;
-        p.val = wm;
-        p.idx = widx;
-        p.nan = wnan ? 1 : 0;
+        p.val = r.val;
+        p.idx = r.idx;
+        p.nan = r.nan ? 1 : 0;
         p.pad = 0;
-        a.part[row_id * a.C1 + c] = p;
+        a.part[job] = p;     // job = (b * (N+1) + r) * C1 + c
     }
 }
 
@@ -260,6 +278,250 @@ __global__ __launch_bounds__(kBlock2) void k_greedy_walk(TreeArgs a, int staged)
     }
 }
 
+// ---- one launch for trees of at most 64 nodes --------------------------------
+//
+// Records cross waves as agent-scope relaxed atomics (write-through: the
+// reading wave may run on another XCD), each 64-bit word carrying the call's
+// tag in its high half.  The tag has its top bit set and changes every call,
+// so neither an untagged partial nor a record another call left in the
+// workspace passes for this call's.  Every record has one reader, which clears
+// it after reading: a replay of the same launch (same tag) finds it empty.
+//
+//  * A chunk's record: (tag, value bits), (tag, index | nan << 31).
+//  * The wave of a row's last chunk combines the row: lane c polls chunk c's
+//    record until both words carry the tag (its own chunk it has in
+//    registers), then the wave takes the row's argmax and publishes it as the
+//    row's word (tag, argmax), -1 for a row with a NaN or no index.
+//  * The wave of a tree's last chunk (row N) polls the other rows' words
+//    while it combines its own row, and walks the tree in registers, one lane
+//    per node.
+//  * The status word is written once, by the last tree to finish: each
+//    walking wave adds its tree and its flags to a completion word (tag |
+//    flags << 24 | trees done) by compare-and-swap, a word with another tag
+//    counting as zero trees; the wave that completes the count stores the
+//    status and resets the word.
+//
+// A wave waits only for waves of earlier jobs, dispatched before it.  Every
+// poll is bounded (about a second); a wave that gives up sets SV_DATA_SYNC
+// (outputs invalid) and goes on, so every wave ends.
+
+constexpr int kFoldNodes = kWave;           // N + 1 at most: one lane per node
+constexpr int kFoldTrees = 1024;            // trees per one-launch call at most
+constexpr int kFoldSpin = 1 << 20;          // polls of one record before the wave gives up
+
+__device__ __forceinline__ unsigned long long ld_agent(const unsigned long long *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(unsigned long long *p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tagged(unsigned long long w, uint32_t tag) {
+    return static_cast<uint32_t>(w >> 32) == tag;
+}
+
+// Polls the word pair at p until both carry the tag; clears them.
+__device__ __forceinline__ void poll_pair(unsigned long long *p, uint32_t tag, unsigned long long &w0,
+                                          unsigned long long &w1, int &flags) {
+    int polls = 0;
+    while (!tagged(w0, tag) || !tagged(w1, tag)) {
+        if (++polls > kFoldSpin) {
+            flags |= SV_DATA_SYNC;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        w0 = ld_agent(p);
+        w1 = ld_agent(p + 1);
+    }
+    st_agent(p, 0ull);
+    st_agent(p + 1, 0ull);
+}
+
+// The argmax of the row whose last chunk this wave holds (own): its other
+// chunks' records, one lane per chunk, combined as the two-launch walk does
+// (the largest value, then the lowest index among the chunks holding it);
+// -1 for a row with a NaN or no index.  `pre`: loads to issue first, so that
+// their round trip overlaps this one (the tree walker's row words).
+__device__ __forceinline__ int fold_row(const TreeArgs &a, int64_t row_id, const ChunkMax &own, int &flags) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t tag = a.tag;
+    unsigned long long *rec = a.rec + 2 * row_id * a.C1;
+    float best = -INFINITY;
+    int bidx = INT_MAX;
+    bool nan = false;
+    for (int c0 = 0; c0 < a.C1; c0 += kWave) {
+        const int c = c0 + lane;
+        float v = -INFINITY;
+        int i = INT_MAX;
+        bool n = false;
+        if (c == a.C1 - 1) {
+            v = own.val;
+            i = own.idx;
+            n = own.nan;
+        } else if (c < a.C1 - 1) {
+            unsigned long long w0 = ld_agent(rec + 2 * c), w1 = ld_agent(rec + 2 * c + 1);
+            poll_pair(rec + 2 * c, tag, w0, w1, flags);
+            v = __uint_as_float(static_cast<uint32_t>(w0));
+            const uint32_t lo = static_cast<uint32_t>(w1);
+            i = static_cast<int>(lo & 0x7FFFFFFFu);
+            n = (lo >> 31) != 0u;
+        }
+        // the chunk maxima ignore a NaN value: such a chunk carries the flag
+        const float m = wave_max(v == v ? v : -INFINITY);
+        const int mi = wave_min_i((v == m) ? i : INT_MAX);
+        nan |= __ballot(n) != 0ull;
+        if (m > best) {
+            best = m;
+            bidx = mi;
+        } else if (m == best) {
+            bidx = min(bidx, mi);
+        }
+    }
+    if (bidx == INT_MAX || nan) {
+        flags |= SV_DATA_BAD_ROW;
+        return -1;
+    }
+    return bidx;
+}
+
+// The walk of tree b by one wavefront, lane i holding node i (N + 1 <= 64).
+__device__ void fold_walk(const TreeArgs &a, int b, const ChunkMax &own) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int N = a.N;
+    const uint32_t tag = a.tag;
+    int flags = 0;
+    // the other rows' words, in flight while this wave combines row N
+    unsigned long long *rw = a.rowword + int64_t(b) * (N + 1);
+    unsigned long long w = (lane < N) ? ld_agent(rw + lane) : 0ull;
+    const int am_n = fold_row(a, int64_t(b) * (N + 1) + N, own, flags);
+    int am = am_n;
+    if (lane < N) {
+        int polls = 0;
+        while (!tagged(w, tag)) {
+            if (++polls > kFoldSpin) {
+                flags |= SV_DATA_SYNC;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            w = ld_agent(rw + lane);
+        }
+        st_agent(rw + lane, 0ull);
+        am = static_cast<int>(static_cast<uint32_t>(w));
+        if (am == -2) {                     // its row combine gave up waiting
+            flags |= SV_DATA_SYNC;
+            am = -1;
+        } else if (am < 0) {
+            flags |= SV_DATA_BAD_ROW;
+        }
+    }
+    int par = -1, tok = -1;
+    if (lane >= 1 && lane <= N) {
+        par = a.parent[int64_t(b) * N + lane - 1];
+        tok = a.node_token[int64_t(b) * N + lane - 1];
+    }
+    const bool par_ok = lane >= 1 && lane <= N && par >= 0 && par < lane;
+    const int am_par = __shfl(am, par_ok ? par : 0);
+    // (ancestor, value): the depth while every node passed so far matched, a
+    // large negative number once one did not (the root: depth 0, ok)
+    int up = 0, dep = (lane <= N) ? 0 : kRejected;
+    if (lane >= 1 && lane <= N) {
+        dep = kRejected;
+        if (!par_ok) {
+            flags |= SV_DATA_BAD_TREE;       // never followed: a rejected root child
+        } else {
+            up = par;
+            if (tok < 0 || tok >= a.V) flags |= SV_DATA_BAD_TOKEN;
+            else if (am_par >= 0 && tok == am_par) dep = 1;
+        }
+    }
+    while (__ballot(up != 0) != 0ull) {
+        const int du = __shfl(dep, up);
+        const int uu = __shfl(up, up);
+        if (up != 0) {
+            dep += du;
+            up = uu;
+        }
+    }
+    const int key = (lane <= N && dep >= 0) ? dep * 2048 + (2047 - lane) : -1;
+    const int best_key = wave_max_i(key);         // the root's key is at least 2047
+    const int best = 2047 - best_key % 2048;
+    const int best_d = best_key / 2048;
+    const int keep = min(best_d, a.Dmax);
+    if (best_d > a.Dmax) flags |= SV_DATA_DEPTH;
+    // the root path of best: lane d holds the node at depth d
+    int mypath = 0;
+    {
+        int v = best;
+        for (int d = best_d; d >= 1; --d) {
+            if (lane == d) mypath = v;
+            v = __builtin_amdgcn_readlane(par, v);
+        }
+    }
+    const int p_next = __shfl(mypath, (lane + 1) & (kWave - 1));   // path[lane + 1]
+    const int tok_next = __shfl(tok, p_next & (kWave - 1));
+    const int last = keep > 0 ? __builtin_amdgcn_readlane(mypath, keep) : 0;
+    const int bonus = __builtin_amdgcn_readlane(am, last);
+    for (int i = lane; i <= a.Dmax; i += kWave) {
+        int v = -1;
+        if (i < keep) v = tok_next;
+        else if (i == keep) v = bonus;
+        a.out_tokens[int64_t(b) * (a.Dmax + 1) + i] = v;
+        if (i < a.Dmax) a.accepted_nodes[int64_t(b) * a.Dmax + i] = (i < keep) ? p_next : -1;
+    }
+    const int fl = wave_or8(flags);
+    if (lane == 0) {
+        a.accepted[b] = keep;
+        // count the tree in the completion word; the last tree stores the status
+        const unsigned long long tagw = static_cast<unsigned long long>(tag) << 32;
+        unsigned long long old = ld_agent(a.done);
+        unsigned long long cnt, acc;
+        for (;;) {
+            const bool mine = tagged(old, tag);
+            cnt = mine ? (old & 0xFFFFFFull) : 0ull;
+            acc = (mine ? ((old >> 24) & 0xFFull) : 0ull) | static_cast<unsigned long long>(fl & 0xFF);
+            const unsigned long long nw = tagw | (acc << 24) | (cnt + 1);
+            if (__hip_atomic_compare_exchange_strong(a.done, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+                break;
+        }
+        if (cnt + 1 == static_cast<unsigned long long>(a.B)) {
+            *a.status = static_cast<int32_t>(acc);
+            st_agent(a.done, 0ull);
+        }
+    }
+}
+
+// Row argmax; the wave of a row's last chunk combines the row, and the wave
+// of a tree's last chunk walks the tree.
+template <class DT, int NV>
+__global__ __launch_bounds__(kBlock) void k_greedy_fold(TreeArgs a, int n_jobs) {
+    const int job = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves +
+                                                   static_cast<int>(threadIdx.x) / kWave);
+    if (job >= n_jobs) return;
+    const ChunkMax r = chunk_argmax<DT, NV>(a, static_cast<unsigned>(job));
+    const int64_t row_id = job / a.C1;
+    if ((job + 1) % a.C1 != 0) {
+        if ((threadIdx.x & (kWave - 1)) == 0) {
+            const unsigned long long tagw = static_cast<unsigned long long>(a.tag) << 32;
+            st_agent(a.rec + 2 * int64_t(job), tagw | __float_as_uint(r.val));
+            st_agent(a.rec + 2 * int64_t(job) + 1,
+                     tagw | (static_cast<uint32_t>(r.idx) & 0x7FFFFFFFu) | (r.nan ? 0x80000000u : 0u));
+        }
+        return;
+    }
+    const int b = static_cast<int>(row_id / (a.N + 1));
+    if (row_id % (a.N + 1) != a.N) {
+        int flags = 0;
+        const int am = fold_row(a, row_id, r, flags);
+        if ((threadIdx.x & (kWave - 1)) == 0) {
+            // a SYNC failure marks the row (its argmax is then not trusted) as -1 with the flag
+            const unsigned long long tagw = static_cast<unsigned long long>(a.tag) << 32;
+            st_agent(a.rowword + row_id, tagw | static_cast<uint32_t>((flags & SV_DATA_SYNC) ? -2 : am));
+        }
+        return;
+    }
+    fold_walk(a, b, r);
+}
+
 // Tree-attention mask (EAGLE explainer, "3. 验证阶段树形attention": to verify
 // a tree in one target pass each candidate may attend only to its ancestor
 // path).  Grid (request, slice): every block stages its request's parent
@@ -332,6 +594,20 @@ sv_status run_tree(const TreeArgs &a0, hipStream_t stream, int which, hipEvent_t
     const int nv = choose_stream_nv(rows, a.V, DT::kVec);
     a.C1 = c1_for(a.V, nv, DT::kVec);
     if (rows * a.C1 >= (int64_t(1) << 31)) return SV_EINVAL;
+    if (which == 3 && a.N + 1 <= kFoldNodes && a.B <= kFoldTrees) {
+        // one launch: the walk in the argmax launch's tail
+        static std::atomic<uint32_t> calls{0};
+        a.tag = 0x80000000u | (calls.fetch_add(1u, std::memory_order_relaxed) & 0x7FFFFFFFu);
+        const int jobs = static_cast<int>(rows * a.C1);
+        const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, cdiv(jobs, kWaves))));
+        if (nv == 8)
+            launch_timed(k_greedy_fold<DT, 8>, grid, dim3(kBlock), 0, stream, ev_start, ev_stop, a, jobs);
+        else if (nv == 4)
+            launch_timed(k_greedy_fold<DT, 4>, grid, dim3(kBlock), 0, stream, ev_start, ev_stop, a, jobs);
+        else
+            launch_timed(k_greedy_fold<DT, 2>, grid, dim3(kBlock), 0, stream, ev_start, ev_stop, a, jobs);
+        return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+    }
     if (which & 1) {
         const int jobs = static_cast<int>(rows * a.C1);
         const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, cdiv(jobs, kWaves))));
@@ -355,7 +631,8 @@ sv_status run_tree(const TreeArgs &a0, hipStream_t stream, int which, hipEvent_t
 }
 
 // Validates the greedy call and runs the launches in `which` (1: row argmax,
-// 2: walk).  Argument errors return before any HIP call.
+// 2: walk, 3: the whole call, in one launch for trees of at most 64 nodes).
+// Argument errors return before any HIP call.
 sv_status greedy_call(const void *target_logits, int64_t ld_t, sv_dtype dtype, int B, int N,
                       int V, const int32_t *parent, const int32_t *node_token, int32_t *accepted,
                       int32_t *out_tokens, int32_t *accepted_nodes, int Dmax, int32_t *status,
@@ -390,6 +667,10 @@ sv_status greedy_call(const void *target_logits, int64_t ld_t, sv_dtype dtype, i
     a.accepted_nodes = accepted_nodes;
     a.status = status ? status : reinterpret_cast<int32_t *>(ws + L.status);
     a.part = reinterpret_cast<ArgPart *>(ws + L.part);
+    a.rec = reinterpret_cast<unsigned long long *>(ws + L.part);
+    a.rowword = reinterpret_cast<unsigned long long *>(ws + L.rowword);
+    a.done = reinterpret_cast<unsigned long long *>(ws + L.done);
+    a.tag = 0;
     return dtype == SV_BF16 ? run_tree<Bf16>(a, stream, which, ev_start, ev_stop)
                             : run_tree<F32>(a, stream, which, ev_start, ev_stop);
 }
@@ -421,6 +702,16 @@ sv_status sv_tree_row_argmax(const void *target_logits, int64_t ld_t, sv_dtype d
                              hipStream_t stream) {
     return greedy_call(target_logits, ld_t, dtype, B, N, V, parent, node_token, accepted, out_tokens,
                        accepted_nodes, Dmax, status, workspace, workspace_bytes, stream, 1);
+}
+
+sv_status sv_tree_verify_greedy_timed(const void *target_logits, int64_t ld_t, sv_dtype dtype, int B,
+                                      int N, int V, const int32_t *parent, const int32_t *node_token,
+                                      int32_t *accepted, int32_t *out_tokens, int32_t *accepted_nodes,
+                                      int Dmax, int32_t *status, void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream, hipEvent_t kernel_start, hipEvent_t kernel_stop) {
+    return greedy_call(target_logits, ld_t, dtype, B, N, V, parent, node_token, accepted, out_tokens,
+                       accepted_nodes, Dmax, status, workspace, workspace_bytes, stream, 3, kernel_start,
+                       kernel_stop);
 }
 
 sv_status sv_tree_row_argmax_timed(const void *target_logits, int64_t ld_t, sv_dtype dtype, int B,

@@ -60,6 +60,7 @@ SIGNATURES = {
     "sv_tree_row_argmax": (_GREEDY_ARGS, _I),
     "sv_tree_greedy_walk": (_GREEDY_ARGS, _I),
     "sv_tree_row_argmax_timed": (_GREEDY_ARGS + [_P, _P], _I),
+    "sv_tree_verify_greedy_timed": (_GREEDY_ARGS + [_P, _P], _I),
     "sv_tree_attention_mask": ([_P, _I, _I, _P, _I, _P, _P, _P], _I),
     "sv_tree_attention_mask_timed": ([_P, _I, _I, _P, _I, _P, _P, _P, _P, _P], _I),
     "sv_tree_multi_workspace_bytes": ([_I, _I, _I], _S),
@@ -401,8 +402,13 @@ class TreeGreedyCall:
                         _ptr(o.accepted_nodes), int(Dmax), _ptr(o.status), _ptr(self.workspace),
                         self.workspace.numel(), _stream(stream))
 
-    def run(self) -> TreeGreedyOut:
-        _check(lib().sv_tree_verify_greedy(*self._cached), "sv_tree_verify_greedy")
+    def run(self, events=None) -> TreeGreedyOut:
+        """The whole call; ``events`` = (start, stop) times its first launch."""
+        if events is None:
+            _check(lib().sv_tree_verify_greedy(*self._cached), "sv_tree_verify_greedy")
+        else:
+            _check(lib().sv_tree_verify_greedy_timed(*self._cached, *events),
+                   "sv_tree_verify_greedy_timed")
         return self.out
 
     def row_argmax(self, events=None):

@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
                             "sv_chain_row_stats_timed", "sv_chain_verify_ex",
                             "sv_tree_workspace_bytes", "sv_tree_verify_greedy",
                             "sv_tree_row_argmax", "sv_tree_greedy_walk",
-                            "sv_tree_row_argmax_timed", "sv_tree_attention_mask",
+                            "sv_tree_row_argmax_timed", "sv_tree_verify_greedy_timed",
+                            "sv_tree_attention_mask",
                             "sv_tree_attention_mask_timed", "sv_tree_verify_path",
                             "sv_tree_verify_path_ex", "sv_tree_multi_workspace_bytes",
                             "sv_tree_verify_multi", "sv_tree_verify_multi_ex",
@@ -172,7 +173,7 @@ def test_chain_without_drafts_needs_no_draft_tensor():
 
 
 GREEDY_ENTRIES = ["sv_tree_verify_greedy", "sv_tree_row_argmax", "sv_tree_greedy_walk",
-                  "sv_tree_row_argmax_timed"]
+                  "sv_tree_row_argmax_timed", "sv_tree_verify_greedy_timed"]
 
 
 def greedy_call(fn="sv_tree_verify_greedy", **kw):
