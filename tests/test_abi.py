@@ -57,11 +57,12 @@ def _header_enum(name):
 
 
 def test_status_codes_and_data_bits():
-    """The return codes and data-status bits the header fixes.  Against the
-    survey's sketch of the boundary they differ on purpose: SV_ESHAPE is not
-    used (shape errors are SV_EINVAL), SV_ENULL, SV_EALIGN and SV_ETOOBIG are
-    added, so the codes are renumbered; data errors are OR-ed bits of one
-    status word rather than a first-error code."""
+    """The return codes and data-status bits the header fixes.  There is no
+    separate shape code (a bad size is SV_EINVAL); null pointers, misaligned
+    logits and the no-alloc call's size limit have codes of their own
+    (SV_ENULL, SV_EALIGN, SV_ETOOBIG); data errors are OR-ed bits of one
+    status word, so that a call reports every kind it met, not only the
+    first."""
     codes = _header_enum("sv_status")
     assert codes == {"SV_OK": 0, "SV_EINVAL": 1, "SV_ENULL": 2, "SV_EALIGN": 3,
                      "SV_EWORKSPACE": 4, "SV_EDTYPE": 5, "SV_EHIP": 6, "SV_ETOOBIG": 7}
