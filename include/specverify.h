@@ -290,7 +290,7 @@ size_t sv_tree_workspace_bytes(int B, int N, int V);
  * tree's last row chunk walks that tree once the tree's other chunk and row
  * records (tagged with the call, write-through) are in; it waits only for
  * waves of earlier jobs, dispatched before it.  The status word is stored once,
- * by the last tree to finish.  Other sizes take the two launches below.  In
+ * by the wave of the batch's last tree.  Other sizes take the two launches below.  In
  * the one-launch form every wait is bounded (about a second): a wave that
  * gives up sets SV_DATA_SYNC, and the call's outputs are then invalid.
  */

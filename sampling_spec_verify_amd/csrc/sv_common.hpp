@@ -102,11 +102,11 @@ struct TreeArgs {
     int32_t *accepted_nodes;
     int32_t *status;
     ArgPart *part;                // [B, N+1, C1]
-    // one-launch call: the same slots as tagged record pairs, the completion
-    // word and the call's tag
+    // one-launch call: the same slots as tagged record pairs, row and tree
+    // words, and the call's tag
     unsigned long long *rec;      // [B, N+1, C1, 2]
     unsigned long long *rowword;  // [B, N+1]: each row's argmax
-    unsigned long long *done;
+    unsigned long long *treeflag; // [B]: each tree's flags
     uint32_t tag;
 };
 
@@ -188,17 +188,17 @@ inline int64_t alpha_layout_total(int B, int P, int V) {
 }
 
 struct TreeLayout {
-    int64_t status, done, part, rowword, total;
+    int64_t status, part, rowword, treeflag, total;
 };
 
 inline TreeLayout tree_layout(int B, int N, int V) {
     TreeLayout L;
     const int64_t c1max = c1_for(V, kMinNV, kMinVec);
     L.status = 0;
-    L.done = 64;
     L.part = 256;
     L.rowword = L.part + align256(int64_t(B) * (N + 1) * c1max * int64_t(sizeof(ArgPart)));
-    L.total = L.rowword + align256(int64_t(B) * (N + 1) * 8);
+    L.treeflag = L.rowword + align256(int64_t(B) * (N + 1) * 8);
+    L.total = L.treeflag + align256(int64_t(B) * 8);
     return L;
 }
 

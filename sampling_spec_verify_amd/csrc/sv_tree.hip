@@ -295,18 +295,17 @@ __global__ __launch_bounds__(kBlock2) void k_greedy_walk(TreeArgs a, int staged)
 //  * The wave of a tree's last chunk (row N) polls the other rows' words
 //    while it combines its own row, and walks the tree in registers, one lane
 //    per node.
-//  * The status word is written once, by the last tree to finish: each
-//    walking wave adds its tree and its flags to a completion word (tag |
-//    flags << 24 | trees done) by compare-and-swap, a word with another tag
-//    counting as zero trees; the wave that completes the count stores the
-//    status and resets the word.
+//  * The status word is stored once, by the wave of the batch's last tree
+//    (the grid's last job): every other walking wave stores its tree's flags
+//    as a word (tag, flags), and the last one polls those words while it
+//    combines its own row, so that its whole tail is one round trip.
 //
 // A wave waits only for waves of earlier jobs, dispatched before it.  Every
 // poll is bounded (about a second); a wave that gives up sets SV_DATA_SYNC
 // (outputs invalid) and goes on, so every wave ends.
 
 constexpr int kFoldNodes = kWave;           // N + 1 at most: one lane per node
-constexpr int kFoldTrees = 1024;            // trees per one-launch call at most
+constexpr int kFoldTrees = 1024;            // trees per one-launch call at most (flag words polled by one wave)
 constexpr int kFoldSpin = 1 << 20;          // polls of one record before the wave gives up
 
 __device__ __forceinline__ unsigned long long ld_agent(const unsigned long long *p) {
@@ -392,6 +391,9 @@ __device__ void fold_walk(const TreeArgs &a, int b, const ChunkMax &own) {
     // the other rows' words, in flight while this wave combines row N
     unsigned long long *rw = a.rowword + int64_t(b) * (N + 1);
     unsigned long long w = (lane < N) ? ld_agent(rw + lane) : 0ull;
+    // the batch's last tree: the other trees' flag words, also in flight
+    const bool last_tree = (b == a.B - 1);
+    unsigned long long fw = (last_tree && lane < b) ? ld_agent(a.treeflag + lane) : 0ull;
     const int am_n = fold_row(a, int64_t(b) * (N + 1) + N, own, flags);
     int am = am_n;
     if (lane < N) {
@@ -467,27 +469,33 @@ __device__ void fold_walk(const TreeArgs &a, int b, const ChunkMax &own) {
         a.out_tokens[int64_t(b) * (a.Dmax + 1) + i] = v;
         if (i < a.Dmax) a.accepted_nodes[int64_t(b) * a.Dmax + i] = (i < keep) ? p_next : -1;
     }
-    const int fl = wave_or8(flags);
-    if (lane == 0) {
-        a.accepted[b] = keep;
-        // count the tree in the completion word; the last tree stores the status
-        const unsigned long long tagw = static_cast<unsigned long long>(tag) << 32;
-        unsigned long long old = ld_agent(a.done);
-        unsigned long long cnt, acc;
-        for (;;) {
-            const bool mine = tagged(old, tag);
-            cnt = mine ? (old & 0xFFFFFFull) : 0ull;
-            acc = (mine ? ((old >> 24) & 0xFFull) : 0ull) | static_cast<unsigned long long>(fl & 0xFF);
-            const unsigned long long nw = tagw | (acc << 24) | (cnt + 1);
-            if (__hip_atomic_compare_exchange_strong(a.done, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT))
-                break;
-        }
-        if (cnt + 1 == static_cast<unsigned long long>(a.B)) {
-            *a.status = static_cast<int32_t>(acc);
-            st_agent(a.done, 0ull);
+    if (lane == 0) a.accepted[b] = keep;
+    if (!last_tree) {
+        const int fl = wave_or8(flags);
+        if (lane == 0) st_agent(a.treeflag + b, (static_cast<unsigned long long>(tag) << 32) | static_cast<uint32_t>(fl));
+        return;
+    }
+    // the status: this tree's flags and every other tree's flag word
+    int other = 0;
+    for (int t0 = 0; t0 < b; t0 += kWave) {
+        const int t = t0 + lane;
+        if (t < b) {
+            if (t0 > 0) fw = ld_agent(a.treeflag + t);
+            int polls = 0;
+            while (!tagged(fw, tag)) {
+                if (++polls > kFoldSpin) {
+                    flags |= SV_DATA_SYNC;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                fw = ld_agent(a.treeflag + t);
+            }
+            st_agent(a.treeflag + t, 0ull);
+            other |= static_cast<int>(static_cast<uint32_t>(fw));
         }
     }
+    const int fl = wave_or8(flags | (other & 0xFF));
+    if (lane == 0) *a.status = fl;
 }
 
 // Row argmax; the wave of a row's last chunk combines the row, and the wave
@@ -669,7 +677,7 @@ sv_status greedy_call(const void *target_logits, int64_t ld_t, sv_dtype dtype, i
     a.part = reinterpret_cast<ArgPart *>(ws + L.part);
     a.rec = reinterpret_cast<unsigned long long *>(ws + L.part);
     a.rowword = reinterpret_cast<unsigned long long *>(ws + L.rowword);
-    a.done = reinterpret_cast<unsigned long long *>(ws + L.done);
+    a.treeflag = reinterpret_cast<unsigned long long *>(ws + L.treeflag);
     a.tag = 0;
     return dtype == SV_BF16 ? run_tree<Bf16>(a, stream, which, ev_start, ev_stop)
                             : run_tree<F32>(a, stream, which, ev_start, ev_stop);
