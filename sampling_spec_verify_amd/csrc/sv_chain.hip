@@ -865,19 +865,30 @@ __device__ __forceinline__ int locate_wave(const ChainArgs &a, int b, const Samp
     // 1. this lane's run: piece masses (and, for the bonus row, chunk shifts)
     double tot = 0.0;
     float sm = -INFINITY;
-#pragma unroll 16
-    for (int j = 0; j < pp; ++j) {
-        const int p = p0 + j;
-        if (p < np) {
+    // batches of 8 pieces with every load in flight: the loads are not
+    // guarded (an index past the row's pieces reads the last one, unused),
+    // so no branch separates them
+    for (int j0 = 0; j0 < pp; j0 += 8) {
+        double mv[8];
+        float sv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int p = min(p0 + j0 + k, np - 1);
             const double *rc = cr + int64_t(p / kPieces) * a.rec_stride;
-            const double m = collect(&rc[2 + p % kPieces]);
-            stage[p] = m;
-            if (MODE == kBonus) {
-                const float sp = static_cast<float>(collect(&rc[0]));
-                sstage[p] = sp;
-                sm = fmaxf(sm, sp);
-            } else {
-                tot += m;                            // residual chunks share shift 0
+            mv[k] = collect(&rc[2 + p % kPieces]);
+            if (MODE == kBonus) sv[k] = static_cast<float>(collect(&rc[0]));
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int p = p0 + j0 + k;
+            if (j0 + k < pp && p < np) {
+                stage[p] = mv[k];
+                if (MODE == kBonus) {
+                    sstage[p] = sv[k];
+                    sm = fmaxf(sm, sv[k]);
+                } else {
+                    tot += mv[k];                    // residual chunks share shift 0
+                }
             }
         }
     }

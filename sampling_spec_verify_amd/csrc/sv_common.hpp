@@ -3,6 +3,7 @@
 // validation.  Validation runs on the host before any HIP call.
 #pragma once
 
+#include <atomic>
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -241,6 +242,14 @@ inline void launch_timed(Kernel kernel, dim3 grid, dim3 block, uint32_t lds, hip
         hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev_start, ev_stop, 0u, args...);
     else
         hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+}
+
+// A tag for the records one call hands between its waves: the top bit set
+// (so no untagged value, index or zero word matches it) and a process-wide
+// count below it (so no other call's records carry it).
+inline uint32_t next_call_tag() {
+    static std::atomic<uint32_t> calls{0};
+    return 0x80000000u | (calls.fetch_add(1u, std::memory_order_relaxed) & 0x7FFFFFFFu);
 }
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

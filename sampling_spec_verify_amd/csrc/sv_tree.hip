@@ -25,7 +25,6 @@
 #include <math.h>
 
 #include <algorithm>
-#include <atomic>
 
 #include "sv_common.hpp"
 #include "sv_device.hpp"
@@ -604,8 +603,7 @@ sv_status run_tree(const TreeArgs &a0, hipStream_t stream, int which, hipEvent_t
     if (rows * a.C1 >= (int64_t(1) << 31)) return SV_EINVAL;
     if (which == 3 && a.N + 1 <= kFoldNodes && a.B <= kFoldTrees) {
         // one launch: the walk in the argmax launch's tail
-        static std::atomic<uint32_t> calls{0};
-        a.tag = 0x80000000u | (calls.fetch_add(1u, std::memory_order_relaxed) & 0x7FFFFFFFu);
+        a.tag = next_call_tag();
         const int jobs = static_cast<int>(rows * a.C1);
         const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, cdiv(jobs, kWaves))));
         if (nv == 8)
