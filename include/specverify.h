@@ -63,10 +63,20 @@ typedef enum {
     SV_EWORKSPACE = 4,  /* workspace NULL, misaligned or smaller than required */
     SV_EDTYPE = 5,      /* unknown sv_dtype */
     SV_EHIP = 6,        /* a kernel launch failed */
-    SV_ETOOBIG = 7      /* sv_chain_verify_noalloc: the sizes need more than its fixed scratch */
+    SV_ETOOBIG = 7,     /* sv_chain_verify_noalloc: the sizes need more than its fixed scratch */
+    /* Not codes: they give the type the range of int, so that any int a C
+     * caller passes (sv_status_string(99)) is a value of the type in C++ too. */
+    SV_STATUS_INT_MIN_ = -0x7fffffff - 1,
+    SV_STATUS_INT_MAX_ = 0x7fffffff
 } sv_status;
 
-typedef enum { SV_BF16 = 0, SV_F32 = 1 } sv_dtype;
+typedef enum {
+    SV_BF16 = 0,
+    SV_F32 = 1,
+    /* not dtypes: the range of int, as for sv_status (an unknown dtype returns SV_EDTYPE) */
+    SV_DTYPE_INT_MIN_ = -0x7fffffff - 1,
+    SV_DTYPE_INT_MAX_ = 0x7fffffff
+} sv_dtype;
 
 /* Where the target and draft models are mixed ([RAPID]): SV_MIX_PROB is the
  * mixture equation of section "2) 推理时知识迁移", p~ = (1 - lambda) p_t +

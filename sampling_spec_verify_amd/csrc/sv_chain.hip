@@ -1453,6 +1453,7 @@ const char *sv_status_string(sv_status s) {
         case SV_EDTYPE: return "SV_EDTYPE: unknown dtype";
         case SV_EHIP: return "SV_EHIP: kernel launch failed";
         case SV_ETOOBIG: return "SV_ETOOBIG: the call needs more scratch than sv_chain_verify_noalloc holds";
+        default: break;
     }
     return "unknown sv_status";
 }

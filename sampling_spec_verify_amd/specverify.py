@@ -14,7 +14,9 @@ import os
 from typing import NamedTuple, Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libspecverify.so")
+# SPECVERIFY_LIB names another build of the same library (the host-sanitizer
+# build of the ABI tests); the binding raises if the file is missing.
+LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(HERE, "libspecverify.so")
 
 SV_OK, SV_EINVAL, SV_ENULL, SV_EALIGN, SV_EWORKSPACE, SV_EDTYPE, SV_EHIP, SV_ETOOBIG = range(8)
 SV_NOALLOC_SCRATCH_BYTES = 16 << 20

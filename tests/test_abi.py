@@ -53,7 +53,8 @@ def test_status_strings():
 def _header_enum(name):
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     body = re.search(r"typedef enum \{([^}]*)\} " + name + ";", text).group(1)
-    return {k: int(v) for k, v in re.findall(r"(SV_[A-Z0-9_]+)\s*=\s*(\d+)", body)}
+    # names ending in "_" only widen the type to the range of int
+    return {k: int(v) for k, v in re.findall(r"(SV_[A-Z0-9_]+)\s*=\s*(\d+)", body) if not k.endswith("_")}
 
 
 def test_status_codes_and_data_bits():
