@@ -130,10 +130,13 @@ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 // Row-stats wave-chunk: 64 lanes x NV vectors x VEC elements.
 inline int c1_for(int V, int NV, int vec) { return static_cast<int>(cdiv(V, 64LL * NV * vec)); }
 // Vectors per lane of a streaming wave-job: 8 (8 KB of bf16 per wave) unless
-// that leaves fewer than 2048 jobs to spread over the chip, then 4 or 2.
+// that leaves fewer than 512 jobs (two per compute unit), then 4 or 2.  Below
+// that, smaller jobs only multiply the partials the resolve combines: on one
+// request of 8 positions at V = 128256 a threshold of 2048 jobs gave 2 KB jobs
+// and a 15.7 us call, 512 gives 8 KB jobs and 15.2 us.
 inline int choose_stream_nv(int64_t rows, int V, int vec) {
     int nv = 8;
-    while (nv > kMinNV && rows * c1_for(V, nv, vec) < 2048) nv >>= 1;
+    while (nv > kMinNV && rows * c1_for(V, nv, vec) < 512) nv >>= 1;
     return nv;
 }
 
