@@ -1327,8 +1327,10 @@ sv_status run_typed(const ChainReq &q, int which) {
             launch_timed(k_resolve_mass<DT, 8>, grid, dim3(kBlock2), ldsb, q.stream, e0, e1, a, staged);
         } else if (a.NV2 == 4) {
             launch_timed(k_resolve_mass<DT, 4>, grid, dim3(kBlock2), ldsb, q.stream, e0, e1, a, staged);
-        } else {
+        } else if (a.NV2 == 2) {
             launch_timed(k_resolve_mass<DT, 2>, grid, dim3(kBlock2), ldsb, q.stream, e0, e1, a, staged);
+        } else {
+            launch_timed(k_resolve_mass<DT, 1>, grid, dim3(kBlock2), ldsb, q.stream, e0, e1, a, staged);
         }
         if (hipGetLastError() != hipSuccess) return SV_EHIP;
     }

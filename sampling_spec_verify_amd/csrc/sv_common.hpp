@@ -144,11 +144,13 @@ inline int c2_for(int V, int vec, int nv2) {
     return static_cast<int>(cdiv(V, int64_t(kBlock2) * nv2 * vec));
 }
 
-// Vectors per lane of a sampling chunk: the smallest of 2, 4, 8 that keeps
+// Vectors per lane of a sampling chunk: the smallest of 1, 2, 4, 8 that keeps
 // the chunk grid of launch 2 within one block per compute unit (256), as far
-// as larger chunks still help.
+// as larger chunks still help.  Small batches take one vector: their sampling
+// rows then spread over twice the compute units, which halves each wave's
+// residual weights (one request of 8 positions at V = 128256: 16 blocks).
 inline int choose_nv2(int B, int V, int vec) {
-    int nv2 = 2;
+    int nv2 = (c2_for(V, vec, 1) <= kMaxC2) ? 1 : 2;
     while (nv2 < 8 && int64_t(B) * c2_for(V, vec, nv2) > 256 &&
            c2_for(V, vec, 2 * nv2) < c2_for(V, vec, nv2))
         nv2 *= 2;
