@@ -138,14 +138,6 @@ __device__ __forceinline__ bool slot_position(const ChainArgs &a, int r, int &b,
     return geo_position_valid(a.g, b, i);
 }
 
-// alpha z_t + beta z_q - s in fp32 with alpha = m[0] + m[1], beta = m[2] + m[3]
-// (the hi + lo splits): the large products first, each fma rounding once,
-// then the two small corrections.  Near the largest mixed logit (the terms
-// that carry the mass) the result is within about 1e-7 of the exact value.
-__device__ __forceinline__ float mixed_expo(float zt, float zq, const float (&m)[4], float s) {
-    return fmaf(zq, m[3], fmaf(zt, m[1], fmaf(zq, m[2], fmaf(zt, m[0], -s))));
-}
-
 __device__ __forceinline__ const char *row_ptr(const Geo &g, int tensor, int b, int r) {
     if (tensor == 0)
         return g.tgt + (int64_t(b) * g.req_t * g.ld_t + int64_t(r) * g.ld_t) * g.elem;
@@ -1337,6 +1329,29 @@ sv_status run_typed(const ChainReq &q, int which) {
     return SV_OK;
 }
 
+// Row statistics of rows 0 .. R-1 of every request of [B, R, V] target and
+// draft logits: the first launch of a chain call with one position per row and
+// no drafted tokens.
+template <class DT>
+sv_status rows_stats_typed(ChainArgs a, hipStream_t stream, int nv) {
+    const int jobs = static_cast<int>(int64_t(a.B) * a.g.Pcap * (a.space == 1 ? 1 : 2) * a.C1);
+    const dim3 grid(static_cast<unsigned>(jobs > 0 ? cdiv(jobs, kStatsWaves) : 1));
+    const dim3 block(kStatsWaves * kWave);
+    if (a.space == 1) {
+        if (nv == 4) hipLaunchKernelGGL((k_row_stats_logit<DT, 4>), grid, block, 0, stream, a, jobs);
+        else hipLaunchKernelGGL((k_row_stats_logit<DT, 2>), grid, block, 0, stream, a, jobs);
+    } else if (nv == 8 && jobs >= kPrioJobs) {
+        hipLaunchKernelGGL((k_row_stats<DT, 8, true>), grid, block, 0, stream, a, jobs);
+    } else if (nv == 8) {
+        hipLaunchKernelGGL((k_row_stats<DT, 8, false>), grid, block, 0, stream, a, jobs);
+    } else if (nv == 4) {
+        hipLaunchKernelGGL((k_row_stats<DT, 4, false>), grid, block, 0, stream, a, jobs);
+    } else {
+        hipLaunchKernelGGL((k_row_stats<DT, 2, false>), grid, block, 0, stream, a, jobs);
+    }
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
 template <class DT, int NV>
 void launch_alpha(const ChainArgs &a, hipStream_t stream) {
     const int groups = (a.C1 + kWaves - 1) / kWaves;
@@ -1442,6 +1457,56 @@ sv_status scratch_for_current_device(void **out) {
 }
 
 }  // namespace
+
+namespace sv {
+
+int rows_stats_chunks(int B, int R, int V, sv_dtype dtype, int space) {
+    const int vec = 16 / elem_bytes(dtype);
+    const int nv = (space == 1) ? (int64_t(B) * R * c1_for(V, 4, vec) < 2048 ? 2 : 4)
+                                : choose_stream_nv(2LL * B * R, V, vec);
+    return c1_for(V, nv, vec);
+}
+
+sv_status rows_stats(const void *tgt, int64_t ld_t, const void *drf, int64_t ld_q, sv_dtype dtype, int B, int R,
+                     int V, float lam, float T, int space, Part *part1, int *count, int32_t *status,
+                     hipStream_t stream) {
+    const int eb = elem_bytes(dtype);
+    const int vec = 16 / eb;
+    const int nv = (space == 1) ? (int64_t(B) * R * c1_for(V, 4, vec) < 2048 ? 2 : 4)
+                                : choose_stream_nv(2LL * B * R, V, vec);
+    ChainArgs a{};
+    a.g.tgt = static_cast<const char *>(tgt);
+    a.g.drf = static_cast<const char *>(drf);
+    a.g.ld_t = ld_t;
+    a.g.ld_q = ld_q;
+    a.g.req_t = R;
+    a.g.req_q = R;
+    a.g.elem = eb;
+    a.g.V = V;
+    a.g.P = R;
+    a.g.Pcap = R;
+    a.g.N = 0;
+    a.g.tokens = nullptr;
+    a.g.draft_len = nullptr;
+    a.g.path = nullptr;
+    a.packed = 0;
+    a.B = B;
+    a.lam = lam;
+    temperature_split(T, &a.c_hi, &a.c_lo, &a.c_d);
+    a.status = status;
+    a.part1 = part1;
+    a.count = count;
+    a.C1 = c1_for(V, nv, vec);
+    a.ch1 = 64 * nv * vec;
+    a.space = space;
+    a.alpha_c = (1.0 - static_cast<double>(lam)) * a.c_d;
+    a.beta_c = static_cast<double>(lam) * a.c_d;
+    split_positive(a.alpha_c, &a.al_hi, &a.al_lo);
+    split_positive(a.beta_c, &a.be_hi, &a.be_lo);
+    return dtype == SV_BF16 ? rows_stats_typed<Bf16>(a, stream, nv) : rows_stats_typed<F32>(a, stream, nv);
+}
+
+}  // namespace sv
 
 extern "C" {
 

@@ -257,6 +257,16 @@ inline uint32_t next_call_tag() {
     return 0x80000000u | (calls.fetch_add(1u, std::memory_order_relaxed) & 0x7FFFFFFFu);
 }
 
+// Row statistics of rows 0 .. R-1 of every request of [B, R, V] target and
+// draft logits (the chain's first launch, one position per row): partials
+// [B, R, 2, C1] into part1, C1 = rows_stats_chunks(...).  Space 1: slot 0 of
+// a row holds the logit-space mixture's statistics, as in the chain.  count
+// (B ints) is cleared, status cleared.  Host code; enqueued on stream.
+int rows_stats_chunks(int B, int R, int V, sv_dtype dtype, int space);
+sv_status rows_stats(const void *tgt, int64_t ld_t, const void *drf, int64_t ld_q, sv_dtype dtype, int B, int R,
+                     int V, float lam, float T, int space, Part *part1, int *count, int32_t *status,
+                     hipStream_t stream);
+
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline int elem_bytes(sv_dtype d) { return d == SV_BF16 ? 2 : (d == SV_F32 ? 4 : 0); }

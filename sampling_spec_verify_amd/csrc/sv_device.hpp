@@ -143,6 +143,14 @@ __device__ __forceinline__ double exp2_d(double x) {
     return ldexp(1.41421356237309504880 * p, static_cast<int>(k));
 }
 
+// alpha z_t + beta z_q - s in fp32 with alpha = m[0] + m[1], beta = m[2] + m[3]
+// (the hi + lo splits): the large products first, each fma rounding once,
+// then the two small corrections.  Near the largest mixed logit (the terms
+// that carry the mass) the result is within about 1e-7 of the exact value.
+__device__ __forceinline__ float mixed_expo(float zt, float zq, const float (&m)[4], float s) {
+    return fmaf(zq, m[3], fmaf(zt, m[1], fmaf(zq, m[2], fmaf(zt, m[0], -s))));
+}
+
 // max(0, 1 - 2^e) in fp32 with an error of a few ulps relative to the result
 // itself, also where 2^e is close to 1 (the residual weight of an element whose
 // two probabilities nearly agree).  0 for e >= 0 and for NaN.  For

@@ -67,6 +67,9 @@ struct MultiArgs {
     int G;                                // blocks per tree; block g owns vocabulary slice g
     unsigned long long *pub;              // [B, G, 3, kSlot] values published at a barrier (bit patterns)
     unsigned *ticket;                     // start-order counter that assigns each block its (tree, slice)
+    const Part *part1;                    // [B, N+1, 2, C1]: chunk partials of every row's statistics
+    int C1;
+    float mx[4];                          // logit space: (1 - lambda) c and lambda c as hi + lo
 };
 
 struct MultiShared {
@@ -251,9 +254,10 @@ struct RowPair {
 __device__ __forceinline__ float m_pow2(float z, float c_hi, float c_lo, float s) {
     return __builtin_amdgcn_exp2f(fmaf(z, c_lo, fmaf(z, c_hi, -s)));
 }
-__device__ __forceinline__ float m_pow2_mixed(float zt, float zq, double al, double be, float s) {
-    return __builtin_amdgcn_exp2f(static_cast<float>(
-        fma(static_cast<double>(zt), al, fma(static_cast<double>(zq), be, -static_cast<double>(s)))));
+// 2^(alpha z_t + beta z_q - s), the exponent formed as the row-statistics
+// launch forms it (so the node's sums and its elements agree)
+__device__ __forceinline__ float m_pow2_mixed(float zt, float zq, const float (&mx)[4], float s) {
+    return __builtin_amdgcn_exp2f(mixed_expo(zt, zq, mx, s));
 }
 
 // p~(v) and q(v) of one element from its logits and the node's statistics
@@ -263,7 +267,7 @@ __device__ __forceinline__ void m_probs(const MultiArgs &a, const MultiShared &s
     const double iA = sh.iA, iB = sh.iB;
     q = static_cast<double>(m_pow2(zq, a.c_hi, a.c_lo, static_cast<float>(sh.sB))) * iB;
     if (a.space == 1) {
-        pm = static_cast<double>(m_pow2_mixed(zt, zq, a.al, a.be, static_cast<float>(sh.sA))) * iA;
+        pm = static_cast<double>(m_pow2_mixed(zt, zq, a.mx, static_cast<float>(sh.sA))) * iA;
     } else {
         const double pt = static_cast<double>(m_pow2(zt, a.c_hi, a.c_lo, static_cast<float>(sh.sA))) * iA;
         pm = (1.0 - static_cast<double>(a.lam)) * pt + static_cast<double>(a.lam) * q;
@@ -280,7 +284,7 @@ __device__ __forceinline__ float first_residual(const MultiArgs &a, const MultiS
     const float d = zq - zt;
     const float g = one_minus_exp2(fmaf(d, a.d_hi, fmaf(d, a.d_lo, sh.k0)));
     if (a.space == 1)
-        return static_cast<float>(static_cast<double>(m_pow2_mixed(zt, zq, a.al, a.be, static_cast<float>(sh.sA))) *
+        return static_cast<float>(static_cast<double>(m_pow2_mixed(zt, zq, a.mx, static_cast<float>(sh.sA))) *
                                   sh.iA * static_cast<double>(g));
     const double pt = static_cast<double>(m_pow2(zt, a.c_hi, a.c_lo, static_cast<float>(sh.sA))) * sh.iA;
     return static_cast<float>((1.0 - static_cast<double>(a.lam)) * pt * static_cast<double>(g));
@@ -335,7 +339,7 @@ __device__ void pass_stats(const MultiArgs &a, MultiShared &sh, int &phase, cons
             const float su = (sa == -INFINITY) ? 0.0f : sa;
             float acc = 0.0f;
             for (int e = 0; e < VEC; ++e)
-                acc += mixed ? m_pow2_mixed(ft[e], fq[e], a.al, a.be, su) : m_pow2(ft[e], a.c_hi, a.c_lo, su);
+                acc += mixed ? m_pow2_mixed(ft[e], fq[e], a.mx, su) : m_pow2(ft[e], a.c_hi, a.c_lo, su);
             aa += static_cast<double>(acc);
             if (!target_only) {
                 const float cq = (mq == -INFINITY) ? -INFINITY : ceilf(mq * a.c_hi);
@@ -378,6 +382,45 @@ __device__ void pass_stats(const MultiArgs &a, MultiShared &sh, int &phase, cons
         sh.SB = target_only ? 1.0 : SBt;
         sh.iA = 1.0 / SAt;
         sh.iB = target_only ? 1.0 : 1.0 / SBt;
+        sh.k0 = target_only ? 0.0f : static_cast<float>((tA - tB) + log2(SAt / SBt));
+    }
+    __syncthreads();
+}
+
+// The statistics of node u's rows from the chunk partials of the row-statistics
+// launch that precedes the walk (one position per row of the tree): wave 0
+// combines row A (the target, or the logit-space mixture), wave 1 the draft
+// row, in fp64 over the chunks in order.  No barrier between the tree's blocks:
+// each combines the same partials the same way.  target_only: row A alone.
+__device__ void load_stats(const MultiArgs &a, MultiShared &sh, int b, int u, bool target_only) {
+    const int wv = static_cast<int>(threadIdx.x) / kWave, lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+    if (wv == 0 || (wv == 1 && !target_only)) {
+        const Part *p = a.part1 + ((int64_t(b) * (a.N + 1) + u) * 2 + wv) * a.C1;
+        float smax = -INFINITY;
+        for (int c = lane; c < a.C1; c += kWave) smax = fmaxf(smax, p[c].s);
+        smax = wave_max(smax);
+        double S = 0.0;
+        for (int c = lane; c < a.C1; c += kWave) {
+            const Part q = p[c];
+            if (q.s != -INFINITY) S += q.S * pow2_shift_d(static_cast<double>(q.s) - static_cast<double>(smax));
+        }
+        S = wave_sum_d(S);
+        if (lane == 0) {
+            sh.red[wv] = S;
+            sh.redf[wv] = smax;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const double tA = sh.redf[0], SAt = sh.red[0];
+        const double tB = target_only ? 0.0 : static_cast<double>(sh.redf[1]);
+        const double SBt = target_only ? 1.0 : sh.red[1];
+        sh.sA = tA;
+        sh.SA = SAt;
+        sh.sB = tB;
+        sh.SB = SBt;
+        sh.iA = 1.0 / SAt;
+        sh.iB = 1.0 / SBt;
         sh.k0 = target_only ? 0.0f : static_cast<float>((tA - tB) + log2(SAt / SBt));
     }
     __syncthreads();
@@ -603,8 +646,10 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
         const char *rq = qb + int64_t(u) * a.ld_q * a.elem;
         const int first = (depth < a.Dmax) ? sh.head[u] : -1;
         if (first < 0) {
-            // bonus: the target's own softmax(z/T) at this node
-            pass_stats<DT>(a, sh, phase, rt, rq, true);
+            // bonus: the target's own softmax(z/T) at this node (in logit
+            // space the precomputed row A is the mixture: a pass of its own)
+            if (a.space == 1) pass_stats<DT>(a, sh, phase, rt, rq, true);
+            else load_stats(a, sh, b, u, true);
             tok = pass_draw<DT, kDrawBonus>(a, sh, phase, rt, rq, nullptr, us);
             if (tok < 0 && t == 0) sh.flags |= SV_DATA_BAD_ROW;
             break;
@@ -625,7 +670,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
                 }
             }
         }
-        pass_stats<DT>(a, sh, phase, rt, rq, false);
+        load_stats(a, sh, b, u, false);
 #pragma unroll
         for (int k = 0; k < kPre; ++k) {
             const int i = t + k * kMB;
@@ -762,14 +807,22 @@ namespace {
 using namespace sv;
 
 // status word (when the caller passes none) at 0 and the ticket counter at 64,
-// published slots [B, kMaxG, 3, kSlot], residual rows [B, 2, V]
+// published slots [B, kMaxG, 3, kSlot], residual rows [B, 2, V], the row
+// statistics' chunk partials [B, N+1, 2, C1] and their launch's counters [B]
 constexpr int64_t kTicketOffset = 64;
 int64_t multi_layout_pub() { return 256; }
 int64_t multi_layout_buf(int B) {
     return multi_layout_pub() + align256(int64_t(B) * kMaxG * kRot * kSlot * int64_t(sizeof(double)));
 }
-int64_t multi_layout_total(int B, int V) {
+int64_t multi_layout_part(int B, int V) {
     return multi_layout_buf(B) + align256(int64_t(B) * 2 * V * int64_t(sizeof(float)));
+}
+int64_t multi_layout_count(int B, int N, int V) {
+    return multi_layout_part(B, V) +
+           align256(int64_t(B) * (N + 1) * 2 * c1_for(V, kMinNV, kMinVec) * int64_t(sizeof(Part)));
+}
+int64_t multi_layout_total(int B, int N, int V) {
+    return multi_layout_count(B, N, V) + align256(int64_t(B) * int64_t(sizeof(int)));
 }
 
 // Blocks per tree: each block keeps at least one tile of the row; by default
@@ -792,7 +845,8 @@ sv_status verify_multi(const void *target_logits, int64_t ld_t, const void *draf
     const int eb = elem_bytes(dtype);
     if (eb == 0) return SV_EDTYPE;
     if (B < 0 || N < 0 || N > SV_MAX_TREE_NODES || V < 1 || Dmax < 0 || Dmax > SV_MAX_POSITIONS ||
-        B > (1 << 30) || int64_t(V) > (int64_t(1) << 28))
+        B > (1 << 30) || int64_t(V) > (int64_t(1) << 28) ||
+        int64_t(B) * (N + 1) * 2 * c1_for(V, kMinNV, kMinVec) >= (int64_t(1) << 31))
         return SV_EINVAL;
     sv_status st = check_scalars(lambda, temperature);
     if (st != SV_OK) return st;
@@ -802,7 +856,7 @@ sv_status verify_multi(const void *target_logits, int64_t ld_t, const void *draf
     if ((st = check_logits(target_logits, ld_t, V, eb)) != SV_OK) return st;
     if ((st = check_logits(draft_logits, ld_q, V, eb)) != SV_OK) return st;
     if (!workspace || !aligned16(workspace) ||
-        workspace_bytes < static_cast<size_t>(multi_layout_total(B, V)))
+        workspace_bytes < static_cast<size_t>(multi_layout_total(B, N, V)))
         return SV_EWORKSPACE;
     MultiArgs a;
     a.tgt = static_cast<const char *>(target_logits);
@@ -823,8 +877,11 @@ sv_status verify_multi(const void *target_logits, int64_t ld_t, const void *draf
     a.space = (mix_space == SV_MIX_LOGIT && lambda > 0.0f && lambda < 1.0f) ? 1 : 0;
     a.al = (1.0 - static_cast<double>(lambda)) * a.c_d;
     a.be = static_cast<double>(lambda) * a.c_d;
+    a.mx[0] = a.mx[1] = a.mx[2] = a.mx[3] = 0.0f;
     if (a.space == 1) {
         split_positive(a.al, &a.d_hi, &a.d_lo);
+        split_positive(a.al, &a.mx[0], &a.mx[1]);
+        split_positive(a.be, &a.mx[2], &a.mx[3]);
     } else {
         a.d_hi = a.c_hi;
         a.d_lo = a.c_lo;
@@ -838,6 +895,8 @@ sv_status verify_multi(const void *target_logits, int64_t ld_t, const void *draf
     a.pub = reinterpret_cast<unsigned long long *>(ws + multi_layout_pub());
     a.buf = reinterpret_cast<float *>(ws + multi_layout_buf(B));
     a.ticket = reinterpret_cast<unsigned *>(ws + kTicketOffset);
+    a.part1 = reinterpret_cast<const Part *>(ws + multi_layout_part(B, V));
+    a.C1 = rows_stats_chunks(B, N + 1, V, dtype, a.space);
     // A tree's blocks wait for one another; the start-order tickets make any
     // grid progress as long as G blocks fit at once.  By default B * G stays
     // within the resident capacity, so every tree runs in the first round.  An
@@ -853,6 +912,13 @@ sv_status verify_multi(const void *target_logits, int64_t ld_t, const void *draf
     const int64_t n_slots = int64_t(B) * a.G * kRot * kSlot;
     hipLaunchKernelGGL(k_multi_clear, dim3(static_cast<unsigned>(std::min<int64_t>(cdiv(n_slots, 256), 1024))),
                        dim3(256), 0, stream, a.status, a.ticket, a.pub, n_slots);
+    // every row's statistics in one streaming launch over the whole GPU: the
+    // walk then combines a node's chunk partials instead of a pass and a
+    // barrier of its own
+    st = rows_stats(target_logits, ld_t, draft_logits, ld_q, dtype, B, N + 1, V, lambda, temperature, a.space,
+                    reinterpret_cast<Part *>(ws + multi_layout_part(B, V)),
+                    reinterpret_cast<int *>(ws + multi_layout_count(B, N, V)), a.status, stream);
+    if (st != SV_OK) return st;
     const dim3 grid(static_cast<unsigned>(int64_t(B) * a.G));
     if (dtype == SV_BF16) {
         hipLaunchKernelGGL(k_tree_multi<Bf16>, grid, dim3(kMB), 0, stream, a);
@@ -868,7 +934,7 @@ extern "C" {
 
 size_t sv_tree_multi_workspace_bytes(int B, int N, int V) {
     if (B < 0 || N < 0 || N > SV_MAX_TREE_NODES || V < 1) return 0;
-    return static_cast<size_t>(multi_layout_total(B, V));
+    return static_cast<size_t>(multi_layout_total(B, N, V));
 }
 
 sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t, const void *draft_logits,
