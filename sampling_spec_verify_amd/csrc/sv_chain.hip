@@ -219,6 +219,11 @@ __device__ __forceinline__ void clear_counts(const ChainArgs &a) {
     for (int i = static_cast<int>(blockIdx.x) * THREADS + static_cast<int>(threadIdx.x); i < a.B;
          i += static_cast<int>(gridDim.x) * THREADS)
         a.count[i] = 0;
+    if (a.fill != nullptr) {
+        for (int64_t i = int64_t(blockIdx.x) * THREADS + threadIdx.x; i < a.fill_n; i += int64_t(gridDim.x) * THREADS)
+            a.fill[i] = a.fill_val;
+        if (blockIdx.x == 0 && threadIdx.x == 0) *a.zero_word = 0u;
+    }
 }
 
 // One wavefront per job; the job index is made wave-uniform so that its
@@ -1265,6 +1270,10 @@ ChainArgs make_args(const ChainReq &q, int vec, int nv) {
     a.NV2 = choose_nv2(q.B, q.V, vec);
     a.C2 = c2_for(q.V, vec, a.NV2);
     a.rec_stride = chunk_rec_doubles(a.NV2);
+    a.fill = nullptr;
+    a.fill_n = 0;
+    a.fill_val = 0;
+    a.zero_word = nullptr;
     a.space = q.space;
     a.alpha_c = (1.0 - static_cast<double>(q.lam)) * a.c_d;
     a.beta_c = static_cast<double>(q.lam) * a.c_d;
@@ -1469,7 +1478,8 @@ int rows_stats_chunks(int B, int R, int V, sv_dtype dtype, int space) {
 
 sv_status rows_stats(const void *tgt, int64_t ld_t, const void *drf, int64_t ld_q, sv_dtype dtype, int B, int R,
                      int V, float lam, float T, int space, Part *part1, int *count, int32_t *status,
-                     hipStream_t stream) {
+                     hipStream_t stream, unsigned long long *fill, int64_t fill_n, unsigned long long fill_val,
+                     unsigned *zero_word) {
     const int eb = elem_bytes(dtype);
     const int vec = 16 / eb;
     const int nv = (space == 1) ? (int64_t(B) * R * c1_for(V, 4, vec) < 2048 ? 2 : 4)
@@ -1503,6 +1513,10 @@ sv_status rows_stats(const void *tgt, int64_t ld_t, const void *drf, int64_t ld_
     a.beta_c = static_cast<double>(lam) * a.c_d;
     split_positive(a.alpha_c, &a.al_hi, &a.al_lo);
     split_positive(a.beta_c, &a.be_hi, &a.be_lo);
+    a.fill = fill;
+    a.fill_n = fill_n;
+    a.fill_val = fill_val;
+    a.zero_word = zero_word;
     return dtype == SV_BF16 ? rows_stats_typed<Bf16>(a, stream, nv) : rows_stats_typed<F32>(a, stream, nv);
 }
 

@@ -88,6 +88,12 @@ struct ChainArgs {
     double alpha_c, beta_c;       // logit space: (1 - lambda) c and lambda c, c = log2(e)/T, fp64
     float al_hi, al_lo, be_hi, be_lo;   // the same split as hi + lo, each part > 0 (fp32 exponents)
     double *alpha_part;           // [B, Pcap, C1] workspace: per-chunk sum of min(p~, q)
+    // words the row-statistics launch also sets for a caller that runs after
+    // it (the multi-branch walk's barrier slots and ticket); NULL: none
+    unsigned long long *fill;
+    int64_t fill_n;
+    unsigned long long fill_val;
+    unsigned *zero_word;
     float *alpha;                 // [B, P] out: expected acceptance of each drafted position
 };
 
@@ -261,11 +267,13 @@ inline uint32_t next_call_tag() {
 // draft logits (the chain's first launch, one position per row): partials
 // [B, R, 2, C1] into part1, C1 = rows_stats_chunks(...).  Space 1: slot 0 of
 // a row holds the logit-space mixture's statistics, as in the chain.  count
-// (B ints) is cleared, status cleared.  Host code; enqueued on stream.
+// (B ints) is cleared, status cleared, fill[0 .. fill_n) set to fill_val and
+// *zero_word to 0 (when given).  Host code; enqueued on stream.
 int rows_stats_chunks(int B, int R, int V, sv_dtype dtype, int space);
 sv_status rows_stats(const void *tgt, int64_t ld_t, const void *drf, int64_t ld_q, sv_dtype dtype, int B, int R,
                      int V, float lam, float T, int space, Part *part1, int *count, int32_t *status,
-                     hipStream_t stream);
+                     hipStream_t stream, unsigned long long *fill = nullptr, int64_t fill_n = 0,
+                     unsigned long long fill_val = 0, unsigned *zero_word = nullptr);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

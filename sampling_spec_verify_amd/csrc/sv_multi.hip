@@ -789,17 +789,6 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
     }
 }
 
-// Clears the status word and the ticket counter and empties every published
-// slot of the trees.
-__global__ void k_multi_clear(int32_t *status, unsigned *ticket, unsigned long long *pub, int64_t n) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        *status = 0;
-        *ticket = 0u;
-    }
-    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
-        pub[i] = kEmpty;
-}
-
 }  // namespace sv
 
 namespace {
@@ -910,14 +899,14 @@ sv_status verify_multi(const void *target_logits, int64_t ld_t, const void *draf
         return SV_EHIP;
     a.G = choose_g(B, V, 16 / eb, units * std::max(per_unit, 0), blocks_per_tree);
     const int64_t n_slots = int64_t(B) * a.G * kRot * kSlot;
-    hipLaunchKernelGGL(k_multi_clear, dim3(static_cast<unsigned>(std::min<int64_t>(cdiv(n_slots, 256), 1024))),
-                       dim3(256), 0, stream, a.status, a.ticket, a.pub, n_slots);
     // every row's statistics in one streaming launch over the whole GPU: the
     // walk then combines a node's chunk partials instead of a pass and a
-    // barrier of its own
+    // barrier of its own.  The launch also clears the status word, empties
+    // the walk's barrier slots and resets its ticket counter.
     st = rows_stats(target_logits, ld_t, draft_logits, ld_q, dtype, B, N + 1, V, lambda, temperature, a.space,
                     reinterpret_cast<Part *>(ws + multi_layout_part(B, V)),
-                    reinterpret_cast<int *>(ws + multi_layout_count(B, N, V)), a.status, stream);
+                    reinterpret_cast<int *>(ws + multi_layout_count(B, N, V)), a.status, stream, a.pub, n_slots,
+                    kEmpty, a.ticket);
     if (st != SV_OK) return st;
     const dim3 grid(static_cast<unsigned>(int64_t(B) * a.G));
     if (dtype == SV_BF16) {
