@@ -108,9 +108,10 @@ typedef enum { SV_MIX_PROB = 0, SV_MIX_LOGIT = 1 } sv_mix_space;
 #define SV_DATA_BAD_TREE    0x10 /* parent or path entry invalid: node never accepted / path cut */
 #define SV_DATA_FALLBACK    0x20 /* residual mass was zero after a rejection: sampled p~ instead */
 #define SV_DATA_DEPTH       0x40 /* accepted tree path deeper than Dmax: cut at Dmax nodes */
-#define SV_DATA_SYNC        0x80 /* sv_tree_verify_multi, one-launch sv_tree_verify_greedy: a wait
-                                    for another block's or wave's values gave up (other work held
-                                    the GPU's compute units); the call's outputs are invalid */
+#define SV_DATA_SYNC        0x80 /* sv_tree_verify_multi, one-launch sv_tree_verify_greedy,
+                                    sv_chain_acceptance_rate: a wait for another block's or wave's
+                                    values gave up (other work held the GPU's compute units); the
+                                    call's outputs are invalid */
 
 /* Human-readable name of a status code (static storage, host memory). */
 const char *sv_status_string(sv_status s);
@@ -256,13 +257,17 @@ sv_status sv_chain_verify_ex(const void *target_logits, int64_t ld_t,
  * this sum).  It needs no drafted tokens or uniforms.  Telemetry for a host
  * policy that adapts the draft length or lambda ([EAGLE] "4. 草稿长度和接受率
  * 的权衡"; [RAPID] section 2: lambda is schedulable).  Costs one more read of
- * every drafted row: three launches (row statistics, per-chunk min masses,
- * a fixed-order reduce).
+ * every drafted row: two launches (row statistics, which also set every
+ * alpha to 0; per-chunk min masses, each position's chunks summed in a fixed
+ * order by the wave of its last chunk, from tagged records that the reader
+ * clears).
  *
  *  Arguments as sv_chain_verify (draft_len may be NULL); mix_space an
  *  sv_mix_space.  alpha [B, K] float out (0 past draft_len[b]; NaN where a
  *  row is bad, with SV_DATA_BAD_ROW in *status).  workspace of at least
- *  sv_chain_acceptance_workspace_bytes(B, K, V) bytes.
+ *  sv_chain_acceptance_workspace_bytes(B, K, V) bytes.  A position's summing
+ *  wave waits only for blocks dispatched before its own; if that wait gives
+ *  up (about a second), its alpha is NaN and SV_DATA_SYNC is set.
  */
 size_t sv_chain_acceptance_workspace_bytes(int B, int K, int V);
 sv_status sv_chain_acceptance_rate(const void *target_logits, int64_t ld_t,

@@ -224,6 +224,10 @@ __device__ __forceinline__ void clear_counts(const ChainArgs &a) {
             a.fill[i] = a.fill_val;
         if (blockIdx.x == 0 && threadIdx.x == 0) *a.zero_word = 0u;
     }
+    if (a.zero_f != nullptr) {
+        for (int64_t i = int64_t(blockIdx.x) * THREADS + threadIdx.x; i < a.zero_f_n; i += int64_t(gridDim.x) * THREADS)
+            a.zero_f[i] = 0.0f;
+    }
 }
 
 // One wavefront per job; the job index is made wave-uniform so that its
@@ -481,6 +485,37 @@ __device__ __forceinline__ void combine_row(const Part *p, int C1, float &s_out,
     off_out = ok ? static_cast<float>(static_cast<double>(smax) + log2(S)) : NAN;
 }
 
+// alpha of one position, by the wave of its last chunk (own: that chunk's
+// sum): the other chunks' tagged sums, one lane per chunk, each lane adding
+// its chunks in chunk order, then a fixed-order wave sum.  The position's
+// blocks are dispatched before the block of its last chunk, so the wave waits
+// only for waves already started; a wave that gives up stores NaN and sets
+// SV_DATA_SYNC.  A NaN sum (a bad row) sets SV_DATA_BAD_ROW.
+__device__ __forceinline__ void alpha_fold(const ChainArgs &a, unsigned long long *rec, double own, int64_t pos) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t tag = a.tag;
+    int flags = 0;
+    double s = 0.0;
+    for (int c0 = 0; c0 < a.C1; c0 += kWave) {
+        const int c = c0 + lane;
+        if (c == a.C1 - 1) {
+            s += own;
+        } else if (c < a.C1 - 1) {
+            unsigned long long w0 = ld_agent(rec + 2 * c), w1 = ld_agent(rec + 2 * c + 1);
+            poll_pair(rec + 2 * c, tag, w0, w1, flags);
+            s += __longlong_as_double(static_cast<long long>((w1 << 32) | (w0 & 0xFFFFFFFFull)));
+        }
+    }
+    s = wave_sum_d(s);
+    const bool sync = __ballot(flags != 0) != 0ull;
+    if (lane == 0) {
+        const float out = sync ? NAN : static_cast<float>(s);
+        a.alpha[pos] = out;
+        const int f = (sync ? SV_DATA_SYNC : 0) | (!(out == out) && !sync ? SV_DATA_BAD_ROW : 0);
+        if (f) atomicOr(a.status, f);
+    }
+}
+
 // One block per (request, position, group of 4 chunks): wave 0 combines the
 // target (or mixed, in logit space) row's statistics and wave 1 the draft
 // row's, then wave w reduces chunk 4 g + w to the fp64 sum of
@@ -562,25 +597,17 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
     // a bad row (its statistics are NaN) makes alpha NaN; fminf alone would
     // drop a NaN probability in favour of the other one
     if (!(ti == ti && qi == qi)) tot = NAN;
-    if (lane == 0) a.alpha_part[(int64_t(b) * a.g.Pcap + i) * a.C1 + c] = tot;
-}
-
-// alpha of every position, summing its chunk partials in chunk order; 0 for
-// undrafted positions.  Sets SV_DATA_BAD_ROW when a drafted row is bad.
-__global__ __launch_bounds__(kBlock) void k_alpha_reduce(ChainArgs a) {
-    const int64_t pos = int64_t(blockIdx.x) * kBlock + threadIdx.x;
-    if (pos >= int64_t(a.B) * a.g.P) return;
-    const int b = static_cast<int>(pos / a.g.P);
-    const int i = static_cast<int>(pos % a.g.P);
-    float out = 0.0f;
-    if (i < a.g.Pcap && geo_position_valid(a.g, b, i)) {
-        const double *p = a.alpha_part + (int64_t(b) * a.g.Pcap + i) * a.C1;
-        double s = 0.0;
-        for (int c = 0; c < a.C1; ++c) s += p[c];
-        out = static_cast<float>(s);
-        if (!(out == out)) atomicOr(a.status, SV_DATA_BAD_ROW);
+    unsigned long long *rec = a.alpha_rec + (int64_t(b) * a.g.Pcap + i) * a.C1 * 2;
+    if (c != a.C1 - 1) {
+        if (lane == 0) {
+            const unsigned long long tagw = static_cast<unsigned long long>(a.tag) << 32;
+            const unsigned long long bits = static_cast<unsigned long long>(__double_as_longlong(tot));
+            st_agent(rec + 2 * c, tagw | (bits & 0xFFFFFFFFull));
+            st_agent(rec + 2 * c + 1, tagw | (bits >> 32));
+        }
+        return;
     }
-    a.alpha[pos] = out;
+    alpha_fold(a, rec, tot, int64_t(b) * a.g.P + i);
 }
 
 struct ResolveShared {
@@ -1185,6 +1212,8 @@ struct ChainReq {
     hipStream_t stream;
     hipEvent_t ev_start, ev_stop;   // optional: attached to the row-statistics launch
     int space;                      // 1: logit-space mixture (only for 0 < lambda < 1)
+    float *zero_f;                  // optional: floats the row-statistics launch sets to 0
+    int64_t zero_f_n;
 };
 
 int choose_nv(int B, int P, int V, int vec) { return choose_stream_nv(2LL * B * P, V, vec); }
@@ -1274,6 +1303,10 @@ ChainArgs make_args(const ChainReq &q, int vec, int nv) {
     a.fill_n = 0;
     a.fill_val = 0;
     a.zero_word = nullptr;
+    a.zero_f = q.zero_f;
+    a.zero_f_n = q.zero_f_n;
+    a.alpha_rec = nullptr;
+    a.tag = 0;
     a.space = q.space;
     a.alpha_c = (1.0 - static_cast<double>(q.lam)) * a.c_d;
     a.beta_c = static_cast<double>(q.lam) * a.c_d;
@@ -1374,23 +1407,26 @@ void launch_alpha(const ChainArgs &a, hipStream_t stream) {
 }
 
 // The acceptance-rate call: row statistics (as the verify call's first
-// launch, no drafted tokens), the per-chunk min(p~, q) masses, the reduce.
+// launch, no drafted tokens, which also clears alpha), then the per-chunk
+// min(p~, q) masses, each position summed by the wave of its last chunk.
 template <class DT>
 sv_status run_alpha_typed(const ChainReq &q, float *alpha) {
     const int nv = choose_nv_mode(q, DT::kVec);
     ChainArgs a = make_args(q, DT::kVec, nv);
-    a.alpha_part = reinterpret_cast<double *>(static_cast<char *>(q.ws) +
-                                              alpha_layout_parts(q.B, pcap(q), q.V));
+    a.alpha_rec = reinterpret_cast<unsigned long long *>(static_cast<char *>(q.ws) +
+                                                         alpha_layout_parts(q.B, pcap(q), q.V));
+    a.tag = next_call_tag();
     a.alpha = alpha;
-    sv_status st = run_typed<DT>(q, 1);
+    // the statistics launch also clears every alpha (undrafted positions stay 0)
+    ChainReq qs = q;
+    qs.zero_f = alpha;
+    qs.zero_f_n = int64_t(q.B) * q.P;
+    sv_status st = run_typed<DT>(qs, 1);
     if (st != SV_OK) return st;
     if (a.g.Pcap > 0) {
         if (nv == 8) launch_alpha<DT, 8>(a, q.stream);
         else if (nv == 4) launch_alpha<DT, 4>(a, q.stream);
         else launch_alpha<DT, 2>(a, q.stream);
-        const int64_t n = int64_t(q.B) * q.P;
-        hipLaunchKernelGGL(k_alpha_reduce, dim3(static_cast<unsigned>(cdiv(n, kBlock))), dim3(kBlock), 0,
-                           q.stream, a);
     }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
@@ -1433,6 +1469,8 @@ ChainReq chain_req(const void *t, int64_t ld_t, const void *d, int64_t ld_q, sv_
     q.ev_start = nullptr;
     q.ev_stop = nullptr;
     q.space = 0;
+    q.zero_f = nullptr;
+    q.zero_f_n = 0;
     return q;
 }
 

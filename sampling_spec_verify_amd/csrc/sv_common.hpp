@@ -87,13 +87,19 @@ struct ChainArgs {
     int space;                    // 0: probability-space mixture; 1: logit space (0 < lambda < 1)
     double alpha_c, beta_c;       // logit space: (1 - lambda) c and lambda c, c = log2(e)/T, fp64
     float al_hi, al_lo, be_hi, be_lo;   // the same split as hi + lo, each part > 0 (fp32 exponents)
-    double *alpha_part;           // [B, Pcap, C1] workspace: per-chunk sum of min(p~, q)
+    // [B, Pcap, C1, 2] workspace: each chunk's sum of min(p~, q) as a tagged
+    // word pair (low, high half of the double), and the call's tag
+    unsigned long long *alpha_rec;
+    uint32_t tag;
     // words the row-statistics launch also sets for a caller that runs after
-    // it (the multi-branch walk's barrier slots and ticket); NULL: none
+    // it (the multi-branch walk's barrier slots and ticket; the
+    // acceptance-rate output, every position of which starts at 0); NULL: none
     unsigned long long *fill;
     int64_t fill_n;
     unsigned long long fill_val;
     unsigned *zero_word;
+    float *zero_f;
+    int64_t zero_f_n;
     float *alpha;                 // [B, P] out: expected acceptance of each drafted position
 };
 
@@ -192,11 +198,10 @@ inline ChainLayout chain_layout(int B, int P, int V) {
 }
 
 // The acceptance-rate call: the chain layout, then the per-chunk partial sums
-// of min(p~, q), one double per (request, position, chunk).
+// of min(p~, q), one tagged word pair (16 bytes) per (request, position, chunk).
 inline int64_t alpha_layout_parts(int B, int P, int V) { return chain_layout(B, P, V).total; }
 inline int64_t alpha_layout_total(int B, int P, int V) {
-    return alpha_layout_parts(B, P, V) +
-           align256(int64_t(B) * P * c1_for(V, kMinNV, kMinVec) * int64_t(sizeof(double)));
+    return alpha_layout_parts(B, P, V) + align256(int64_t(B) * P * c1_for(V, kMinNV, kMinVec) * 16);
 }
 
 struct TreeLayout {

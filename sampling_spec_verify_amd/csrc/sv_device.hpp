@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "specverify.h"
+
 namespace sv {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -169,6 +171,47 @@ __device__ __forceinline__ float one_minus_exp2(float e) {
     const float small = -e * p;
     const float large = 1.0f - __builtin_amdgcn_exp2f(e);
     return fmaxf((e < -0.5f) ? large : small, 0.0f);  // e >= 0 gives small <= 0; NaN gives 0
+}
+
+// ---------------------------------------------------------------------------
+// tagged hand-over words between the waves of one launch
+// ---------------------------------------------------------------------------
+//
+// A 64-bit word carries the call's tag in its high half and 32 bits of payload
+// in its low half.  It is written as an agent-scope relaxed atomic store
+// (write-through, so visible to every XCD's L2) and read as an agent-scope
+// atomic load.  A reader polls until the tag appears and then clears the word,
+// so a later call (or a replay of the same captured launch, which keeps its
+// tag) never takes it for its own.
+
+constexpr int kPollSpin = 1 << 20;          // polls of one word before the wave gives up
+
+__device__ __forceinline__ unsigned long long ld_agent(const unsigned long long *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(unsigned long long *p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tagged(unsigned long long w, uint32_t tag) {
+    return static_cast<uint32_t>(w >> 32) == tag;
+}
+
+// Polls the word pair at p until both carry the tag (w0, w1: the words
+// already loaded); clears them.  A wave that gives up sets SV_DATA_SYNC.
+__device__ __forceinline__ void poll_pair(unsigned long long *p, uint32_t tag, unsigned long long &w0,
+                                          unsigned long long &w1, int &flags) {
+    int polls = 0;
+    while (!tagged(w0, tag) || !tagged(w1, tag)) {
+        if (++polls > kPollSpin) {
+            flags |= SV_DATA_SYNC;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        w0 = ld_agent(p);
+        w1 = ld_agent(p + 1);
+    }
+    st_agent(p, 0ull);
+    st_agent(p + 1, 0ull);
 }
 
 // ---------------------------------------------------------------------------

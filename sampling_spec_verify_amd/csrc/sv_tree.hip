@@ -305,34 +305,6 @@ __global__ __launch_bounds__(kBlock2) void k_greedy_walk(TreeArgs a, int staged)
 
 constexpr int kFoldNodes = kWave;           // N + 1 at most: one lane per node
 constexpr int kFoldTrees = 1024;            // trees per one-launch call at most (flag words polled by one wave)
-constexpr int kFoldSpin = 1 << 20;          // polls of one record before the wave gives up
-
-__device__ __forceinline__ unsigned long long ld_agent(const unsigned long long *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(unsigned long long *p, unsigned long long v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ bool tagged(unsigned long long w, uint32_t tag) {
-    return static_cast<uint32_t>(w >> 32) == tag;
-}
-
-// Polls the word pair at p until both carry the tag; clears them.
-__device__ __forceinline__ void poll_pair(unsigned long long *p, uint32_t tag, unsigned long long &w0,
-                                          unsigned long long &w1, int &flags) {
-    int polls = 0;
-    while (!tagged(w0, tag) || !tagged(w1, tag)) {
-        if (++polls > kFoldSpin) {
-            flags |= SV_DATA_SYNC;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        w0 = ld_agent(p);
-        w1 = ld_agent(p + 1);
-    }
-    st_agent(p, 0ull);
-    st_agent(p + 1, 0ull);
-}
 
 // The argmax of the row whose last chunk this wave holds (own): its other
 // chunks' records, one lane per chunk, combined as the two-launch walk does
@@ -398,7 +370,7 @@ __device__ void fold_walk(const TreeArgs &a, int b, const ChunkMax &own) {
     if (lane < N) {
         int polls = 0;
         while (!tagged(w, tag)) {
-            if (++polls > kFoldSpin) {
+            if (++polls > kPollSpin) {
                 flags |= SV_DATA_SYNC;
                 break;
             }
@@ -482,7 +454,7 @@ __device__ void fold_walk(const TreeArgs &a, int b, const ChunkMax &own) {
             if (t0 > 0) fw = ld_agent(a.treeflag + t);
             int polls = 0;
             while (!tagged(fw, tag)) {
-                if (++polls > kFoldSpin) {
+                if (++polls > kPollSpin) {
                     flags |= SV_DATA_SYNC;
                     break;
                 }
