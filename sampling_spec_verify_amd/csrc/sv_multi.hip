@@ -63,7 +63,8 @@ struct MultiArgs {
     int32_t *accepted, *out_tokens, *accepted_nodes;
     float *accept_prob;                   // [B, N] or NULL
     int32_t *status;
-    float *buf;                           // [B, 2, V] residual ping-pong
+    float *buf;                           // [B, 2, Vp] residual ping-pong
+    int Vp;                               // residual row stride: V rounded up to 8 floats
     int G;                                // blocks per tree; block g owns vocabulary slice g
     unsigned long long *pub;              // [B, G, 3, kSlot] values published at a barrier (bit patterns)
     unsigned *ticket;                     // start-order counter that assigns each block its (tree, slice)
@@ -426,12 +427,37 @@ __device__ void load_stats(const MultiArgs &a, MultiShared &sh, int b, int u, bo
     __syncthreads();
 }
 
+// The VEC fp32 values of vector gv of a residual row (16-byte loads; the
+// row stride Vp keeps every vector aligned), and their store.
+template <int VEC>
+__device__ __forceinline__ void load_res_vec(const float *row, int gv, float (&f)[VEC]) {
+#pragma unroll
+    for (int h = 0; h < VEC / 4; ++h) {
+        const u32x4 d = *reinterpret_cast<const u32x4 *>(row + int64_t(gv) * VEC + 4 * h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[4 * h + j] = __uint_as_float(d[j]);
+    }
+}
+template <int VEC>
+__device__ __forceinline__ void store_res_vec(float *row, int gv, const float (&f)[VEC]) {
+#pragma unroll
+    for (int h = 0; h < VEC / 4; ++h) {
+        u32x4 d;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = __float_as_uint(f[4 * h + j]);
+        *reinterpret_cast<u32x4 *>(row + int64_t(gv) * VEC + 4 * h) = d;
+    }
+}
+
 // Residual after a rejection: w(v) = max(0, r(v) - q(v)) with r = p~ (first
 // rejection, from the logits: first_residual) or the previous residual
 // in[v] / Zin; w is
 // stored (fp32) in out, where only this block reads it again (its slice), and
 // its fp64 sum over the tree's slices returned.  The child tests form w at a
-// child's token again from the same values and operations.
+// child's token again from the same values and operations.  Each thread
+// loads all its vectors (logits and the previous residual) before any
+// arithmetic, forms each vector's weights in registers and stores them as
+// whole vectors (0 past V, inside the padded row).
 template <class DT>
 __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, int &phase, const char *row_t,
                                 const char *row_q, const float *in, double Zin, float *out) {
@@ -442,33 +468,36 @@ __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, int &phase,
     double tot = 0.0;
     for (int g0 = sl.lo; g0 < sl.hi; g0 += kMB * kMU) {
         u32x4 dt[kMU], dq[kMU];
+        float pin[kMU][VEC];
 #pragma unroll
         for (int k = 0; k < kMU; ++k) {
             const int gv = g0 + k * kMB + static_cast<int>(threadIdx.x);
             dt[k] = load_row_vec<DT, false>(row_t, gv < sl.hi ? gv : nvec, V);
             dq[k] = load_row_vec<DT, false>(row_q, gv < sl.hi ? gv : nvec, V);
+            if (in != nullptr) load_res_vec<VEC>(in, gv < sl.hi ? gv : sl.lo, pin[k]);
         }
 #pragma unroll
         for (int k = 0; k < kMU; ++k) {
             const int gv = g0 + k * kMB + static_cast<int>(threadIdx.x);
             if (gv >= sl.hi) continue;
-            float ft[VEC], fq[VEC];
+            float ft[VEC], fq[VEC], w[VEC];
             DT::unpack(dt[k], ft);
             DT::unpack(dq[k], fq);
+#pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const int v = gv * VEC + e;
-                if (v >= V) break;
-                float w;
+                float we;
                 if (in == nullptr) {
-                    w = first_residual(a, sh, ft[e], fq[e]);
+                    we = first_residual(a, sh, ft[e], fq[e]);
                 } else {
                     double pm, q;
                     m_probs<DT>(a, sh, ft[e], fq[e], pm, q);
-                    w = static_cast<float>(fmax(0.0, static_cast<double>(in[v]) / Zin - q));
+                    we = static_cast<float>(fmax(0.0, static_cast<double>(pin[k][e]) / Zin - q));
                 }
-                out[v] = w;
-                tot += static_cast<double>(w);
+                w[e] = (gv * VEC + e < V) ? we : 0.0f;
             }
+            store_res_vec<VEC>(out, gv, w);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) tot += static_cast<double>(w[e]);
         }
     }
     const double mine[kSlot] = {mblock_sum(tot, sh), 0.0, 0.0, 0.0};
@@ -502,13 +531,17 @@ __device__ __forceinline__ double tile_weights(const MultiArgs &a, const MultiSh
     constexpr int VEC = DT::kVec;
     const int V = a.V;
     const int gl = (gv < hi) ? gv : (V + VEC - 1) / VEC;      // past the slice: a -inf vector
-    float ft[VEC], fq[VEC];
+    float ft[VEC], fq[VEC], fb[VEC];
     if (KIND != kDrawBuffer) DT::unpack(load_row_vec<DT, false>(row_t, gl, V), ft);
     if (KIND == kDrawMixture) DT::unpack(load_row_vec<DT, false>(row_q, gl, V), fq);
+    if (KIND == kDrawBuffer) load_res_vec<VEC>(buf, (gv < hi) ? gv : hi - 1, fb);
     double sum = 0.0;
+#pragma unroll
     for (int e = 0; e < VEC; ++e) {
         const int v = gv * VEC + e;
-        w[e] = (gv < hi && v < V) ? draw_weight<DT, KIND>(a, sh, ft[e], fq[e], buf, v) : 0.0;
+        const double we = (KIND == kDrawBuffer) ? static_cast<double>(fb[e])
+                                                : draw_weight<DT, KIND>(a, sh, ft[e], fq[e], buf, v);
+        w[e] = (gv < hi && v < V) ? we : 0.0;
         if (!(w[e] > 0.0)) w[e] = 0.0;
         sum += w[e];
         if (w[e] > 0.0) last = v;
@@ -636,8 +669,8 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
 
     const char *tb = a.tgt + int64_t(b) * (N + 1) * a.ld_t * a.elem;
     const char *qb = a.drf + int64_t(b) * (N + 1) * a.ld_q * a.elem;
-    float *buf0 = a.buf + int64_t(b) * 2 * V;
-    float *buf1 = buf0 + V;
+    float *buf0 = a.buf + int64_t(b) * 2 * a.Vp;
+    float *buf1 = buf0 + a.Vp;
     const double us = static_cast<double>(a.u_sample[b]);
     int u = 0, depth = 0, tok = -1;
     bool done = false;
@@ -796,15 +829,16 @@ namespace {
 using namespace sv;
 
 // status word (when the caller passes none) at 0 and the ticket counter at 64,
-// published slots [B, kMaxG, 3, kSlot], residual rows [B, 2, V], the row
+// published slots [B, kMaxG, 3, kSlot], residual rows [B, 2, Vp] (Vp = V rounded up to 8), the row
 // statistics' chunk partials [B, N+1, 2, C1] and their launch's counters [B]
 constexpr int64_t kTicketOffset = 64;
 int64_t multi_layout_pub() { return 256; }
 int64_t multi_layout_buf(int B) {
     return multi_layout_pub() + align256(int64_t(B) * kMaxG * kRot * kSlot * int64_t(sizeof(double)));
 }
+int64_t multi_residual_stride(int V) { return (int64_t(V) + 7) / 8 * 8; }
 int64_t multi_layout_part(int B, int V) {
-    return multi_layout_buf(B) + align256(int64_t(B) * 2 * V * int64_t(sizeof(float)));
+    return multi_layout_buf(B) + align256(int64_t(B) * 2 * multi_residual_stride(V) * int64_t(sizeof(float)));
 }
 int64_t multi_layout_count(int B, int N, int V) {
     return multi_layout_part(B, V) +
@@ -883,6 +917,7 @@ sv_status verify_multi(const void *target_logits, int64_t ld_t, const void *draf
     a.status = status ? status : reinterpret_cast<int32_t *>(ws);
     a.pub = reinterpret_cast<unsigned long long *>(ws + multi_layout_pub());
     a.buf = reinterpret_cast<float *>(ws + multi_layout_buf(B));
+    a.Vp = static_cast<int>(multi_residual_stride(V));
     a.ticket = reinterpret_cast<unsigned *>(ws + kTicketOffset);
     a.part1 = reinterpret_cast<const Part *>(ws + multi_layout_part(B, V));
     a.C1 = rows_stats_chunks(B, N + 1, V, dtype, a.space);
