@@ -45,6 +45,7 @@ constexpr int kMB = 512;                  // threads of a walk block (1024 spill
 constexpr int kMW = kMB / kWave;          // its waves
 constexpr int kMU = 2;                    // tiles of a pass in flight per thread
 constexpr int kMNodes = SV_MAX_TREE_NODES + 1;
+constexpr int kSpec = (kMB / 64 - 2) / 2;  // statistics slots filled ahead of need (waves 2 and up, two per node)
 constexpr int kMaxG = 16;                 // blocks per tree at most
 constexpr int kSlot = 4;                  // doubles a block publishes per barrier
 constexpr int kSpinLimit = 1 << 20;       // polls of a barrier before it is given up (about 1 s)
@@ -80,6 +81,7 @@ struct MultiShared {
     int tok[kMNodes];
     double zs[kMNodes];                   // residual masses of the current node, in order
     float czt[kMNodes], czq[kMNodes];     // target / draft logit of each child's token at its parent's rows
+    float ua[kMNodes];                    // acceptance uniform of each node's draft
     int path[SV_MAX_POSITIONS + 1];
     double red[kMW];
     float redf[kMW];
@@ -88,6 +90,11 @@ struct MultiShared {
     double iA, iB;                        // 1 / SA, 1 / SB
     float k0;                             // q(v) / A(v) = 2^((z_q - z_t) d + k0)
     double gath[kMaxG][kSlot];            // every block's published values after a barrier
+    // statistics combined ahead of need: slot k holds the rows (A, B) of node
+    // spec_node[k] (-1: none) as shift and sum
+    int spec_node[kSpec];
+    double spec_s[kSpec][2], spec_S[kSpec][2];
+    int spec_hit;
     int flags, decision, token, broken;
     int tree, slice;                      // this block's role, from its start-order ticket
 };
@@ -393,38 +400,95 @@ __device__ void pass_stats(const MultiArgs &a, MultiShared &sh, int &phase, cons
 // combines row A (the target, or the logit-space mixture), wave 1 the draft
 // row, in fp64 over the chunks in order.  No barrier between the tree's blocks:
 // each combines the same partials the same way.  target_only: row A alone.
+// One row's (shift, sum) from its chunk partials, by one whole wave (results
+// uniform over the wave): row 0 is A, row 1 is B of node u.
+__device__ __forceinline__ void row_combine(const MultiArgs &a, int b, int u, int row, float &smax_out,
+                                            double &S_out) {
+    const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+    const Part *p = a.part1 + ((int64_t(b) * (a.N + 1) + u) * 2 + row) * a.C1;
+    float smax = -INFINITY;
+    for (int c = lane; c < a.C1; c += kWave) smax = fmaxf(smax, p[c].s);
+    smax = wave_max(smax);
+    double S = 0.0;
+    for (int c = lane; c < a.C1; c += kWave) {
+        const Part q = p[c];
+        if (q.s != -INFINITY) S += q.S * pow2_shift_d(static_cast<double>(q.s) - static_cast<double>(smax));
+    }
+    smax_out = smax;
+    S_out = wave_sum_d(S);
+}
+
+// The node's statistics in shared memory from its rows' (shift, sum); one thread.
+__device__ __forceinline__ void set_stats(MultiShared &sh, double tA, double SAt, double tB, double SBt,
+                                          bool target_only) {
+    if (target_only) {
+        tB = 0.0;
+        SBt = 1.0;
+    }
+    sh.sA = tA;
+    sh.SA = SAt;
+    sh.sB = tB;
+    sh.SB = SBt;
+    sh.iA = 1.0 / SAt;
+    sh.iB = 1.0 / SBt;
+    sh.k0 = target_only ? 0.0f : static_cast<float>((tA - tB) + log2(SAt / SBt));
+}
+
 __device__ void load_stats(const MultiArgs &a, MultiShared &sh, int b, int u, bool target_only) {
     const int wv = static_cast<int>(threadIdx.x) / kWave, lane = static_cast<int>(threadIdx.x) & (kWave - 1);
     if (wv == 0 || (wv == 1 && !target_only)) {
-        const Part *p = a.part1 + ((int64_t(b) * (a.N + 1) + u) * 2 + wv) * a.C1;
-        float smax = -INFINITY;
-        for (int c = lane; c < a.C1; c += kWave) smax = fmaxf(smax, p[c].s);
-        smax = wave_max(smax);
-        double S = 0.0;
-        for (int c = lane; c < a.C1; c += kWave) {
-            const Part q = p[c];
-            if (q.s != -INFINITY) S += q.S * pow2_shift_d(static_cast<double>(q.s) - static_cast<double>(smax));
-        }
-        S = wave_sum_d(S);
+        float smax;
+        double S;
+        row_combine(a, b, u, wv, smax, S);
         if (lane == 0) {
             sh.red[wv] = S;
             sh.redf[wv] = smax;
         }
     }
     __syncthreads();
+    if (threadIdx.x == 0)
+        set_stats(sh, sh.redf[0], sh.red[0], target_only ? 0.0 : static_cast<double>(sh.redf[1]),
+                  target_only ? 1.0 : sh.red[1], target_only);
+    __syncthreads();
+}
+
+// Statistics ahead of need: waves 2 .. 2 kSpec + 1 combine the rows of the
+// given nodes (two waves per node) into the slots, with no barrier: the
+// caller's next block barrier publishes them.  Thread 0 records the nodes.
+__device__ __forceinline__ void spec_stats(const MultiArgs &a, MultiShared &sh, int b, const int (&nodes)[kSpec]) {
+    const int wv = static_cast<int>(threadIdx.x) / kWave, lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+    if (threadIdx.x == 0)
+        for (int k = 0; k < kSpec; ++k) sh.spec_node[k] = nodes[k];
+    if (wv >= 2 && wv < 2 + 2 * kSpec) {
+        const int k = (wv - 2) >> 1, row = (wv - 2) & 1;
+        if (nodes[k] >= 0) {
+            float smax;
+            double S;
+            row_combine(a, b, nodes[k], row, smax, S);
+            if (lane == 0) {
+                sh.spec_s[k][row] = static_cast<double>(smax);
+                sh.spec_S[k][row] = S;
+            }
+        }
+    }
+}
+
+// Node u's statistics from a slot filled ahead of need, if one holds it (the
+// same values load_stats would set); every slot is emptied.  Block barrier.
+__device__ __forceinline__ bool take_spec(MultiShared &sh, int u, bool target_only) {
     if (threadIdx.x == 0) {
-        const double tA = sh.redf[0], SAt = sh.red[0];
-        const double tB = target_only ? 0.0 : static_cast<double>(sh.redf[1]);
-        const double SBt = target_only ? 1.0 : sh.red[1];
-        sh.sA = tA;
-        sh.SA = SAt;
-        sh.sB = tB;
-        sh.SB = SBt;
-        sh.iA = 1.0 / SAt;
-        sh.iB = 1.0 / SBt;
-        sh.k0 = target_only ? 0.0f : static_cast<float>((tA - tB) + log2(SAt / SBt));
+        int hit = 0;
+        for (int k = 0; k < kSpec; ++k) {
+            if (!hit && sh.spec_node[k] == u) {
+                set_stats(sh, sh.spec_s[k][0], sh.spec_S[k][0], sh.spec_s[k][1], sh.spec_S[k][1], target_only);
+                hit = 1;
+            }
+            sh.spec_node[k] = -1;
+        }
+        sh.spec_hit = hit;
     }
     __syncthreads();
+    return sh.spec_hit != 0;
 }
 
 // The VEC fp32 values of vector gv of a residual row (16-byte loads; the
@@ -645,6 +709,13 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
         sh.next[i] = -1;
         sh.tok[i] = (i > 0) ? a.node_token[int64_t(b) * N + i - 1] : -1;
         sh.par[i] = (i > 0) ? a.parent[int64_t(b) * N + i - 1] : -1;
+        sh.ua[i] = (i > 0) ? a.u_accept[int64_t(b) * N + i - 1] : 0.0f;
+    }
+    {
+        // the root's statistics, combined while the tree is read
+        int nodes[kSpec];
+        for (int k = 0; k < kSpec; ++k) nodes[k] = (k == 0) ? 0 : -1;
+        spec_stats(a, sh, b, nodes);
     }
     if (a.accept_prob != nullptr && g == 0)
         for (int i = t; i < N; i += kMB) a.accept_prob[int64_t(b) * N + i] = -1.0f;
@@ -674,43 +745,51 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
     const double us = static_cast<double>(a.u_sample[b]);
     int u = 0, depth = 0, tok = -1;
     bool done = false;
+    bool kids_ready = false;            // the children's logits of node u are in sh.czt / sh.czq
     while (!done) {
         const char *rt = tb + int64_t(u) * a.ld_t * a.elem;
         const char *rq = qb + int64_t(u) * a.ld_q * a.elem;
         const int first = (depth < a.Dmax) ? sh.head[u] : -1;
+        // the node's statistics, when combined ahead of need
+        const bool have = take_spec(sh, u, first < 0);
         if (first < 0) {
             // bonus: the target's own softmax(z/T) at this node (in logit
             // space the precomputed row A is the mixture: a pass of its own)
             if (a.space == 1) pass_stats<DT>(a, sh, phase, rt, rq, true);
-            else load_stats(a, sh, b, u, true);
+            else if (!have) load_stats(a, sh, b, u, true);
             tok = pass_draw<DT, kDrawBonus>(a, sh, phase, rt, rq, nullptr, us);
             if (tok < 0 && t == 0) sh.flags |= SV_DATA_BAD_ROW;
             break;
         }
-        // the children's two logits, loaded by the threads of their node ids
-        // while the statistics pass runs, for thread 0's child tests
+        // the children's two logits, for thread 0's child tests: loaded by
+        // the threads of their node ids while the statistics combine, unless
+        // the parent's visit loaded them already (see below)
         constexpr int kPre = (kMNodes + kMB - 1) / kMB;
-        float pzt[kPre], pzq[kPre];
+        if (!kids_ready) {
+            float pzt[kPre], pzq[kPre];
 #pragma unroll
-        for (int k = 0; k < kPre; ++k) {
-            const int i = t + k * kMB;
-            pzt[k] = pzq[k] = 0.0f;
-            if (i >= 1 && i <= N && sh.par[i] == u) {
-                const int x = sh.tok[i];
-                if (x >= 0 && x < V) {
-                    pzt[k] = DT::load1(rt, x);
-                    pzq[k] = DT::load1(rq, x);
+            for (int k = 0; k < kPre; ++k) {
+                const int i = t + k * kMB;
+                pzt[k] = pzq[k] = 0.0f;
+                if (i >= 1 && i <= N && sh.par[i] == u) {
+                    const int x = sh.tok[i];
+                    if (x >= 0 && x < V) {
+                        pzt[k] = DT::load1(rt, x);
+                        pzq[k] = DT::load1(rq, x);
+                    }
                 }
             }
-        }
-        load_stats(a, sh, b, u, false);
+            if (!have) load_stats(a, sh, b, u, false);
 #pragma unroll
-        for (int k = 0; k < kPre; ++k) {
-            const int i = t + k * kMB;
-            if (i >= 1 && i <= N && sh.par[i] == u) {
-                sh.czt[i] = pzt[k];
-                sh.czq[i] = pzq[k];
+            for (int k = 0; k < kPre; ++k) {
+                const int i = t + k * kMB;
+                if (i >= 1 && i <= N && sh.par[i] == u) {
+                    sh.czt[i] = pzt[k];
+                    sh.czq[i] = pzq[k];
+                }
             }
+        } else if (!have) {
+            load_stats(a, sh, b, u, false);
         }
         __syncthreads();
         if (!(sh.SA > 0.0) || !isfinite(sh.SA) || !(sh.SB > 0.0) || !isfinite(sh.SB) ||
@@ -725,6 +804,37 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
         int nrej = 0;                    // residuals formed at this node; their masses in sh.zs
         int c = first, nxt = -1;
         bool drawn = false;
+        {
+            // the first children's statistics, combined while thread 0
+            // tests the first child (the test's barrier publishes them)
+            int nodes[kSpec];
+            int cc = first;
+            for (int k = 0; k < kSpec; ++k) {
+                nodes[k] = cc;
+                cc = (cc >= 0) ? sh.next[cc] : -1;
+            }
+            spec_stats(a, sh, b, nodes);
+            // and the grandchildren's two logits at their parents' rows, for
+            // the tests at whichever child is accepted; node i is taken by
+            // thread i + 64, so that wave 0 (thread 0 tests) loads nothing
+            // for trees of fewer than kMB - 64 nodes
+            constexpr int kPre2 = (kMNodes + kWave + kMB - 1) / kMB;
+#pragma unroll
+            for (int k = 0; k < kPre2; ++k) {
+                const int i = t - kWave + k * kMB;
+                if (i < 1 || i > N) continue;
+                const int pi = sh.par[i];
+                if (pi < 1 || pi > N || sh.par[pi] != u) continue;
+                const int x = sh.tok[i];
+                float zt = 0.0f, zq = 0.0f;
+                if (x >= 0 && x < V) {
+                    zt = DT::load1(tb + int64_t(pi) * a.ld_t * a.elem, x);
+                    zq = DT::load1(qb + int64_t(pi) * a.ld_q * a.elem, x);
+                }
+                sh.czt[i] = zt;
+                sh.czq[i] = zq;
+            }
+        }
         while (c >= 0) {
             if (t == 0) {
                 const int x = sh.tok[c];
@@ -766,7 +876,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
                 }
                 if (a.accept_prob != nullptr && g == 0)
                     a.accept_prob[int64_t(b) * N + c - 1] = static_cast<float>(acc_p);
-                const float uc = a.u_accept[int64_t(b) * N + c - 1];
+                const float uc = sh.ua[c];
                 sh.decision = (static_cast<double>(uc) < acc_p) ? 1 : 0;
             }
             __syncthreads();
@@ -797,6 +907,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
             if (t == 0 && depth < SV_MAX_POSITIONS) sh.path[depth] = nxt;
             u = nxt;
             ++depth;
+            kids_ready = true;
             __syncthreads();
             continue;
         }
