@@ -46,6 +46,8 @@ constexpr int kMW = kMB / kWave;          // its waves
 constexpr int kMU = 2;                    // tiles of a pass in flight per thread
 constexpr int kMNodes = SV_MAX_TREE_NODES + 1;
 constexpr int kSpec = (kMB / 64 - 2) / 2;  // statistics slots filled ahead of need (waves 2 and up, two per node)
+constexpr int kTabNodes = 64;              // trees of at most this many nodes ...
+constexpr int kTabParts = 2048;            // ... and chunk partials: every node's statistics at the start
 constexpr int kMaxG = 16;                 // blocks per tree at most
 constexpr int kSlot = 4;                  // doubles a block publishes per barrier
 constexpr int kSpinLimit = 1 << 20;       // polls of a barrier before it is given up (about 1 s)
@@ -95,6 +97,14 @@ struct MultiShared {
     int spec_node[kSpec];
     double spec_s[kSpec][2], spec_S[kSpec][2];
     int spec_hit;
+    // small trees: every row's chunk partials staged, then every node's rows
+    float tab_ps[kTabParts];
+    double tab_pS[kTabParts];
+    double tab_s[kTabNodes][2], tab_S[kTabNodes][2];
+    double tab_iA[kTabNodes], tab_iB[kTabNodes];    // 1 / S of each row
+    float tab_k0[kTabNodes];
+    double tab_acc[kTabNodes];            // a first child's acceptance probability at its parent
+    int tab_fl[kTabNodes];                // and the flags its test raises
     int flags, decision, token, broken;
     int tree, slice;                      // this block's role, from its start-order ticket
 };
@@ -473,11 +483,44 @@ __device__ __forceinline__ void spec_stats(const MultiArgs &a, MultiShared &sh, 
     }
 }
 
-// Node u's statistics from a slot filled ahead of need, if one holds it (the
-// same values load_stats would set); every slot is emptied.  Block barrier.
-__device__ __forceinline__ bool take_spec(MultiShared &sh, int u, bool target_only) {
+// Row j (node j / 2, row j % 2) of a small tree from its staged partials, by
+// one whole wave: the operations of row_combine in the same order.
+__device__ __forceinline__ void tab_combine(MultiShared &sh, int C1, int j) {
+    const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+    const float *ps = sh.tab_ps + j * C1;
+    const double *pS = sh.tab_pS + j * C1;
+    float smax = -INFINITY;
+    for (int c = lane; c < C1; c += kWave) smax = fmaxf(smax, ps[c]);
+    smax = wave_max(smax);
+    double S = 0.0;
+    for (int c = lane; c < C1; c += kWave) {
+        const float sc = ps[c];
+        if (sc != -INFINITY) S += pS[c] * pow2_shift_d(static_cast<double>(sc) - static_cast<double>(smax));
+    }
+    S = wave_sum_d(S);
+    if (lane == 0) {
+        sh.tab_s[j >> 1][j & 1] = static_cast<double>(smax);
+        sh.tab_S[j >> 1][j & 1] = S;
+    }
+}
+
+// Node u's statistics from the small tree's table, or from a slot filled
+// ahead of need if one holds it (the same values load_stats would set);
+// every slot is emptied.  Block barrier.
+__device__ __forceinline__ bool take_spec(MultiShared &sh, int u, bool target_only, bool tab) {
     if (threadIdx.x == 0) {
         int hit = 0;
+        if (tab) {
+            // the values set_stats forms, computed once per node at the start
+            sh.sA = sh.tab_s[u][0];
+            sh.SA = sh.tab_S[u][0];
+            sh.iA = sh.tab_iA[u];
+            sh.sB = target_only ? 0.0 : sh.tab_s[u][1];
+            sh.SB = target_only ? 1.0 : sh.tab_S[u][1];
+            sh.iB = target_only ? 1.0 : sh.tab_iB[u];
+            sh.k0 = target_only ? 0.0f : sh.tab_k0[u];
+            hit = 1;
+        }
         for (int k = 0; k < kSpec; ++k) {
             if (!hit && sh.spec_node[k] == u) {
                 set_stats(sh, sh.spec_s[k][0], sh.spec_S[k][0], sh.spec_s[k][1], sh.spec_S[k][1], target_only);
@@ -688,6 +731,33 @@ __device__ int pass_draw(const MultiArgs &a, MultiShared &sh, int &phase, const 
     return (tok >= 0) ? tok : glast;        // t rounded to the very top: the last positive weight
 }
 
+// Acceptance probability of child token x (logits zt, zq at its parent's
+// rows) while no residual has been formed at the parent: min(1, p~(x) / q(x))
+// in fp64 from the parent's row statistics; q(x) = 0 accepts iff p~(x) > 0.
+// fl gets SV_DATA_BAD_TOKEN or SV_DATA_ZERO_Q.
+__device__ __forceinline__ double first_child_acc(const MultiArgs &a, double sA, double SA, double sB, double SB,
+                                                  int x, float zt, float zq, int &fl) {
+    if (x < 0 || x >= a.V) {
+        fl |= SV_DATA_BAD_TOKEN;
+        return 0.0;
+    }
+    const double q = (zq == -INFINITY) ? 0.0 : exp2_d(static_cast<double>(zq) * a.c_d - sB) / SB;
+    double r;
+    if (a.space == 1) {
+        r = (zt == -INFINITY || zq == -INFINITY)
+                ? 0.0
+                : exp2_d(a.al * static_cast<double>(zt) + a.be * static_cast<double>(zq) - sA) / SA;
+    } else {
+        const double pt = (zt == -INFINITY) ? 0.0 : exp2_d(static_cast<double>(zt) * a.c_d - sA) / SA;
+        r = (1.0 - static_cast<double>(a.lam)) * pt + static_cast<double>(a.lam) * q;
+    }
+    if (q == 0.0) {
+        fl |= SV_DATA_ZERO_Q;
+        return (r > 0.0) ? 1.0 : 0.0;
+    }
+    return fmin(1.0, r / q);
+}
+
 // ---- the walk ----------------------------------------------------------------
 
 template <class DT>
@@ -711,7 +781,17 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
         sh.par[i] = (i > 0) ? a.parent[int64_t(b) * N + i - 1] : -1;
         sh.ua[i] = (i > 0) ? a.u_accept[int64_t(b) * N + i - 1] : 0.0f;
     }
-    {
+    // a small tree: every row's chunk partials, staged while the tree is read
+    const int n_parts = 2 * (N + 1) * a.C1;
+    const bool tab = (N + 1 <= kTabNodes) && (n_parts <= kTabParts);
+    if (tab) {
+        const Part *pp = a.part1 + int64_t(b) * n_parts;
+        for (int i = t; i < n_parts; i += kMB) {
+            const Part q = pp[i];
+            sh.tab_ps[i] = q.s;
+            sh.tab_pS[i] = q.S;
+        }
+    } else {
         // the root's statistics, combined while the tree is read
         int nodes[kSpec];
         for (int k = 0; k < kSpec; ++k) nodes[k] = (k == 0) ? 0 : -1;
@@ -736,22 +816,62 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
             sh.head[p] = i;
         }
     }
-    __syncthreads();
-
     const char *tb = a.tgt + int64_t(b) * (N + 1) * a.ld_t * a.elem;
     const char *qb = a.drf + int64_t(b) * (N + 1) * a.ld_q * a.elem;
+    if (tab) {
+        // every node's two logits at its parent's rows (node i by thread
+        // i + 64) and every node's two rows, by waves 1 and up while thread 0
+        // links
+        const int i = t - kWave;
+        float zt = 0.0f, zq = 0.0f;
+        const bool mine = i >= 1 && i <= N && sh.par[i] >= 0 && sh.par[i] <= N;
+        if (mine) {
+            const int x = sh.tok[i];
+            if (x >= 0 && x < V) {
+                zt = DT::load1(tb + int64_t(sh.par[i]) * a.ld_t * a.elem, x);
+                zq = DT::load1(qb + int64_t(sh.par[i]) * a.ld_q * a.elem, x);
+            }
+        }
+        const int wv = t / kWave;
+        if (wv >= 1)
+            for (int j = wv - 1; j < 2 * (N + 1); j += kMB / kWave - 1) tab_combine(sh, a.C1, j);
+        if (mine) {
+            sh.czt[i] = zt;
+            sh.czq[i] = zq;
+        }
+    }
+    __syncthreads();
+    if (tab) {
+        // every node's derived statistics (as set_stats forms them), and each
+        // first child's test at its parent, one thread per node
+        for (int v = t; v <= N; v += kMB) {
+            const double SAv = sh.tab_S[v][0], SBv = sh.tab_S[v][1];
+            sh.tab_iA[v] = 1.0 / SAv;
+            sh.tab_iB[v] = 1.0 / SBv;
+            sh.tab_k0[v] = static_cast<float>((sh.tab_s[v][0] - sh.tab_s[v][1]) + log2(SAv / SBv));
+            const int p = (v >= 1) ? sh.par[v] : -1;
+            if (p >= 0 && p < v && sh.head[p] == v) {
+                int fl = 0;
+                sh.tab_acc[v] = first_child_acc(a, sh.tab_s[p][0], sh.tab_S[p][0], sh.tab_s[p][1], sh.tab_S[p][1],
+                                                sh.tok[v], sh.czt[v], sh.czq[v], fl);
+                sh.tab_fl[v] = fl;
+            }
+        }
+        __syncthreads();
+    }
+
     float *buf0 = a.buf + int64_t(b) * 2 * a.Vp;
     float *buf1 = buf0 + a.Vp;
     const double us = static_cast<double>(a.u_sample[b]);
     int u = 0, depth = 0, tok = -1;
     bool done = false;
-    bool kids_ready = false;            // the children's logits of node u are in sh.czt / sh.czq
+    bool kids_ready = tab;              // the children's logits of node u are in sh.czt / sh.czq
     while (!done) {
         const char *rt = tb + int64_t(u) * a.ld_t * a.elem;
         const char *rq = qb + int64_t(u) * a.ld_q * a.elem;
         const int first = (depth < a.Dmax) ? sh.head[u] : -1;
         // the node's statistics, when combined ahead of need
-        const bool have = take_spec(sh, u, first < 0);
+        const bool have = take_spec(sh, u, first < 0, tab);
         if (first < 0) {
             // bonus: the target's own softmax(z/T) at this node (in logit
             // space the precomputed row A is the mixture: a pass of its own)
@@ -791,7 +911,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
         } else if (!have) {
             load_stats(a, sh, b, u, false);
         }
-        __syncthreads();
+        if (!kids_ready || !have) __syncthreads();       // (uniform) shared values were written
         if (!(sh.SA > 0.0) || !isfinite(sh.SA) || !(sh.SB > 0.0) || !isfinite(sh.SB) ||
             !isfinite(sh.sA) || !isfinite(sh.sB)) {
             if (t == 0) sh.flags |= SV_DATA_BAD_ROW;
@@ -806,21 +926,25 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
         bool drawn = false;
         {
             // the first children's statistics, combined while thread 0
-            // tests the first child (the test's barrier publishes them)
-            int nodes[kSpec];
-            int cc = first;
-            for (int k = 0; k < kSpec; ++k) {
-                nodes[k] = cc;
-                cc = (cc >= 0) ? sh.next[cc] : -1;
+            // tests the first child (the test's barrier publishes them);
+            // a small tree has every node's in its table already
+            if (!tab) {
+                int nodes[kSpec];
+                int cc = first;
+                for (int k = 0; k < kSpec; ++k) {
+                    nodes[k] = cc;
+                    cc = (cc >= 0) ? sh.next[cc] : -1;
+                }
+                spec_stats(a, sh, b, nodes);
             }
-            spec_stats(a, sh, b, nodes);
             // and the grandchildren's two logits at their parents' rows, for
             // the tests at whichever child is accepted; node i is taken by
             // thread i + 64, so that wave 0 (thread 0 tests) loads nothing
-            // for trees of fewer than kMB - 64 nodes
+            // for trees of fewer than kMB - 64 nodes (a small tree has
+            // every node's already)
             constexpr int kPre2 = (kMNodes + kWave + kMB - 1) / kMB;
 #pragma unroll
-            for (int k = 0; k < kPre2; ++k) {
+            for (int k = 0; k < (tab ? 0 : kPre2); ++k) {
                 const int i = t - kWave + k * kMB;
                 if (i < 1 || i > N) continue;
                 const int pi = sh.par[i];
@@ -839,34 +963,29 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
             if (t == 0) {
                 const int x = sh.tok[c];
                 double acc_p = 0.0;
-                if (x < 0 || x >= V) {
+                if (cur == nullptr) {
+                    // fp64 from the gathered logits (a small tree's first
+                    // children: computed with the tree's table)
+                    int fl = 0;
+                    if (tab && c == first) {
+                        acc_p = sh.tab_acc[c];
+                        fl = sh.tab_fl[c];
+                    } else {
+                        acc_p = first_child_acc(a, sh.sA, sh.SA, sh.sB, sh.SB, x, sh.czt[c], sh.czq[c], fl);
+                    }
+                    sh.flags |= fl;
+                } else if (x < 0 || x >= V) {
                     sh.flags |= SV_DATA_BAD_TOKEN;
                 } else {
+                    // the stored residual at x, formed again with the residual
+                    // pass's own operations from the logits, q(x) and the masses
                     const float zt = sh.czt[c];
                     const float zq = sh.czq[c];
-                    double q, r;
-                    if (cur == nullptr) {
-                        // fp64 from the gathered logits
-                        q = (zq == -INFINITY) ? 0.0
-                                              : exp2_d(static_cast<double>(zq) * a.c_d - sh.sB) / sh.SB;
-                        if (a.space == 1) {
-                            r = (zt == -INFINITY || zq == -INFINITY)
-                                    ? 0.0
-                                    : exp2_d(a.al * static_cast<double>(zt) + a.be * static_cast<double>(zq) - sh.sA) / sh.SA;
-                        } else {
-                            const double pt = (zt == -INFINITY) ? 0.0
-                                                                : exp2_d(static_cast<double>(zt) * a.c_d - sh.sA) / sh.SA;
-                            r = (1.0 - static_cast<double>(a.lam)) * pt + static_cast<double>(a.lam) * q;
-                        }
-                    } else {
-                        // the stored residual at x, formed again with the residual
-                        // pass's own operations from the logits, q(x) and the masses
-                        double pm;
-                        m_probs<DT>(a, sh, zt, zq, pm, q);
-                        r = static_cast<double>(first_residual(a, sh, zt, zq)) / sh.zs[1];
-                        for (int j = 2; j <= nrej; ++j)
-                            r = static_cast<double>(static_cast<float>(fmax(0.0, r - q))) / sh.zs[j];
-                    }
+                    double pm, q;
+                    m_probs<DT>(a, sh, zt, zq, pm, q);
+                    double r = static_cast<double>(first_residual(a, sh, zt, zq)) / sh.zs[1];
+                    for (int j = 2; j <= nrej; ++j)
+                        r = static_cast<double>(static_cast<float>(fmax(0.0, r - q))) / sh.zs[j];
                     if (q == 0.0) {
                         sh.flags |= SV_DATA_ZERO_Q;
                         acc_p = (r > 0.0) ? 1.0 : 0.0;
@@ -908,8 +1027,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
             u = nxt;
             ++depth;
             kids_ready = true;
-            __syncthreads();
-            continue;
+            continue;               // the next node's first barrier follows its statistics
         }
         // every child rejected: draw from the last residual
         tok = pass_draw<DT, kDrawBuffer>(a, sh, phase, rt, rq, cur, us);
