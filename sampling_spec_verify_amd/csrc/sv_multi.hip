@@ -483,24 +483,49 @@ __device__ __forceinline__ void spec_stats(const MultiArgs &a, MultiShared &sh, 
     }
 }
 
-// Row j (node j / 2, row j % 2) of a small tree from its staged partials, by
-// one whole wave: the operations of row_combine in the same order.
-__device__ __forceinline__ void tab_combine(MultiShared &sh, int C1, int j) {
-    const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
-    const float *ps = sh.tab_ps + j * C1;
-    const double *pS = sh.tab_pS + j * C1;
-    float smax = -INFINITY;
-    for (int c = lane; c < C1; c += kWave) smax = fmaxf(smax, ps[c]);
-    smax = wave_max(smax);
-    double S = 0.0;
-    for (int c = lane; c < C1; c += kWave) {
-        const float sc = ps[c];
-        if (sc != -INFINITY) S += pS[c] * pow2_shift_d(static_cast<double>(sc) - static_cast<double>(smax));
-    }
-    S = wave_sum_d(S);
-    if (lane == 0) {
-        sh.tab_s[j >> 1][j & 1] = static_cast<double>(smax);
-        sh.tab_S[j >> 1][j & 1] = S;
+// Maximum and sum over the 8 lanes of an aligned group (lane moves xor 1,
+// xor 2, then the mirror within 8 lanes); every lane of the group gets the
+// same result.  The maximum orders floats by integer keys, as wave_max.
+__device__ __forceinline__ float octet_max(float v) {
+    const int b = i_of(v);
+    int k = b ^ ((b >> 31) & 0x7fffffff);
+    k = max(k, dpp<kDppXor1>(k));
+    k = max(k, dpp<kDppXor2>(k));
+    k = max(k, dpp<kDppHalfMirror>(k));
+    return f_of(k ^ ((k >> 31) & 0x7fffffff));
+}
+__device__ __forceinline__ double octet_sum_d(double v) {
+    v += dpp_d<kDppXor1>(v);
+    v += dpp_d<kDppXor2>(v);
+    v += dpp_d<kDppHalfMirror>(v);
+    return v;
+}
+
+// Every row of a small tree from its staged partials: row j (node j / 2, row
+// j % 2) by the 8 lanes of group j of the block, each lane taking chunks
+// l, l + 8, ... in order (the row_combine operations on the same values, in
+// a fixed order of its own).  Every thread calls it.
+__device__ __forceinline__ void tab_combine_all(MultiShared &sh, int C1, int rows) {
+    const int t = static_cast<int>(threadIdx.x);
+    const int l8 = t & 7;
+    for (int j0 = 0; j0 < rows; j0 += kMB / 8) {
+        const int j = j0 + t / 8;
+        const bool on = j < rows;
+        const float *ps = sh.tab_ps + (on ? j : 0) * C1;
+        const double *pS = sh.tab_pS + (on ? j : 0) * C1;
+        float smax = -INFINITY;
+        for (int c = l8; c < C1; c += 8) smax = fmaxf(smax, ps[c]);
+        smax = octet_max(smax);
+        double S = 0.0;
+        for (int c = l8; c < C1; c += 8) {
+            const float sc = ps[c];
+            if (sc != -INFINITY) S += pS[c] * pow2_shift_d(static_cast<double>(sc) - static_cast<double>(smax));
+        }
+        S = octet_sum_d(S);
+        if (on && l8 == 0) {
+            sh.tab_s[j >> 1][j & 1] = static_cast<double>(smax);
+            sh.tab_S[j >> 1][j & 1] = S;
+        }
     }
 }
 
@@ -820,8 +845,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
     const char *qb = a.drf + int64_t(b) * (N + 1) * a.ld_q * a.elem;
     if (tab) {
         // every node's two logits at its parent's rows (node i by thread
-        // i + 64) and every node's two rows, by waves 1 and up while thread 0
-        // links
+        // i + 64), and every node's two rows
         const int i = t - kWave;
         float zt = 0.0f, zq = 0.0f;
         const bool mine = i >= 1 && i <= N && sh.par[i] >= 0 && sh.par[i] <= N;
@@ -832,9 +856,7 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
                 zq = DT::load1(qb + int64_t(sh.par[i]) * a.ld_q * a.elem, x);
             }
         }
-        const int wv = t / kWave;
-        if (wv >= 1)
-            for (int j = wv - 1; j < 2 * (N + 1); j += kMB / kWave - 1) tab_combine(sh, a.C1, j);
+        tab_combine_all(sh, a.C1, 2 * (N + 1));
         if (mine) {
             sh.czt[i] = zt;
             sh.czq[i] = zq;
