@@ -98,6 +98,8 @@ typedef enum { SV_MIX_PROB = 0, SV_MIX_LOGIT = 1 } sv_mix_space;
  * accept larger vocabularies. */
 #define SV_MAX_VOCAB_BF16 2097152
 #define SV_MAX_VOCAB_F32 1048576
+/* Largest number of cooperating blocks per tree of the multi-branch call. */
+#define SV_MAX_BLOCKS_PER_TREE 32
 
 /* Bits of the device-side status word. */
 #define SV_DATA_BAD_TOKEN   0x01 /* a drafted or node token outside [0, V): that draft is rejected */
@@ -457,7 +459,8 @@ sv_status sv_tree_verify_path_ex(const void *target_logits, int64_t ld_t,
  *  workspace: sv_tree_multi_workspace_bytes(B, N, V) bytes (two fp32
  *  residual rows per request).
  *
- * Each tree is walked by G cooperating 512-thread blocks (G up to 16; by
+ * Each tree is walked by G cooperating 512-thread blocks (G up to
+ * SV_MAX_BLOCKS_PER_TREE; by
  * default as many as let all B * G blocks fit the GPU at once), each owning a
  * slice of the vocabulary: every sum over the vocabulary is a pass of the
  * blocks over their slices, combined at a barrier of the tree's blocks.  The
@@ -486,9 +489,9 @@ sv_status sv_tree_verify_multi(const void *target_logits, int64_t ld_t,
                                hipStream_t stream);
 
 /* sv_tree_verify_multi with the number of blocks per tree chosen by the
- * caller: blocks_per_tree 0 is the automatic choice above, 1..16 asks for that
- * many (fewer when the row has fewer 512-vector tiles than that); outside
- * 0..16 returns SV_EINVAL.  Outputs follow the same rule for every choice; the
+ * caller: blocks_per_tree 0 is the automatic choice above, 1 ..
+ * SV_MAX_BLOCKS_PER_TREE asks for that many (fewer when the row has fewer
+ * 512-vector tiles than that); outside that range (and 0) returns SV_EINVAL.  Outputs follow the same rule for every choice; the
  * acceptance values may differ in the last bits, since the per-slice sums are
  * combined in another grouping. */
 sv_status sv_tree_verify_multi_ex(const void *target_logits, int64_t ld_t,

@@ -18,8 +18,9 @@
 // token is drawn from the last residual; a node without children (or at depth
 // Dmax) emits the bonus token from the target's own softmax(z/T).
 //
-// G cooperating 512-thread blocks walk each tree (G up to 16, as many as fit
-// the GPU with the other trees' blocks), block g owning vocabulary slice g.
+// G cooperating 512-thread blocks walk each tree (G up to
+// SV_MAX_BLOCKS_PER_TREE, as many as fit the GPU with the other trees'
+// blocks), block g owning vocabulary slice g.
 // Every block takes every decision of the walk from the same combined values;
 // each step that needs a sum over the vocabulary is a pass of every block over
 // its slice of the node's two rows, combined at a barrier of the tree's
@@ -48,7 +49,7 @@ constexpr int kMNodes = SV_MAX_TREE_NODES + 1;
 constexpr int kSpec = (kMB / 64 - 2) / 2;  // statistics slots filled ahead of need (waves 2 and up, two per node)
 constexpr int kTabNodes = 64;              // trees of at most this many nodes ...
 constexpr int kTabParts = 2048;            // ... and chunk partials: every node's statistics at the start
-constexpr int kMaxG = 16;                 // blocks per tree at most
+constexpr int kMaxG = SV_MAX_BLOCKS_PER_TREE;   // blocks per tree at most
 constexpr int kSlot = 4;                  // doubles a block publishes per barrier
 constexpr int kSpinLimit = 1 << 20;       // polls of a barrier before it is given up (about 1 s)
 

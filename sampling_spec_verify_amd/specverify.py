@@ -27,6 +27,7 @@ SV_MAX_POSITIONS = 64
 SV_MAX_TREE_NODES = 1024
 SV_MAX_VOCAB_BF16 = 1 << 21
 SV_MAX_VOCAB_F32 = 1 << 20
+SV_MAX_BLOCKS_PER_TREE = 32
 DATA_FLAGS = {
     0x01: "BAD_TOKEN", 0x02: "BAD_ROW", 0x04: "ZERO_Q", 0x08: "BAD_LENGTH",
     0x10: "BAD_TREE", 0x20: "FALLBACK", 0x40: "DEPTH", 0x80: "SYNC",

@@ -302,12 +302,12 @@ def test_multi_argument_errors(kw, code):
     if kw.get("wsb") == "short":
         kw = dict(wsb=sv.lib().sv_tree_multi_workspace_bytes(2, 5, 128) - 16)
     assert multi_call(**kw) == code
-    for g in (0, 1, 16):
+    for g in (0, 1, sv.SV_MAX_BLOCKS_PER_TREE):
         assert multi_call(ex=g, **kw) == code
 
 
-@pytest.mark.parametrize("g", [-1, 17, 1 << 20])
-def test_multi_ex_rejects_block_counts_outside_0_to_16(g):
+@pytest.mark.parametrize("g", [-1, sv.SV_MAX_BLOCKS_PER_TREE + 1, 1 << 20])
+def test_multi_ex_rejects_block_counts_outside_the_range(g):
     assert multi_call(ex=g) == sv.SV_EINVAL
     assert multi_call(ex=g, B=0, t=None, acc=None) == sv.SV_EINVAL
 
@@ -336,6 +336,7 @@ def test_header_constants_match_the_binding():
     assert int(re.search(r"#define SV_MAX_TREE_NODES\s+(\d+)", text).group(1)) == sv.SV_MAX_TREE_NODES
     assert int(re.search(r"#define SV_MAX_VOCAB_BF16\s+(\d+)", text).group(1)) == sv.SV_MAX_VOCAB_BF16
     assert int(re.search(r"#define SV_MAX_VOCAB_F32\s+(\d+)", text).group(1)) == sv.SV_MAX_VOCAB_F32
+    assert int(re.search(r"#define SV_MAX_BLOCKS_PER_TREE\s+(\d+)", text).group(1)) == sv.SV_MAX_BLOCKS_PER_TREE
 
 
 @pytest.mark.parametrize("fn", ["sv_chain_verify", "sv_chain_row_stats", "sv_chain_accept_resample",

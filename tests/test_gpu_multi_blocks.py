@@ -27,7 +27,7 @@ def _gpu():
     sv.lib()
 
 
-@pytest.mark.parametrize("blocks", [1, 2, 5, 16])
+@pytest.mark.parametrize("blocks", [1, 2, 5, 16, 32])
 def test_multi_every_block_count_matches_the_oracle(blocks):
     x = synth.config("c5")
     x.lam = 0.3
