@@ -590,15 +590,21 @@ __device__ __forceinline__ void store_res_vec(float *row, int gv, const float (&
 // child's token again from the same values and operations.  Each thread
 // loads all its vectors (logits and the previous residual) before any
 // arithmetic, forms each vector's weights in registers and stores them as
-// whole vectors (0 past V, inside the padded row).
+// whole vectors (0 past V, inside the padded row).  draw_next: the draw from
+// this residual follows (the node's last child was rejected), so the pass
+// also forms what the draw's first pass would from the stored values (the
+// slice's tile-scan total and last positive weight) and publishes them with
+// the mass at the same barrier: sh.gath[g] = {mass, total, last}.
 template <class DT>
 __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, int &phase, const char *row_t,
-                                const char *row_q, const float *in, double Zin, float *out) {
+                                const char *row_q, const float *in, double Zin, float *out, bool draw_next) {
     constexpr int VEC = DT::kVec;
     const int V = a.V;
     const int nvec = (V + VEC - 1) / VEC;
     const Slice sl = my_slice(a, sh, nvec);
     double tot = 0.0;
+    double carry = 0.0;
+    int last = -1;
     for (int g0 = sl.lo; g0 < sl.hi; g0 += kMB * kMU) {
         u32x4 dt[kMU], dq[kMU];
         float pin[kMU][VEC];
@@ -612,30 +618,49 @@ __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, int &phase,
 #pragma unroll
         for (int k = 0; k < kMU; ++k) {
             const int gv = g0 + k * kMB + static_cast<int>(threadIdx.x);
-            if (gv >= sl.hi) continue;
-            float ft[VEC], fq[VEC], w[VEC];
-            DT::unpack(dt[k], ft);
-            DT::unpack(dq[k], fq);
+            double vsum = 0.0;
+            if (gv < sl.hi) {
+                float ft[VEC], fq[VEC], w[VEC];
+                DT::unpack(dt[k], ft);
+                DT::unpack(dq[k], fq);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                float we;
-                if (in == nullptr) {
-                    we = first_residual(a, sh, ft[e], fq[e]);
-                } else {
-                    double pm, q;
-                    m_probs<DT>(a, sh, ft[e], fq[e], pm, q);
-                    we = static_cast<float>(fmax(0.0, static_cast<double>(pin[k][e]) / Zin - q));
+                for (int e = 0; e < VEC; ++e) {
+                    float we;
+                    if (in == nullptr) {
+                        we = first_residual(a, sh, ft[e], fq[e]);
+                    } else {
+                        double pm, q;
+                        m_probs<DT>(a, sh, ft[e], fq[e], pm, q);
+                        we = static_cast<float>(fmax(0.0, static_cast<double>(pin[k][e]) / Zin - q));
+                    }
+                    w[e] = (gv * VEC + e < V) ? we : 0.0f;
                 }
-                w[e] = (gv * VEC + e < V) ? we : 0.0f;
-            }
-            store_res_vec<VEC>(out, gv, w);
+                store_res_vec<VEC>(out, gv, w);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) tot += static_cast<double>(w[e]);
+                for (int e = 0; e < VEC; ++e) {
+                    tot += static_cast<double>(w[e]);
+                    // the draw's tile weight of the stored value (tile_weights)
+                    double wd = static_cast<double>(w[e]);
+                    if (!(wd > 0.0)) wd = 0.0;
+                    vsum += wd;
+                    if (wd > 0.0) last = gv * VEC + e;
+                }
+            }
+            // the draw's tiles: kMB vectors from the slice's start (uniform)
+            if (draw_next && g0 + k * kMB < sl.hi) carry = mblock_scan(vsum, carry, sh).total;
         }
     }
-    const double mine[kSlot] = {mblock_sum(tot, sh), 0.0, 0.0, 0.0};
-    publish_vals(a, sh, phase, mine, 1);
-    tree_barrier(a, sh, phase, 1);
+    const double msum = mblock_sum(tot, sh);
+    if (draw_next) {
+        last = mblock_max_i(last, sh);
+        const double mine[kSlot] = {msum, carry, static_cast<double>(last), 0.0};
+        publish_vals(a, sh, phase, mine, 3);
+        tree_barrier(a, sh, phase, 3);
+    } else {
+        const double mine[kSlot] = {msum, 0.0, 0.0, 0.0};
+        publish_vals(a, sh, phase, mine, 1);
+        tree_barrier(a, sh, phase, 1);
+    }
     double Z = 0.0;
     for (int g = 0; g < a.G; ++g) Z += sh.gath[g][0];
     return Z;
@@ -691,31 +716,36 @@ __device__ __forceinline__ double tile_weights(const MultiArgs &a, const MultiSh
 // publishes the token.
 template <class DT, int KIND>
 __device__ int pass_draw(const MultiArgs &a, MultiShared &sh, int &phase, const char *row_t,
-                         const char *row_q, const float *buf, double u) {
+                         const char *row_q, const float *buf, double u, bool given = false) {
     constexpr int VEC = DT::kVec;
     const int nvec = (a.V + VEC - 1) / VEC;
     const Slice sl = my_slice(a, sh, nvec);
     const int g = sh.slice;
-    double carry = 0.0;
-    int last = -1;
-    for (int g0 = sl.lo; g0 < sl.hi; g0 += kMB) {
-        double w[VEC];
-        const double sum = tile_weights<DT, KIND>(a, sh, row_t, row_q, buf, g0 + static_cast<int>(threadIdx.x),
-                                                  sl.hi, w, last);
-        carry = mblock_scan(sum, carry, sh).total;
+    // given: the residual pass that wrote buf published the slice totals and
+    // last positive weights already (sh.gath[i][1], sh.gath[i][2])
+    const int ic = given ? 1 : 0, il = given ? 2 : 1;
+    if (!given) {
+        double carry = 0.0;
+        int last = -1;
+        for (int g0 = sl.lo; g0 < sl.hi; g0 += kMB) {
+            double w[VEC];
+            const double sum = tile_weights<DT, KIND>(a, sh, row_t, row_q, buf,
+                                                      g0 + static_cast<int>(threadIdx.x), sl.hi, w, last);
+            carry = mblock_scan(sum, carry, sh).total;
+        }
+        last = mblock_max_i(last, sh);
+        const double mine[kSlot] = {carry, static_cast<double>(last), 0.0, 0.0};
+        publish_vals(a, sh, phase, mine, 2);
+        tree_barrier(a, sh, phase, 2);
     }
-    last = mblock_max_i(last, sh);
-    const double mine[kSlot] = {carry, static_cast<double>(last), 0.0, 0.0};
-    publish_vals(a, sh, phase, mine, 2);
-    tree_barrier(a, sh, phase, 2);
     double base = 0.0, W = 0.0;
     int glast = -1;
     for (int i = 0; i < a.G; ++i) {
         if (i == g) base = W;
-        W += sh.gath[i][0];
-        glast = max(glast, static_cast<int>(sh.gath[i][1]));
+        W += sh.gath[i][ic];
+        glast = max(glast, static_cast<int>(sh.gath[i][il]));
     }
-    const double mytot = sh.gath[g][0];
+    const double mytot = sh.gath[g][ic];
     if (!(W > 0.0) || !isfinite(W)) return -1;                 // the same in every block
     const double t = u * W;
     int mytok = -1;
@@ -746,7 +776,7 @@ __device__ int pass_draw(const MultiArgs &a, MultiShared &sh, int &phase, const 
             if (sh.token >= 0) break;
         }
         // t rounded past this slice's last prefix: its last positive weight
-        mytok = (sh.token >= 0) ? sh.token : static_cast<int>(sh.gath[g][1]);
+        mytok = (sh.token >= 0) ? sh.token : static_cast<int>(sh.gath[g][il]);
         __syncthreads();
     }
     const double mt[kSlot] = {static_cast<double>(mytok), 0.0, 0.0, 0.0};
@@ -1028,7 +1058,8 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
             }
             // rejected: the residual becomes the next child's target
             float *out = (cur == buf0) ? buf1 : buf0;
-            const double Zn = pass_residual<DT>(a, sh, phase, rt, rq, cur, Z, out);
+            const bool last_child = sh.next[c] < 0;
+            const double Zn = pass_residual<DT>(a, sh, phase, rt, rq, cur, Z, out, last_child);
             if (!(Zn > 0.0) || !isfinite(Zn)) {
                 // zero residual mass (rounding): draw from the current target
                 if (t == 0) sh.flags |= SV_DATA_FALLBACK;
@@ -1052,8 +1083,9 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
             kids_ready = true;
             continue;               // the next node's first barrier follows its statistics
         }
-        // every child rejected: draw from the last residual
-        tok = pass_draw<DT, kDrawBuffer>(a, sh, phase, rt, rq, cur, us);
+        // every child rejected: draw from the last residual, whose pass
+        // published the draw's slice totals
+        tok = pass_draw<DT, kDrawBuffer>(a, sh, phase, rt, rq, cur, us, true);
         if (tok < 0 && t == 0) sh.flags |= SV_DATA_BAD_ROW;
         done = true;
     }
