@@ -21,13 +21,17 @@
 // G cooperating 512-thread blocks walk each tree (G up to
 // SV_MAX_BLOCKS_PER_TREE, as many as fit the GPU with the other trees'
 // blocks), block g owning vocabulary slice g.
-// Every block takes every decision of the walk from the same combined values;
-// each step that needs a sum over the vocabulary is a pass of every block over
-// its slice of the node's two rows, combined at a barrier of the tree's
-// blocks: the row statistics (as the chain's, integer shifts, fp64 sums), the
+// Every block takes every decision of the walk from the same combined values.
+// The row statistics of every tree row come from a row-statistics launch
+// before the walk (chunk partials, combined by the walk in fp64): a small
+// tree combines all its rows, loads every node's logits at its parent's rows
+// and forms each first child's test when it starts; a larger one combines a
+// node's children's rows while the first child is tested.  Each step that
+// needs a sum over the vocabulary is a pass of every block over its slice of
+// the node's two rows, combined at a barrier of the tree's blocks: the
 // residual after a rejection (written to a ping-pong fp32 buffer of the
 // workspace with its fp64 mass), and an inverse CDF over slice totals, then
-// within the slice holding the draw.  Acceptance of the first child uses the
+// within the slice holding the draw.  Acceptance of a first child uses the
 // gathered logits in fp64; a later child forms the residual at its token again
 // with the residual pass's own operations (bitwise the stored value), so no
 // block reads another block's slice of the residual.
