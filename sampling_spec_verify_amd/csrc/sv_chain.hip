@@ -467,14 +467,18 @@ __device__ __forceinline__ double vec_sum(const float *w) {
 // row bad (1 / S is then NaN).
 // Row statistics from the chunk partials: the shift s and 1 / S, and also
 // off = s + log2 S, so that log2 p(v) = z c - off (NaN for a bad row).
-__device__ __forceinline__ void combine_row(const Part *p, int C1, float &s_out, float &inv_out,
-                                            float &off_out) {
+// first: p[lane] when lane < C1, loaded by the caller ahead of other loads.
+__device__ __forceinline__ void combine_row(const Part *p, int C1, const Part &first, float &s_out,
+                                            float &inv_out, float &off_out) {
     const int lane = threadIdx.x & (kWave - 1);
     float smax = -INFINITY;
-    for (int c = lane; c < C1; c += kWave) smax = fmaxf(smax, p[c].s);
+    if (lane < C1) smax = fmaxf(smax, first.s);
+    for (int c = lane + kWave; c < C1; c += kWave) smax = fmaxf(smax, p[c].s);
     smax = wave_max(smax);
     double S = 0.0;
-    for (int c = lane; c < C1; c += kWave) {
+    if (lane < C1 && first.s != -INFINITY)
+        S += first.S * pow2_shift_d(static_cast<double>(first.s) - static_cast<double>(smax));
+    for (int c = lane + kWave; c < C1; c += kWave) {
         const Part q = p[c];
         if (q.s != -INFINITY) S += q.S * pow2_shift_d(static_cast<double>(q.s) - static_cast<double>(smax));
     }
@@ -536,11 +540,16 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
     int b, i;
     if (!slot_position(a, job / groups, b, i)) return;     // uniform over the block
     const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    // the chunk's loads do not depend on the row statistics: issue them first
-    // so that they are in flight while waves 0 and 1 combine the partials
+    // waves 0 and 1 load their row's first 64 chunk partials first (they
+    // return first), then every wave its chunk of both rows, which does not
+    // depend on the row statistics: the partials are combined while the
+    // chunks are in flight
     const int c = grp * kWaves + wv;
     constexpr int VEC = DT::kVec;
     const int V = a.g.V;
+    const Part *parts = a.part1 + (int64_t(b) * a.g.Pcap + i) * 2 * a.C1;
+    Part first;
+    if (wv < 2 && lane < a.C1) first = parts[wv * a.C1 + lane];
     const int r = geo_row(a.g, b, i);
     const char *row_t = row_ptr(a.g, 0, b, r);
     const char *row_q = row_ptr(a.g, 1, b, r);
@@ -548,10 +557,9 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
     u32x4 dt[NV], dq[NV];
     load_chunk<DT, NV>(row_t, v0, lane, V, dt);
     load_chunk<DT, NV>(row_q, v0, lane, V, dq);
-    const Part *parts = a.part1 + (int64_t(b) * a.g.Pcap + i) * 2 * a.C1;
     if (wv < 2) {
         float s_, inv_, off_;
-        combine_row(parts + wv * a.C1, a.C1, s_, inv_, off_);
+        combine_row(parts + wv * a.C1, a.C1, first, s_, inv_, off_);
         if (lane == 0) {
             if (wv == 0) {
                 st_s = s_;
