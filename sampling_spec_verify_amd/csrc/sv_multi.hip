@@ -864,7 +864,24 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
         sh.broken = 0;
     }
     __syncthreads();
-    if (t == 0) {
+    if (tab) {
+        // children lists in node order, one node per thread: node i's first
+        // child and its next sibling are the first later nodes whose parent
+        // is i, and is i's parent (the lists the serial linking below forms)
+        for (int i = t; i <= N; i += kMB) {
+            const int p = sh.par[i];
+            const bool linked = i >= 1 && p >= 0 && p < i;
+            if (i >= 1 && !linked) atomicOr(&sh.flags, SV_DATA_BAD_TREE);   // never tested
+            int hd = -1, nx = -1;
+            for (int j = i + 1; j <= N; ++j) {
+                const int pj = sh.par[j];
+                if (hd < 0 && pj == i) hd = j;
+                if (linked && nx < 0 && pj == p) nx = j;
+            }
+            sh.head[i] = hd;
+            sh.next[i] = nx;
+        }
+    } else if (t == 0) {
         // children lists in node order: link from the last node down
         for (int i = N; i >= 1; --i) {
             const int p = sh.par[i];
