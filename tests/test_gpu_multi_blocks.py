@@ -7,7 +7,8 @@ tree's blocks on the GPU at once: a grid of more blocks than the compute units
 hold runs its trees in rounds.  These cases check that every choice of blocks
 per tree, that wide grid included, gives the oracle's walk ([SD] "Tree
 Speculation", the chain rule of [EAGLE] section 1 applied to what a rejection
-leaves) with the status word clear.
+leaves) with the status word clear, and that replays of one captured call on
+one workspace follow the oracle with new logits each time.
 """
 import numpy as np
 import pytest
@@ -15,7 +16,8 @@ import torch
 
 from sampling_spec_verify_amd import specverify as sv
 from sampling_spec_verify_amd import synth
-from tests.test_gpu_parity import _multi_case
+from tests.gpu_util import dev, dev_logits, to_host
+from tests.test_gpu_parity import _multi_case, compare_multi
 
 pytestmark = pytest.mark.gpu
 
@@ -60,3 +62,46 @@ def test_multi_block_counts_agree_with_each_other():
     tested = g1.accept_prob >= 0
     np.testing.assert_array_equal(tested, g16.accept_prob >= 0)
     assert float(np.abs(g1.accept_prob[tested] - g16.accept_prob[tested]).max(initial=0.0)) <= 1e-6
+
+
+def test_graph_replays_with_new_logits_between_replays():
+    """Replays of one captured call (the statistics launch and the walk) on one
+    workspace, with new logits written between replays, follow the oracle every
+    time: the statistics launch empties the walk's barrier slots, resets its
+    ticket counter and clears the status word on every replay."""
+    B, N, V = 6, 20, 20000
+    xs = [synth.make_random_tree(9800 + k, B, N, V, "bf16", sharp=1.0, sigma_q=2.0, lam=0.2)
+          for k in range(4)]
+    for x in xs[1:]:                         # one tree shape and one set of uniforms
+        x.parent[:] = xs[0].parent
+        x.node_token[:] = xs[0].node_token
+        x.u_node[:] = xs[0].u_node
+        x.u_sample[:] = xs[0].u_sample
+    x0 = xs[0]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        t = dev_logits(x0.target, "bf16")
+        d = dev_logits(x0.draft, "bf16")
+        par, tok, un, us = dev(x0.parent), dev(x0.node_token), dev(x0.u_node), dev(x0.u_sample)
+        ws = torch.empty(int(sv.lib().sv_tree_multi_workspace_bytes(B, N, V)), dtype=torch.uint8,
+                         device="cuda:0")
+        sv.tree_verify_multi(t, d, par, tok, un, us, x0.Dmax, x0.lam, x0.temperature, "prob",
+                             stream=s, workspace=ws)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        out = sv.tree_verify_multi(t, d, par, tok, un, us, x0.Dmax, x0.lam, x0.temperature, "prob",
+                                   stream=s, workspace=ws)
+    for rep in range(8):
+        x = xs[rep % 4]
+        with torch.cuda.stream(s):
+            t.copy_(dev_logits(x.target, "bf16"))
+            d.copy_(dev_logits(x.draft, "bf16"))
+            for o in out:
+                o.fill_(-7)
+            g.replay()
+        s.synchronize()
+        print(f"[multi blocks] graph replay {rep}", flush=True)
+        h = to_host(out)
+        assert int(h.status[0]) == 0, sv.decode_flags(int(h.status[0]))
+        compare_multi(x, h, x0.Dmax, label=f"multi graph replay {rep}")

@@ -588,7 +588,13 @@ def _multi_case(x, Dmax=None, space="prob", label="multi", blocks_per_tree=0):
     g = sv.tree_verify_multi(dev_logits(x.target, x.dtype), dev_logits(x.draft, x.dtype),
                              dev(x.parent), dev(x.node_token), dev(x.u_node), dev(x.u_sample), Dmax,
                              x.lam, x.temperature, space, blocks_per_tree=blocks_per_tree)
-    g = to_host(g)
+    return compare_multi(x, to_host(g), Dmax, space, label)
+
+
+def compare_multi(x, g, Dmax, space="prob", label="multi"):
+    """Host outputs g of a multi-branch call against the oracle: bitwise equal
+    outside requests whose draws the oracle flags, acceptance values within
+    ACCEPT_PROB_TOL; the flagged count bounded."""
     acc, out, nodes, ap, flag, det = oracle.tree_multi(
         x.widened(x.target), x.widened(x.draft), x.parent, x.node_token, x.u_node, x.u_sample,
         x.lam, x.temperature, Dmax, space)
