@@ -149,7 +149,9 @@ __device__ __forceinline__ const char *row_ptr(const Geo &g, int tensor, int b, 
 // ---------------------------------------------------------------------------
 
 // One job: wave-chunk c of one drafted row, reduced by one wavefront.
-template <class DT, int NV>
+// LEAF (tree rows, one per node): the draft row of a node that no node names
+// as its parent is never read, so its wave stores an empty partial instead.
+template <class DT, int NV, bool LEAF = false>
 __device__ __forceinline__ void row_chunk_stats(const ChainArgs &a, unsigned job) {
     const unsigned C1 = static_cast<unsigned>(a.C1);
     const int c = static_cast<int>(job % C1);
@@ -157,6 +159,26 @@ __device__ __forceinline__ void row_chunk_stats(const ChainArgs &a, unsigned job
     const int tensor = static_cast<int>(rest & 1u);
     int b, i;
     if (!slot_position(a, static_cast<int>(rest >> 1), b, i)) return;
+    if (LEAF && tensor == 1) {
+        const int32_t *par = a.leaf_par + int64_t(b) * a.leaf_N;
+        const int lane0 = threadIdx.x & (kWave - 1);
+        bool has = false;
+        for (int j0 = 0; j0 < a.leaf_N; j0 += kWave) {
+            const int j = j0 + lane0;
+            const int pj = (j < a.leaf_N) ? par[j] : -1;
+            has = has || (__ballot(pj == i) != 0ull);
+        }
+        if (!has) {
+            if (lane0 == 0) {
+                Part p;
+                p.s = -INFINITY;
+                p.z = 0.0f;
+                p.S = 0.0;
+                a.part1[(int64_t(b) * a.g.Pcap + i) * 2 * a.C1 + a.C1 + c] = p;
+            }
+            return;
+        }
+    }
     const char *row = row_ptr(a.g, tensor, b, geo_row(a.g, b, i));
     // the wave whose chunk holds the drafted token also gathers its logit
     // no drafted tokens (the acceptance-rate call): nothing to gather
@@ -249,12 +271,12 @@ constexpr int kStatsWaves = 2;
 // grids keep one priority.
 constexpr int kPrioJobs = 2 * 256 * 28;
 
-template <class DT, int NV, bool PRIO>
+template <class DT, int NV, bool PRIO, bool LEAF = false>
 __global__ __launch_bounds__(kStatsWaves * kWave) void k_row_stats(ChainArgs a, int n_jobs) {
     if (PRIO) __builtin_amdgcn_s_setprio(3);
     const int job = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kStatsWaves +
                                                    static_cast<int>(threadIdx.x) / kWave);
-    if (job < n_jobs) row_chunk_stats<DT, NV>(a, static_cast<unsigned>(job));
+    if (job < n_jobs) row_chunk_stats<DT, NV, LEAF>(a, static_cast<unsigned>(job));
     // cleared last: a store ahead of the job's reads would keep the compiler
     // from issuing them as scalar loads
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
@@ -1313,6 +1335,8 @@ ChainArgs make_args(const ChainReq &q, int vec, int nv) {
     a.zero_word = nullptr;
     a.zero_f = q.zero_f;
     a.zero_f_n = q.zero_f_n;
+    a.leaf_par = nullptr;
+    a.leaf_N = 0;
     a.alpha_rec = nullptr;
     a.tag = 0;
     a.space = q.space;
@@ -1390,6 +1414,10 @@ sv_status rows_stats_typed(ChainArgs a, hipStream_t stream, int nv) {
     if (a.space == 1) {
         if (nv == 4) hipLaunchKernelGGL((k_row_stats_logit<DT, 4>), grid, block, 0, stream, a, jobs);
         else hipLaunchKernelGGL((k_row_stats_logit<DT, 2>), grid, block, 0, stream, a, jobs);
+    } else if (a.leaf_par != nullptr) {
+        if (nv == 8) hipLaunchKernelGGL((k_row_stats<DT, 8, false, true>), grid, block, 0, stream, a, jobs);
+        else if (nv == 4) hipLaunchKernelGGL((k_row_stats<DT, 4, false, true>), grid, block, 0, stream, a, jobs);
+        else hipLaunchKernelGGL((k_row_stats<DT, 2, false, true>), grid, block, 0, stream, a, jobs);
     } else if (nv == 8 && jobs >= kPrioJobs) {
         hipLaunchKernelGGL((k_row_stats<DT, 8, true>), grid, block, 0, stream, a, jobs);
     } else if (nv == 8) {
@@ -1525,7 +1553,7 @@ int rows_stats_chunks(int B, int R, int V, sv_dtype dtype, int space) {
 sv_status rows_stats(const void *tgt, int64_t ld_t, const void *drf, int64_t ld_q, sv_dtype dtype, int B, int R,
                      int V, float lam, float T, int space, Part *part1, int *count, int32_t *status,
                      hipStream_t stream, unsigned long long *fill, int64_t fill_n, unsigned long long fill_val,
-                     unsigned *zero_word) {
+                     unsigned *zero_word, const int32_t *leaf_par) {
     const int eb = elem_bytes(dtype);
     const int vec = 16 / eb;
     const int nv = (space == 1) ? (int64_t(B) * R * c1_for(V, 4, vec) < 2048 ? 2 : 4)
@@ -1563,6 +1591,8 @@ sv_status rows_stats(const void *tgt, int64_t ld_t, const void *drf, int64_t ld_
     a.fill_n = fill_n;
     a.fill_val = fill_val;
     a.zero_word = zero_word;
+    a.leaf_par = leaf_par;
+    a.leaf_N = R - 1;
     return dtype == SV_BF16 ? rows_stats_typed<Bf16>(a, stream, nv) : rows_stats_typed<F32>(a, stream, nv);
 }
 

@@ -100,6 +100,10 @@ struct ChainArgs {
     unsigned *zero_word;
     float *zero_f;
     int64_t zero_f_n;
+    // tree rows (one position per node): the parent array [B, leaf_N] whose
+    // childless nodes' draft rows are skipped; NULL: every row
+    const int32_t *leaf_par;
+    int leaf_N;
     float *alpha;                 // [B, P] out: expected acceptance of each drafted position
 };
 
@@ -273,12 +277,16 @@ inline uint32_t next_call_tag() {
 // [B, R, 2, C1] into part1, C1 = rows_stats_chunks(...).  Space 1: slot 0 of
 // a row holds the logit-space mixture's statistics, as in the chain.  count
 // (B ints) is cleared, status cleared, fill[0 .. fill_n) set to fill_val and
-// *zero_word to 0 (when given).  Host code; enqueued on stream.
+// *zero_word to 0 (when given).  leaf_par: the [B, R - 1] parent array of
+// trees whose row r belongs to node r; the draft row of a node without
+// children is then skipped (its partials read as an empty row).  Host code;
+// enqueued on stream.
 int rows_stats_chunks(int B, int R, int V, sv_dtype dtype, int space);
 sv_status rows_stats(const void *tgt, int64_t ld_t, const void *drf, int64_t ld_q, sv_dtype dtype, int B, int R,
                      int V, float lam, float T, int space, Part *part1, int *count, int32_t *status,
                      hipStream_t stream, unsigned long long *fill = nullptr, int64_t fill_n = 0,
-                     unsigned long long fill_val = 0, unsigned *zero_word = nullptr);
+                     unsigned long long fill_val = 0, unsigned *zero_word = nullptr,
+                     const int32_t *leaf_par = nullptr);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -22,8 +22,9 @@
 // SV_MAX_BLOCKS_PER_TREE, as many as fit the GPU with the other trees'
 // blocks), block g owning vocabulary slice g.
 // Every block takes every decision of the walk from the same combined values.
-// The row statistics of every tree row come from a row-statistics launch
-// before the walk (chunk partials, combined by the walk in fp64): a small
+// The row statistics of every tree row (but the draft rows of childless
+// nodes, which no test reads) come from a row-statistics launch before the
+// walk (chunk partials, combined by the walk in fp64): a small
 // tree combines all its rows, loads every node's logits at its parent's rows
 // and forms each first child's test when it starts; a larger one combines a
 // node's children's rows while the first child is tested.  Each step that
@@ -1246,7 +1247,7 @@ sv_status verify_multi(const void *target_logits, int64_t ld_t, const void *draf
     st = rows_stats(target_logits, ld_t, draft_logits, ld_q, dtype, B, N + 1, V, lambda, temperature, a.space,
                     reinterpret_cast<Part *>(ws + multi_layout_part(B, V)),
                     reinterpret_cast<int *>(ws + multi_layout_count(B, N, V)), a.status, stream, a.pub, n_slots,
-                    kEmpty, a.ticket);
+                    kEmpty, a.ticket, parent);
     if (st != SV_OK) return st;
     const dim3 grid(static_cast<unsigned>(int64_t(B) * a.G));
     if (dtype == SV_BF16) {
