@@ -673,16 +673,17 @@ __device__ double pass_residual(const MultiArgs &a, MultiShared &sh, int &phase,
 
 enum MultiDraw { kDrawBonus = 0, kDrawBuffer = 1, kDrawMixture = 2 };
 
-// Weight of element v for a draw: the bonus 2^(z_t c - s) (unnormalised),
-// a stored residual, or p~ itself.
+// Weight of an element for a draw: the bonus 2^(z_t c - s) (unnormalised),
+// or p~ itself (a stored residual is read as whole vectors by tile_weights).
 template <class DT, int KIND>
-__device__ __forceinline__ double draw_weight(const MultiArgs &a, const MultiShared &sh, float zt,
-                                              float zq, const float *buf, int v) {
-    if (KIND == kDrawBonus) return static_cast<double>(m_pow2(zt, a.c_hi, a.c_lo, static_cast<float>(sh.sA)));
-    if (KIND == kDrawBuffer) return static_cast<double>(buf[v]);
-    double pm, q;
-    m_probs<DT>(a, sh, zt, zq, pm, q);
-    return pm;
+__device__ __forceinline__ double draw_weight(const MultiArgs &a, const MultiShared &sh, float zt, float zq) {
+    if constexpr (KIND == kDrawBonus) {
+        return static_cast<double>(m_pow2(zt, a.c_hi, a.c_lo, static_cast<float>(sh.sA)));
+    } else {
+        double pm, q;
+        m_probs<DT>(a, sh, zt, zq, pm, q);
+        return pm;
+    }
 }
 
 // Weights of vector gv of the slice ending at vector hi (0 past it), their
@@ -702,8 +703,9 @@ __device__ __forceinline__ double tile_weights(const MultiArgs &a, const MultiSh
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
         const int v = gv * VEC + e;
-        const double we = (KIND == kDrawBuffer) ? static_cast<double>(fb[e])
-                                                : draw_weight<DT, KIND>(a, sh, ft[e], fq[e], buf, v);
+        double we;
+        if constexpr (KIND == kDrawBuffer) we = static_cast<double>(fb[e]);
+        else we = draw_weight<DT, KIND>(a, sh, ft[e], fq[e]);
         w[e] = (gv < hi && v < V) ? we : 0.0;
         if (!(w[e] > 0.0)) w[e] = 0.0;
         sum += w[e];
