@@ -457,14 +457,17 @@ sv_status sv_tree_verify_path_ex(const void *target_logits, int64_t ld_t,
  *  parent is never tested; BAD_TOKEN: rejected; ZERO_Q; FALLBACK: a residual
  *  had zero mass and its current target was drawn from; BAD_ROW).
  *  workspace: sv_tree_multi_workspace_bytes(B, N, V) bytes (two fp32
- *  residual rows per request).
+ *  residual rows per request, the barrier slots, and the chunk partials of
+ *  every tree row).
  *
+ * Launches: a row-statistics launch over every row of every tree (skipping
+ * the draft rows of childless nodes in probability space), then the walk.
  * Each tree is walked by G cooperating 512-thread blocks (G up to
- * SV_MAX_BLOCKS_PER_TREE; by
- * default as many as let all B * G blocks fit the GPU at once), each owning a
- * slice of the vocabulary: every sum over the vocabulary is a pass of the
- * blocks over their slices, combined at a barrier of the tree's blocks.  The
- * call is bound by that chain of passes rather than by HBM bandwidth.
+ * SV_MAX_BLOCKS_PER_TREE; by default as many as let all B * G blocks fit the
+ * GPU at once), each owning a slice of the vocabulary: every sum over the
+ * vocabulary is a pass of the blocks over their slices, combined at a barrier
+ * of the tree's blocks.  The walk is bound by that chain of passes rather than
+ * by HBM bandwidth.
  *
  * Residency contract.  A tree's blocks wait for one another.  Each block takes
  * its tree and slice from a start-order ticket, so a block only ever waits for
