@@ -460,8 +460,8 @@ sv_status sv_tree_verify_path_ex(const void *target_logits, int64_t ld_t,
  *  residual rows per request, the barrier slots, and the chunk partials of
  *  every tree row).
  *
- * Launches: a row-statistics launch over every row of every tree (skipping
- * the draft rows of childless nodes in probability space), then the walk.
+ * Launches: a row-statistics launch over the rows of every tree (all but
+ * those of childless nodes that no step reads), then the walk.
  * Each tree is walked by G cooperating 512-thread blocks (G up to
  * SV_MAX_BLOCKS_PER_TREE; by default as many as let all B * G blocks fit the
  * GPU at once), each owning a slice of the vocabulary: every sum over the

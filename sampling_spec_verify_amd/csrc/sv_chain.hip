@@ -148,6 +148,29 @@ __device__ __forceinline__ const char *row_ptr(const Geo &g, int tensor, int b, 
 // launch 1: row statistics
 // ---------------------------------------------------------------------------
 
+// Whether node i of tree b is some node's parent (tree rows, one per node:
+// a.leaf_par [B, leaf_N]); one ballot per 64 parents, uniform over the wave.
+__device__ __forceinline__ bool node_has_child(const ChainArgs &a, int b, int i) {
+    const int32_t *par = a.leaf_par + int64_t(b) * a.leaf_N;
+    const int lane = threadIdx.x & (kWave - 1);
+    bool has = false;
+    for (int j0 = 0; j0 < a.leaf_N; j0 += kWave) {
+        const int j = j0 + lane;
+        const int pj = (j < a.leaf_N) ? par[j] : -1;
+        has = has || (__ballot(pj == i) != 0ull);
+    }
+    return has;
+}
+
+// An empty partial (no element, sum 0) for chunk c of slot `slot` of (b, i).
+__device__ __forceinline__ void empty_partial(const ChainArgs &a, int b, int i, int slot, int c) {
+    Part p;
+    p.s = -INFINITY;
+    p.z = 0.0f;
+    p.S = 0.0;
+    a.part1[(int64_t(b) * a.g.Pcap + i) * 2 * a.C1 + int64_t(slot) * a.C1 + c] = p;
+}
+
 // One job: wave-chunk c of one drafted row, reduced by one wavefront.
 // LEAF (tree rows, one per node): the draft row of a node that no node names
 // as its parent is never read, so its wave stores an empty partial instead.
@@ -159,25 +182,9 @@ __device__ __forceinline__ void row_chunk_stats(const ChainArgs &a, unsigned job
     const int tensor = static_cast<int>(rest & 1u);
     int b, i;
     if (!slot_position(a, static_cast<int>(rest >> 1), b, i)) return;
-    if (LEAF && tensor == 1) {
-        const int32_t *par = a.leaf_par + int64_t(b) * a.leaf_N;
-        const int lane0 = threadIdx.x & (kWave - 1);
-        bool has = false;
-        for (int j0 = 0; j0 < a.leaf_N; j0 += kWave) {
-            const int j = j0 + lane0;
-            const int pj = (j < a.leaf_N) ? par[j] : -1;
-            has = has || (__ballot(pj == i) != 0ull);
-        }
-        if (!has) {
-            if (lane0 == 0) {
-                Part p;
-                p.s = -INFINITY;
-                p.z = 0.0f;
-                p.S = 0.0;
-                a.part1[(int64_t(b) * a.g.Pcap + i) * 2 * a.C1 + a.C1 + c] = p;
-            }
-            return;
-        }
+    if (LEAF && tensor == 1 && !node_has_child(a, b, i)) {
+        if ((threadIdx.x & (kWave - 1)) == 0) empty_partial(a, b, i, 1, c);
+        return;
     }
     const char *row = row_ptr(a.g, tensor, b, geo_row(a.g, b, i));
     // the wave whose chunk holds the drafted token also gathers its logit
@@ -294,12 +301,22 @@ __global__ __launch_bounds__(kStatsWaves * kWave) void k_row_stats(ChainArgs a, 
 // alpha z_t + beta z_q from above (alpha, beta >= 0), and the slot carries the
 // drafted token's target logit.  Slot 1 receives the draft row's partial
 // exactly as in probability space.
-template <class DT, int NV>
+// LEAF (tree rows, one per node): a node without children is never tested
+// from, and its bonus row is the target's own softmax, which the walk forms
+// itself in logit space; its wave stores empty partials for both slots.
+template <class DT, int NV, bool LEAF = false>
 __device__ __forceinline__ void row_chunk_stats_logit(const ChainArgs &a, unsigned job) {
     const unsigned C1 = static_cast<unsigned>(a.C1);
     const int c = static_cast<int>(job % C1);
     int b, i;
     if (!slot_position(a, static_cast<int>(job / C1), b, i)) return;
+    if (LEAF && !node_has_child(a, b, i)) {
+        if ((threadIdx.x & (kWave - 1)) == 0) {
+            empty_partial(a, b, i, 0, c);
+            empty_partial(a, b, i, 1, c);
+        }
+        return;
+    }
     const int r = geo_row(a.g, b, i);
     const char *row_t = row_ptr(a.g, 0, b, r);
     const char *row_q = row_ptr(a.g, 1, b, r);
@@ -375,11 +392,11 @@ __device__ __forceinline__ void row_chunk_stats_logit(const ChainArgs &a, unsign
     }
 }
 
-template <class DT, int NV>
+template <class DT, int NV, bool LEAF = false>
 __global__ __launch_bounds__(kStatsWaves * kWave) void k_row_stats_logit(ChainArgs a, int n_jobs) {
     const int job = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kStatsWaves +
                                                    static_cast<int>(threadIdx.x) / kWave);
-    if (job < n_jobs) row_chunk_stats_logit<DT, NV>(a, static_cast<unsigned>(job));
+    if (job < n_jobs) row_chunk_stats_logit<DT, NV, LEAF>(a, static_cast<unsigned>(job));
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
     clear_counts<kStatsWaves * kWave>(a);
 }
@@ -1411,7 +1428,10 @@ sv_status rows_stats_typed(ChainArgs a, hipStream_t stream, int nv) {
     const int jobs = static_cast<int>(int64_t(a.B) * a.g.Pcap * (a.space == 1 ? 1 : 2) * a.C1);
     const dim3 grid(static_cast<unsigned>(jobs > 0 ? cdiv(jobs, kStatsWaves) : 1));
     const dim3 block(kStatsWaves * kWave);
-    if (a.space == 1) {
+    if (a.space == 1 && a.leaf_par != nullptr) {
+        if (nv == 4) hipLaunchKernelGGL((k_row_stats_logit<DT, 4, true>), grid, block, 0, stream, a, jobs);
+        else hipLaunchKernelGGL((k_row_stats_logit<DT, 2, true>), grid, block, 0, stream, a, jobs);
+    } else if (a.space == 1) {
         if (nv == 4) hipLaunchKernelGGL((k_row_stats_logit<DT, 4>), grid, block, 0, stream, a, jobs);
         else hipLaunchKernelGGL((k_row_stats_logit<DT, 2>), grid, block, 0, stream, a, jobs);
     } else if (a.leaf_par != nullptr) {
