@@ -944,6 +944,30 @@ __global__ __launch_bounds__(kMB) void k_tree_multi(MultiArgs a) {
     bool done = false;
     bool kids_ready = tab;              // the children's logits of node u are in sh.czt / sh.czq
     while (!done) {
+        if (tab) {
+            // a small tree's accepted first children need no block barrier:
+            // every thread follows them through the table (the same values
+            // in every block), down to the first node whose first child is
+            // rejected, has a row the walk must flag, or is absent
+            for (;;) {
+                const int c = (depth < a.Dmax) ? sh.head[u] : -1;
+                if (c < 0) break;
+                const double SAu = sh.tab_S[u][0], SBu = sh.tab_S[u][1];
+                if (!(SAu > 0.0) || !isfinite(SAu) || !(SBu > 0.0) || !isfinite(SBu) ||
+                    !isfinite(sh.tab_s[u][0]) || !isfinite(sh.tab_s[u][1]))
+                    break;
+                const double acc_p = sh.tab_acc[c];
+                if (!(static_cast<double>(sh.ua[c]) < acc_p)) break;
+                if (t == 0) {
+                    sh.flags |= sh.tab_fl[c];
+                    if (a.accept_prob != nullptr && g == 0)
+                        a.accept_prob[int64_t(b) * N + c - 1] = static_cast<float>(acc_p);
+                    if (depth < SV_MAX_POSITIONS) sh.path[depth] = c;
+                }
+                u = c;
+                ++depth;
+            }
+        }
         const char *rt = tb + int64_t(u) * a.ld_t * a.elem;
         const char *rq = qb + int64_t(u) * a.ld_q * a.elem;
         const int first = (depth < a.Dmax) ? sh.head[u] : -1;
