@@ -105,3 +105,24 @@ def test_graph_replays_with_new_logits_between_replays():
         h = to_host(out)
         assert int(h.status[0]) == 0, sv.decode_flags(int(h.status[0]))
         compare_multi(x, h, x0.Dmax, label=f"multi graph replay {rep}")
+
+
+@pytest.mark.parametrize("B,N,V,dtype", [
+    (2, 31, 128256, "bf16"),     # 2 x 32 rows x 32 chunks = 2048 partials: the table's limit
+    (2, 32, 128256, "bf16"),     # 2112 partials: combined on the way
+    (3, 62, 3000, "fp32"),       # 63 nodes
+    (3, 63, 3000, "fp32"),       # 64 nodes: the largest tabled tree
+    (3, 64, 3000, "fp32"),       # 65 nodes: combined on the way
+], ids=["N31-at-parts-limit", "N32-past-parts-limit", "N62", "N63-at-node-limit", "N64-past-node-limit"])
+def test_statistics_table_limits(B, N, V, dtype):
+    """A tree of at most 64 nodes whose rows' chunk partials fit the table has
+    every node's statistics, logits and first-child test formed at its start;
+    a larger one combines them on the way.  Both sides of both limits follow
+    the oracle, in both spaces."""
+    for space, lam in (("prob", 0.0), ("logit", 0.3)):
+        if V > 100000:      # the tree workload's recipe (peaked rows: draws far from boundaries)
+            x = synth.make_tree(9900 + N, B, N, V, dtype, lam=lam, sigma_q=1.5)
+        else:
+            x = synth.make_random_tree(9900 + N, B, N, V, dtype, sharp=1.0, sigma_q=2.0, lam=lam)
+        g, _ = _multi_case(x, space=space, label=f"table limits N={N} V={V} {space}")
+        assert int(g.status[0]) == 0
