@@ -575,8 +575,9 @@ def bench_multi(args):
         "gpu_ms_per_step": ev0.elapsed_time(ev1) / K, "cpu_baseline": cpu,
         "parity_sample": parity, "status_word": int(g[4][0]),
         "accepted_depths": g[0].tolist(),
-        "note": "up to 16 cooperating 512-thread blocks walk each tree; bound by the chain "
-                "of barriers between the walk's vocabulary passes",
+        "note": "a row-statistics launch over the tree rows, then up to 32 cooperating "
+                "512-thread blocks walk each tree; bound by the chain of barriers between "
+                "the walk's vocabulary passes",
     }
     print(json.dumps(line), flush=True)
 
