@@ -671,6 +671,52 @@ struct ResolveShared {
     int K, n, flags;
 };
 
+// Every drafted row's (shift, sum) from its C1 chunk partials, one wave per
+// row, in fp64 and a fixed order, with the drafted token's logit; STAGED reads
+// the partials from shared memory, otherwise from the workspace.
+template <bool STAGED>
+__device__ __forceinline__ void combine_rows(const ChainArgs &a, const Geo &g, ResolveShared &sh, int K, int C1,
+                                             int64_t pbase, const float *ps, const double *pS, const float *pz) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+#pragma unroll 1
+    for (int j = wv; j < 2 * K; j += kWaves2) {
+        float smax = -INFINITY;
+#pragma unroll 1
+        for (int c = lane; c < C1; c += kWave)
+            smax = fmaxf(smax, STAGED ? ps[j * C1 + c] : a.part1[pbase + int64_t(j) * C1 + c].s);
+        smax = wave_max(smax);
+        double S = 0.0;
+#pragma unroll 1
+        for (int c = lane; c < C1; c += kWave) {
+            float s;
+            double Sc;
+            if (STAGED) {
+                s = ps[j * C1 + c];
+                Sc = pS[j * C1 + c];
+            } else {
+                const Part p = a.part1[pbase + int64_t(j) * C1 + c];
+                s = p.s;
+                Sc = p.S;
+            }
+            if (s != -INFINITY) S += Sc * pow2_shift_d(static_cast<double>(s) - static_cast<double>(smax));
+        }
+        S = wave_sum_d(S);
+        if (lane == 0) {
+            const int x = sh.x[j >> 1];
+            float zx = NAN;
+            if (x >= 0 && x < g.V) {
+                const int cx = x / a.ch1;
+                zx = STAGED ? pz[j * C1 + cx] : a.part1[pbase + int64_t(j) * C1 + cx].z;
+            }
+            sh.zx[j] = zx;
+            sh.s[j] = smax;
+            sh.S[j] = S;
+            sh.row_bad[j] = !(S > 0.0) || !isfinite(S) || !isfinite(smax);
+        }
+    }
+}
+
 // Resolve request b: positions, row statistics (from the staged partials of
 // launch 1, which also carry the drafted token's logit), acceptance
 // probabilities and the first rejection.  One parallel load round (path mode:
@@ -734,42 +780,9 @@ __device__ __forceinline__ void resolve_request(const ChainArgs &a, int b, Resol
     __syncthreads();
     const int K = sh.K;
     // row statistics: combine the C1 chunk partials of every row in fp64
-#pragma unroll 1
-    for (int j = wv; j < 2 * K; j += kWaves2) {
-        float smax = -INFINITY;
-#pragma unroll 1
-        for (int c = lane; c < C1; c += kWave)
-            smax = fmaxf(smax, staged ? ps[j * C1 + c] : a.part1[pbase + int64_t(j) * C1 + c].s);
-        smax = wave_max(smax);
-        double S = 0.0;
-#pragma unroll 1
-        for (int c = lane; c < C1; c += kWave) {
-            float s;
-            double Sc;
-            if (staged) {
-                s = ps[j * C1 + c];
-                Sc = pS[j * C1 + c];
-            } else {
-                const Part p = a.part1[pbase + int64_t(j) * C1 + c];
-                s = p.s;
-                Sc = p.S;
-            }
-            if (s != -INFINITY) S += Sc * pow2_shift_d(static_cast<double>(s) - static_cast<double>(smax));
-        }
-        S = wave_sum_d(S);
-        if (lane == 0) {
-            const int x = sh.x[j >> 1];
-            float zx = NAN;
-            if (x >= 0 && x < g.V) {
-                const int cx = x / a.ch1;
-                zx = staged ? pz[j * C1 + cx] : a.part1[pbase + int64_t(j) * C1 + cx].z;
-            }
-            sh.zx[j] = zx;
-            sh.s[j] = smax;
-            sh.S[j] = S;
-            sh.row_bad[j] = !(S > 0.0) || !isfinite(S) || !isfinite(smax);
-        }
-    }
+    // (two loops, so that the staged one reads shared memory only)
+    if (staged) combine_rows<true>(a, g, sh, K, C1, pbase, ps, pS, pz);
+    else combine_rows<false>(a, g, sh, K, C1, pbase, ps, pS, pz);
     __syncthreads();
     if (wv == 0) {
         bool rej = false;

@@ -137,6 +137,37 @@ __global__ __launch_bounds__(kBlock) void k_row_argmax(TreeArgs a, int n_jobs) {
 constexpr int kNodes = SV_MAX_TREE_NODES + 1;
 constexpr int kRejected = -(1 << 20);       // below any sum of <= kNodes depths
 
+// Every row's argmax from its C1 chunk partials (rows 0..N at p + base, C1
+// each), one wave per row; a row with no value or a NaN gets -1 and flags
+// the call.
+__device__ __forceinline__ void argmax_rows(const ArgPart *parts, int64_t base, int C1, int N, int *am,
+                                            int *flags) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+#pragma unroll 1
+    for (int r = wv; r <= N; r += kWaves2) {
+        const ArgPart *p = parts + base + int64_t(r) * C1;
+        float v = -INFINITY;
+#pragma unroll 1
+        for (int c = lane; c < C1; c += kWave) v = fmaxf(v, p[c].val);
+        v = wave_max(v);
+        int idx = INT_MAX;
+        int nan = 0;
+#pragma unroll 1
+        for (int c = lane; c < C1; c += kWave) {
+            const ArgPart q = p[c];
+            if (q.val == v) idx = min(idx, q.idx);
+            nan |= q.nan;
+        }
+        idx = wave_min_i(idx);
+        const bool anynan = __ballot(nan != 0) != 0ull;
+        if (lane == 0) {
+            am[r] = (idx == INT_MAX || anynan) ? -1 : idx;
+            if (idx == INT_MAX || anynan) atomicOr(flags, SV_DATA_BAD_ROW);
+        }
+    }
+}
+
 __global__ __launch_bounds__(kBlock2) void k_greedy_walk(TreeArgs a, int staged) {
     __shared__ int am[kNodes];
     __shared__ int par[kNodes];
@@ -162,29 +193,10 @@ __global__ __launch_bounds__(kBlock2) void k_greedy_walk(TreeArgs a, int staged)
     }
     __syncthreads();
 
-    // argmax of every row: largest value, lowest index among equals
-#pragma unroll 1
-    for (int r = wv; r <= N; r += kWaves2) {
-        const ArgPart *p = staged ? stage + r * a.C1 : a.part + pbase + int64_t(r) * a.C1;
-        float v = -INFINITY;
-#pragma unroll 1
-        for (int c = lane; c < a.C1; c += kWave) v = fmaxf(v, p[c].val);
-        v = wave_max(v);
-        int idx = INT_MAX;
-        int nan = 0;
-#pragma unroll 1
-        for (int c = lane; c < a.C1; c += kWave) {
-            const ArgPart q = p[c];
-            if (q.val == v) idx = min(idx, q.idx);
-            nan |= q.nan;
-        }
-        idx = wave_min_i(idx);
-        const bool anynan = __ballot(nan != 0) != 0ull;
-        if (lane == 0) {
-            am[r] = (idx == INT_MAX || anynan) ? -1 : idx;
-            if (idx == INT_MAX || anynan) atomicOr(&sh_flags, SV_DATA_BAD_ROW);
-        }
-    }
+    // argmax of every row: largest value, lowest index among equals (two
+    // loops, so that the staged one reads shared memory only)
+    if (staged) argmax_rows(stage, 0, a.C1, N, am, &sh_flags);
+    else argmax_rows(a.part, pbase, a.C1, N, am, &sh_flags);
     __syncthreads();
 
     // one edge per node: parent and whether the node's token matches
