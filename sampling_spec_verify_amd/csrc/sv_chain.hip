@@ -666,6 +666,7 @@ struct ResolveShared {
     int x[SV_MAX_POSITIONS];
     int rowi[SV_MAX_POSITIONS + 1];     // request row of position i (i <= K)
     int pathv[SV_MAX_POSITIONS];
+    int tokn[SV_MAX_TREE_NODES];        // path mode: every node's drafted token
     float u[SV_MAX_POSITIONS];
     float f[kWaves2];
     int K, n, flags;
@@ -719,8 +720,7 @@ __device__ __forceinline__ void combine_rows(const ChainArgs &a, const Geo &g, R
 
 // Resolve request b: positions, row statistics (from the staged partials of
 // launch 1, which also carry the drafted token's logit), acceptance
-// probabilities and the first rejection.  One parallel load round (path mode:
-// two).
+// probabilities and the first rejection.  One parallel load round.
 template <class DT>
 __device__ __forceinline__ void resolve_request(const ChainArgs &a, int b, ResolveShared &sh,
                                                 float *ps, double *pS, float *pz, bool staged) {
@@ -730,30 +730,55 @@ __device__ __forceinline__ void resolve_request(const ChainArgs &a, int b, Resol
     const Geo &g = a.g;
     const int P = g.P, Pc = g.Pcap, C1 = a.C1;
     const int64_t pbase = int64_t(b) * Pc * 2 * C1;
-    if (staged) {
-        for (int idx = t; idx < 2 * Pc * C1; idx += kBlock2) {
-            const Part p = a.part1[pbase + idx];
-            ps[idx] = p.s;
-            pz[idx] = p.z;
-            pS[idx] = p.S;
+    // Every load of the first round goes out before any value is used: the
+    // partials, the position's uniform and token (or path node) and the
+    // draft length are read into registers, then stored to shared memory.
+    // (Stored as they arrived, a loop's waits would hold back the loads after
+    // it: three round trips instead of one.)
+    static_assert(kStageMax % kBlock2 == 0, "whole staging rounds");
+    constexpr int kStageIter = kStageMax / kBlock2;
+    const int n_stage = staged ? 2 * Pc * C1 : 0;
+    Part pr[kStageIter];
+#pragma unroll
+    for (int k = 0; k < kStageIter; ++k) {
+        const int idx = t + k * kBlock2;
+        if (idx < n_stage) pr[k] = a.part1[pbase + idx];
+    }
+    float uv = 0.0f;
+    int xv = 0;
+    if (t < Pc) {
+        uv = a.u_accept[int64_t(b) * P + t];
+        xv = (g.path == nullptr) ? g.tokens[int64_t(b) * P + t] : g.path[int64_t(b) * P + t];
+    }
+    // path mode: every node's token (the path picks them after the walk)
+    static_assert(SV_MAX_TREE_NODES <= kBlock2, "one node per thread");
+    int tn = 0;
+    if (g.path != nullptr && t < g.N) tn = g.tokens[int64_t(b) * g.N + t];
+    const bool lead = t == 0 && g.path == nullptr;
+    int k_len = P;
+    if (lead && g.draft_len != nullptr) k_len = g.draft_len[b];
+#pragma unroll
+    for (int k = 0; k < kStageIter; ++k) {
+        const int idx = t + k * kBlock2;
+        if (idx < n_stage) {
+            ps[idx] = pr[k].s;
+            pz[idx] = pr[k].z;
+            pS[idx] = pr[k].S;
         }
     }
     if (t < Pc) {
-        sh.u[t] = a.u_accept[int64_t(b) * P + t];
-        if (g.path == nullptr) sh.x[t] = g.tokens[int64_t(b) * P + t];
-        else sh.pathv[t] = g.path[int64_t(b) * P + t];
+        sh.u[t] = uv;
+        if (g.path == nullptr) sh.x[t] = xv;
+        else sh.pathv[t] = xv;
     }
-    if (t == 0 && g.path == nullptr) {
+    if (g.path != nullptr && t < g.N) sh.tokn[t] = tn;
+    if (lead) {
         int fl = 0;
-        int k = P;
-        if (g.draft_len != nullptr) {
-            k = g.draft_len[b];
-            if (k < 0 || k > P) {
-                fl |= SV_DATA_BAD_LENGTH;
-                k = min(max(k, 0), P);
-            }
+        if (k_len < 0 || k_len > P) {
+            fl |= SV_DATA_BAD_LENGTH;
+            k_len = min(max(k_len, 0), P);
         }
-        sh.K = k;
+        sh.K = k_len;
         sh.flags = fl;
     }
     __syncthreads();
@@ -772,7 +797,7 @@ __device__ __forceinline__ void resolve_request(const ChainArgs &a, int b, Resol
             sh.flags = fl;
         }
         __syncthreads();
-        if (t < sh.K) sh.x[t] = g.tokens[int64_t(b) * g.N + sh.pathv[t] - 1];
+        if (t < sh.K) sh.x[t] = sh.tokn[sh.pathv[t] - 1];
         if (t <= sh.K) sh.rowi[t] = (t == 0) ? 0 : sh.pathv[t - 1];
     } else if (t <= Pc) {
         sh.rowi[t] = t;
@@ -1142,8 +1167,8 @@ __device__ __forceinline__ int sample_mixture_wave(const SampleCtx &S, double u)
 // r.n by wave 0 of the block that completed the request's mass blocks.
 template <class DT, int NV2>
 __device__ __forceinline__ void draw_request(const ChainArgs &a, int b, const ReqRecord &r,
-                                             const SampleCtx &S, double *stage) {
-    const double u = static_cast<double>(a.u_sample[b]);
+                                             const SampleCtx &S, double *stage, float u_s) {
+    const double u = static_cast<double>(u_s);
     int flags = 0;
     // At lambda = 1, p~ = q and the residual max(0, p~ - q) is identically
     // zero (a rejection there means q(x) = 0): straight to the fallback, p~.
@@ -1181,6 +1206,8 @@ __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int stage
     double *pS = dyn;
     float *ps = reinterpret_cast<float *>(dyn + stage_n);
     float *pz = ps + stage_n;
+    // the draw's uniform, read now so that the drawing wave does not wait for it
+    const float u_s = a.u_sample[b];
     resolve_request<DT>(a, b, sh, ps, pS, pz, staged != 0);
 
     const int n = sh.n, K = sh.K;
@@ -1240,7 +1267,7 @@ __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int stage
     __syncthreads();
     if (!last || threadIdx.x >= kWave) return;     // uniform, then whole waves
     // the resolve staging area is free again: it holds the piece masses
-    draw_request<DT, NV2>(a, b, r, S, dyn);
+    draw_request<DT, NV2>(a, b, r, S, dyn, u_s);
 }
 
 }  // namespace sv
