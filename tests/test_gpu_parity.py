@@ -289,6 +289,7 @@ def test_greedy_split_calls_equal_full_call():
 @pytest.mark.parametrize("seed,B,N,V,dtype,lam,T", [
     (1, 6, 12, 3000, "fp32", 0.0, 1.0), (2, 4, 40, 20000, "bf16", 0.3, 0.8),
     (3, 3, 5, 17, "fp32", 0.5, 1.2),
+    (4, 2, 1024, 300, "fp32", 0.2, 1.0),        # the most nodes a tree may have: one per resolve thread
 ])
 def test_path_random_trees(seed, B, N, V, dtype, lam, T):
     x = synth.make_random_tree(400 + seed, B, N, V, dtype, sharp=1.0, lam=lam, temperature=T)
