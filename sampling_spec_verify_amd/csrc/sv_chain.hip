@@ -594,8 +594,8 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
     const char *row_q = row_ptr(a.g, 1, b, r);
     const int v0 = min(c, a.C1 - 1) * (kWave * NV);
     u32x4 dt[NV], dq[NV];
-    load_chunk<DT, NV>(row_t, v0, lane, V, dt);
-    load_chunk<DT, NV>(row_q, v0, lane, V, dq);
+    load_chunk_clamped<DT, NV>(row_t, v0, lane, V, dt);
+    load_chunk_clamped<DT, NV>(row_q, v0, lane, V, dq);
     if (wv < 2) {
         float s_, inv_, off_;
         combine_row(parts + wv * a.C1, a.C1, first, s_, inv_, off_);
@@ -613,6 +613,8 @@ __global__ __launch_bounds__(kBlock) void k_alpha_mass(ChainArgs a) {
     }
     __syncthreads();
     if (c >= a.C1) return;
+    mask_chunk<DT, NV>(v0, lane, V, dt);
+    mask_chunk<DT, NV>(v0, lane, V, dq);
     const float c_hi = a.c_hi, c_lo = a.c_lo;
     const float ts = st_s, ti = st_i, qs = sq_s, qi = sq_i;
     const float w_t = 1.0f - a.lam, w_q = a.lam;

@@ -109,6 +109,42 @@ __device__ __forceinline__ void load_chunk(const char *row, int v0, int lane, in
     }
 }
 
+// load_chunk's vectors as two steps, for a kernel that uses other loads issued
+// before the chunk while the chunk is in flight: the loads go out in straight
+// code (lanes past the row read its last vector again), so that waiting for
+// those earlier loads does not wait for the chunk; mask_chunk then gives the
+// elements past the row -inf (a wave-uniform test: only a row's last chunk).
+template <class DT, int NV>
+__device__ __forceinline__ void load_chunk_clamped(const char *row, int v0, int lane, int V, u32x4 (&d)[NV]) {
+    const int last = (V + DT::kVec - 1) / DT::kVec - 1;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) d[n] = load16(row + int64_t(min(v0 + n * kWave + lane, last)) * 16);
+}
+
+template <class DT, int NV>
+__device__ __forceinline__ void mask_chunk(int v0, int lane, int V, u32x4 (&d)[NV]) {
+    if (v0 + NV * kWave <= V / DT::kVec) return;
+    const int last = (V + DT::kVec - 1) / DT::kVec - 1;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        const int gv = v0 + n * kWave + lane;
+        if (gv > last) {
+            d[n] = u32x4{DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord, DT::kNegInfWord};
+        } else if ((V % DT::kVec) != 0 && gv == last) {
+            const int valid = V - gv * DT::kVec;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (DT::kVec == 8) {
+                    if (2 * j >= valid) d[n][j] = 0xff80ff80u;
+                    else if (2 * j + 1 >= valid) d[n][j] = (d[n][j] & 0x0000ffffu) | 0xff800000u;
+                } else if (j >= valid) {
+                    d[n][j] = 0xff800000u;
+                }
+            }
+        }
+    }
+}
+
 // 2^d for an integer-valued d <= 0 (a difference of two integer shifts),
 // exactly; 0 below the smallest subnormal.
 __device__ __forceinline__ float pow2_shift(float d) {
