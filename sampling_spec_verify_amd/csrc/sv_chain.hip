@@ -1259,15 +1259,19 @@ __global__ __launch_bounds__(kBlock2) void k_resolve_mass(ChainArgs a, int stage
     // draws the token alone.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        last = __hip_atomic_fetch_add(&a.count[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               a.C2 - 1;
-        // every block of the request has counted: zero again, so that this
-        // launch may be repeated on the same statistics (new uniforms)
-        if (last) __hip_atomic_store(&a.count[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.C2 > 1) {
+        if (threadIdx.x == 0) {
+            last = __hip_atomic_fetch_add(&a.count[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   a.C2 - 1;
+            // every block of the request has counted: zero again, so that this
+            // launch may be repeated on the same statistics (new uniforms)
+            if (last) __hip_atomic_store(&a.count[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!last) return;                         // uniform
     }
-    __syncthreads();
-    if (!last || threadIdx.x >= kWave) return;     // uniform, then whole waves
+    // (a row of one chunk: the request's only block draws, with no count)
+    if (threadIdx.x >= kWave) return;              // whole waves
     // the resolve staging area is free again: it holds the piece masses
     draw_request<DT, NV2>(a, b, r, S, dyn, u_s);
 }
